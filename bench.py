@@ -1,0 +1,182 @@
+"""Benchmark of the fused ranking head (scores + logsumexp + top-K) on one GPU.
+
+Default workload: 1,024 users x 1,000,000 items, D = 4,096, K = 500, bf16
+(the large compute-bound catalog).  One step = one full call of the head on
+inputs already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload large|batch|gemv|tiny|cand]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("user×item scores/sec (TFLOP/s) for fused score+lse+top-K; "
+          "% of MFMA/HBM roofline")
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="large", choices=["large", "batch", "gemv", "tiny", "cand"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target host time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def to_dev(a, dev, torch):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def cpu_baseline(d, K, target_s, cand):
+    """The oracle on a bounded sample of the same workload: whole users."""
+    from oracle import oracle
+    oracle.build()
+    B = d["B"]
+    users = [0]
+    t0 = time.perf_counter()
+    if cand:
+        oracle.cand(d["H"], d["E"], d["offsets"], d["ids"], K, users=users)
+    else:
+        oracle.full(d["H"], d["E"], K, users=users)
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(B, target_s / max(t1, 1e-3))))
+    users = list(np.linspace(0, B - 1, n).astype(np.int64))
+    t0 = time.perf_counter()
+    if cand:
+        oracle.cand(d["H"], d["E"], d["offsets"], d["ids"], K, users=users)
+        units = int(sum(d["offsets"][u + 1] - d["offsets"][u] for u in users))
+    else:
+        oracle.full(d["H"], d["E"], K, users=users)
+        units = n * d["M"]
+    t = time.perf_counter() - t0
+    return dict(value=units / t, unit="scores/s", cores=oracle.threads(), kind="oracle",
+                sample="%d of %d users, %d scores with lse and full sort, %.1f s" % (n, B, units, t))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from full_catalog_ranking_amd import genrec, synth
+
+    dev = torch.device("cuda:0")
+    genrec.lib()
+    cfg = synth.WORKLOADS[args.workload]
+    K = cfg["K"]
+    t0 = time.perf_counter()
+    d = synth.make_workload(args.workload)
+    log("inputs generated in %.1f s" % (time.perf_counter() - t0))
+    B, D, M = d["B"], d["D"], d["M"]
+    H, E = to_dev(d["H"], dev, torch), to_dev(d["E"], dev, torch)
+    cand = args.workload == "cand"
+    if cand:
+        off = torch.from_numpy(d["offsets"]).to(dev)
+        ids = torch.from_numpy(d["ids"]).to(dev)
+        nnz = int(d["ids"].size)
+        ws = torch.empty(genrec.cand_workspace_bytes(B, D, M, nnz, K, H.dtype), dtype=torch.uint8, device=dev)
+        units = nnz
+    else:
+        ws = torch.empty(genrec.workspace_bytes(B, D, M, K, H.dtype), dtype=torch.uint8, device=dev)
+        units = B * M
+    out = (torch.empty((B, K), dtype=torch.int32, device=dev),
+           torch.empty((B, K), dtype=torch.float32, device=dev),
+           torch.empty((B,), dtype=torch.float32, device=dev))
+    prof = genrec.Profiler(max_launches=8 * (args.steps + 1))
+
+    def step(p=None):
+        if cand:
+            genrec.score_candidates_topk(H, E, off, ids, K, workspace=ws, out=out, profiler=p)
+        else:
+            genrec.score_lse_topk(H, E, K, workspace=ws, out=out, profiler=p)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+    # timed region: every step records its kernels into the profiler (HIP events on the
+    # stream the kernels run on); the events add no synchronisation
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step(prof)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    kern = prof.summary()
+    log("step %.3f ms; kernels %s" % (ms, {k: "%.3f ms x%d" % (v[1] / v[0], v[0]) for k, v in kern.items()}))
+
+    n_main, t_main = kern["main_score"]
+    main_ms = t_main / n_main
+    flops = 2.0 * D * units
+    if cand or not genrec.describe_plan(B, D, M, K, H.dtype)["path"] == "mfma":
+        # VALU path over streamed / gathered rows: HBM-bound
+        elem = 2 if H.dtype == torch.bfloat16 else 4
+        if cand:
+            uniq = np.unique(d["ids"]).size
+            alg_bytes = uniq * D * elem + B * D * elem + nnz * 4 + (B + 1) * 8
+        else:
+            alg_bytes = M * D * elem + B * D * elem
+        achieved = alg_bytes / (main_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=achieved / HBM_PEAK_GBS, traffic=None)
+    else:
+        peak = MFMA_BF16_PEAK_TFLOPS
+        achieved = flops / (main_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s", frac=achieved / peak,
+                    traffic=None)
+    roof["kernel"] = "mfma_score_kernel<1>" if roof["bound"] == "mfma" else "stream_score_kernel"
+    roof["kernel_ms"] = main_ms
+
+    res = {
+        "metric": METRIC,
+        "value": units / (ms * 1e-3),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if H.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "D": D, "M": M, "K": K,
+                   **({"nnz": units} if cand else {})},
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "kernels_ms": {k: v[1] / v[0] for k, v in kern.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        del H, E, ws
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(d, K, args.cpu_seconds, cand)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

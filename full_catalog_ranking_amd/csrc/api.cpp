@@ -1,0 +1,364 @@
+// C ABI of libgenrec.so: argument validation, planning, and stream-ordered
+// launches.  See include/genrec.h for the contract of each entry point.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/genrec.h"
+#include "launch.hpp"
+#include "plan.hpp"
+
+using namespace genrec;
+
+namespace {
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shape/pointer checks shared by both entry points.  Returns GENREC_OK or the
+// status to report; never touches the device.
+int check_common(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K,
+                 const int32_t* out_idx, const float* out_scores, const float* out_lse) {
+    if (dtype != GENREC_BF16 && dtype != GENREC_F32) return GENREC_ERR_INVALID_ARG;
+    if (B <= 0 || D <= 0 || M <= 0 || K <= 0) return GENREC_ERR_INVALID_ARG;
+    if (!H || !E || !out_idx || !out_scores || !out_lse) return GENREC_ERR_INVALID_ARG;
+    if (!aligned(H, 16) || !aligned(E, 16)) return GENREC_ERR_INVALID_ARG;
+    if (!aligned(out_idx, 4) || !aligned(out_scores, 4) || !aligned(out_lse, 4))
+        return GENREC_ERR_INVALID_ARG;
+    if (K > GENREC_KMAX) return GENREC_ERR_UNSUPPORTED;
+    if (M >= ((int64_t)1 << 31)) return GENREC_ERR_UNSUPPORTED;
+    if (D % (dtype == GENREC_BF16 ? 8 : 4) != 0) return GENREC_ERR_UNSUPPORTED;
+    return GENREC_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? GENREC_OK : GENREC_ERR_HIP; }
+
+template <class T>
+inline T* at(void* ws, size_t off) {
+    return (T*)((uint8_t*)ws + off);
+}
+
+}  // namespace
+
+struct genrec_profiler {
+    int cap = 0, n = 0;
+    hipEvent_t* ev = nullptr;  // 2 per launch
+    int* kind = nullptr;
+};
+
+namespace {
+
+// Runs one launch, bracketed by profiler events when a profiler is given.
+template <class F>
+hipError_t timed(genrec_profiler* prof, int kind, hipStream_t s, F&& launch) {
+    if (!prof || prof->n >= prof->cap) return launch();
+    hipError_t e = hipEventRecord(prof->ev[2 * prof->n], s);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(prof->ev[2 * prof->n + 1], s);
+    if (e != hipSuccess) return e;
+    prof->kind[prof->n++] = kind;
+    return hipSuccess;
+}
+
+enum { KIND_SAMPLE = 0, KIND_THRESHOLD = 1, KIND_MAIN = 2, KIND_MERGE = 3, KIND_PLAN = 4 };
+
+}  // namespace
+
+extern "C" {
+
+genrec_profiler* genrec_profiler_create(int max_launches) {
+    if (max_launches <= 0) return nullptr;
+    genrec_profiler* p = new (std::nothrow) genrec_profiler();
+    if (!p) return nullptr;
+    p->ev = new (std::nothrow) hipEvent_t[2 * (size_t)max_launches]();
+    p->kind = new (std::nothrow) int[max_launches]();
+    if (!p->ev || !p->kind) {
+        delete[] p->ev;
+        delete[] p->kind;
+        delete p;
+        return nullptr;
+    }
+    for (int i = 0; i < 2 * max_launches; ++i) {
+        if (hipEventCreate(&p->ev[i]) != hipSuccess) {
+            for (int j = 0; j < i; ++j) (void)hipEventDestroy(p->ev[j]);
+            delete[] p->ev;
+            delete[] p->kind;
+            delete p;
+            return nullptr;
+        }
+    }
+    p->cap = max_launches;
+    return p;
+}
+
+void genrec_profiler_destroy(genrec_profiler* p) {
+    if (!p) return;
+    for (int i = 0; i < 2 * p->cap; ++i) (void)hipEventDestroy(p->ev[i]);
+    delete[] p->ev;
+    delete[] p->kind;
+    delete p;
+}
+
+int genrec_profiler_reset(genrec_profiler* p) {
+    if (!p) return GENREC_ERR_INVALID_ARG;
+    p->n = 0;
+    return GENREC_OK;
+}
+
+int genrec_profiler_summary(genrec_profiler* p, int* counts, double* total_ms) {
+    if (!p || !counts || !total_ms) return GENREC_ERR_INVALID_ARG;
+    for (int k = 0; k < GENREC_NUM_KERNEL_KINDS; ++k) {
+        counts[k] = 0;
+        total_ms[k] = 0.0;
+    }
+    if (p->n == 0) return GENREC_OK;
+    if (hipEventSynchronize(p->ev[2 * p->n - 1]) != hipSuccess) return GENREC_ERR_HIP;
+    for (int i = 0; i < p->n; ++i) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, p->ev[2 * i], p->ev[2 * i + 1]) != hipSuccess) return GENREC_ERR_HIP;
+        counts[p->kind[i]] += 1;
+        total_ms[p->kind[i]] += ms;
+    }
+    return GENREC_OK;
+}
+
+
+int genrec_version(void) { return 10000; }
+
+const char* genrec_status_string(int status) {
+    switch (status) {
+        case GENREC_OK: return "GENREC_OK";
+        case GENREC_ERR_INVALID_ARG: return "GENREC_ERR_INVALID_ARG";
+        case GENREC_ERR_UNSUPPORTED: return "GENREC_ERR_UNSUPPORTED";
+        case GENREC_ERR_WORKSPACE: return "GENREC_ERR_WORKSPACE";
+        case GENREC_ERR_HIP: return "GENREC_ERR_HIP";
+        default: return "GENREC_UNKNOWN_STATUS";
+    }
+}
+
+size_t genrec_score_lse_topk_workspace(int B, int D, int64_t M, int K, int dtype) {
+    static const float dummy[4] = {0, 0, 0, 0};
+    if (check_common(dummy, dummy, dtype, B, D, M, K, (const int32_t*)dummy, dummy, dummy) != GENREC_OK)
+        return 0;
+    return plan_dense(B, D, M, K, dtype).total;
+}
+
+int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, size_t len) {
+    static const float dummy[4] = {0, 0, 0, 0};
+    const int st = check_common(dummy, dummy, dtype, B, D, M, K, (const int32_t*)dummy, dummy, dummy);
+    if (st != GENREC_OK) return st;
+    if (!buf || len == 0) return GENREC_ERR_INVALID_ARG;
+    const DensePlan p = plan_dense(B, D, M, K, dtype);
+    snprintf(buf, len,
+             "{\"path\":\"%s\",\"sample\":%d,\"stride\":%lld,\"n_sample\":%lld,\"UT\":%d,\"P\":%d,"
+             "\"tiles_per_chunk\":%d,\"CH\":%lld,\"workspace\":%zu}",
+             p.mfma ? "mfma" : "stream", p.sample ? 1 : 0, (long long)p.stride, (long long)p.n_sample,
+             p.main.UT, p.main.P, p.main.base + (p.main.rem ? 1 : 0), (long long)p.main.CH, p.total);
+    return GENREC_OK;
+}
+
+int genrec_score_lse_topk(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K,
+                          int32_t* out_idx, float* out_scores, float* out_lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    return genrec_score_lse_topk_profiled(H, E, dtype, B, D, M, K, out_idx, out_scores, out_lse, workspace,
+                                          workspace_bytes, stream, nullptr);
+}
+
+int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K,
+                                   int32_t* out_idx, float* out_scores, float* out_lse, void* workspace,
+                                   size_t workspace_bytes, void* stream, genrec_profiler* prof) {
+    int st = check_common(H, E, dtype, B, D, M, K, out_idx, out_scores, out_lse);
+    if (st != GENREC_OK) return st;
+    const DensePlan p = plan_dense(B, D, M, K, dtype);
+    if (!workspace || workspace_bytes < p.total) return GENREC_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+
+    float* theta = at<float>(workspace, p.off_theta);
+    float* sample = at<float>(workspace, p.off_sample);
+    float* pm = at<float>(workspace, p.off_pm);
+    float* pl = at<float>(workspace, p.off_pl);
+    int* pcnt = at<int>(workspace, p.off_pcnt);
+    int64_t* preg = at<int64_t>(workspace, p.off_preg);
+    uint64_t* keys = at<uint64_t>(workspace, p.off_keys);
+    const bool f32 = dtype == GENREC_F32;
+
+    if (p.mfma) {
+        MfmaArgs a{};
+        a.H = (const uint16_t*)H;
+        a.E = (const uint16_t*)E;
+        a.B = B;
+        a.D = D;
+        a.M = M;
+        if (p.sample) {
+            a.n_items = p.n_sample;
+            a.stride = p.stride;
+            a.UT = p.pre.UT;
+            a.P = p.pre.P;
+            a.base = p.pre.base;
+            a.rem = p.pre.rem;
+            a.sample_out = sample;
+            if ((st = hip_status(timed(prof, KIND_SAMPLE, s, [&] { return launch_mfma(a, 0, s); }))) != GENREC_OK) return st;
+            if ((st = hip_status(timed(prof, KIND_THRESHOLD, s, [&] { return launch_threshold(sample, p.n_sample, K, theta, B, s); }))) != GENREC_OK) return st;
+        }
+        a.n_items = M;
+        a.stride = 1;
+        a.UT = p.main.UT;
+        a.P = p.main.P;
+        a.base = p.main.base;
+        a.rem = p.main.rem;
+        a.sample_out = nullptr;
+        a.theta = p.sample ? theta : nullptr;
+        a.keys = keys;
+        a.pm = pm;
+        a.pl = pl;
+        a.pcnt = pcnt;
+        a.preg = preg;
+        if ((st = hip_status(timed(prof, KIND_MAIN, s, [&] { return launch_mfma(a, 1, s); }))) != GENREC_OK) return st;
+    } else {
+        StreamArgs a{};
+        a.H = H;
+        a.E = E;
+        a.B = B;
+        a.D = D;
+        a.M = M;
+        if (p.sample) {
+            a.n_items = p.n_sample;
+            a.stride = p.stride;
+            a.CH = p.pre.CH;
+            a.P = p.pre.P;
+            a.sample_out = sample;
+            if ((st = hip_status(timed(prof, KIND_SAMPLE, s, [&] { return launch_stream(a, 0, f32, (int64_t)B * p.pre.P, s); }))) != GENREC_OK) return st;
+            if ((st = hip_status(timed(prof, KIND_THRESHOLD, s, [&] { return launch_threshold(sample, p.n_sample, K, theta, B, s); }))) != GENREC_OK) return st;
+        }
+        a.n_items = M;
+        a.stride = 1;
+        a.CH = p.main.CH;
+        a.P = p.main.P;
+        a.sample_out = nullptr;
+        a.theta = p.sample ? theta : nullptr;
+        a.keys = keys;
+        a.pm = pm;
+        a.pl = pl;
+        a.pcnt = pcnt;
+        a.preg = preg;
+        if ((st = hip_status(timed(prof, KIND_MAIN, s, [&] { return launch_stream(a, 1, f32, (int64_t)B * p.main.P, s); }))) != GENREC_OK) return st;
+    }
+    MergeArgs m{};
+    m.B = B;
+    m.K = K;
+    m.P = p.main.P;
+    m.piece_begin = nullptr;
+    m.keys = keys;
+    m.pm = pm;
+    m.pl = pl;
+    m.pcnt = pcnt;
+    m.preg = preg;
+    m.out_idx = out_idx;
+    m.out_scores = out_scores;
+    m.out_lse = out_lse;
+    m.clear_err = at<int64_t>(workspace, p.off_hdr);
+    return hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }));
+}
+
+size_t genrec_score_candidates_topk_workspace(int B, int D, int64_t M, int64_t nnz, int K, int dtype) {
+    static const float dummy[4] = {0, 0, 0, 0};
+    if (check_common(dummy, dummy, dtype, B, D, M, K, (const int32_t*)dummy, dummy, dummy) != GENREC_OK)
+        return 0;
+    if (nnz < 0) return 0;
+    return plan_cand(B, nnz).total;
+}
+
+int genrec_score_candidates_topk(const void* H, const void* E, int dtype, const int64_t* cand_offsets,
+                                 const int32_t* cand_ids, int B, int D, int64_t M, int64_t nnz, int K,
+                                 int32_t* out_idx, float* out_scores, float* out_lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return genrec_score_candidates_topk_profiled(H, E, dtype, cand_offsets, cand_ids, B, D, M, nnz, K, out_idx,
+                                                 out_scores, out_lse, workspace, workspace_bytes, stream, nullptr);
+}
+
+int genrec_score_candidates_topk_profiled(const void* H, const void* E, int dtype, const int64_t* cand_offsets,
+                                          const int32_t* cand_ids, int B, int D, int64_t M, int64_t nnz, int K,
+                                          int32_t* out_idx, float* out_scores, float* out_lse, void* workspace,
+                                          size_t workspace_bytes, void* stream, genrec_profiler* prof) {
+    int st = check_common(H, E, dtype, B, D, M, K, out_idx, out_scores, out_lse);
+    if (st != GENREC_OK) return st;
+    if (nnz < 0 || !cand_offsets || (nnz > 0 && !cand_ids)) return GENREC_ERR_INVALID_ARG;
+    if (!aligned(cand_offsets, 8) || !aligned(cand_ids, 4)) return GENREC_ERR_INVALID_ARG;
+    const CandPlan p = plan_cand(B, nnz);
+    if (!workspace || workspace_bytes < p.total) return GENREC_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+
+    int64_t* err = at<int64_t>(workspace, p.off_hdr + kHdrErrIds);
+    int* n_pieces = at<int>(workspace, p.off_hdr + kHdrPieces);
+    int* piece_begin = at<int>(workspace, p.off_begin);
+    CandPiece* table = at<CandPiece>(workspace, p.off_table);
+    float* pm = at<float>(workspace, p.off_pm);
+    float* pl = at<float>(workspace, p.off_pl);
+    int* pcnt = at<int>(workspace, p.off_pcnt);
+    int64_t* preg = at<int64_t>(workspace, p.off_preg);
+    uint64_t* keys = at<uint64_t>(workspace, p.off_keys);
+
+    CandPlanArgs c{};
+    c.offsets = cand_offsets;
+    c.B = B;
+    c.nnz = nnz;
+    c.piece_begin = piece_begin;
+    c.table = table;
+    c.n_pieces = n_pieces;
+    c.err = err;
+    if ((st = hip_status(timed(prof, KIND_PLAN, s, [&] { return launch_cand_plan(c, s); }))) != GENREC_OK) return st;
+
+    StreamArgs a{};
+    a.H = H;
+    a.E = E;
+    a.B = B;
+    a.D = D;
+    a.M = M;
+    a.ids = cand_ids;
+    a.n_pieces = n_pieces;
+    a.table = table;
+    a.theta = nullptr;
+    a.keys = keys;
+    a.pm = pm;
+    a.pl = pl;
+    a.pcnt = pcnt;
+    a.preg = preg;
+    a.err = err;
+    if ((st = hip_status(timed(prof, KIND_MAIN, s, [&] { return launch_stream(a, 2, dtype == GENREC_F32, p.n_pieces_max, s); }))) != GENREC_OK)
+        return st;
+
+    MergeArgs m{};
+    m.B = B;
+    m.K = K;
+    m.P = 0;
+    m.piece_begin = piece_begin;
+    m.keys = keys;
+    m.pm = pm;
+    m.pl = pl;
+    m.pcnt = pcnt;
+    m.preg = preg;
+    m.out_idx = out_idx;
+    m.out_scores = out_scores;
+    m.out_lse = out_lse;
+    m.clear_err = nullptr;
+    return hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }));
+}
+
+int genrec_get_device_errors(const void* workspace, void* stream, int64_t* n_bad_ids, int64_t* n_bad_offsets) {
+    if (!workspace) return GENREC_ERR_INVALID_ARG;
+    int64_t h[2] = {0, 0};
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(h, workspace, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess) return GENREC_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return GENREC_ERR_HIP;
+    if (n_bad_ids) *n_bad_ids = h[0];
+    if (n_bad_offsets) *n_bad_offsets = h[1];
+    return GENREC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,916 @@
+// Ranking-head kernels for gfx950 (CDNA4, MI355X).
+//
+// The operation (GenRec concept page, scoring formula s = E^T h; GenRec
+// explainer page, "overall picture": softmax over the catalog or candidate set,
+// then descending sort) is split into stream-ordered kernels:
+//
+//  mfma_score_kernel   S-tile = E-tile . H-tile^T on bf16 MFMA (32x32x16),
+//                      E and H tiles staged through LDS; the epilogue keeps an
+//                      online (max, sum-exp) per user and appends every score
+//                      that reaches the user's threshold to a candidate region.
+//                      The score matrix itself is never written out.
+//  stream_score_kernel the same epilogue for few users or per-user candidate
+//                      lists: VALU dot products (v_dot2_f32_bf16 / fp32 FMA)
+//                      over gathered rows, one 16-byte load per lane per row
+//                      step, eight rows in flight per wave.
+//  threshold_kernel    per user, the K-th largest score of a strided catalog
+//                      sample: a lower bound of the K-th largest catalog score,
+//                      used as the candidate threshold of the main pass.
+//  merge_kernel        per user, lse from the per-piece (max, sum-exp) pairs
+//                      and the exact top-K of the candidates (range-narrowing
+//                      histogram select + bitonic sort), written sorted.
+//  cand_plan_kernel    CSR offsets -> work list of fixed-size list pieces.
+#include <float.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace genrec {
+
+// ---------------------------------------------------------------------------
+// Dense MFMA path
+// ---------------------------------------------------------------------------
+constexpr int MF_TI = 256;   // items per tile (MFMA rows)
+constexpr int MF_TU = 256;   // users per tile (MFMA columns)
+constexpr int MF_BK = 32;    // reduction depth per LDS stage
+constexpr int MF_NS = 4;     // LDS ring stages (3 in flight while one is read)
+constexpr int MF_NT = 256;   // threads (4 waves, 2 x 2 layout of 128 x 128 wave tiles)
+constexpr int MF_ROWB = MF_BK * 2;                   // bytes per staged row (64)
+constexpr int MF_STAGE = (MF_TI + MF_TU) * MF_ROWB;  // 32 KiB per stage
+constexpr int MF_DMA = (MF_TI * MF_ROWB) / (16 * kWave) / (MF_NT / kWave);  // DMA ops per wave per operand per stage (4)
+
+// 16-byte chunk swizzle within a 64-byte staged row: conflict-free
+// ds_read_b128 of 32 consecutive rows at one k-chunk for 32- or 64-bank LDS.
+__device__ __forceinline__ int mf_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left alone (gfx9 encoding).
+#define MF_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
+
+template <int MODE>
+__global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[MF_NS][MF_STAGE];
+    __shared__ int s_cnt[MF_TU];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wi = w & 1, wu = w >> 1;
+
+    // Blocks are dealt round-robin to the 8 XCDs; renumber them so that the
+    // user tiles sharing one catalog chunk sit on one XCD (one L2) together.
+    const int nblk = gridDim.x;
+    int L = blockIdx.x;
+    if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int c = L / a.UT, ut = L - c * a.UT;
+    const int64_t tile0 = (int64_t)c * a.base + min(c, a.rem);
+    const int ntiles = a.base + (c < a.rem ? 1 : 0);
+    const int u0 = ut * MF_TU;
+    const int nk = (a.D + MF_BK - 1) / MF_BK;
+
+    if (MODE == 1) s_cnt[tid] = 0;
+
+    // DMA mapping: wave w, op j writes staged rows (j*4 + w)*16 .. +16, 1 KiB;
+    // lane l fills row +l/4 at chunk position l%4 with global chunk pos^swz.
+    const int drow = lane >> 2, dpos = lane & 3;
+    int64_t e_off[MF_DMA];  // element offset of this lane's E row (k excluded)
+    int h_off[MF_DMA];
+    int dchunk[MF_DMA];
+    bool h_ok[MF_DMA];
+#pragma unroll
+    for (int j = 0; j < MF_DMA; ++j) {
+        const int row = (j * 4 + w) * 16 + drow;
+        dchunk[j] = (dpos ^ mf_swz(row)) * 8;
+        const int uu = u0 + row;
+        h_ok[j] = uu < a.B;
+        h_off[j] = (h_ok[j] ? uu : 0) * a.D;
+        e_off[j] = row;  // item row within the tile; offset formed per tile
+    }
+    int64_t e_row_off[MF_DMA];  // per tile: element offset of item row
+    auto tile_rows = [&](int64_t j0) {
+#pragma unroll
+        for (int j = 0; j < MF_DMA; ++j) {
+            int64_t jj = j0 + e_off[j];
+            jj = jj < a.n_items ? jj : a.n_items - 1;  // clamp: rows past the end are masked later
+            e_row_off[j] = jj * a.stride * (int64_t)a.D;
+        }
+    };
+    // Issue the DMA of one k-step (both operands) into stage stg.
+    auto dma = [&](int stg, int k0) {
+        uint8_t* sE = smem[stg];
+        uint8_t* sH = smem[stg] + MF_TI * MF_ROWB;
+#pragma unroll
+        for (int j = 0; j < MF_DMA; ++j) {
+            const int kk = min(k0 + dchunk[j], a.D - 8);  // k tail: any in-bounds chunk, zero-masked below
+            lds_dma16(a.E + e_row_off[j] + kk, sE + (j * 4 + w) * 1024);
+            lds_dma16(a.H + h_off[j] + kk, sH + (j * 4 + w) * 1024);
+        }
+    };
+
+    f32x16_t acc[4][4];
+    auto compute = [&](int stg, int k0) {
+        const uint8_t* sE = smem[stg];
+        const uint8_t* sH = smem[stg] + MF_TI * MF_ROWB;
+#pragma unroll
+        for (int ks = 0; ks < MF_BK / 16; ++ks) {
+            const int chunk = ks * 2 + (lane >> 5);
+            // k positions past D hold whatever in-bounds chunk was loaded: zero them
+            const bool kin = k0 + chunk * 8 < a.D;
+            bf16x8_t av[4], bv[4];
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                const int row = wi * 128 + ib * 32 + (lane & 31);
+                av[ib] = *(const bf16x8_t*)(sE + row * MF_ROWB + ((chunk ^ mf_swz(row)) << 4));
+            }
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub) {
+                const int row = wu * 128 + ub * 32 + (lane & 31);
+                bv[ub] = *(const bf16x8_t*)(sH + row * MF_ROWB + ((chunk ^ mf_swz(row)) << 4));
+                if ((a.D % MF_BK) != 0 && !kin) bv[ub] = bf16x8_t{};
+            }
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+                for (int ub = 0; ub < 4; ++ub)
+                    acc[ib][ub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ib], bv[ub], acc[ib][ub], 0, 0, 0);
+        }
+    };
+
+    // Per lane: user column (lane & 31) of each 32-wide user block ub; the
+    // accumulator element r of block (ib, ub) is item row
+    //   wi*128 + ib*32 + (r/4)*8 + (lane/32)*4 + r%4  of the tile.
+    float m_[4], l_[4], th_[4];
+#pragma unroll
+    for (int ub = 0; ub < 4; ++ub) {
+        const int u = u0 + wu * 128 + ub * 32 + (lane & 31);
+        m_[ub] = -INFINITY;
+        l_[ub] = 0.f;
+        float t = -FLT_MAX;
+        if (MODE == 1 && a.theta != nullptr && u < a.B) t = fmaxf(a.theta[u], -FLT_MAX);
+        th_[ub] = (u < a.B) ? t : INFINITY;  // users past B never append
+        (void)h_ok;
+    }
+    const int64_t chunk_item0 = tile0 * MF_TI;
+    const int lrow0 = wi * 128 + (lane >> 5) * 4;
+
+    auto epilogue = [&](int64_t j0) {
+        const int64_t left = a.n_items - j0;
+        const int lim = left < MF_TI ? (int)left : MF_TI;  // valid tile rows
+        const bool full = lim == MF_TI;
+#pragma unroll
+        for (int ub = 0; ub < 4; ++ub) {
+            const int ul = wu * 128 + ub * 32 + (lane & 31);
+            const int u = u0 + ul;
+            if (MODE == 0) {
+                if (u < a.B) {
+                    float* orow = a.sample_out + (int64_t)u * a.n_items + j0;
+#pragma unroll
+                    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int jl = lrow0 + ib * 32 + (r >> 2) * 8 + (r & 3);
+                            if (full || jl < lim) orow[jl] = acc[ib][ub][r];
+                        }
+                }
+                continue;
+            }
+            // One pass against a reference max: the running max, or the first
+            // element of the tile on the first tile.  Terms are exp(s - ref);
+            // the sum is rescaled to the new running max afterwards.  A tile
+            // whose scores exceed ref by more than 64 nats (not finite in the
+            // sum's range) is summed again against its own max.
+            float ref = m_[ub];
+            if (ref == -INFINITY) ref = acc[0][ub][0];
+            const float rb = ref * kLog2e;
+            const float th = th_[ub];
+            float tmax = -INFINITY, lsum = 0.f;
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int jl = lrow0 + ib * 32 + (r >> 2) * 8 + (r & 3);
+                    const float s = (full || jl < lim) ? acc[ib][ub][r] : -INFINITY;
+                    tmax = fmaxf(tmax, s);
+                    lsum += fast_exp2(fmaf(s, kLog2e, -rb));
+                    if (s >= th) {
+                        const int pos = atomicAdd(&s_cnt[ul], 1);
+                        a.keys[(int64_t)u * a.M + chunk_item0 + pos] = rank_key(s, (uint32_t)(j0 + jl));
+                    }
+                }
+            if (tmax == -INFINITY) continue;  // every item of this lane masked
+            if (tmax - ref > 64.f) {
+                lsum = 0.f;
+                const float tb = tmax * kLog2e;
+                for (int ib = 0; ib < 4; ++ib)
+                    for (int r = 0; r < 16; ++r) {
+                        const int jl = lrow0 + ib * 32 + (r >> 2) * 8 + (r & 3);
+                        if (full || jl < lim) lsum += fast_exp2(fmaf(acc[ib][ub][r], kLog2e, -tb));
+                    }
+                ref = tmax;
+            }
+            // l_ * e^{m_} + lsum * e^{ref}  ->  new (m, l) with m = max(m_, tmax)
+            const float mnew = fmaxf(m_[ub], tmax);
+            l_[ub] = l_[ub] * fast_exp2((m_[ub] - mnew) * kLog2e) + lsum * fast_exp2((ref - mnew) * kLog2e);
+            m_[ub] = mnew;
+        }
+    };
+
+    // Pipeline over the flat sequence of (tile, k-step): the DMA of step+3
+    // is issued before the MFMAs of step; every wave then waits until its
+    // own DMA of step+1 has landed (vector-memory loads retire in order, so
+    // "at most the two youngest steps outstanding" suffices even with the
+    // epilogue's stores in between) and meets the others at the barrier,
+    // which also retires all reads of the stage that step+4 overwrites.
+    const int total = ntiles * nk;
+    int lt = 0, lk = 0;  // next step to load
+    auto issue = [&](int step) {
+        if (lk == 0) tile_rows((tile0 + lt) * MF_TI);
+        dma(step % MF_NS, lk * MF_BK);
+        if (++lk == nk) { lk = 0; ++lt; }
+    };
+    for (int q = 0; q < MF_NS - 1; ++q)
+        if (q < total) issue(q);
+    if (total >= 3) MF_WAIT_VMCNT(2 * 2 * MF_DMA);
+    else if (total == 2) MF_WAIT_VMCNT(2 * MF_DMA);
+    else MF_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+
+    int step = 0;
+    for (int t = 0; t < ntiles; ++t) {
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub) acc[ib][ub] = f32x16_t{};
+        for (int k = 0; k < nk; ++k, ++step) {
+            if (step + MF_NS - 1 < total) issue(step + MF_NS - 1);
+            compute(step % MF_NS, k * MF_BK);
+            const int ahead = min(total - 1 - step, MF_NS - 1);  // steps already issued beyond this one
+            if (ahead >= 3) MF_WAIT_VMCNT(2 * 2 * MF_DMA);
+            else if (ahead == 2) MF_WAIT_VMCNT(2 * MF_DMA);
+            else MF_WAIT_VMCNT(0);
+            __builtin_amdgcn_s_barrier();
+        }
+        epilogue((tile0 + t) * MF_TI);
+    }
+
+    if (MODE == 1) {
+        // Combine the four lane groups that hold each user: (wi, lane/32).
+        float2* sml = (float2*)smem[0];
+#pragma unroll
+        for (int ub = 0; ub < 4; ++ub) {
+            const int ul = wu * 128 + ub * 32 + (lane & 31);
+            sml[ul * 4 + wi * 2 + (lane >> 5)] = make_float2(m_[ub], l_[ub]);
+        }
+        __syncthreads();
+        const int u = u0 + tid;
+        if (u < a.B) {
+            LseState st;
+            st.init();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float2 v = sml[tid * 4 + q];
+                st.merge(v.x, v.y);
+            }
+            const int64_t piece = (int64_t)u * a.P + c;
+            a.pm[piece] = st.m;
+            a.pl[piece] = st.l;
+            a.pcnt[piece] = s_cnt[tid];
+            a.preg[piece] = (int64_t)u * a.M + chunk_item0;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming (VALU) path: few users, fp32 inputs, per-user candidate lists
+// ---------------------------------------------------------------------------
+constexpr int ST_NT = 256;
+constexpr int ST_U = 8;  // rows in flight per wave
+
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<uint16_t> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ float dot(uint4 e, uint4 h, float acc) {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.x), __builtin_bit_cast(bf16x2_t, h.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.y), __builtin_bit_cast(bf16x2_t, h.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.z), __builtin_bit_cast(bf16x2_t, h.z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.w), __builtin_bit_cast(bf16x2_t, h.w), acc, false);
+        return acc;
+    }
+};
+template <>
+struct Vec16<float> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ float dot(uint4 e, uint4 h, float acc) {
+        acc = fmaf(__uint_as_float(e.x), __uint_as_float(h.x), acc);
+        acc = fmaf(__uint_as_float(e.y), __uint_as_float(h.y), acc);
+        acc = fmaf(__uint_as_float(e.z), __uint_as_float(h.z), acc);
+        acc = fmaf(__uint_as_float(e.w), __uint_as_float(h.w), acc);
+        return acc;
+    }
+};
+
+// Sum eight per-lane partials over the wave so that lanes 8g..8g+7 end with
+// the total of partial g (a butterfly reduce-scatter: 10 shuffles, not 48).
+__device__ __forceinline__ float reduce_scatter8(float (&v)[ST_U], int lane) {
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float send = b5 ? v[i] : v[i + 4];
+        const float keep = b5 ? v[i + 4] : v[i];
+        v[i] = keep + __shfl_xor(send, 32);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float send = b4 ? v[i] : v[i + 2];
+        const float keep = b4 ? v[i + 2] : v[i];
+        v[i] = keep + __shfl_xor(send, 16);
+    }
+    {
+        const float send = b3 ? v[0] : v[1];
+        const float keep = b3 ? v[1] : v[0];
+        v[0] = keep + __shfl_xor(send, 8);
+    }
+    float s = v[0];
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 1);
+    return s;
+}
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(ST_NT) void stream_score_kernel(StreamArgs a) {
+    __shared__ int s_cnt;
+    __shared__ float2 s_ml[ST_NT / kWave];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    constexpr int VEC = Vec16<T>::N;
+
+    int b;
+    int64_t n, region, piece, jbeg = 0, e0 = 0;
+    if (MODE == 2) {
+        piece = blockIdx.x;
+        if (piece >= *a.n_pieces) return;
+        const CandPiece rec = a.table[piece];
+        b = rec.user;
+        n = rec.len;
+        e0 = rec.e0;
+        region = e0;
+    } else {
+        const int cidx = blockIdx.x / a.B;
+        b = blockIdx.x - cidx * a.B;
+        jbeg = (int64_t)cidx * a.CH;
+        n = min((int64_t)a.CH, a.n_items - jbeg);
+        piece = (int64_t)b * a.P + cidx;
+        region = (int64_t)b * a.M + jbeg;
+    }
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+
+    const T* E = (const T*)a.E;
+    const T* h = (const T*)a.H + (int64_t)b * a.D;
+    float th = -FLT_MAX;
+    if (MODE != 0 && a.theta != nullptr) th = fmaxf(a.theta[b], -FLT_MAX);
+    LseState st;
+    st.init();
+
+    for (int64_t g0 = (int64_t)w * ST_U; g0 < n; g0 += (ST_NT / kWave) * ST_U) {
+        int64_t item[ST_U];
+        bool ok[ST_U];
+        if (MODE == 2) {
+            int myid = -1;
+            if (lane < ST_U && g0 + lane < n) myid = a.ids[e0 + g0 + lane];
+            const bool bad = lane < ST_U && g0 + lane < n && (myid < 0 || (int64_t)myid >= a.M);
+            const uint64_t badmask = __ballot(bad);
+            if (lane == 0 && badmask) atomicAdd((unsigned long long*)a.err, (unsigned long long)__popcll(badmask));
+#pragma unroll
+            for (int u = 0; u < ST_U; ++u) {
+                const int id = __shfl(myid, u);
+                ok[u] = g0 + u < n && id >= 0 && (int64_t)id < a.M;
+                item[u] = ok[u] ? id : 0;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < ST_U; ++u) {
+                ok[u] = g0 + u < n;
+                item[u] = (jbeg + g0 + u) * a.stride;
+            }
+        }
+        float acc[ST_U];
+#pragma unroll
+        for (int u = 0; u < ST_U; ++u) acc[u] = 0.f;
+#pragma unroll 2
+        for (int d = lane * VEC; d < a.D; d += kWave * VEC) {
+            const uint4 hv = *(const uint4*)(h + d);
+            uint4 ev[ST_U];
+#pragma unroll
+            for (int u = 0; u < ST_U; ++u)
+                ev[u] = ok[u] ? *(const uint4*)(E + item[u] * a.D + d) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < ST_U; ++u) acc[u] = Vec16<T>::dot(ev[u], hv, acc[u]);
+        }
+        const float s = reduce_scatter8(acc, lane);
+        const int u = lane >> 3;
+        bool mine = (lane & 7) == 0;
+#pragma unroll
+        for (int q = 0; q < ST_U; ++q)
+            if (q == u) mine = mine && ok[q];
+        if (mine) {
+            int64_t it = 0;
+#pragma unroll
+            for (int q = 0; q < ST_U; ++q)
+                if (q == u) it = item[q];
+            if (MODE == 0) {
+                a.sample_out[(int64_t)b * a.n_items + jbeg + g0 + u] = s;
+            } else {
+                st.add(s);
+                if (s >= th) {
+                    const int pos = atomicAdd(&s_cnt, 1);
+                    a.keys[region + pos] = rank_key(s, (uint32_t)it);
+                }
+            }
+        }
+    }
+    if (MODE == 0) return;
+
+    // (max, sum-exp) over the wave, then over the four waves.
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float m2 = __shfl_xor(st.m, o), l2 = __shfl_xor(st.l, o);
+        st.merge(m2, l2);
+    }
+    if (lane == 0) s_ml[w] = make_float2(st.m, st.l);
+    __syncthreads();
+    if (tid == 0) {
+        LseState t;
+        t.init();
+        for (int q = 0; q < ST_NT / kWave; ++q) t.merge(s_ml[q].x, s_ml[q].y);
+        a.pm[piece] = t.m;
+        a.pl[piece] = t.l;
+        a.pcnt[piece] = s_cnt;
+        a.preg[piece] = region;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Block-level selection of the k-th largest 64-bit key
+// ---------------------------------------------------------------------------
+constexpr int SEL_NT = 256;
+constexpr int SEL_NB = 256;    // histogram bins per narrowing pass
+constexpr int SEL_GCAP = 2048; // candidates gathered into LDS for the final sort
+constexpr int SEL_UNR = 8;     // independent loads in flight per thread
+
+struct SelShared {
+    unsigned long long red_lo[SEL_NT / kWave], red_hi[SEL_NT / kWave];
+    int hist[SEL_NB];
+    int cnt_a, cnt_b;
+    uint64_t gbuf[SEL_GCAP];
+    uint64_t out[GENREC_KMAX];
+};
+
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long t = __shfl_xor(v, o);
+        v = t < v ? t : v;
+    }
+    return v;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long t = __shfl_xor(v, o);
+        v = t > v ? t : v;
+    }
+    return v;
+}
+
+// Bitonic sort, descending, of buf[0..n) padded to a power of two with zeros.
+__device__ void block_sort_desc(uint64_t* buf, int n) {
+    int p2 = 1;
+    while (p2 < n) p2 <<= 1;
+    for (int i = n + threadIdx.x; i < p2; i += blockDim.x) buf[i] = 0;
+    __syncthreads();
+    for (int k = 2; k <= p2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < p2; i += blockDim.x) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint64_t x = buf[i], y = buf[ixj];
+                    const bool desc = (i & k) == 0;
+                    if (desc ? (x < y) : (x > y)) {
+                        buf[i] = y;
+                        buf[ixj] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Finds the k-th largest key (1 <= k <= n) among the keys the source yields
+// and, with COLLECT, leaves the k largest keys in sh.out[0..k) (unsorted).
+// Returns the k-th largest key.  Every pass reads the source once:
+//   1. min / max of all keys;
+//   2. while more than SEL_GCAP keys remain in the candidate range [lo, hi],
+//      histogram the range into 256 power-of-two-wide bins and narrow it to
+//      the bin holding the k-th largest;
+//   3. gather the range into LDS (and, with COLLECT, every key above it into
+//      sh.out), sort the range and pick.
+template <bool COLLECT, class Src>
+__device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    unsigned long long lo = ~0ull, hi = 0;
+    src.for_each([&](uint64_t key) {
+        lo = key < lo ? key : lo;
+        hi = key > hi ? key : hi;
+    });
+    lo = wave_min_u64(lo);
+    hi = wave_max_u64(hi);
+    if (lane == 0) { sh.red_lo[w] = lo; sh.red_hi[w] = hi; }
+    __syncthreads();
+    lo = sh.red_lo[0];
+    hi = sh.red_hi[0];
+    for (int q = 1; q < SEL_NT / kWave; ++q) {
+        lo = sh.red_lo[q] < lo ? sh.red_lo[q] : lo;
+        hi = sh.red_hi[q] > hi ? sh.red_hi[q] : hi;
+    }
+    __syncthreads();
+
+    int64_t n_range = src.total();
+    int k_rem = k;
+    while (lo != hi && n_range > SEL_GCAP) {
+        const unsigned long long span = hi - lo;
+        const int shift = max(0, 64 - __clzll(span) - 8);  // (hi - lo) >> shift < 256
+        for (int i = tid; i < SEL_NB; i += SEL_NT) sh.hist[i] = 0;
+        __syncthreads();
+        const unsigned long long clo = lo, chi = hi;
+        src.for_each([&](uint64_t key) {
+            if (key >= clo && key <= chi) atomicAdd(&sh.hist[(int)((key - clo) >> shift)], 1);
+        });
+        __syncthreads();
+        // Wave 0 finds bin d with above(d) < k_rem <= above(d) + hist[d].
+        if (w == 0) {
+            int v[SEL_NB / kWave];
+            int tsum = 0;
+#pragma unroll
+            for (int i = 0; i < SEL_NB / kWave; ++i) {  // lane owns bins [4*lane, 4*lane+4) (top-down order below)
+                v[i] = sh.hist[SEL_NB - 1 - (lane * (SEL_NB / kWave) + i)];
+                tsum += v[i];
+            }
+            // exclusive prefix over lanes of tsum (counts of higher bins)
+            int incl = tsum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(incl, o);
+                if (lane >= o) incl += t;
+            }
+            int run = incl - tsum;
+#pragma unroll
+            for (int i = 0; i < SEL_NB / kWave; ++i) {
+                if (run < k_rem && k_rem <= run + v[i]) {
+                    sh.cnt_a = SEL_NB - 1 - (lane * (SEL_NB / kWave) + i);  // bin
+                    sh.cnt_b = run;                                         // keys above it
+                }
+                run += v[i];
+            }
+        }
+        __syncthreads();
+        const int d = sh.cnt_a;
+        k_rem -= sh.cnt_b;
+        n_range = sh.hist[d];
+        lo = clo + ((unsigned long long)d << shift);
+        const unsigned long long top = lo + ((1ull << shift) - 1);
+        hi = top < chi ? top : chi;
+        __syncthreads();
+    }
+
+    // Final pass: gather the range, and (COLLECT) everything above it.
+    if (tid == 0) { sh.cnt_a = 0; sh.cnt_b = 0; }
+    __syncthreads();
+    const unsigned long long flo = lo, fhi = hi;
+    const bool single = flo == fhi;
+    const int n_above = k - k_rem;
+    src.for_each([&](uint64_t key) {
+        if (key > fhi) {
+            if (COLLECT) sh.out[atomicAdd(&sh.cnt_a, 1)] = key;
+        } else if (key >= flo && !single) {
+            sh.gbuf[atomicAdd(&sh.cnt_b, 1)] = key;
+        }
+    });
+    __syncthreads();
+    uint64_t kth;
+    if (single) {
+        kth = flo;
+        if (COLLECT)
+            for (int i = tid; i < k_rem; i += SEL_NT) sh.out[n_above + i] = flo;
+    } else {
+        block_sort_desc(sh.gbuf, (int)n_range);
+        kth = sh.gbuf[k_rem - 1];
+        if (COLLECT)
+            for (int i = tid; i < k_rem; i += SEL_NT) sh.out[n_above + i] = sh.gbuf[i];
+    }
+    __syncthreads();
+    return kth;
+}
+
+// Source: one dense fp32 score row (the catalog sample of one user).
+struct DenseRowSrc {
+    const float* row;
+    int64_t n;
+    __device__ int64_t total() const { return n; }
+    template <class F>
+    __device__ void for_each(F&& f) const {
+        for (int64_t e0 = threadIdx.x; e0 < n; e0 += (int64_t)SEL_NT * SEL_UNR) {
+            float v[SEL_UNR];
+#pragma unroll
+            for (int q = 0; q < SEL_UNR; ++q) {
+                const int64_t e = e0 + (int64_t)q * SEL_NT;
+                v[q] = e < n ? row[e] : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q < SEL_UNR; ++q) {
+                const int64_t e = e0 + (int64_t)q * SEL_NT;
+                if (e < n) f(rank_key(v[q], (uint32_t)e));
+            }
+        }
+    }
+};
+
+__global__ __launch_bounds__(SEL_NT) void threshold_kernel(const float* sample, int64_t n_sample, int K,
+                                                           float* theta) {
+    __shared__ SelShared sh;
+    const int b = blockIdx.x;
+    if (n_sample < K) {
+        if (threadIdx.x == 0) theta[b] = -INFINITY;
+        return;
+    }
+    DenseRowSrc src{sample + (int64_t)b * n_sample, n_sample};
+    const uint64_t kth = block_select<false>(src, K, sh);
+    if (threadIdx.x == 0) {
+        const float t = key_score(kth);
+        // A hair lower than the sampled K-th score: still a valid lower bound
+        // of the catalog's K-th score, and robust to any rounding difference.
+        theta[b] = t - fabsf(t) * 0x1p-20f - FLT_MIN;
+    }
+}
+
+// Source: the candidate regions of one user's pieces.
+constexpr int MG_PB = 1024;  // pieces staged in LDS per batch
+
+struct PieceShared {
+    int64_t base[MG_PB];
+    int pref[MG_PB + 1];
+    int wsum[SEL_NT / kWave];
+};
+
+struct PieceSrc {
+    const uint64_t* keys;
+    const int* pcnt;
+    const int64_t* preg;
+    int64_t p0, p1;
+    int64_t n;  // total keys
+    PieceShared* ps;
+    __device__ int64_t total() const { return n; }
+    template <class F>
+    __device__ void for_each(F&& f) const {
+        const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+        for (int64_t pb = p0; pb < p1; pb += MG_PB) {
+            const int np = (int)min((int64_t)MG_PB, p1 - pb);
+            // exclusive scan of the batch's counts (4 per thread)
+            int cv[MG_PB / SEL_NT];
+            int tsum = 0;
+#pragma unroll
+            for (int i = 0; i < MG_PB / SEL_NT; ++i) {
+                const int p = tid * (MG_PB / SEL_NT) + i;
+                cv[i] = p < np ? pcnt[pb + p] : 0;
+                if (p < np) ps->base[p] = preg[pb + p];
+                tsum += cv[i];
+            }
+            int incl = tsum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(incl, o);
+                if (lane >= o) incl += t;
+            }
+            if (lane == 63) ps->wsum[w] = incl;
+            __syncthreads();
+            int off = 0;
+            for (int q = 0; q < w; ++q) off += ps->wsum[q];
+            int run = off + incl - tsum;
+#pragma unroll
+            for (int i = 0; i < MG_PB / SEL_NT; ++i) {
+                ps->pref[tid * (MG_PB / SEL_NT) + i] = run;
+                run += cv[i];
+            }
+            if (tid == SEL_NT - 1) ps->pref[MG_PB] = run;
+            __syncthreads();
+            const int tot = ps->pref[MG_PB];
+            int pi = 0;
+            for (int e0 = tid; e0 < tot; e0 += SEL_NT * SEL_UNR) {
+                uint64_t kv[SEL_UNR];
+#pragma unroll
+                for (int q = 0; q < SEL_UNR; ++q) {
+                    const int e = e0 + q * SEL_NT;
+                    if (e < tot) {
+                        while (ps->pref[pi + 1] <= e) ++pi;
+                        kv[q] = keys[ps->base[pi] + (e - ps->pref[pi])];
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < SEL_UNR; ++q)
+                    if (e0 + q * SEL_NT < tot) f(kv[q]);
+            }
+            __syncthreads();
+        }
+    }
+};
+
+__global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
+    __shared__ SelShared sh;
+    __shared__ PieceShared ps;
+    __shared__ float2 s_ml[SEL_NT / kWave];
+    __shared__ unsigned long long s_n[SEL_NT / kWave];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (b == 0 && tid == 0 && a.clear_err != nullptr) {
+        a.clear_err[0] = 0;
+        a.clear_err[1] = 0;
+    }
+    int64_t p0, p1;
+    if (a.piece_begin != nullptr) {
+        p0 = a.piece_begin[b];
+        p1 = a.piece_begin[b + 1];
+    } else {
+        p0 = (int64_t)b * a.P;
+        p1 = p0 + a.P;
+    }
+    // lse and candidate count over the user's pieces
+    LseState st;
+    st.init();
+    unsigned long long n = 0;
+    for (int64_t p = p0 + tid; p < p1; p += SEL_NT) {
+        st.merge(a.pm[p], a.pl[p]);
+        n += (unsigned long long)a.pcnt[p];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float m2 = __shfl_xor(st.m, o), l2 = __shfl_xor(st.l, o);
+        st.merge(m2, l2);
+        n += __shfl_xor(n, o);
+    }
+    if (lane == 0) { s_ml[w] = make_float2(st.m, st.l); s_n[w] = n; }
+    __syncthreads();
+    LseState tot;
+    tot.init();
+    unsigned long long ntot = 0;
+    for (int q = 0; q < SEL_NT / kWave; ++q) { tot.merge(s_ml[q].x, s_ml[q].y); ntot += s_n[q]; }
+    if (tid == 0)
+        a.out_lse[b] = tot.l > 0.f ? tot.m + __builtin_amdgcn_logf(tot.l) * kLn2 : -INFINITY;
+
+    const int K = a.K;
+    const int keff = (int)min((unsigned long long)K, ntot);
+    int32_t* oidx = a.out_idx + (int64_t)b * K;
+    float* osc = a.out_scores + (int64_t)b * K;
+    if (keff > 0) {
+        PieceSrc src{a.keys, a.pcnt, a.preg, p0, p1, (int64_t)ntot, &ps};
+        block_select<true>(src, keff, sh);
+        block_sort_desc(sh.out, keff);
+    }
+    for (int i = tid; i < K; i += SEL_NT) {
+        if (i < keff) {
+            const uint64_t key = sh.out[i];
+            oidx[i] = (int32_t)key_id(key);
+            osc[i] = key_score(key);
+        } else {
+            oidx[i] = -1;
+            osc[i] = -INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Candidate lists: CSR offsets -> pieces of at most CAND_PIECE entries
+// ---------------------------------------------------------------------------
+constexpr int PL_NT = 1024;
+
+__global__ __launch_bounds__(PL_NT) void cand_plan_kernel(CandPlanArgs a) {
+    __shared__ int64_t s_wmax[PL_NT / kWave];
+    __shared__ int s_wsum[PL_NT / kWave];
+    __shared__ int64_t s_carry_end;
+    __shared__ int s_carry_pieces;
+    __shared__ int s_bad;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid == 0) {
+        s_carry_end = 0;
+        s_carry_pieces = 0;
+        s_bad = 0;
+        a.err[0] = 0;
+        a.err[1] = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base < a.B; base += PL_NT) {
+        const int b = base + tid;
+        int64_t o0 = 0, o1 = 0;
+        if (b < a.B) {
+            o0 = a.offsets[b];
+            o1 = a.offsets[b + 1];
+        }
+        // prefix max of earlier list ends: a list must start at or after it
+        int64_t endv = b < a.B ? o1 : 0;
+        int64_t incl = endv;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t t = __shfl_up(incl, o);
+            if (lane >= o) incl = t > incl ? t : incl;
+        }
+        if (lane == 63) s_wmax[w] = incl;
+        __syncthreads();
+        int64_t prev = s_carry_end;
+        for (int q = 0; q < w; ++q) prev = s_wmax[q] > prev ? s_wmax[q] : prev;
+        int64_t excl = __shfl_up(incl, 1);
+        if (lane > 0) prev = excl > prev ? excl : prev;
+        const bool valid = b < a.B && o0 >= prev && o0 >= 0 && o1 >= o0 && o1 <= a.nnz;
+        if (b < a.B && !valid) atomicAdd(&s_bad, 1);
+        const int64_t len = valid ? o1 - o0 : 0;
+        const int np = (int)((len + CAND_PIECE - 1) / CAND_PIECE);
+        // exclusive scan of piece counts
+        int pinc = np;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(pinc, o);
+            if (lane >= o) pinc += t;
+        }
+        if (lane == 63) s_wsum[w] = pinc;
+        __syncthreads();
+        int pofs = s_carry_pieces;
+        for (int q = 0; q < w; ++q) pofs += s_wsum[q];
+        const int first = pofs + pinc - np;
+        if (b < a.B) {
+            a.piece_begin[b] = first;
+            for (int j = 0; j < np; ++j) {
+                CandPiece rec;
+                rec.user = b;
+                rec.len = (int)min((int64_t)CAND_PIECE, len - (int64_t)j * CAND_PIECE);
+                rec.e0 = o0 + (int64_t)j * CAND_PIECE;
+                a.table[first + j] = rec;
+            }
+        }
+        __syncthreads();  // every read of the carries and wave partials is done
+        if (tid == PL_NT - 1) s_carry_pieces = first + np;
+        if (tid == 0) {
+            int64_t m = s_carry_end;
+            for (int q = 0; q < PL_NT / kWave; ++q) m = s_wmax[q] > m ? s_wmax[q] : m;
+            s_carry_end = m;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        a.piece_begin[a.B] = s_carry_pieces;
+        *a.n_pieces = s_carry_pieces;
+        a.err[1] = s_bad;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s) {
+    const int grid = a.UT * a.P;
+    if (mode == 0) hipLaunchKernelGGL(mfma_score_kernel<0>, dim3(grid), dim3(MF_NT), 0, s, a);
+    else hipLaunchKernelGGL(mfma_score_kernel<1>, dim3(grid), dim3(MF_NT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, hipStream_t s) {
+    if (grid <= 0) return hipSuccess;
+    if (f32) {
+        if (mode == 0) hipLaunchKernelGGL((stream_score_kernel<float, 0>), dim3(grid), dim3(ST_NT), 0, s, a);
+        else if (mode == 1) hipLaunchKernelGGL((stream_score_kernel<float, 1>), dim3(grid), dim3(ST_NT), 0, s, a);
+        else hipLaunchKernelGGL((stream_score_kernel<float, 2>), dim3(grid), dim3(ST_NT), 0, s, a);
+    } else {
+        if (mode == 0) hipLaunchKernelGGL((stream_score_kernel<uint16_t, 0>), dim3(grid), dim3(ST_NT), 0, s, a);
+        else if (mode == 1) hipLaunchKernelGGL((stream_score_kernel<uint16_t, 1>), dim3(grid), dim3(ST_NT), 0, s, a);
+        else hipLaunchKernelGGL((stream_score_kernel<uint16_t, 2>), dim3(grid), dim3(ST_NT), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_threshold(const float* sample, int64_t n_sample, int K, float* theta, int B,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(threshold_kernel, dim3(B), dim3(SEL_NT), 0, s, sample, n_sample, K, theta);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(merge_kernel, dim3(a.B), dim3(SEL_NT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_cand_plan(const CandPlanArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(cand_plan_kernel, dim3(1), dim3(PL_NT), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace genrec

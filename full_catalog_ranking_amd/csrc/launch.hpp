@@ -1,0 +1,88 @@
+// Kernel argument blocks and launchers (internal to libgenrec.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/genrec.h"
+
+namespace genrec {
+
+constexpr int CAND_PIECE = 256;  // candidate-list entries per work piece
+
+struct MfmaArgs {
+    const uint16_t* H;
+    const uint16_t* E;
+    int B, D;
+    int64_t M;
+    int64_t n_items, stride;  // items j < n_items, catalog row j * stride
+    int UT, P, base, rem;     // user tiles; P chunks of base(+1) item tiles
+    float* sample_out;        // mode 0: [B][n_items] scores
+    const float* theta;       // mode 1: [B] candidate thresholds (or null)
+    uint64_t* keys;           // mode 1: candidate regions, [B][M]
+    float* pm;                // per piece (user b, chunk c) at b*P + c
+    float* pl;
+    int* pcnt;
+    int64_t* preg;
+};
+
+struct CandPiece {
+    int user;
+    int len;
+    int64_t e0;
+};
+
+struct StreamArgs {
+    const void* H;
+    const void* E;
+    int B, D;
+    int64_t M;
+    int64_t n_items, stride;  // dense modes
+    int64_t CH;               // dense modes: items per chunk
+    int P;                    // dense modes: chunks per user
+    const int32_t* ids;       // candidate mode
+    const int* n_pieces;
+    const CandPiece* table;
+    float* sample_out;
+    const float* theta;
+    uint64_t* keys;
+    float* pm;
+    float* pl;
+    int* pcnt;
+    int64_t* preg;
+    int64_t* err;
+};
+
+struct MergeArgs {
+    int B, K;
+    int P;                   // dense: pieces of user b are [b*P, (b+1)*P)
+    const int* piece_begin;  // candidates: [B+1]
+    const uint64_t* keys;
+    const float* pm;
+    const float* pl;
+    const int* pcnt;
+    const int64_t* preg;
+    int32_t* out_idx;
+    float* out_scores;
+    float* out_lse;
+    int64_t* clear_err;  // zeroed by block 0 when non-null
+};
+
+struct CandPlanArgs {
+    const int64_t* offsets;
+    int B;
+    int64_t nnz;
+    int* piece_begin;
+    CandPiece* table;
+    int* n_pieces;
+    int64_t* err;
+};
+
+hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s);
+hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, hipStream_t s);
+hipError_t launch_threshold(const float* sample, int64_t n_sample, int K, float* theta, int B,
+                            hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_cand_plan(const CandPlanArgs& a, hipStream_t s);
+
+}  // namespace genrec

@@ -1,0 +1,127 @@
+// Host-side planning for the ranking head: variant choice, work split and
+// workspace layout.  Pure C++ (no HIP), so it can be unit-tested on any host.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace genrec {
+
+constexpr int kNumCU = 256;            // MI355X compute units
+constexpr int kMfmaTileItems = 256;    // items per MFMA tile
+constexpr int kMfmaTileUsers = 256;    // users per MFMA tile
+constexpr int kStreamMaxB = 8;         // bf16 batches up to this size use the VALU path
+constexpr int64_t kSampleMinM = 65536; // smaller catalogs skip the threshold pre-pass
+constexpr int64_t kSampleMinStride = 32;
+constexpr int64_t kSampleMax = 32768;  // sampled items per user at most
+constexpr int64_t kStreamPieces = 2048;  // target work pieces of the VALU path
+constexpr int64_t kStreamChunkAlign = 32;
+constexpr int kCandPiece = 256;        // candidate entries per piece (matches the kernels)
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Chunking {
+    int UT = 1, P = 1, base = 0, rem = 0;  // MFMA: P chunks of base(+1) tiles over UT user tiles
+    int64_t CH = 0;                        // VALU: items per chunk (P chunks)
+};
+
+struct DensePlan {
+    bool mfma = false;
+    bool sample = false;
+    int64_t stride = 1, n_sample = 0;
+    Chunking main, pre;
+    int64_t n_pieces = 0;
+    size_t off_hdr = 0, off_theta = 0, off_sample = 0, off_pm = 0, off_pl = 0, off_pcnt = 0,
+           off_preg = 0, off_keys = 0, total = 0;
+};
+
+inline Chunking chunk_mfma(int B, int64_t n_items) {
+    Chunking c;
+    c.UT = (int)ceil_div(B, kMfmaTileUsers);
+    const int64_t nt = ceil_div(n_items, kMfmaTileItems);
+    const int64_t want = std::max<int64_t>(1, kNumCU / c.UT);
+    c.P = (int)std::max<int64_t>(1, std::min(nt, want));
+    c.base = (int)(nt / c.P);
+    c.rem = (int)(nt % c.P);
+    return c;
+}
+
+inline Chunking chunk_stream(int B, int64_t n_items) {
+    Chunking c;
+    int64_t ch = ceil_div(n_items * (int64_t)B, kStreamPieces);
+    ch = std::max<int64_t>(kStreamChunkAlign, ceil_div(ch, kStreamChunkAlign) * kStreamChunkAlign);
+    c.CH = ch;
+    c.P = (int)ceil_div(n_items, ch);
+    return c;
+}
+
+// dtype: 0 = bf16, 1 = f32.
+inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
+    (void)D;
+    DensePlan p;
+    p.mfma = dtype == 0 && B > kStreamMaxB;
+    p.stride = std::max<int64_t>(kSampleMinStride, ceil_div(M, kSampleMax));
+    p.n_sample = ceil_div(M, p.stride);
+    p.sample = M >= kSampleMinM && p.n_sample >= 4 * (int64_t)K;
+    p.main = p.mfma ? chunk_mfma(B, M) : chunk_stream(B, M);
+    if (p.sample) p.pre = p.mfma ? chunk_mfma(B, p.n_sample) : chunk_stream(B, p.n_sample);
+    p.n_pieces = (int64_t)B * p.main.P;
+    size_t o = 0;
+    p.off_hdr = o;
+    o += 256;
+    p.off_theta = o;
+    o = align_up(o + sizeof(float) * (size_t)B, 256);
+    p.off_sample = o;
+    if (p.sample) o = align_up(o + sizeof(float) * (size_t)B * (size_t)p.n_sample, 256);
+    p.off_pm = o;
+    o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
+    p.off_pl = o;
+    o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
+    p.off_pcnt = o;
+    o = align_up(o + sizeof(int) * (size_t)p.n_pieces, 256);
+    p.off_preg = o;
+    o = align_up(o + sizeof(int64_t) * (size_t)p.n_pieces, 256);
+    p.off_keys = o;
+    o = align_up(o + sizeof(uint64_t) * (size_t)B * (size_t)M, 256);
+    p.total = o;
+    return p;
+}
+
+struct CandPlan {
+    int64_t n_pieces_max = 0;
+    size_t off_hdr = 0, off_begin = 0, off_table = 0, off_pm = 0, off_pl = 0, off_pcnt = 0,
+           off_preg = 0, off_keys = 0, total = 0;
+};
+
+// Header of every workspace: int64 bad-id count, int64 bad-offset count,
+// int32 piece count.
+constexpr size_t kHdrErrIds = 0, kHdrErrOffsets = 8, kHdrPieces = 16;
+
+inline CandPlan plan_cand(int B, int64_t nnz) {
+    CandPlan p;
+    p.n_pieces_max = nnz / kCandPiece + B;
+    size_t o = 0;
+    p.off_hdr = o;
+    o += 256;
+    p.off_begin = o;
+    o = align_up(o + sizeof(int) * ((size_t)B + 1), 256);
+    p.off_table = o;
+    o = align_up(o + 16 * (size_t)p.n_pieces_max, 256);
+    p.off_pm = o;
+    o = align_up(o + sizeof(float) * (size_t)p.n_pieces_max, 256);
+    p.off_pl = o;
+    o = align_up(o + sizeof(float) * (size_t)p.n_pieces_max, 256);
+    p.off_pcnt = o;
+    o = align_up(o + sizeof(int) * (size_t)p.n_pieces_max, 256);
+    p.off_preg = o;
+    o = align_up(o + sizeof(int64_t) * (size_t)p.n_pieces_max, 256);
+    p.off_keys = o;
+    o = align_up(o + sizeof(uint64_t) * (size_t)std::max<int64_t>(nnz, 1), 256);
+    p.total = o;
+    return p;
+}
+
+}  // namespace genrec

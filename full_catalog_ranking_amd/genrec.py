@@ -1,0 +1,236 @@
+"""Python binding of libgenrec.so (ctypes): argument marshalling only.
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+ranking head runs in the library's HIP kernels.  If the library is missing
+or cannot be loaded this module raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgenrec.so")
+
+GENREC_BF16, GENREC_F32 = 0, 1
+KMAX = 1024
+
+EXPORTED = (
+    "genrec_score_lse_topk_workspace",
+    "genrec_score_lse_topk",
+    "genrec_score_candidates_topk_workspace",
+    "genrec_score_candidates_topk",
+    "genrec_get_device_errors",
+    "genrec_describe_plan",
+    "genrec_status_string",
+    "genrec_version",
+    "genrec_profiler_create",
+    "genrec_profiler_destroy",
+    "genrec_profiler_reset",
+    "genrec_profiler_summary",
+    "genrec_score_lse_topk_profiled",
+    "genrec_score_candidates_topk_profiled",
+)
+KERNEL_KINDS = ("sample_score", "threshold", "main_score", "merge", "cand_plan")
+
+
+class GenrecError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s failed: %s (%d)" % (where, status_string(status), status))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgenrec.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libgenrec.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.genrec_score_lse_topk_workspace.argtypes = [I, I, I64, I, I]
+        L.genrec_score_lse_topk_workspace.restype = SZ
+        L.genrec_score_lse_topk.argtypes = [P, P, I, I, I, I64, I, P, P, P, P, SZ, P]
+        L.genrec_score_lse_topk.restype = I
+        L.genrec_score_candidates_topk_workspace.argtypes = [I, I, I64, I64, I, I]
+        L.genrec_score_candidates_topk_workspace.restype = SZ
+        L.genrec_score_candidates_topk.argtypes = [P, P, I, P, P, I, I, I64, I64, I, P, P, P, P, SZ, P]
+        L.genrec_score_candidates_topk.restype = I
+        L.genrec_get_device_errors.argtypes = [P, P, P, P]
+        L.genrec_get_device_errors.restype = I
+        L.genrec_describe_plan.argtypes = [I, I, I64, I, I, ctypes.c_char_p, SZ]
+        L.genrec_describe_plan.restype = I
+        L.genrec_status_string.argtypes = [I]
+        L.genrec_status_string.restype = ctypes.c_char_p
+        L.genrec_version.restype = I
+        L.genrec_profiler_create.argtypes = [I]
+        L.genrec_profiler_create.restype = P
+        L.genrec_profiler_destroy.argtypes = [P]
+        L.genrec_profiler_reset.argtypes = [P]
+        L.genrec_profiler_reset.restype = I
+        L.genrec_profiler_summary.argtypes = [P, P, P]
+        L.genrec_profiler_summary.restype = I
+        L.genrec_score_lse_topk_profiled.argtypes = L.genrec_score_lse_topk.argtypes + [P]
+        L.genrec_score_lse_topk_profiled.restype = I
+        L.genrec_score_candidates_topk_profiled.argtypes = L.genrec_score_candidates_topk.argtypes + [P]
+        L.genrec_score_candidates_topk_profiled.restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().genrec_status_string(int(status)).decode()
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return GENREC_BF16
+    if t == torch.float32:
+        return GENREC_F32
+    raise TypeError("H and E must be bfloat16 or float32, got %s" % t)
+
+
+def workspace_bytes(B: int, D: int, M: int, K: int, dtype: torch.dtype) -> int:
+    return int(lib().genrec_score_lse_topk_workspace(B, D, M, K, dtype_code(dtype)))
+
+
+def cand_workspace_bytes(B: int, D: int, M: int, nnz: int, K: int, dtype: torch.dtype) -> int:
+    return int(lib().genrec_score_candidates_topk_workspace(B, D, M, nnz, K, dtype_code(dtype)))
+
+
+def describe_plan(B: int, D: int, M: int, K: int, dtype: torch.dtype) -> dict:
+    buf = ctypes.create_string_buffer(512)
+    st = lib().genrec_describe_plan(B, D, M, K, dtype_code(dtype), buf, 512)
+    if st != 0:
+        raise GenrecError(st, "genrec_describe_plan")
+    return json.loads(buf.value.decode())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_inputs(H: torch.Tensor, E: torch.Tensor):
+    if not (H.is_cuda and E.is_cuda):
+        raise ValueError("H and E must be device tensors")
+    if H.dim() != 2 or E.dim() != 2 or H.shape[1] != E.shape[1]:
+        raise ValueError("H must be (B, D) and E (M, D), got %s and %s" % (tuple(H.shape), tuple(E.shape)))
+    if H.dtype != E.dtype:
+        raise ValueError("H and E must share a dtype")
+    if not (H.is_contiguous() and E.is_contiguous()):
+        raise ValueError("H and E must be contiguous")
+
+
+def _outputs(B: int, K: int, device):
+    idx = torch.empty((B, K), dtype=torch.int32, device=device)
+    sc = torch.empty((B, K), dtype=torch.float32, device=device)
+    ls = torch.empty((B,), dtype=torch.float32, device=device)
+    return idx, sc, ls
+
+
+class Profiler:
+    """HIP-event timing of every kernel the profiled calls launch."""
+
+    def __init__(self, max_launches: int = 4096):
+        self.h = lib().genrec_profiler_create(max_launches)
+        if not self.h:
+            raise RuntimeError("genrec_profiler_create failed")
+
+    def reset(self):
+        lib().genrec_profiler_reset(self.h)
+
+    def summary(self) -> dict:
+        """{kind: (launches, total_ms)} -- synchronises on the last recorded event."""
+        counts = (ctypes.c_int * len(KERNEL_KINDS))()
+        ms = (ctypes.c_double * len(KERNEL_KINDS))()
+        st = lib().genrec_profiler_summary(self.h, counts, ms)
+        if st != 0:
+            raise GenrecError(st, "genrec_profiler_summary")
+        return {k: (counts[i], ms[i]) for i, k in enumerate(KERNEL_KINDS) if counts[i]}
+
+    def __del__(self):
+        try:
+            if self.h:
+                lib().genrec_profiler_destroy(self.h)
+                self.h = None
+        except Exception:
+            pass
+
+
+def score_lse_topk(H: torch.Tensor, E: torch.Tensor, K: int, workspace: torch.Tensor | None = None,
+                   out=None, profiler: Profiler | None = None):
+    """Full-catalog ranking head: returns (idx int32 [B,K], scores f32 [B,K], lse f32 [B])."""
+    _check_inputs(H, E)
+    B, D = H.shape
+    M = E.shape[0]
+    need = workspace_bytes(B, D, M, K, H.dtype)
+    if need == 0:
+        raise GenrecError(lib().genrec_score_lse_topk(None, None, dtype_code(H.dtype), B, D, M, K,
+                                                      None, None, None, None, 0, None),
+                          "genrec_score_lse_topk")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=H.device)
+    idx, sc, ls = out if out is not None else _outputs(B, K, H.device)
+    args = (_ptr(H), _ptr(E), dtype_code(H.dtype), B, D, M, K, _ptr(idx), _ptr(sc), _ptr(ls),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(H.device))
+    if profiler is None:
+        st = lib().genrec_score_lse_topk(*args)
+    else:
+        st = lib().genrec_score_lse_topk_profiled(*args, profiler.h)
+    if st != 0:
+        raise GenrecError(st, "genrec_score_lse_topk")
+    return idx, sc, ls
+
+
+def score_candidates_topk(H: torch.Tensor, E: torch.Tensor, offsets: torch.Tensor, ids: torch.Tensor,
+                          K: int, workspace: torch.Tensor | None = None, out=None,
+                          profiler: Profiler | None = None):
+    """Candidate-set ranking head over CSR lists (offsets int64 [B+1], ids int32 [nnz])."""
+    _check_inputs(H, E)
+    if offsets.dtype != torch.int64 or ids.dtype != torch.int32:
+        raise TypeError("offsets must be int64 and ids int32")
+    if not (offsets.is_cuda and ids.is_cuda and offsets.is_contiguous() and ids.is_contiguous()):
+        raise ValueError("offsets and ids must be contiguous device tensors")
+    B, D = H.shape
+    M = E.shape[0]
+    if offsets.numel() != B + 1:
+        raise ValueError("offsets must hold B+1 entries")
+    nnz = ids.numel()
+    need = cand_workspace_bytes(B, D, M, nnz, K, H.dtype)
+    if need == 0:
+        raise GenrecError(lib().genrec_score_candidates_topk(None, None, dtype_code(H.dtype), None, None, B, D,
+                                                             M, nnz, K, None, None, None, None, 0, None),
+                          "genrec_score_candidates_topk")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=H.device)
+    idx, sc, ls = out if out is not None else _outputs(B, K, H.device)
+    args = (_ptr(H), _ptr(E), dtype_code(H.dtype), _ptr(offsets), _ptr(ids) if nnz else None, B, D, M, nnz, K,
+            _ptr(idx), _ptr(sc), _ptr(ls), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream_handle(H.device))
+    if profiler is None:
+        st = lib().genrec_score_candidates_topk(*args)
+    else:
+        st = lib().genrec_score_candidates_topk_profiled(*args, profiler.h)
+    if st != 0:
+        raise GenrecError(st, "genrec_score_candidates_topk")
+    return idx, sc, ls, workspace
+
+
+def device_errors(workspace: torch.Tensor) -> tuple[int, int]:
+    """(skipped out-of-range ids, users with malformed offsets) of the last candidate call."""
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = lib().genrec_get_device_errors(_ptr(workspace), _stream_handle(workspace.device),
+                                        ctypes.byref(a), ctypes.byref(b))
+    if st != 0:
+        raise GenrecError(st, "genrec_get_device_errors")
+    return a.value, b.value

@@ -1,0 +1,166 @@
+/*
+ * genrec.h -- C ABI of the MI355X (gfx950) ranking-head library, libgenrec.so.
+ *
+ * The library scores a batch of pooled user vectors H (B x D) against an item
+ * catalog E (M x D) and returns, per user, the softmax normaliser (logsumexp)
+ * of the scores and the top-K items ranked by score.  The full B x M score
+ * matrix is never written to device memory.
+ *
+ * Sources of the operation:
+ *  - GenRec concept page (techistory.net scratchpad, page 13), scoring
+ *    formula s = E^T h and its two PyTorch demos: the ranking head is a
+ *    bias-free inner product of the user vector with every item embedding,
+ *    computed for the whole catalog at once; the catalog is held as (M, D).
+ *  - GenRec explainer page (koktn.github.io, "overall picture" section):
+ *    s_i = phi(h, e_i); the scores are softmax-normalised over the catalog or
+ *    over a candidate set and sorted in descending order to give the ranking;
+ *    the paper targets full-catalog ranking or top-K ranking over a
+ *    separately given candidate set.
+ *  - HSTU explainer page (koktn.github.io, "ranking and retrieval" section):
+ *    retrieval over the atomic-ID catalog by MIPS, i.e. exact maximum inner
+ *    product top-K, which is the same computation.
+ *
+ * Conventions shared by all entry points
+ *  - Every array argument is a DEVICE pointer owned by the caller.  The library
+ *    allocates nothing and keeps no state between calls; scratch space is the
+ *    caller's `workspace`, whose size the matching *_workspace() query returns.
+ *    Two calls that may run concurrently need distinct workspaces.
+ *  - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t,
+ *    NULL = the default stream).  Argument errors are detected on the host
+ *    before anything is launched and returned synchronously; launch failures
+ *    return GENREC_ERR_HIP; faults inside kernels surface at stream sync.
+ *  - Layouts: H is [B][D], E is [M][D], both row-major and contiguous
+ *    (D innermost).  dtype GENREC_BF16 means bfloat16 elements, GENREC_F32
+ *    means float32.  Scores are accumulated in fp32.
+ *  - Outputs: out_idx [B][K] int32 catalog ids, out_scores [B][K] float32 raw
+ *    scores s (not log-probabilities; log-softmax = s - lse), sorted by score
+ *    descending with ties broken by the lower catalog id; out_lse [B] float32,
+ *    lse_b = ln sum_i exp(s_bi) over the catalog (or the user's list).
+ *    When fewer than K items exist (K > M, or a list shorter than K) the tail
+ *    is padded with id -1 and score -inf; an empty set gives lse = -inf.
+ *  - Supported: 1 <= K <= GENREC_KMAX, B >= 1, 1 <= M < 2^31,
+ *    D >= 1 with D % 8 == 0 (bf16) or D % 4 == 0 (f32), H and E 16-byte
+ *    aligned.  Non-finite inputs are not supported.
+ *  - Entry points never abort and no C++ exception crosses the ABI.
+ */
+#ifndef GENREC_H
+#define GENREC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GENREC_OK = 0,
+    GENREC_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad alignment      */
+    GENREC_ERR_UNSUPPORTED = -2, /* shape outside the supported set (K, D multiple, M)  */
+    GENREC_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than the query returned    */
+    GENREC_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed           */
+} genrec_status;
+
+typedef enum { GENREC_BF16 = 0, GENREC_F32 = 1 } genrec_dtype;
+
+#define GENREC_KMAX 1024
+
+/* Workspace bytes needed by genrec_score_lse_topk for these sizes (0 if the
+ * arguments are unsupported).  The value depends only on the arguments. */
+size_t genrec_score_lse_topk_workspace(int B, int D, int64_t M, int K, int dtype);
+
+/*
+ * Full-catalog ranking head: for every user b < B,
+ *   s_bi    = sum_d H[b][d] * E[i][d]            for all items i < M
+ *   lse_b   = ln sum_i exp(s_bi)
+ *   top-K   = the K items with the largest s_bi (ties: lower id first)
+ * H: [B][D], E: [M][D] of `dtype`; out_idx, out_scores: [B][K]; out_lse: [B].
+ * workspace: device memory of at least genrec_score_lse_topk_workspace(...)
+ * bytes, 256-byte aligned; its contents on entry do not matter.
+ */
+int genrec_score_lse_topk(const void* H, const void* E, int dtype,
+                          int B, int D, int64_t M, int K,
+                          int32_t* out_idx, float* out_scores, float* out_lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by genrec_score_candidates_topk (0 if unsupported). */
+size_t genrec_score_candidates_topk_workspace(int B, int D, int64_t M, int64_t nnz, int K,
+                                              int dtype);
+
+/*
+ * Candidate-set ranking head: user b scores only its own list
+ *   ids[cand_offsets[b] .. cand_offsets[b+1])      (CSR, catalog ids)
+ * and returns lse over those entries and the top-K entries (as catalog ids,
+ * ties broken by the lower id).  cand_offsets: [B+1] int64 with
+ * cand_offsets[0] == 0, non-decreasing, cand_offsets[B] == nnz; cand_ids:
+ * [nnz] int32.  Each entry is scored as given: a duplicated id counts twice.
+ * Ids outside [0, M) are skipped and counted; malformed offsets make the
+ * affected users empty and are counted too (see genrec_get_device_errors).
+ * nnz may be 0 (then cand_ids may be NULL).
+ */
+int genrec_score_candidates_topk(const void* H, const void* E, int dtype,
+                                 const int64_t* cand_offsets, const int32_t* cand_ids,
+                                 int B, int D, int64_t M, int64_t nnz, int K,
+                                 int32_t* out_idx, float* out_scores, float* out_lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Reads the device error counters that the last candidate call on this
+ * workspace wrote: *n_bad_ids = number of skipped out-of-range ids,
+ * *n_bad_offsets = number of users whose offsets were malformed.  Either
+ * output pointer may be NULL.  Synchronises `stream`.
+ */
+int genrec_get_device_errors(const void* workspace, void* stream, int64_t* n_bad_ids,
+                             int64_t* n_bad_offsets);
+
+/* Introspection: writes into buf (at most len bytes, NUL-terminated) a JSON
+ * object describing how genrec_score_lse_topk would run these sizes: the
+ * scoring path ("mfma" or "stream"), whether the sampled-threshold pre-pass
+ * runs, the work split and the workspace size.  Host-only, touches no device.
+ * Returns GENREC_OK or the status the compute call would return for the
+ * shape. */
+int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, size_t len);
+
+/*
+ * Kernel-level timing with HIP events.  A profiler records an event pair
+ * around every kernel that the *_profiled entry points launch, without
+ * synchronising; genrec_profiler_summary() synchronises on the last event and
+ * returns, per kernel kind, the number of launches and their summed duration
+ * in milliseconds.  Kinds: 0 sampled-threshold scoring pass, 1 threshold
+ * selection, 2 main scoring pass (MFMA or VALU), 3 top-K merge, 4 candidate
+ * work-list plan.  One profiler holds up to `max_launches` launches; further
+ * launches are not recorded.  A profiler may only be used by one stream at a
+ * time.  create returns NULL on failure.
+ */
+#define GENREC_NUM_KERNEL_KINDS 5
+typedef struct genrec_profiler genrec_profiler;
+genrec_profiler* genrec_profiler_create(int max_launches);
+void genrec_profiler_destroy(genrec_profiler* prof);
+int genrec_profiler_reset(genrec_profiler* prof);
+int genrec_profiler_summary(genrec_profiler* prof, int* counts, double* total_ms);
+
+/* Same as genrec_score_lse_topk / genrec_score_candidates_topk, recording
+ * every launch into `prof` (which may be NULL). */
+int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype,
+                                   int B, int D, int64_t M, int K,
+                                   int32_t* out_idx, float* out_scores, float* out_lse,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   genrec_profiler* prof);
+int genrec_score_candidates_topk_profiled(const void* H, const void* E, int dtype,
+                                          const int64_t* cand_offsets, const int32_t* cand_ids,
+                                          int B, int D, int64_t M, int64_t nnz, int K,
+                                          int32_t* out_idx, float* out_scores, float* out_lse,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          genrec_profiler* prof);
+
+/* Human-readable name of a genrec_status value (static storage). */
+const char* genrec_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int genrec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GENREC_H */

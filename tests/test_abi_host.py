@@ -1,0 +1,107 @@
+"""C ABI of libgenrec.so on the host: exported symbols, argument validation
+and workspace planning.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from full_catalog_ranking_amd import genrec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(genrec.LIB_PATH):
+        pytest.skip("libgenrec.so not built")
+    return genrec.lib()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "genrec.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(genrec_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported(L):
+    names = header_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(genrec.EXPORTED)
+
+
+def test_status_strings(L):
+    assert genrec.status_string(OK) == "GENREC_OK"
+    assert genrec.status_string(UNSUPPORTED) == "GENREC_ERR_UNSUPPORTED"
+    assert L.genrec_version() == 10000
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced on these paths
+
+
+def call_dense(L, H=FAKE, E=FAKE, dtype=0, B=4, D=64, M=100, K=10, oi=FAKE, os_=FAKE, ol=FAKE,
+               ws=FAKE, wsb=0):
+    return L.genrec_score_lse_topk(H, E, dtype, B, D, M, K, oi, os_, ol, ws, wsb, None)
+
+
+def test_dense_argument_errors(L):
+    assert call_dense(L, H=None) == INVALID
+    assert call_dense(L, E=None) == INVALID
+    assert call_dense(L, oi=None) == INVALID
+    assert call_dense(L, dtype=7) == INVALID
+    assert call_dense(L, B=0) == INVALID
+    assert call_dense(L, D=-8) == INVALID
+    assert call_dense(L, M=0) == INVALID
+    assert call_dense(L, K=0) == INVALID
+    assert call_dense(L, K=1025) == UNSUPPORTED
+    assert call_dense(L, D=12) == UNSUPPORTED            # bf16 needs D % 8 == 0
+    assert call_dense(L, dtype=1, D=12) != UNSUPPORTED   # fp32 needs D % 4 == 0 ...
+    assert call_dense(L, dtype=1, D=6) == UNSUPPORTED
+    assert call_dense(L, M=1 << 31) == UNSUPPORTED
+    assert call_dense(L, H=FAKE + 8) == INVALID          # misaligned
+    assert call_dense(L, ws=None, wsb=1 << 40) == WORKSPACE
+    need = L.genrec_score_lse_topk_workspace(4, 64, 100, 10, 0)
+    assert need > 0
+    assert call_dense(L, wsb=need - 1) == WORKSPACE
+    assert call_dense(L, ws=FAKE + 16, wsb=need) == INVALID  # workspace must be 256-byte aligned
+
+
+def test_candidate_argument_errors(L):
+    f = L.genrec_score_candidates_topk
+    assert f(FAKE, FAKE, 0, None, FAKE, 4, 64, 100, 10, 5, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert f(FAKE, FAKE, 0, FAKE, None, 4, 64, 100, 10, 5, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 4, 64, 100, -1, 5, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 4, 64, 100, 10, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == INVALID
+    need = L.genrec_score_candidates_topk_workspace(4, 64, 100, 10, 5, 0)
+    assert need > 0
+    assert f(FAKE, FAKE, 0, FAKE, FAKE, 4, 64, 100, 10, 5, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert L.genrec_get_device_errors(None, None, None, None) == INVALID
+
+
+def test_workspace_queries(L):
+    assert L.genrec_score_lse_topk_workspace(0, 64, 100, 10, 0) == 0
+    assert L.genrec_score_lse_topk_workspace(4, 64, 100, 2000, 0) == 0
+    big = L.genrec_score_lse_topk_workspace(1024, 4096, 1_000_000, 500, 0)
+    # candidate regions dominate: 8 bytes per (user, item)
+    assert 1024 * 1_000_000 * 8 <= big <= 1024 * 1_000_000 * 8 * 1.05
+    c = L.genrec_score_candidates_topk_workspace(4096, 2048, 1_000_000, 6_400_000, 100, 0)
+    assert 6_400_000 * 8 <= c <= 6_400_000 * 8 * 1.5
+
+
+def test_plan_selection(L):
+    import torch
+    p = genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)
+    assert p["path"] == "mfma" and p["sample"] == 1 and p["UT"] == 4 and p["P"] == 64
+    p = genrec.describe_plan(256, 2048, 100_000, 100, torch.bfloat16)
+    assert p["path"] == "mfma" and p["sample"] == 1 and p["P"] == 256
+    p = genrec.describe_plan(1, 2048, 5000, 100, torch.bfloat16)
+    assert p["path"] == "stream" and p["sample"] == 0
+    p = genrec.describe_plan(4, 256, 5000, 10, torch.float32)
+    assert p["path"] == "stream"
+    p = genrec.describe_plan(9, 64, 50, 64, torch.bfloat16)
+    assert p["path"] == "mfma" and p["sample"] == 0
+    with pytest.raises(genrec.GenrecError):
+        genrec.describe_plan(4, 12, 100, 10, torch.bfloat16)
