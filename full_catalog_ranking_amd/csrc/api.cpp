@@ -30,6 +30,7 @@ int check_common(const void* H, const void* E, int dtype, int B, int D, int64_t 
     if (K > GENREC_KMAX) return GENREC_ERR_UNSUPPORTED;
     if (M >= ((int64_t)1 << 31)) return GENREC_ERR_UNSUPPORTED;
     if (D % (dtype == GENREC_BF16 ? 8 : 4) != 0) return GENREC_ERR_UNSUPPORTED;
+    if (D > GENREC_DMAX) return GENREC_ERR_UNSUPPORTED;
     return GENREC_OK;
 }
 
@@ -195,8 +196,8 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
         a.D = D;
         a.M = M;
         if (p.sample) {
-            a.n_items = p.n_sample;
-            a.stride = p.stride;
+            a.n_tiles = (int)p.sample_tiles;
+            a.tile_stride = (int)p.stride;
             a.UT = p.pre.UT;
             a.P = p.pre.P;
             a.base = p.pre.base;
@@ -205,8 +206,8 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
             if ((st = hip_status(timed(prof, KIND_SAMPLE, s, [&] { return launch_mfma(a, 0, s); }))) != GENREC_OK) return st;
             if ((st = hip_status(timed(prof, KIND_THRESHOLD, s, [&] { return launch_threshold(sample, p.n_sample, K, theta, B, s); }))) != GENREC_OK) return st;
         }
-        a.n_items = M;
-        a.stride = 1;
+        a.n_tiles = (int)ceil_div(M, kMfmaTileItems);
+        a.tile_stride = 1;
         a.UT = p.main.UT;
         a.P = p.main.P;
         a.base = p.main.base;
@@ -228,7 +229,7 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
         a.M = M;
         if (p.sample) {
             a.n_items = p.n_sample;
-            a.stride = p.stride;
+            a.tile_stride = (int)p.stride;
             a.CH = p.pre.CH;
             a.P = p.pre.P;
             a.sample_out = sample;
@@ -236,7 +237,7 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
             if ((st = hip_status(timed(prof, KIND_THRESHOLD, s, [&] { return launch_threshold(sample, p.n_sample, K, theta, B, s); }))) != GENREC_OK) return st;
         }
         a.n_items = M;
-        a.stride = 1;
+        a.tile_stride = 1;
         a.CH = p.main.CH;
         a.P = p.main.P;
         a.sample_out = nullptr;

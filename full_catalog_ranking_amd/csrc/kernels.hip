@@ -13,8 +13,8 @@
 //                      lists: VALU dot products (v_dot2_f32_bf16 / fp32 FMA)
 //                      over gathered rows, one 16-byte load per lane per row
 //                      step, eight rows in flight per wave.
-//  threshold_kernel    per user, the K-th largest score of a strided catalog
-//                      sample: a lower bound of the K-th largest catalog score,
+//  threshold_kernel    per user, the K-th largest score of a sample of whole
+//                      catalog tiles: a lower bound of the K-th largest score,
 //                      used as the candidate threshold of the main pass.
 //  merge_kernel        per user, lse from the per-piece (max, sum-exp) pairs
 //                      and the exact top-K of the candidates (range-narrowing
@@ -24,25 +24,13 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "mfma_layout.hpp"
 
 namespace genrec {
 
 // ---------------------------------------------------------------------------
 // Dense MFMA path
 // ---------------------------------------------------------------------------
-constexpr int MF_TI = 256;   // items per tile (MFMA rows)
-constexpr int MF_TU = 256;   // users per tile (MFMA columns)
-constexpr int MF_BK = 32;    // reduction depth per LDS stage
-constexpr int MF_NS = 4;     // LDS ring stages (3 in flight while one is read)
-constexpr int MF_NT = 256;   // threads (4 waves, 2 x 2 layout of 128 x 128 wave tiles)
-constexpr int MF_ROWB = MF_BK * 2;                   // bytes per staged row (64)
-constexpr int MF_STAGE = (MF_TI + MF_TU) * MF_ROWB;  // 32 KiB per stage
-constexpr int MF_DMA = (MF_TI * MF_ROWB) / (16 * kWave) / (MF_NT / kWave);  // DMA ops per wave per operand per stage (4)
-
-// 16-byte chunk swizzle within a 64-byte staged row: conflict-free
-// ds_read_b128 of 32 consecutive rows at one k-chunk for 32- or 64-bank LDS.
-__device__ __forceinline__ int mf_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-
 __device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_wave_base) {
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
@@ -50,10 +38,11 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_wave_base)
 // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left alone (gfx9 encoding).
 #define MF_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
 
-template <int MODE>
+template <int MODE, bool KTAIL>
 __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[MF_NS][MF_STAGE];
     __shared__ int s_cnt[MF_TU];
+    __shared__ __attribute__((aligned(16))) float s_x[(MF_NT / kWave) * kWave * 16];  // epilogue staging, 16 KiB
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w & 1, wu = w >> 1;
@@ -64,77 +53,81 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     int L = blockIdx.x;
     if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
     const int c = L / a.UT, ut = L - c * a.UT;
-    const int64_t tile0 = (int64_t)c * a.base + min(c, a.rem);
+    const int tile0 = c * a.base + min(c, a.rem);  // first pass-tile of this chunk
     const int ntiles = a.base + (c < a.rem ? 1 : 0);
     const int u0 = ut * MF_TU;
     const int nk = (a.D + MF_BK - 1) / MF_BK;
+    const int D = a.D;
 
     if (MODE == 1) s_cnt[tid] = 0;
+    __syncthreads();
 
-    // DMA mapping: wave w, op j writes staged rows (j*4 + w)*16 .. +16, 1 KiB;
-    // lane l fills row +l/4 at chunk position l%4 with global chunk pos^swz.
-    const int drow = lane >> 2, dpos = lane & 3;
-    int64_t e_off[MF_DMA];  // element offset of this lane's E row (k excluded)
-    int h_off[MF_DMA];
-    int dchunk[MF_DMA];
-    bool h_ok[MF_DMA];
-#pragma unroll
-    for (int j = 0; j < MF_DMA; ++j) {
-        const int row = (j * 4 + w) * 16 + drow;
-        dchunk[j] = (dpos ^ mf_swz(row)) * 8;
-        const int uu = u0 + row;
-        h_ok[j] = uu < a.B;
-        h_off[j] = (h_ok[j] ? uu : 0) * a.D;
-        e_off[j] = row;  // item row within the tile; offset formed per tile
-    }
-    int64_t e_row_off[MF_DMA];  // per tile: element offset of item row
-    auto tile_rows = [&](int64_t j0) {
-#pragma unroll
-        for (int j = 0; j < MF_DMA; ++j) {
-            int64_t jj = j0 + e_off[j];
-            jj = jj < a.n_items ? jj : a.n_items - 1;  // clamp: rows past the end are masked later
-            e_row_off[j] = jj * a.stride * (int64_t)a.D;
-        }
+    // Pass-tile t holds catalog rows [t*G*256, t*G*256 + 256) clipped to M.
+    auto tile_item0 = [&](int t) -> int64_t { return (int64_t)t * a.tile_stride * MF_TI; };
+    auto tile_valid = [&](int t) -> int {
+        const int64_t left = a.M - tile_item0(t);
+        return left < MF_TI ? (int)left : MF_TI;
     };
+
+    // DMA (mfma_layout.hpp): every op of a lane reads one k-chunk at a 32-bit
+    // per-lane offset from a wave-uniform base that advances 64 rows per op.
+    const int drow = mf_dma_row0(w, lane);
+    const int dchunk = mf_dma_kchunk(w, lane) * 8;  // element offset of the k-chunk
+    const uint32_t lane_off = (uint32_t)(drow * D + dchunk);
+    const int h_valid = a.B - u0 < MF_TU ? a.B - u0 : MF_TU;
+    int dma_t = 0;      // pass-tile being loaded
+    int dma_valid = 0;  // its valid rows
     // Issue the DMA of one k-step (both operands) into stage stg.
     auto dma = [&](int stg, int k0) {
         uint8_t* sE = smem[stg];
         uint8_t* sH = smem[stg] + MF_TI * MF_ROWB;
+        const uint16_t* eb = a.E + tile_item0(dma_t) * D + k0;
+        const uint16_t* hb = a.H + (int64_t)u0 * D + k0;
+        int over = 0;
+        if (KTAIL) {  // k chunks past D re-read the row's last chunk; zeroed at use
+            over = k0 + dchunk + 8 - D;
+            over = over > 0 ? over : 0;
+        }
 #pragma unroll
         for (int j = 0; j < MF_DMA; ++j) {
-            const int kk = min(k0 + dchunk[j], a.D - 8);  // k tail: any in-bounds chunk, zero-masked below
-            lds_dma16(a.E + e_row_off[j] + kk, sE + (j * 4 + w) * 1024);
-            lds_dma16(a.H + h_off[j] + kk, sH + (j * 4 + w) * 1024);
+            const uint16_t* ep;
+            const uint16_t* hp;
+            if (dma_valid == MF_TI) ep = eb + (int64_t)j * 64 * D + lane_off;
+            else ep = eb + (int64_t)mf_src_row(mf_dma_row(w, lane, j), dma_valid) * D + dchunk;
+            if (h_valid == MF_TU) hp = hb + (int64_t)j * 64 * D + lane_off;
+            else hp = hb + (int64_t)mf_src_row(mf_dma_row(w, lane, j), h_valid) * D + dchunk;
+            if (KTAIL) { ep -= over; hp -= over; }
+            lds_dma16(ep, sE + mf_dma_lds_byte(w, 0, j) );
+            lds_dma16(hp, sH + mf_dma_lds_byte(w, 0, j) );
         }
     };
 
     f32x16_t acc[4][4];
-    auto compute = [&](int stg, int k0) {
+    // MFMA operand fragments of one 16-deep k-slice: lane holds 8 consecutive
+    // k of row (lane & 31) of each 32-row block, k-chunk (lane >> 5).
+    struct Frag {
+        bf16x8_t a[4], b[4];
+    };
+    auto load_frag = [&](Frag& f, int stg, int ks, int k0) {
         const uint8_t* sE = smem[stg];
         const uint8_t* sH = smem[stg] + MF_TI * MF_ROWB;
+        const int chunk = ks * 2 + (lane >> 5);
+        const bool kin = !KTAIL || k0 + chunk * 8 < a.D;  // k past D: zero the user side
 #pragma unroll
-        for (int ks = 0; ks < MF_BK / 16; ++ks) {
-            const int chunk = ks * 2 + (lane >> 5);
-            // k positions past D hold whatever in-bounds chunk was loaded: zero them
-            const bool kin = k0 + chunk * 8 < a.D;
-            bf16x8_t av[4], bv[4];
+        for (int ib = 0; ib < 4; ++ib)
+            f.a[ib] = *(const bf16x8_t*)(sE + mf_frag_lds_byte(wi * 128 + ib * 32 + (lane & 31), chunk));
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib) {
-                const int row = wi * 128 + ib * 32 + (lane & 31);
-                av[ib] = *(const bf16x8_t*)(sE + row * MF_ROWB + ((chunk ^ mf_swz(row)) << 4));
-            }
-#pragma unroll
-            for (int ub = 0; ub < 4; ++ub) {
-                const int row = wu * 128 + ub * 32 + (lane & 31);
-                bv[ub] = *(const bf16x8_t*)(sH + row * MF_ROWB + ((chunk ^ mf_swz(row)) << 4));
-                if ((a.D % MF_BK) != 0 && !kin) bv[ub] = bf16x8_t{};
-            }
-#pragma unroll
-            for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-                for (int ub = 0; ub < 4; ++ub)
-                    acc[ib][ub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ib], bv[ub], acc[ib][ub], 0, 0, 0);
+        for (int ub = 0; ub < 4; ++ub) {
+            f.b[ub] = *(const bf16x8_t*)(sH + mf_frag_lds_byte(wu * 128 + ub * 32 + (lane & 31), chunk));
+            if (!kin) f.b[ub] = bf16x8_t{};
         }
+    };
+    auto mma = [&](const Frag& f) {
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+            for (int ub = 0; ub < 4; ++ub)
+                acc[ib][ub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ib], f.b[ub], acc[ib][ub], 0, 0, 0);
     };
 
     // Per lane: user column (lane & 31) of each 32-wide user block ub; the
@@ -149,70 +142,63 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         float t = -FLT_MAX;
         if (MODE == 1 && a.theta != nullptr && u < a.B) t = fmaxf(a.theta[u], -FLT_MAX);
         th_[ub] = (u < a.B) ? t : INFINITY;  // users past B never append
-        (void)h_ok;
     }
-    const int64_t chunk_item0 = tile0 * MF_TI;
+    const int64_t chunk_item0 = tile_item0(tile0);  // catalog row of the chunk start (mode 1: G = 1)
     const int lrow0 = wi * 128 + (lane >> 5) * 4;
+    const int64_t n_pass = (int64_t)a.n_tiles * MF_TI;  // mode 0: row length of sample_out
 
-    auto epilogue = [&](int64_t j0) {
-        const int64_t left = a.n_items - j0;
-        const int lim = left < MF_TI ? (int)left : MF_TI;  // valid tile rows
-        const bool full = lim == MF_TI;
+    auto epilogue = [&](int t) {
+        const int lim = tile_valid(t);  // valid tile rows
+        const int64_t j0 = tile_item0(t);
+        float* xs = s_x + w * (16 * kWave) + lane * 16;  // this lane's 16-float slot
 #pragma unroll
         for (int ub = 0; ub < 4; ++ub) {
             const int ul = wu * 128 + ub * 32 + (lane & 31);
             const int u = u0 + ul;
             if (MODE == 0) {
                 if (u < a.B) {
-                    float* orow = a.sample_out + (int64_t)u * a.n_items + j0;
+                    float* orow = a.sample_out + (int64_t)u * n_pass + (int64_t)t * MF_TI;
 #pragma unroll
                     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int jl = lrow0 + ib * 32 + (r >> 2) * 8 + (r & 3);
-                            if (full || jl < lim) orow[jl] = acc[ib][ub][r];
+                            if (jl < lim) orow[jl] = acc[ib][ub][r];
                         }
                 }
                 continue;
             }
-            // One pass against a reference max: the running max, or the first
-            // element of the tile on the first tile.  Terms are exp(s - ref);
-            // the sum is rescaled to the new running max afterwards.  A tile
-            // whose scores exceed ref by more than 64 nats (not finite in the
-            // sum's range) is summed again against its own max.
-            float ref = m_[ub];
-            if (ref == -INFINITY) ref = acc[0][ub][0];
-            const float rb = ref * kLog2e;
+            // Sum of exp(s - ref) against a reference: the running max (or, on
+            // the first tile, row 0 of the tile).  A score more than 64 nats
+            // above the reference moves the reference there first, so no term
+            // can overflow; terms far below it underflow harmlessly.
             const float th = th_[ub];
-            float tmax = -INFINITY, lsum = 0.f;
+            float ref = m_[ub] == -INFINITY ? acc[0][ub][0] : m_[ub];
+            float rb = ref * kLog2e, lsum = 0.f;
 #pragma unroll
-            for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                *(f32x16_t*)xs = acc[ib][ub];  // via LDS: one score live at a time
+#pragma unroll 2
                 for (int r = 0; r < 16; ++r) {
                     const int jl = lrow0 + ib * 32 + (r >> 2) * 8 + (r & 3);
-                    const float s = (full || jl < lim) ? acc[ib][ub][r] : -INFINITY;
-                    tmax = fmaxf(tmax, s);
+                    if (jl >= lim) continue;
+                    const float s = xs[r];
+                    if (s > ref + 64.f) {
+                        lsum *= fast_exp2((ref - s) * kLog2e);
+                        ref = s;
+                        rb = s * kLog2e;
+                    }
                     lsum += fast_exp2(fmaf(s, kLog2e, -rb));
                     if (s >= th) {
                         const int pos = atomicAdd(&s_cnt[ul], 1);
                         a.keys[(int64_t)u * a.M + chunk_item0 + pos] = rank_key(s, (uint32_t)(j0 + jl));
                     }
                 }
-            if (tmax == -INFINITY) continue;  // every item of this lane masked
-            if (tmax - ref > 64.f) {
-                lsum = 0.f;
-                const float tb = tmax * kLog2e;
-                for (int ib = 0; ib < 4; ++ib)
-                    for (int r = 0; r < 16; ++r) {
-                        const int jl = lrow0 + ib * 32 + (r >> 2) * 8 + (r & 3);
-                        if (full || jl < lim) lsum += fast_exp2(fmaf(acc[ib][ub][r], kLog2e, -tb));
-                    }
-                ref = tmax;
             }
-            // l_ * e^{m_} + lsum * e^{ref}  ->  new (m, l) with m = max(m_, tmax)
-            const float mnew = fmaxf(m_[ub], tmax);
-            l_[ub] = l_[ub] * fast_exp2((m_[ub] - mnew) * kLog2e) + lsum * fast_exp2((ref - mnew) * kLog2e);
-            m_[ub] = mnew;
+            LseState st{m_[ub], l_[ub]};
+            st.merge(ref, lsum);
+            m_[ub] = st.m;
+            l_[ub] = st.l;
         }
     };
 
@@ -225,7 +211,10 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     const int total = ntiles * nk;
     int lt = 0, lk = 0;  // next step to load
     auto issue = [&](int step) {
-        if (lk == 0) tile_rows((tile0 + lt) * MF_TI);
+        if (lk == 0) {
+            dma_t = tile0 + lt;
+            dma_valid = tile_valid(dma_t);
+        }
         dma(step % MF_NS, lk * MF_BK);
         if (++lk == nk) { lk = 0; ++lt; }
     };
@@ -236,6 +225,11 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     else MF_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
 
+    // Each step: read slice 1 of the current stage while slice 0 runs on the
+    // matrix cores, meet at the barrier, then read slice 0 of the next stage
+    // while slice 1 runs.  LDS latency hides behind 16 MFMAs either way.
+    Frag f0, f1;
+    load_frag(f0, 0, 0, 0);
     int step = 0;
     for (int t = 0; t < ntiles; ++t) {
 #pragma unroll
@@ -244,14 +238,19 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             for (int ub = 0; ub < 4; ++ub) acc[ib][ub] = f32x16_t{};
         for (int k = 0; k < nk; ++k, ++step) {
             if (step + MF_NS - 1 < total) issue(step + MF_NS - 1);
-            compute(step % MF_NS, k * MF_BK);
+            const int stg = step % MF_NS;
+            load_frag(f1, stg, 1, k * MF_BK);
+            mma(f0);
             const int ahead = min(total - 1 - step, MF_NS - 1);  // steps already issued beyond this one
             if (ahead >= 3) MF_WAIT_VMCNT(2 * 2 * MF_DMA);
             else if (ahead == 2) MF_WAIT_VMCNT(2 * MF_DMA);
             else MF_WAIT_VMCNT(0);
             __builtin_amdgcn_s_barrier();
+            // (on the last step this reads a stale stage; the values are never used)
+            load_frag(f0, (step + 1) % MF_NS, 0, k + 1 < nk ? (k + 1) * MF_BK : 0);
+            mma(f1);
         }
-        epilogue((tile0 + t) * MF_TI);
+        epilogue(tile0 + t);
     }
 
     if (MODE == 1) {
@@ -394,7 +393,8 @@ __global__ __launch_bounds__(ST_NT) void stream_score_kernel(StreamArgs a) {
 #pragma unroll
             for (int u = 0; u < ST_U; ++u) {
                 ok[u] = g0 + u < n;
-                item[u] = (jbeg + g0 + u) * a.stride;
+                const int64_t j = jbeg + g0 + u;  // pass index -> catalog row (tile-strided sample)
+                item[u] = (j >> 8) * a.tile_stride * 256 + (j & 255);
             }
         }
         float acc[ST_U];
@@ -878,8 +878,14 @@ __global__ __launch_bounds__(PL_NT) void cand_plan_kernel(CandPlanArgs a) {
 // ---------------------------------------------------------------------------
 hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s) {
     const int grid = a.UT * a.P;
-    if (mode == 0) hipLaunchKernelGGL(mfma_score_kernel<0>, dim3(grid), dim3(MF_NT), 0, s, a);
-    else hipLaunchKernelGGL(mfma_score_kernel<1>, dim3(grid), dim3(MF_NT), 0, s, a);
+    const bool ktail = (a.D % MF_BK) != 0;
+    if (mode == 0) {
+        if (ktail) hipLaunchKernelGGL((mfma_score_kernel<0, true>), dim3(grid), dim3(MF_NT), 0, s, a);
+        else hipLaunchKernelGGL((mfma_score_kernel<0, false>), dim3(grid), dim3(MF_NT), 0, s, a);
+    } else {
+        if (ktail) hipLaunchKernelGGL((mfma_score_kernel<1, true>), dim3(grid), dim3(MF_NT), 0, s, a);
+        else hipLaunchKernelGGL((mfma_score_kernel<1, false>), dim3(grid), dim3(MF_NT), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -15,9 +15,9 @@ struct MfmaArgs {
     const uint16_t* E;
     int B, D;
     int64_t M;
-    int64_t n_items, stride;  // items j < n_items, catalog row j * stride
-    int UT, P, base, rem;     // user tiles; P chunks of base(+1) item tiles
-    float* sample_out;        // mode 0: [B][n_items] scores
+    int n_tiles, tile_stride; // pass-tile t = catalog rows [t*G*256, +256) clipped to M, G = tile_stride
+    int UT, P, base, rem;     // user tiles; P chunks of base(+1) pass-tiles
+    float* sample_out;        // mode 0: [B][n_tiles * 256] scores
     const float* theta;       // mode 1: [B] candidate thresholds (or null)
     uint64_t* keys;           // mode 1: candidate regions, [B][M]
     float* pm;                // per piece (user b, chunk c) at b*P + c
@@ -37,7 +37,8 @@ struct StreamArgs {
     const void* E;
     int B, D;
     int64_t M;
-    int64_t n_items, stride;  // dense modes
+    int64_t n_items;          // dense modes: pass items j < n_items
+    int tile_stride;          // dense modes: item j is catalog row (j/256)*G*256 + j%256, G = tile_stride
     int64_t CH;               // dense modes: items per chunk
     int P;                    // dense modes: chunks per user
     const int32_t* ids;       // candidate mode

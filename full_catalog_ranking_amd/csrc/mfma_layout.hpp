@@ -1,0 +1,45 @@
+// Tile geometry of the MFMA scoring kernel: which catalog / user row and
+// k-chunk every lane moves into LDS, and where the MFMA fragment reads find
+// it.  Host+device so that the host test build can enumerate every case and
+// check bounds and the write/read agreement without a GPU.
+#pragma once
+
+#if defined(__HIPCC__)
+#define GENREC_HD __host__ __device__
+#else
+#define GENREC_HD
+#endif
+
+namespace genrec {
+
+constexpr int MF_TI = 256;   // items per tile (MFMA rows)
+constexpr int MF_TU = 256;   // users per tile (MFMA columns)
+constexpr int MF_BK = 32;    // reduction depth per LDS stage
+constexpr int MF_NS = 4;     // LDS ring stages (3 in flight while one is read)
+constexpr int MF_NT = 256;   // threads: 4 waves in a 2 x 2 layout of 128 x 128 wave tiles
+constexpr int MF_ROWB = MF_BK * 2;                   // bytes per staged row (64)
+constexpr int MF_STAGE = (MF_TI + MF_TU) * MF_ROWB;  // 32 KiB per stage
+constexpr int MF_DMA = 4;    // 16-byte DMA ops per lane per operand per stage
+static_assert(MF_DMA * 4 * 64 * 16 == MF_TI * MF_ROWB, "DMA ops must cover one operand stage");
+
+// 16-byte chunk swizzle within a 64-byte staged row: conflict-free
+// ds_read_b128 of 32 consecutive rows at one k-chunk for 32- or 64-bank LDS.
+GENREC_HD inline int mf_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// DMA: wave w, op j writes the 1 KiB of staged rows (j*4 + w)*16 .. +16; lane
+// l writes 16 bytes at l*16, i.e. staged row (j*4 + w)*16 + l/4 at chunk
+// position l%4, holding global k-chunk (l%4) ^ swz(row).
+GENREC_HD inline int mf_dma_row0(int w, int lane) { return w * 16 + (lane >> 2); }  // staged row of op 0
+GENREC_HD inline int mf_dma_row(int w, int lane, int j) { return mf_dma_row0(w, lane) + 64 * j; }
+// swz(row) is the same for every op j of a lane (64 j changes neither bit
+// field it reads), so one k-chunk offset serves all ops.
+GENREC_HD inline int mf_dma_kchunk(int w, int lane) { return (lane & 3) ^ mf_swz(mf_dma_row0(w, lane)); }
+GENREC_HD inline int mf_dma_lds_byte(int w, int lane, int j) { return (j * 4 + w) * 1024 + lane * 16; }
+// Row actually read for staged row `row` of a tile with `valid` rows: rows
+// past the end re-read the last valid row (their scores are masked later).
+GENREC_HD inline int mf_src_row(int row, int valid) { return row < valid ? row : valid - 1; }
+
+// Fragment read: byte offset of (staged row, k-chunk) within an operand stage.
+GENREC_HD inline int mf_frag_lds_byte(int row, int kchunk) { return row * MF_ROWB + ((kchunk ^ mf_swz(row)) << 4); }
+
+}  // namespace genrec

@@ -14,8 +14,8 @@ constexpr int kMfmaTileItems = 256;    // items per MFMA tile
 constexpr int kMfmaTileUsers = 256;    // users per MFMA tile
 constexpr int kStreamMaxB = 8;         // bf16 batches up to this size use the VALU path
 constexpr int64_t kSampleMinM = 65536; // smaller catalogs skip the threshold pre-pass
-constexpr int64_t kSampleMinStride = 32;
-constexpr int64_t kSampleMax = 32768;  // sampled items per user at most
+constexpr int64_t kSampleMinStride = 32; // sample every G-th catalog tile, G >= 32
+constexpr int64_t kSampleMaxTiles = 128; // sampled items per user at most 128 * 256
 constexpr int64_t kStreamPieces = 2048;  // target work pieces of the VALU path
 constexpr int64_t kStreamChunkAlign = 32;
 constexpr int kCandPiece = 256;        // candidate entries per piece (matches the kernels)
@@ -31,17 +31,19 @@ struct Chunking {
 struct DensePlan {
     bool mfma = false;
     bool sample = false;
-    int64_t stride = 1, n_sample = 0;
+    int64_t stride = 1;        // G: the sample holds catalog tiles 0, G, 2G, ... (full tiles only)
+    int64_t sample_tiles = 0;  // number of sampled 256-row tiles
+    int64_t n_sample = 0;      // sampled items = 256 * sample_tiles
     Chunking main, pre;
     int64_t n_pieces = 0;
     size_t off_hdr = 0, off_theta = 0, off_sample = 0, off_pm = 0, off_pl = 0, off_pcnt = 0,
            off_preg = 0, off_keys = 0, total = 0;
 };
 
-inline Chunking chunk_mfma(int B, int64_t n_items) {
+inline Chunking chunk_mfma(int B, int64_t n_tiles) {
     Chunking c;
     c.UT = (int)ceil_div(B, kMfmaTileUsers);
-    const int64_t nt = ceil_div(n_items, kMfmaTileItems);
+    const int64_t nt = n_tiles;
     const int64_t want = std::max<int64_t>(1, kNumCU / c.UT);
     c.P = (int)std::max<int64_t>(1, std::min(nt, want));
     c.base = (int)(nt / c.P);
@@ -63,11 +65,13 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
     (void)D;
     DensePlan p;
     p.mfma = dtype == 0 && B > kStreamMaxB;
-    p.stride = std::max<int64_t>(kSampleMinStride, ceil_div(M, kSampleMax));
-    p.n_sample = ceil_div(M, p.stride);
+    const int64_t full_tiles = M / kMfmaTileItems;
+    p.stride = std::max<int64_t>(kSampleMinStride, ceil_div(full_tiles, kSampleMaxTiles));
+    p.sample_tiles = ceil_div(full_tiles, p.stride);
+    p.n_sample = p.sample_tiles * kMfmaTileItems;
     p.sample = M >= kSampleMinM && p.n_sample >= 4 * (int64_t)K;
-    p.main = p.mfma ? chunk_mfma(B, M) : chunk_stream(B, M);
-    if (p.sample) p.pre = p.mfma ? chunk_mfma(B, p.n_sample) : chunk_stream(B, p.n_sample);
+    p.main = p.mfma ? chunk_mfma(B, ceil_div(M, kMfmaTileItems)) : chunk_stream(B, M);
+    if (p.sample) p.pre = p.mfma ? chunk_mfma(B, p.sample_tiles) : chunk_stream(B, p.n_sample);
     p.n_pieces = (int64_t)B * p.main.P;
     size_t o = 0;
     p.off_hdr = o;

@@ -39,8 +39,8 @@
  *    When fewer than K items exist (K > M, or a list shorter than K) the tail
  *    is padded with id -1 and score -inf; an empty set gives lse = -inf.
  *  - Supported: 1 <= K <= GENREC_KMAX, B >= 1, 1 <= M < 2^31,
- *    D >= 1 with D % 8 == 0 (bf16) or D % 4 == 0 (f32), H and E 16-byte
- *    aligned.  Non-finite inputs are not supported.
+ *    1 <= D <= GENREC_DMAX with D % 8 == 0 (bf16) or D % 4 == 0 (f32), H and
+ *    E 16-byte aligned.  Non-finite inputs are not supported.
  *  - Entry points never abort and no C++ exception crosses the ABI.
  */
 #ifndef GENREC_H
@@ -64,6 +64,7 @@ typedef enum {
 typedef enum { GENREC_BF16 = 0, GENREC_F32 = 1 } genrec_dtype;
 
 #define GENREC_KMAX 1024
+#define GENREC_DMAX 65536
 
 /* Workspace bytes needed by genrec_score_lse_topk for these sizes (0 if the
  * arguments are unsupported).  The value depends only on the arguments. */

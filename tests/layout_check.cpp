@@ -1,0 +1,88 @@
+// Host check of the MFMA kernel's tile geometry (mfma_layout.hpp): every DMA
+// write lands where the fragment reads look for it, every source row is in
+// bounds for every partial-tile size, and the per-lane 32-bit fast-path
+// offset equals the 64-bit row offset.  Exit status 0 = all checks passed.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../full_catalog_ranking_amd/csrc/mfma_layout.hpp"
+
+using namespace genrec;
+
+static int fails = 0;
+#define CHECK(c, ...)                                 \
+    do {                                              \
+        if (!(c)) {                                   \
+            if (fails < 20) printf(__VA_ARGS__), printf("\n"); \
+            ++fails;                                  \
+        }                                             \
+    } while (0)
+
+int main() {
+    // 1. write/read agreement and coverage of one operand stage
+    static int owner[MF_TI * MF_ROWB / 16];
+    memset(owner, -1, sizeof owner);
+    for (int w = 0; w < 4; ++w)
+        for (int lane = 0; lane < 64; ++lane)
+            for (int j = 0; j < MF_DMA; ++j) {
+                const int row = mf_dma_row(w, lane, j);
+                const int kc = mf_dma_kchunk(w, lane);
+                CHECK(row >= 0 && row < MF_TI, "row %d out of tile", row);
+                CHECK(kc >= 0 && kc < MF_BK / 8, "k-chunk %d out of stage", kc);
+                CHECK(kc == ((lane & 3) ^ mf_swz(row)), "swizzle depends on op: w%d l%d j%d", w, lane, j);
+                const int wr = mf_dma_lds_byte(w, lane, j);
+                CHECK(wr == mf_dma_lds_byte(w, 0, j) + lane * 16, "DMA is not wave-contiguous");
+                CHECK(wr == mf_frag_lds_byte(row, kc), "DMA byte %d != fragment byte %d (row %d kc %d)", wr,
+                      mf_frag_lds_byte(row, kc), row, kc);
+                const int slot = wr / 16;
+                CHECK(slot >= 0 && slot < MF_TI * MF_ROWB / 16, "slot out of stage");
+                if (slot >= 0 && slot < MF_TI * MF_ROWB / 16) {
+                    CHECK(owner[slot] == -1, "slot %d written twice", slot);
+                    owner[slot] = row * 4 + kc;
+                }
+            }
+    for (int s = 0; s < MF_TI * MF_ROWB / 16; ++s) CHECK(owner[s] != -1, "slot %d never written", s);
+    // every (row, k-chunk) pair is read from a distinct slot
+    static int seen[MF_TI * MF_ROWB / 16];
+    memset(seen, 0, sizeof seen);
+    for (int row = 0; row < MF_TI; ++row)
+        for (int kc = 0; kc < MF_BK / 8; ++kc) {
+            const int b = mf_frag_lds_byte(row, kc);
+            CHECK(b >= 0 && b + 16 <= MF_TI * MF_ROWB && b % 16 == 0, "fragment byte %d out of stage", b);
+            if (b >= 0 && b + 16 <= MF_TI * MF_ROWB) ++seen[b / 16];
+        }
+    for (int s = 0; s < MF_TI * MF_ROWB / 16; ++s) CHECK(seen[s] == 1, "slot %d read %d times", s, seen[s]);
+
+    // 2. source rows stay inside partial tiles of every size
+    for (int valid = 1; valid <= MF_TI; ++valid)
+        for (int w = 0; w < 4; ++w)
+            for (int lane = 0; lane < 64; ++lane)
+                for (int j = 0; j < MF_DMA; ++j) {
+                    const int r = mf_src_row(mf_dma_row(w, lane, j), valid);
+                    CHECK(r >= 0 && r < valid, "src row %d outside [0,%d)", r, valid);
+                    if (mf_dma_row(w, lane, j) < valid) CHECK(r == mf_dma_row(w, lane, j), "valid row moved");
+                }
+
+    // 3. the 32-bit fast-path offset equals the 64-bit row offset
+    const int Ds[] = {8, 64, 200, 256, 2048, 4096, 65536};
+    for (int D : Ds)
+        for (int w = 0; w < 4; ++w)
+            for (int lane = 0; lane < 64; ++lane) {
+                const int64_t lane_off = (int64_t)mf_dma_row0(w, lane) * D + mf_dma_kchunk(w, lane) * 8;
+                CHECK(lane_off >= 0 && lane_off < ((int64_t)1 << 31), "lane offset overflows 32 bits");
+                for (int j = 0; j < MF_DMA; ++j) {
+                    const int64_t fast = (int64_t)j * 64 * D + lane_off;
+                    const int64_t slow = (int64_t)mf_src_row(mf_dma_row(w, lane, j), MF_TI) * D + mf_dma_kchunk(w, lane) * 8;
+                    CHECK(fast == slow, "fast %lld != slow %lld", (long long)fast, (long long)slow);
+                    CHECK(fast + 8 <= (int64_t)MF_TI * D + (MF_BK - D % MF_BK) % MF_BK + MF_BK,
+                          "offset past the tile");
+                }
+            }
+    if (fails) {
+        printf("%d layout checks failed\n", fails);
+        return 1;
+    }
+    printf("layout ok\n");
+    return 0;
+}
