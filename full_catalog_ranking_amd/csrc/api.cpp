@@ -215,6 +215,7 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
         a.sample_out = nullptr;
         a.theta = p.sample ? theta : nullptr;
         a.keys = keys;
+        a.key_stride = p.key_stride;
         a.pm = pm;
         a.pl = pl;
         a.pcnt = pcnt;
@@ -252,7 +253,7 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
     MergeArgs m{};
     m.B = B;
     m.K = K;
-    m.P = p.main.P;
+    m.P = p.main.P * p.pieces_per_chunk;
     m.piece_begin = nullptr;
     m.keys = keys;
     m.pm = pm;

@@ -41,8 +41,6 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_wave_base)
 template <int MODE, bool KTAIL>
 __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[MF_NS][MF_STAGE];
-    __shared__ int s_cnt[MF_TU];
-    __shared__ __attribute__((aligned(16))) float s_x[(MF_NT / kWave) * kWave * 16];  // epilogue staging, 16 KiB
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w & 1, wu = w >> 1;
@@ -59,9 +57,6 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     const int nk = (a.D + MF_BK - 1) / MF_BK;
     const int D = a.D;
 
-    if (MODE == 1) s_cnt[tid] = 0;
-    __syncthreads();
-
     // Pass-tile t holds catalog rows [t*G*256, t*G*256 + 256) clipped to M.
     auto tile_item0 = [&](int t) -> int64_t { return (int64_t)t * a.tile_stride * MF_TI; };
     auto tile_valid = [&](int t) -> int {
@@ -69,36 +64,31 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         return left < MF_TI ? (int)left : MF_TI;
     };
 
-    // DMA (mfma_layout.hpp): every op of a lane reads one k-chunk at a 32-bit
-    // per-lane offset from a wave-uniform base that advances 64 rows per op.
-    const int drow = mf_dma_row0(w, lane);
-    const int dchunk = mf_dma_kchunk(w, lane) * 8;  // element offset of the k-chunk
-    const uint32_t lane_off = (uint32_t)(drow * D + dchunk);
+    // ---- DMA (geometry in mfma_layout.hpp) --------------------------------
+    // Every op of a lane reads one k-chunk of one row at a 32-bit per-lane
+    // offset from a wave-uniform base.  Rows past the end of a partial tile
+    // re-read the last valid row; their scores are masked in the epilogue.
+    const int dchunk = mf_dma_kchunk(w, lane) * 8;  // element offset of the lane's k-chunk
     const int h_valid = a.B - u0 < MF_TU ? a.B - u0 : MF_TU;
-    int dma_t = 0;      // pass-tile being loaded
-    int dma_valid = 0;  // its valid rows
-    // Issue the DMA of one k-step (both operands) into stage stg.
-    auto dma = [&](int stg, int k0) {
-        uint8_t* sE = smem[stg];
-        uint8_t* sH = smem[stg] + MF_TI * MF_ROWB;
-        const uint16_t* eb = a.E + tile_item0(dma_t) * D + k0;
-        const uint16_t* hb = a.H + (int64_t)u0 * D + k0;
-        int over = 0;
-        if (KTAIL) {  // k chunks past D re-read the row's last chunk; zeroed at use
-            over = k0 + dchunk + 8 - D;
-            over = over > 0 ? over : 0;
+    uint32_t h_off[MF_DMA];
+#pragma unroll
+    for (int j = 0; j < MF_DMA; ++j) h_off[j] = (uint32_t)(mf_src_row(mf_dma_row(w, lane, j), h_valid) * D + dchunk);
+    const uint16_t* h_tile = a.H + (int64_t)u0 * D;
+
+    auto dma = [&](int stg, int t, int k0) {
+        const int valid = tile_valid(t);
+        const uint16_t* eb = a.E + tile_item0(t) * D + k0;
+        const uint16_t* hb = h_tile + k0;
+        uint32_t over = 0;  // k-chunks past D re-read the row's last chunk (zeroed at use)
+        if (KTAIL) {
+            const int o = k0 + dchunk + 8 - D;
+            over = o > 0 ? (uint32_t)o : 0u;
         }
 #pragma unroll
         for (int j = 0; j < MF_DMA; ++j) {
-            const uint16_t* ep;
-            const uint16_t* hp;
-            if (dma_valid == MF_TI) ep = eb + (int64_t)j * 64 * D + lane_off;
-            else ep = eb + (int64_t)mf_src_row(mf_dma_row(w, lane, j), dma_valid) * D + dchunk;
-            if (h_valid == MF_TU) hp = hb + (int64_t)j * 64 * D + lane_off;
-            else hp = hb + (int64_t)mf_src_row(mf_dma_row(w, lane, j), h_valid) * D + dchunk;
-            if (KTAIL) { ep -= over; hp -= over; }
-            lds_dma16(ep, sE + mf_dma_lds_byte(w, 0, j) );
-            lds_dma16(hp, sH + mf_dma_lds_byte(w, 0, j) );
+            const uint32_t eo = (uint32_t)(mf_src_row(mf_dma_row(w, lane, j), valid) * D + dchunk) - over;
+            lds_dma16(eb + eo, smem[stg] + mf_dma_lds_byte(w, 0, j));
+            lds_dma16(hb + (h_off[j] - over), smem[stg] + MF_TI * MF_ROWB + mf_dma_lds_byte(w, 0, j));
         }
     };
 
@@ -112,7 +102,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         const uint8_t* sE = smem[stg];
         const uint8_t* sH = smem[stg] + MF_TI * MF_ROWB;
         const int chunk = ks * 2 + (lane >> 5);
-        const bool kin = !KTAIL || k0 + chunk * 8 < a.D;  // k past D: zero the user side
+        const bool kin = !KTAIL || k0 + chunk * 8 < D;  // k past D: zero the user side
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
             f.a[ib] = *(const bf16x8_t*)(sE + mf_frag_lds_byte(wi * 128 + ib * 32 + (lane & 31), chunk));
@@ -130,27 +120,37 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                 acc[ib][ub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ib], f.b[ub], acc[ib][ub], 0, 0, 0);
     };
 
-    // Per lane: user column (lane & 31) of each 32-wide user block ub; the
-    // accumulator element r of block (ib, ub) is item row
-    //   wi*128 + ib*32 + (r/4)*8 + (lane/32)*4 + r%4  of the tile.
+    // ---- epilogue state ---------------------------------------------------
+    // Lane owns user column (lane & 31) of each 32-wide user block ub; the
+    // accumulator element r of block (ib, ub) is tile row
+    //   wi*128 + ib*32 + (r/4)*8 + (lane/32)*4 + r%4.
+    // Per (user, chunk) the four lane groups g = (wi, lane/32) that share a
+    // user each own a quarter of the chunk's candidate region and a piece
+    // record: no atomics, no cross-lane combine.
+    const int g = wi * 2 + (lane >> 5);
+    const int lrow0 = wi * 128 + (lane >> 5) * 4;
+    const int64_t chunk_item0 = tile_item0(tile0);  // (mode 1: G = 1)
+    const int64_t n_pass = (int64_t)a.n_tiles * MF_TI;  // mode 0: row length of sample_out
     float m_[4], l_[4], th_[4];
+    int cnt_[4];
 #pragma unroll
     for (int ub = 0; ub < 4; ++ub) {
         const int u = u0 + wu * 128 + ub * 32 + (lane & 31);
         m_[ub] = -INFINITY;
         l_[ub] = 0.f;
+        cnt_[ub] = 0;
         float t = -FLT_MAX;
         if (MODE == 1 && a.theta != nullptr && u < a.B) t = fmaxf(a.theta[u], -FLT_MAX);
         th_[ub] = (u < a.B) ? t : INFINITY;  // users past B never append
     }
-    const int64_t chunk_item0 = tile_item0(tile0);  // catalog row of the chunk start (mode 1: G = 1)
-    const int lrow0 = wi * 128 + (lane >> 5) * 4;
-    const int64_t n_pass = (int64_t)a.n_tiles * MF_TI;  // mode 0: row length of sample_out
 
-    auto epilogue = [&](int t) {
+    auto epilogue = [&](int t, int stg) {
         const int lim = tile_valid(t);  // valid tile rows
         const int64_t j0 = tile_item0(t);
-        float* xs = s_x + w * (16 * kWave) + lane * 16;  // this lane's 16-float slot
+        // Scores go through LDS one quad at a time (it keeps the live register
+        // set small): quad q of a block sits in this wave's own DMA chunk q of
+        // the stage just consumed -- only this wave's next DMA rewrites it.
+        uint8_t* xs = smem[stg] + lane * 16;
 #pragma unroll
         for (int ub = 0; ub < 4; ++ub) {
             const int ul = wu * 128 + ub * 32 + (lane & 31);
@@ -175,23 +175,30 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             const float th = th_[ub];
             float ref = m_[ub] == -INFINITY ? acc[0][ub][0] : m_[ub];
             float rb = ref * kLog2e, lsum = 0.f;
+            uint64_t* kreg = a.keys + (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles;
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
-                *(f32x16_t*)xs = acc[ib][ub];  // via LDS: one score live at a time
-#pragma unroll 2
-                for (int r = 0; r < 16; ++r) {
-                    const int jl = lrow0 + ib * 32 + (r >> 2) * 8 + (r & 3);
-                    if (jl >= lim) continue;
-                    const float s = xs[r];
-                    if (s > ref + 64.f) {
-                        lsum *= fast_exp2((ref - s) * kLog2e);
-                        ref = s;
-                        rb = s * kLog2e;
-                    }
-                    lsum += fast_exp2(fmaf(s, kLog2e, -rb));
-                    if (s >= th) {
-                        const int pos = atomicAdd(&s_cnt[ul], 1);
-                        a.keys[(int64_t)u * a.M + chunk_item0 + pos] = rank_key(s, (uint32_t)(j0 + jl));
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *(float4*)(xs + mf_dma_lds_byte(w, 0, q)) =
+                        make_float4(acc[ib][ub][4 * q], acc[ib][ub][4 * q + 1], acc[ib][ub][4 * q + 2], acc[ib][ub][4 * q + 3]);
+#pragma unroll 1
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v4 = *(const float4*)(xs + mf_dma_lds_byte(w, 0, q));
+                    const float vs[4] = {v4.x, v4.y, v4.z, v4.w};
+                    const int jq = lrow0 + ib * 32 + q * 8;  // rows jq .. jq+3
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int jl = jq + e;
+                        if (jl >= lim) continue;
+                        const float s = vs[e];
+                        if (s > ref + 64.f) {
+                            lsum *= fast_exp2((ref - s) * kLog2e);
+                            ref = s;
+                            rb = s * kLog2e;
+                        }
+                        lsum += fast_exp2(fmaf(s, kLog2e, -rb));
+                        if (s >= th) kreg[cnt_[ub]++] = rank_key(s, (uint32_t)(j0 + jl));
                     }
                 }
             }
@@ -202,80 +209,63 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         }
     };
 
-    // Pipeline over the flat sequence of (tile, k-step): the DMA of step+3
-    // is issued before the MFMAs of step; every wave then waits until its
-    // own DMA of step+1 has landed (vector-memory loads retire in order, so
-    // "at most the two youngest steps outstanding" suffices even with the
-    // epilogue's stores in between) and meets the others at the barrier,
-    // which also retires all reads of the stage that step+4 overwrites.
-    const int total = ntiles * nk;
-    int lt = 0, lk = 0;  // next step to load
-    auto issue = [&](int step) {
-        if (lk == 0) {
-            dma_t = tile0 + lt;
-            dma_valid = tile_valid(dma_t);
-        }
-        dma(step % MF_NS, lk * MF_BK);
+    // ---- pipeline ------------------------------------------------------------
+    // Steps run over the flat sequence (tile, k-step).  Each step issues the
+    // DMA of step+4 (past the end: the last tile again, into a stage nobody
+    // reads, so every step issues the same number of ops), reads slice 1 of
+    // its stage while slice 0 runs on the matrix cores, waits until its own
+    // DMA of step+1 has landed (vector-memory loads retire in order, so "at
+    // most the three youngest steps outstanding" suffices even with epilogue
+    // stores in between), meets the other waves at the barrier -- which also
+    // retires all reads of the stage that the next DMA overwrites -- and reads
+    // slice 0 of the next stage while slice 1 runs.
+    int ls = 0, lt = 0, lk = 0;  // next DMA: stage, tile (chunk-relative), k-step
+    auto issue_next = [&]() {
+        dma(ls, tile0 + min(lt, ntiles - 1), lk * MF_BK);
+        ls = ls + 1 == MF_NS ? 0 : ls + 1;
         if (++lk == nk) { lk = 0; ++lt; }
     };
-    for (int q = 0; q < MF_NS - 1; ++q)
-        if (q < total) issue(q);
-    if (total >= 3) MF_WAIT_VMCNT(2 * 2 * MF_DMA);
-    else if (total == 2) MF_WAIT_VMCNT(2 * MF_DMA);
-    else MF_WAIT_VMCNT(0);
+#pragma unroll
+    for (int q = 0; q < MF_NS - 1; ++q) issue_next();
+    MF_WAIT_VMCNT((MF_NS - 2) * 2 * MF_DMA);
     __builtin_amdgcn_s_barrier();
 
-    // Each step: read slice 1 of the current stage while slice 0 runs on the
-    // matrix cores, meet at the barrier, then read slice 0 of the next stage
-    // while slice 1 runs.  LDS latency hides behind 16 MFMAs either way.
     Frag f0, f1;
     load_frag(f0, 0, 0, 0);
-    int step = 0;
+    int cs = 0;  // stage being computed
     for (int t = 0; t < ntiles; ++t) {
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
             for (int ub = 0; ub < 4; ++ub) acc[ib][ub] = f32x16_t{};
-        for (int k = 0; k < nk; ++k, ++step) {
-            if (step + MF_NS - 1 < total) issue(step + MF_NS - 1);
-            const int stg = step % MF_NS;
-            load_frag(f1, stg, 1, k * MF_BK);
+        int last = 0;
+        for (int k = 0; k < nk; ++k) {
+            issue_next();
+            load_frag(f1, cs, 1, k * MF_BK);
             mma(f0);
-            const int ahead = min(total - 1 - step, MF_NS - 1);  // steps already issued beyond this one
-            if (ahead >= 3) MF_WAIT_VMCNT(2 * 2 * MF_DMA);
-            else if (ahead == 2) MF_WAIT_VMCNT(2 * MF_DMA);
-            else MF_WAIT_VMCNT(0);
+            MF_WAIT_VMCNT((MF_NS - 2) * 2 * MF_DMA);
             __builtin_amdgcn_s_barrier();
-            // (on the last step this reads a stale stage; the values are never used)
-            load_frag(f0, (step + 1) % MF_NS, 0, k + 1 < nk ? (k + 1) * MF_BK : 0);
+            last = cs;
+            cs = cs + 1 == MF_NS ? 0 : cs + 1;
+            // (on the very last step this reads a stage whose data is never used)
+            load_frag(f0, cs, 0, (k + 1 < nk ? k + 1 : 0) * MF_BK);
             mma(f1);
         }
-        epilogue(tile0 + t);
+        epilogue(tile0 + t, last);
     }
+    MF_WAIT_VMCNT(0);
 
     if (MODE == 1) {
-        // Combine the four lane groups that hold each user: (wi, lane/32).
-        float2* sml = (float2*)smem[0];
 #pragma unroll
         for (int ub = 0; ub < 4; ++ub) {
-            const int ul = wu * 128 + ub * 32 + (lane & 31);
-            sml[ul * 4 + wi * 2 + (lane >> 5)] = make_float2(m_[ub], l_[ub]);
-        }
-        __syncthreads();
-        const int u = u0 + tid;
-        if (u < a.B) {
-            LseState st;
-            st.init();
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float2 v = sml[tid * 4 + q];
-                st.merge(v.x, v.y);
+            const int u = u0 + wu * 128 + ub * 32 + (lane & 31);
+            if (u < a.B) {
+                const int64_t piece = ((int64_t)u * a.P + c) * 4 + g;
+                a.pm[piece] = m_[ub];
+                a.pl[piece] = l_[ub];
+                a.pcnt[piece] = cnt_[ub];
+                a.preg[piece] = (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles;
             }
-            const int64_t piece = (int64_t)u * a.P + c;
-            a.pm[piece] = st.m;
-            a.pl[piece] = st.l;
-            a.pcnt[piece] = s_cnt[tid];
-            a.preg[piece] = (int64_t)u * a.M + chunk_item0;
         }
     }
 }

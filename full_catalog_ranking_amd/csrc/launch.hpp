@@ -19,8 +19,9 @@ struct MfmaArgs {
     int UT, P, base, rem;     // user tiles; P chunks of base(+1) pass-tiles
     float* sample_out;        // mode 0: [B][n_tiles * 256] scores
     const float* theta;       // mode 1: [B] candidate thresholds (or null)
-    uint64_t* keys;           // mode 1: candidate regions, [B][M]
-    float* pm;                // per piece (user b, chunk c) at b*P + c
+    uint64_t* keys;           // mode 1: candidate regions, [B][key_stride]
+    int64_t key_stride;       // mode 1: >= 256 * ceil(M / 256)
+    float* pm;                // per piece (user b, chunk c, lane group g) at (b*P + c)*4 + g
     float* pl;
     int* pcnt;
     int64_t* preg;

@@ -15,7 +15,7 @@ namespace genrec {
 constexpr int MF_TI = 256;   // items per tile (MFMA rows)
 constexpr int MF_TU = 256;   // users per tile (MFMA columns)
 constexpr int MF_BK = 32;    // reduction depth per LDS stage
-constexpr int MF_NS = 4;     // LDS ring stages (3 in flight while one is read)
+constexpr int MF_NS = 5;     // LDS ring stages (4 in flight while one is read): 160 KiB
 constexpr int MF_NT = 256;   // threads: 4 waves in a 2 x 2 layout of 128 x 128 wave tiles
 constexpr int MF_ROWB = MF_BK * 2;                   // bytes per staged row (64)
 constexpr int MF_STAGE = (MF_TI + MF_TU) * MF_ROWB;  // 32 KiB per stage

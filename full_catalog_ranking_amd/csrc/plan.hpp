@@ -35,7 +35,9 @@ struct DensePlan {
     int64_t sample_tiles = 0;  // number of sampled 256-row tiles
     int64_t n_sample = 0;      // sampled items = 256 * sample_tiles
     Chunking main, pre;
+    int pieces_per_chunk = 1;  // MFMA: one piece per (user, chunk, lane group) = 4
     int64_t n_pieces = 0;
+    int64_t key_stride = 0;    // candidate-region elements per user
     size_t off_hdr = 0, off_theta = 0, off_sample = 0, off_pm = 0, off_pl = 0, off_pcnt = 0,
            off_preg = 0, off_keys = 0, total = 0;
 };
@@ -72,7 +74,9 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
     p.sample = M >= kSampleMinM && p.n_sample >= 4 * (int64_t)K;
     p.main = p.mfma ? chunk_mfma(B, ceil_div(M, kMfmaTileItems)) : chunk_stream(B, M);
     if (p.sample) p.pre = p.mfma ? chunk_mfma(B, p.sample_tiles) : chunk_stream(B, p.n_sample);
-    p.n_pieces = (int64_t)B * p.main.P;
+    p.pieces_per_chunk = p.mfma ? 4 : 1;
+    p.n_pieces = (int64_t)B * p.main.P * p.pieces_per_chunk;
+    p.key_stride = p.mfma ? ceil_div(M, kMfmaTileItems) * kMfmaTileItems : M;
     size_t o = 0;
     p.off_hdr = o;
     o += 256;
@@ -89,7 +93,7 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
     p.off_preg = o;
     o = align_up(o + sizeof(int64_t) * (size_t)p.n_pieces, 256);
     p.off_keys = o;
-    o = align_up(o + sizeof(uint64_t) * (size_t)B * (size_t)M, 256);
+    o = align_up(o + sizeof(uint64_t) * (size_t)B * (size_t)p.key_stride, 256);
     p.total = o;
     return p;
 }
