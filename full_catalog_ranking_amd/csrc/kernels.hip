@@ -31,9 +31,6 @@ namespace genrec {
 // ---------------------------------------------------------------------------
 // Dense MFMA path
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void lds_dma16(const void* g, uint8_t* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
 
 // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left alone (gfx9 encoding).
 #define MF_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
@@ -65,30 +62,38 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     };
 
     // ---- DMA (geometry in mfma_layout.hpp) --------------------------------
-    // Every op of a lane reads one k-chunk of one row at a 32-bit per-lane
-    // offset from a wave-uniform base.  Rows past the end of a partial tile
-    // re-read the last valid row; their scores are masked in the epilogue.
-    const int dchunk = mf_dma_kchunk(w, lane) * 8;  // element offset of the lane's k-chunk
-    const int h_valid = a.B - u0 < MF_TU ? a.B - u0 : MF_TU;
-    uint32_t h_off[MF_DMA];
+    // buffer_load ... lds through a buffer resource per operand: the base
+    // (wave-uniform, SGPRs) moves with the tile and k-step; each op of a lane
+    // reads at a fixed 32-bit byte offset.  The resource's record count ends at
+    // the last row of the catalog (or of the batch), so rows past the end of a
+    // partial tile read as zeros without any clamping; k-chunks past D read
+    // the next row or zeros and meet zeroed user-side fragments.
+    const int wsu = __builtin_amdgcn_readfirstlane(w);  // wave index, provably uniform
+    uint32_t voff[MF_DMA];
 #pragma unroll
-    for (int j = 0; j < MF_DMA; ++j) h_off[j] = (uint32_t)(mf_src_row(mf_dma_row(w, lane, j), h_valid) * D + dchunk);
-    const uint16_t* h_tile = a.H + (int64_t)u0 * D;
+    for (int j = 0; j < MF_DMA; ++j) voff[j] = (uint32_t)mf_dma_voff(w, lane, j, D);
+    const int64_t row_bytes = (int64_t)D * 2;
+    const int64_t tile_bytes = row_bytes * MF_TI;  // one operand tile, <= 32 MiB
+    const int64_t h_end = (int64_t)(a.B - u0) * row_bytes;  // bytes of H from the user tile on
 
     auto dma = [&](int stg, int t, int k0) {
-        const int valid = tile_valid(t);
-        const uint16_t* eb = a.E + tile_item0(t) * D + k0;
-        const uint16_t* hb = h_tile + k0;
-        uint32_t over = 0;  // k-chunks past D re-read the row's last chunk (zeroed at use)
-        if (KTAIL) {
-            const int o = k0 + dchunk + 8 - D;
-            over = o > 0 ? (uint32_t)o : 0u;
-        }
+        const int64_t e0 = tile_item0(t) * row_bytes;  // byte offset of the tile in E
+        const int64_t e_left = a.M * row_bytes - e0 - (int64_t)k0 * 2;
+        const int64_t h_left = h_end - (int64_t)k0 * 2;
+        const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const char*)a.E + e0 + (int64_t)k0 * 2), (short)0,
+            (int)(e_left < tile_bytes ? e_left : tile_bytes), 0x00020000);
+        const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const char*)a.H + (int64_t)u0 * row_bytes + (int64_t)k0 * 2), (short)0,
+            (int)(h_left < tile_bytes ? h_left : tile_bytes), 0x00020000);
+        uint8_t* sE = smem[stg] + wsu * 1024;
+        uint8_t* sH = smem[stg] + MF_TI * MF_ROWB + wsu * 1024;
 #pragma unroll
         for (int j = 0; j < MF_DMA; ++j) {
-            const uint32_t eo = (uint32_t)(mf_src_row(mf_dma_row(w, lane, j), valid) * D + dchunk) - over;
-            lds_dma16(eb + eo, smem[stg] + mf_dma_lds_byte(w, 0, j));
-            lds_dma16(hb + (h_off[j] - over), smem[stg] + MF_TI * MF_ROWB + mf_dma_lds_byte(w, 0, j));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)(sE + j * 4096),
+                                                     16, (int)voff[j], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (__attribute__((address_space(3))) void*)(sH + j * 4096),
+                                                     16, (int)voff[j], 0, 0, 0);
         }
     };
 
@@ -146,6 +151,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 
     auto epilogue = [&](int t, int stg) {
         const int lim = tile_valid(t);  // valid tile rows
+        const bool full = lim == MF_TI;
         const int64_t j0 = tile_item0(t);
         // Scores go through LDS one quad at a time (it keeps the live register
         // set small): quad q of a block sits in this wave's own DMA chunk q of
@@ -185,20 +191,24 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 #pragma unroll 1
                 for (int q = 0; q < 4; ++q) {
                     const float4 v4 = *(const float4*)(xs + mf_dma_lds_byte(w, 0, q));
-                    const float vs[4] = {v4.x, v4.y, v4.z, v4.w};
+                    float v[4] = {v4.x, v4.y, v4.z, v4.w};
                     const int jq = lrow0 + ib * 32 + q * 8;  // rows jq .. jq+3
+                    if (!full) {  // rows past the end: -inf adds nothing and never passes
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int jl = jq + e;
-                        if (jl >= lim) continue;
-                        const float s = vs[e];
-                        if (s > ref + 64.f) {
-                            lsum *= fast_exp2((ref - s) * kLog2e);
-                            ref = s;
-                            rb = s * kLog2e;
-                        }
-                        lsum += fast_exp2(fmaf(s, kLog2e, -rb));
-                        if (s >= th) kreg[cnt_[ub]++] = rank_key(s, (uint32_t)(j0 + jl));
+                        for (int e = 0; e < 4; ++e) v[e] = jq + e < lim ? v[e] : -INFINITY;
+                    }
+                    const float qmax = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+                    if (qmax > ref + 64.f) {
+                        lsum *= fast_exp2((ref - qmax) * kLog2e);
+                        ref = qmax;
+                        rb = qmax * kLog2e;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) lsum += fast_exp2(fmaf(v[e], kLog2e, -rb));
+                    if (qmax >= th) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (v[e] >= th) kreg[cnt_[ub]++] = rank_key(v[e], (uint32_t)(j0 + jq + e));
                     }
                 }
             }
@@ -243,13 +253,31 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             issue_next();
             load_frag(f1, cs, 1, k * MF_BK);
             mma(f0);
+            // schedule: slice-1 reads between the first MFMAs, DMA ops between the rest
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (DMA)
+            }
             MF_WAIT_VMCNT((MF_NS - 2) * 2 * MF_DMA);
             __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
             last = cs;
             cs = cs + 1 == MF_NS ? 0 : cs + 1;
             // (on the very last step this reads a stage whose data is never used)
             load_frag(f0, cs, 0, (k + 1 < nk ? k + 1 : 0) * MF_BK);
             mma(f1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
         }
         epilogue(tile0 + t, last);
     }

@@ -35,9 +35,12 @@ GENREC_HD inline int mf_dma_row(int w, int lane, int j) { return mf_dma_row0(w, 
 // field it reads), so one k-chunk offset serves all ops.
 GENREC_HD inline int mf_dma_kchunk(int w, int lane) { return (lane & 3) ^ mf_swz(mf_dma_row0(w, lane)); }
 GENREC_HD inline int mf_dma_lds_byte(int w, int lane, int j) { return (j * 4 + w) * 1024 + lane * 16; }
-// Row actually read for staged row `row` of a tile with `valid` rows: rows
-// past the end re-read the last valid row (their scores are masked later).
-GENREC_HD inline int mf_src_row(int row, int valid) { return row < valid ? row : valid - 1; }
+// Byte offset, within one operand tile of rows of D elements, that lane
+// `lane` of wave `w` reads for op j (the k-chunk of the stage's k0 is added
+// through the tile base).
+GENREC_HD inline long long mf_dma_voff(int w, int lane, int j, int D) {
+    return ((long long)mf_dma_row(w, lane, j) * D + mf_dma_kchunk(w, lane) * 8) * 2;
+}
 
 // Fragment read: byte offset of (staged row, k-chunk) within an operand stage.
 GENREC_HD inline int mf_frag_lds_byte(int row, int kchunk) { return row * MF_ROWB + ((kchunk ^ mf_swz(row)) << 4); }

@@ -54,31 +54,24 @@ int main() {
         }
     for (int s = 0; s < MF_TI * MF_ROWB / 16; ++s) CHECK(seen[s] == 1, "slot %d read %d times", s, seen[s]);
 
-    // 2. source rows stay inside partial tiles of every size
-    for (int valid = 1; valid <= MF_TI; ++valid)
-        for (int w = 0; w < 4; ++w)
-            for (int lane = 0; lane < 64; ++lane)
-                for (int j = 0; j < MF_DMA; ++j) {
-                    const int r = mf_src_row(mf_dma_row(w, lane, j), valid);
-                    CHECK(r >= 0 && r < valid, "src row %d outside [0,%d)", r, valid);
-                    if (mf_dma_row(w, lane, j) < valid) CHECK(r == mf_dma_row(w, lane, j), "valid row moved");
-                }
-
-    // 3. the 32-bit fast-path offset equals the 64-bit row offset
+    // 2. DMA byte offsets stay inside one operand tile (256 rows of D elements)
+    //    for the k-chunks of a stage, and fit the 32-bit buffer offset
     const int Ds[] = {8, 64, 200, 256, 2048, 4096, 65536};
     for (int D : Ds)
         for (int w = 0; w < 4; ++w)
-            for (int lane = 0; lane < 64; ++lane) {
-                const int64_t lane_off = (int64_t)mf_dma_row0(w, lane) * D + mf_dma_kchunk(w, lane) * 8;
-                CHECK(lane_off >= 0 && lane_off < ((int64_t)1 << 31), "lane offset overflows 32 bits");
+            for (int lane = 0; lane < 64; ++lane)
                 for (int j = 0; j < MF_DMA; ++j) {
-                    const int64_t fast = (int64_t)j * 64 * D + lane_off;
-                    const int64_t slow = (int64_t)mf_src_row(mf_dma_row(w, lane, j), MF_TI) * D + mf_dma_kchunk(w, lane) * 8;
-                    CHECK(fast == slow, "fast %lld != slow %lld", (long long)fast, (long long)slow);
-                    CHECK(fast + 8 <= (int64_t)MF_TI * D + (MF_BK - D % MF_BK) % MF_BK + MF_BK,
+                    const long long off = mf_dma_voff(w, lane, j, D);
+                    const long long row = mf_dma_row(w, lane, j);
+                    CHECK(off >= 0 && off < (1LL << 31), "offset overflows 32 bits");
+                    CHECK(off / 2 - row * D == mf_dma_kchunk(w, lane) * 8, "offset is not row*D + k-chunk");
+                    CHECK(row >= 0 && row < MF_TI, "row outside the tile");
+                    // with the stage's k0 added: the 16 bytes stay inside the tile
+                    // unless they run past D (the k tail, zero-masked at use)
+                    const long long k0_max = ((D - 1) / MF_BK) * MF_BK;
+                    CHECK(off + 2LL * k0_max + 16 <= (long long)MF_TI * D * 2 + 2LL * MF_BK,
                           "offset past the tile");
                 }
-            }
     if (fails) {
         printf("%d layout checks failed\n", fails);
         return 1;
