@@ -40,7 +40,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[MF_NS][MF_STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wi = w & 1, wu = w >> 1;
+    const int wi = w & 1, wu = w >> 1;  // wave tile: items wi*128 .. +128, users wu*64 .. +64
 
     // Blocks are dealt round-robin to the 8 XCDs; renumber them so that the
     // user tiles sharing one catalog chunk sit on one XCD (one L2) together.
@@ -86,22 +86,22 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)((const char*)a.H + (int64_t)u0 * row_bytes + (int64_t)k0 * 2), (short)0,
             (int)(h_left < tile_bytes ? h_left : tile_bytes), 0x00020000);
-        uint8_t* sE = smem[stg] + wsu * 1024;
-        uint8_t* sH = smem[stg] + MF_TI * MF_ROWB + wsu * 1024;
+        uint8_t* sE = smem[stg] + mf_dma_lds_byte(wsu, 0, 0);
+        uint8_t* sH = smem[stg] + MF_TI * MF_ROWB + mf_dma_lds_byte(wsu, 0, 0);
 #pragma unroll
         for (int j = 0; j < MF_DMA; ++j) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)(sE + j * 4096),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)(sE + j * MF_NW * 1024),
                                                      16, (int)voff[j], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (__attribute__((address_space(3))) void*)(sH + j * 4096),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (__attribute__((address_space(3))) void*)(sH + j * MF_NW * 1024),
                                                      16, (int)voff[j], 0, 0, 0);
         }
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][MF_UB];
     // MFMA operand fragments of one 16-deep k-slice: lane holds 8 consecutive
     // k of row (lane & 31) of each 32-row block, k-chunk (lane >> 5).
     struct Frag {
-        bf16x8_t a[4], b[4];
+        bf16x8_t a[4], b[MF_UB];
     };
     auto load_frag = [&](Frag& f, int stg, int ks, int k0) {
         const uint8_t* sE = smem[stg];
@@ -112,8 +112,8 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         for (int ib = 0; ib < 4; ++ib)
             f.a[ib] = *(const bf16x8_t*)(sE + mf_frag_lds_byte(wi * 128 + ib * 32 + (lane & 31), chunk));
 #pragma unroll
-        for (int ub = 0; ub < 4; ++ub) {
-            f.b[ub] = *(const bf16x8_t*)(sH + mf_frag_lds_byte(wu * 128 + ub * 32 + (lane & 31), chunk));
+        for (int ub = 0; ub < MF_UB; ++ub) {
+            f.b[ub] = *(const bf16x8_t*)(sH + mf_frag_lds_byte(wu * MF_WU + ub * 32 + (lane & 31), chunk));
             if (!kin) f.b[ub] = bf16x8_t{};
         }
     };
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-            for (int ub = 0; ub < 4; ++ub)
+            for (int ub = 0; ub < MF_UB; ++ub)
                 acc[ib][ub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ib], f.b[ub], acc[ib][ub], 0, 0, 0);
     };
 
@@ -136,11 +136,11 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     const int lrow0 = wi * 128 + (lane >> 5) * 4;
     const int64_t chunk_item0 = tile_item0(tile0);  // (mode 1: G = 1)
     const int64_t n_pass = (int64_t)a.n_tiles * MF_TI;  // mode 0: row length of sample_out
-    float m_[4], l_[4], th_[4];
-    int cnt_[4];
+    float m_[MF_UB], l_[MF_UB], th_[MF_UB];
+    int cnt_[MF_UB];
 #pragma unroll
-    for (int ub = 0; ub < 4; ++ub) {
-        const int u = u0 + wu * 128 + ub * 32 + (lane & 31);
+    for (int ub = 0; ub < MF_UB; ++ub) {
+        const int u = u0 + wu * MF_WU + ub * 32 + (lane & 31);
         m_[ub] = -INFINITY;
         l_[ub] = 0.f;
         cnt_[ub] = 0;
@@ -154,12 +154,16 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         const bool full = lim == MF_TI;
         const int64_t j0 = tile_item0(t);
         // Scores go through LDS one quad at a time (it keeps the live register
-        // set small): quad q of a block sits in this wave's own DMA chunk q of
-        // the stage just consumed -- only this wave's next DMA rewrites it.
+        // set small): quad q of a block sits in one of this wave's own four
+        // DMA chunks of the stage just consumed -- only this wave's next DMA
+        // rewrites them.
         uint8_t* xs = smem[stg] + lane * 16;
+        auto xq = [&](int q) -> int {
+            return (q >> 1) * (MF_TI * MF_ROWB) + mf_dma_lds_byte(w, 0, q & 1);
+        };
 #pragma unroll
-        for (int ub = 0; ub < 4; ++ub) {
-            const int ul = wu * 128 + ub * 32 + (lane & 31);
+        for (int ub = 0; ub < MF_UB; ++ub) {
+            const int ul = wu * MF_WU + ub * 32 + (lane & 31);
             const int u = u0 + ul;
             if (MODE == 0) {
                 if (u < a.B) {
@@ -186,11 +190,11 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             for (int ib = 0; ib < 4; ++ib) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    *(float4*)(xs + mf_dma_lds_byte(w, 0, q)) =
+                    *(float4*)(xs + xq(q)) =
                         make_float4(acc[ib][ub][4 * q], acc[ib][ub][4 * q + 1], acc[ib][ub][4 * q + 2], acc[ib][ub][4 * q + 3]);
 #pragma unroll 1
                 for (int q = 0; q < 4; ++q) {
-                    const float4 v4 = *(const float4*)(xs + mf_dma_lds_byte(w, 0, q));
+                    const float4 v4 = *(const float4*)(xs + xq(q));
                     float v[4] = {v4.x, v4.y, v4.z, v4.w};
                     const int jq = lrow0 + ib * 32 + q * 8;  // rows jq .. jq+3
                     if (!full) {  // rows past the end: -inf adds nothing and never passes
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-            for (int ub = 0; ub < 4; ++ub) acc[ib][ub] = f32x16_t{};
+            for (int ub = 0; ub < MF_UB; ++ub) acc[ib][ub] = f32x16_t{};
         int last = 0;
         for (int k = 0; k < nk; ++k) {
             issue_next();
@@ -255,14 +259,14 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             mma(f0);
             // schedule: slice-1 reads between the first MFMAs, DMA ops between the rest
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 4 + MF_UB; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 4 * MF_UB - 4 - MF_UB; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read (DMA)
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read (DMA)
             }
             MF_WAIT_VMCNT((MF_NS - 2) * 2 * MF_DMA);
             __builtin_amdgcn_s_barrier();
@@ -273,11 +277,11 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             load_frag(f0, cs, 0, (k + 1 < nk ? k + 1 : 0) * MF_BK);
             mma(f1);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 4 + MF_UB; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * MF_UB - 4 - MF_UB, 1);
         }
         epilogue(tile0 + t, last);
     }
@@ -285,8 +289,8 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 
     if (MODE == 1) {
 #pragma unroll
-        for (int ub = 0; ub < 4; ++ub) {
-            const int u = u0 + wu * 128 + ub * 32 + (lane & 31);
+        for (int ub = 0; ub < MF_UB; ++ub) {
+            const int u = u0 + wu * MF_WU + ub * 32 + (lane & 31);
             if (u < a.B) {
                 const int64_t piece = ((int64_t)u * a.P + c) * 4 + g;
                 a.pm[piece] = m_[ub];

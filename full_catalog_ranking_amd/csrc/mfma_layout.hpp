@@ -16,25 +16,28 @@ constexpr int MF_TI = 256;   // items per tile (MFMA rows)
 constexpr int MF_TU = 256;   // users per tile (MFMA columns)
 constexpr int MF_BK = 32;    // reduction depth per LDS stage
 constexpr int MF_NS = 5;     // LDS ring stages (4 in flight while one is read): 160 KiB
-constexpr int MF_NT = 256;   // threads: 4 waves in a 2 x 2 layout of 128 x 128 wave tiles
+constexpr int MF_NT = 512;   // threads: 8 waves (2 per SIMD) in a 2 x 4 layout of 128 x 64 wave tiles
+constexpr int MF_NW = MF_NT / 64;
+constexpr int MF_WU = 64;    // users per wave tile
+constexpr int MF_UB = MF_WU / 32;  // 32-wide user blocks per wave tile
 constexpr int MF_ROWB = MF_BK * 2;                   // bytes per staged row (64)
 constexpr int MF_STAGE = (MF_TI + MF_TU) * MF_ROWB;  // 32 KiB per stage
-constexpr int MF_DMA = 4;    // 16-byte DMA ops per lane per operand per stage
-static_assert(MF_DMA * 4 * 64 * 16 == MF_TI * MF_ROWB, "DMA ops must cover one operand stage");
+constexpr int MF_DMA = 2;    // 16-byte DMA ops per lane per operand per stage
+static_assert(MF_DMA * MF_NW * 64 * 16 == MF_TI * MF_ROWB, "DMA ops must cover one operand stage");
 
 // 16-byte chunk swizzle within a 64-byte staged row: conflict-free
 // ds_read_b128 of 32 consecutive rows at one k-chunk for 32- or 64-bank LDS.
 GENREC_HD inline int mf_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-// DMA: wave w, op j writes the 1 KiB of staged rows (j*4 + w)*16 .. +16; lane
-// l writes 16 bytes at l*16, i.e. staged row (j*4 + w)*16 + l/4 at chunk
-// position l%4, holding global k-chunk (l%4) ^ swz(row).
+// DMA: wave w, op j writes the 1 KiB of staged rows (j*NW + w)*16 .. +16;
+// lane l writes 16 bytes at l*16, i.e. staged row (j*NW + w)*16 + l/4 at
+// chunk position l%4, holding global k-chunk (l%4) ^ swz(row).
 GENREC_HD inline int mf_dma_row0(int w, int lane) { return w * 16 + (lane >> 2); }  // staged row of op 0
-GENREC_HD inline int mf_dma_row(int w, int lane, int j) { return mf_dma_row0(w, lane) + 64 * j; }
-// swz(row) is the same for every op j of a lane (64 j changes neither bit
-// field it reads), so one k-chunk offset serves all ops.
+GENREC_HD inline int mf_dma_row(int w, int lane, int j) { return mf_dma_row0(w, lane) + MF_NW * 16 * j; }
+// swz(row) is the same for every op j of a lane (NW*16*j = 128 j changes
+// neither bit field it reads), so one k-chunk offset serves all ops.
 GENREC_HD inline int mf_dma_kchunk(int w, int lane) { return (lane & 3) ^ mf_swz(mf_dma_row0(w, lane)); }
-GENREC_HD inline int mf_dma_lds_byte(int w, int lane, int j) { return (j * 4 + w) * 1024 + lane * 16; }
+GENREC_HD inline int mf_dma_lds_byte(int w, int lane, int j) { return (j * MF_NW + w) * 1024 + lane * 16; }
 // Byte offset, within one operand tile of rows of D elements, that lane
 // `lane` of wave `w` reads for op j (the k-chunk of the stage's k0 is added
 // through the tile base).

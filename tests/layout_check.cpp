@@ -23,7 +23,7 @@ int main() {
     // 1. write/read agreement and coverage of one operand stage
     static int owner[MF_TI * MF_ROWB / 16];
     memset(owner, -1, sizeof owner);
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < MF_NW; ++w)
         for (int lane = 0; lane < 64; ++lane)
             for (int j = 0; j < MF_DMA; ++j) {
                 const int row = mf_dma_row(w, lane, j);
@@ -58,7 +58,7 @@ int main() {
     //    for the k-chunks of a stage, and fit the 32-bit buffer offset
     const int Ds[] = {8, 64, 200, 256, 2048, 4096, 65536};
     for (int D : Ds)
-        for (int w = 0; w < 4; ++w)
+        for (int w = 0; w < MF_NW; ++w)
             for (int lane = 0; lane < 64; ++lane)
                 for (int j = 0; j < MF_DMA; ++j) {
                     const long long off = mf_dma_voff(w, lane, j, D);
