@@ -479,15 +479,17 @@ __global__ __launch_bounds__(ST_NT) void stream_score_kernel(StreamArgs a) {
 // Block-level selection of the k-th largest 64-bit key
 // ---------------------------------------------------------------------------
 constexpr int SEL_NT = 256;
-constexpr int SEL_NB = 256;    // histogram bins per narrowing pass
-constexpr int SEL_GCAP = 2048; // candidates gathered into LDS for the final sort
-constexpr int SEL_UNR = 8;     // independent loads in flight per thread
+constexpr int SEL_NB = 256;     // histogram bins per narrowing pass
+constexpr int SEL_GCAP = 4096;  // range gathered into LDS once it holds at most this many keys
+constexpr int SEL_SMALL = 512;  // range sorted once it holds at most this many keys
+constexpr int SEL_UNR = 8;      // independent loads in flight per thread
 
 struct SelShared {
     unsigned long long red_lo[SEL_NT / kWave], red_hi[SEL_NT / kWave];
-    int hist[SEL_NB];
-    int cnt_a, cnt_b;
+    int hist[SEL_NT / kWave][SEL_NB];  // one histogram per wave: less atomic contention
+    int cnt_a, cnt_b, bin, above;
     uint64_t gbuf[SEL_GCAP];
+    uint64_t sbuf[SEL_SMALL];
     uint64_t out[GENREC_KMAX];
 };
 
@@ -532,15 +534,85 @@ __device__ void block_sort_desc(uint64_t* buf, int n) {
     }
 }
 
+// Keys of an LDS array, for the narrowing passes after the gather.
+struct LdsSrc {
+    const uint64_t* buf;
+    int n;
+    template <class F>
+    __device__ void for_each(F&& f) const {
+        for (int i = threadIdx.x; i < n; i += SEL_NT) f(buf[i]);
+    }
+};
+
+// One narrowing pass: histogram the keys of [lo, hi] into 256 power-of-two-
+// wide bins and move [lo, hi] to the bin holding the k_rem-th largest key.
+// k_rem drops by the keys of the bins above it; returns the keys in the bin.
+template <class Src>
+__device__ int64_t narrow(const Src& src, unsigned long long& lo, unsigned long long& hi, int& k_rem,
+                          SelShared& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const unsigned long long span = hi - lo;
+    const int shift = max(0, 64 - __clzll(span) - 8);  // (hi - lo) >> shift < 256
+    for (int i = tid; i < SEL_NB * (SEL_NT / kWave); i += SEL_NT) (&sh.hist[0][0])[i] = 0;
+    __syncthreads();
+    const unsigned long long clo = lo, chi = hi;
+    int* whist = sh.hist[w];
+    src.for_each([&](uint64_t key) {
+        if (key >= clo && key <= chi) atomicAdd(&whist[(int)((key - clo) >> shift)], 1);
+    });
+    __syncthreads();
+    for (int i = tid; i < SEL_NB; i += SEL_NT) {
+        int t = 0;
+#pragma unroll
+        for (int q = 0; q < SEL_NT / kWave; ++q) t += sh.hist[q][i];
+        sh.hist[0][i] = t;
+    }
+    __syncthreads();
+    // wave 0 finds bin d with above(d) < k_rem <= above(d) + hist[d]
+    if (w == 0) {
+        int v[SEL_NB / kWave];
+        int tsum = 0;
+#pragma unroll
+        for (int i = 0; i < SEL_NB / kWave; ++i) {  // lane owns 4 bins, highest bins first
+            v[i] = sh.hist[0][SEL_NB - 1 - (lane * (SEL_NB / kWave) + i)];
+            tsum += v[i];
+        }
+        int incl = tsum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+        }
+        int run = incl - tsum;
+#pragma unroll
+        for (int i = 0; i < SEL_NB / kWave; ++i) {
+            if (run < k_rem && k_rem <= run + v[i]) {
+                sh.bin = SEL_NB - 1 - (lane * (SEL_NB / kWave) + i);
+                sh.above = run;
+            }
+            run += v[i];
+        }
+    }
+    __syncthreads();
+    const int d = sh.bin;
+    k_rem -= sh.above;
+    const int64_t n_bin = sh.hist[0][d];
+    lo = clo + ((unsigned long long)d << shift);
+    const unsigned long long top = lo + ((1ull << shift) - 1);
+    hi = top < chi ? top : chi;
+    __syncthreads();
+    return n_bin;
+}
+
 // Finds the k-th largest key (1 <= k <= n) among the keys the source yields
 // and, with COLLECT, leaves the k largest keys in sh.out[0..k) (unsorted).
-// Returns the k-th largest key.  Every pass reads the source once:
+// Returns the k-th largest key.  Passes over the source:
 //   1. min / max of all keys;
-//   2. while more than SEL_GCAP keys remain in the candidate range [lo, hi],
-//      histogram the range into 256 power-of-two-wide bins and narrow it to
-//      the bin holding the k-th largest;
-//   3. gather the range into LDS (and, with COLLECT, every key above it into
-//      sh.out), sort the range and pick.
+//   2. while the candidate range [lo, hi] holds more than SEL_GCAP keys, a
+//      narrowing pass (histogram of the range, keep the bin of the k-th);
+//   3. gather: the range into LDS and (COLLECT) every key above it into out.
+// Then, in LDS, narrowing continues until at most SEL_SMALL keys remain in
+// the range, which are sorted; keys above the final range join out.
 template <bool COLLECT, class Src>
 __device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -563,76 +635,62 @@ __device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
 
     int64_t n_range = src.total();
     int k_rem = k;
-    while (lo != hi && n_range > SEL_GCAP) {
-        const unsigned long long span = hi - lo;
-        const int shift = max(0, 64 - __clzll(span) - 8);  // (hi - lo) >> shift < 256
-        for (int i = tid; i < SEL_NB; i += SEL_NT) sh.hist[i] = 0;
-        __syncthreads();
-        const unsigned long long clo = lo, chi = hi;
-        src.for_each([&](uint64_t key) {
-            if (key >= clo && key <= chi) atomicAdd(&sh.hist[(int)((key - clo) >> shift)], 1);
-        });
-        __syncthreads();
-        // Wave 0 finds bin d with above(d) < k_rem <= above(d) + hist[d].
-        if (w == 0) {
-            int v[SEL_NB / kWave];
-            int tsum = 0;
-#pragma unroll
-            for (int i = 0; i < SEL_NB / kWave; ++i) {  // lane owns bins [4*lane, 4*lane+4) (top-down order below)
-                v[i] = sh.hist[SEL_NB - 1 - (lane * (SEL_NB / kWave) + i)];
-                tsum += v[i];
-            }
-            // exclusive prefix over lanes of tsum (counts of higher bins)
-            int incl = tsum;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int t = __shfl_up(incl, o);
-                if (lane >= o) incl += t;
-            }
-            int run = incl - tsum;
-#pragma unroll
-            for (int i = 0; i < SEL_NB / kWave; ++i) {
-                if (run < k_rem && k_rem <= run + v[i]) {
-                    sh.cnt_a = SEL_NB - 1 - (lane * (SEL_NB / kWave) + i);  // bin
-                    sh.cnt_b = run;                                         // keys above it
-                }
-                run += v[i];
-            }
-        }
-        __syncthreads();
-        const int d = sh.cnt_a;
-        k_rem -= sh.cnt_b;
-        n_range = sh.hist[d];
-        lo = clo + ((unsigned long long)d << shift);
-        const unsigned long long top = lo + ((1ull << shift) - 1);
-        hi = top < chi ? top : chi;
-        __syncthreads();
-    }
+    while (lo != hi && n_range > SEL_GCAP) n_range = narrow(src, lo, hi, k_rem, sh);
 
-    // Final pass: gather the range, and (COLLECT) everything above it.
+    // gather the range into LDS; keys above it are in the result for sure
     if (tid == 0) { sh.cnt_a = 0; sh.cnt_b = 0; }
     __syncthreads();
-    const unsigned long long flo = lo, fhi = hi;
-    const bool single = flo == fhi;
-    const int n_above = k - k_rem;
-    src.for_each([&](uint64_t key) {
-        if (key > fhi) {
-            if (COLLECT) sh.out[atomicAdd(&sh.cnt_a, 1)] = key;
-        } else if (key >= flo && !single) {
-            sh.gbuf[atomicAdd(&sh.cnt_b, 1)] = key;
-        }
-    });
+    {
+        const unsigned long long flo = lo, fhi = hi;
+        const bool single = flo == fhi;
+        src.for_each([&](uint64_t key) {
+            if (key > fhi) {
+                if (COLLECT) sh.out[atomicAdd(&sh.cnt_a, 1)] = key;
+            } else if (key >= flo && !single) {
+                sh.gbuf[atomicAdd(&sh.cnt_b, 1)] = key;
+            }
+        });
+    }
     __syncthreads();
     uint64_t kth;
-    if (single) {
-        kth = flo;
+    if (lo == hi) {  // every key left in the range is the k-th (equal keys)
+        kth = lo;
+        if (COLLECT) {
+            const int n_above = sh.cnt_a;
+            for (int i = tid; i < k_rem; i += SEL_NT) sh.out[n_above + i] = lo;
+        }
+        __syncthreads();
+        return kth;
+    }
+    const int ng = sh.cnt_b;
+    LdsSrc lsrc{sh.gbuf, ng};
+    while (lo != hi && n_range > SEL_SMALL) n_range = narrow(lsrc, lo, hi, k_rem, sh);
+    // keys of the gathered set above the final range join out; the range is sorted
+    if (tid == 0) sh.cnt_b = 0;
+    __syncthreads();
+    {
+        const unsigned long long flo = lo, fhi = hi;
+        const bool single = flo == fhi;
+        for (int i = tid; i < ng; i += SEL_NT) {
+            const uint64_t key = sh.gbuf[i];
+            if (key > fhi) {
+                if (COLLECT) sh.out[atomicAdd(&sh.cnt_a, 1)] = key;
+            } else if (key >= flo && !single) {
+                sh.sbuf[atomicAdd(&sh.cnt_b, 1)] = key;
+            }
+        }
+    }
+    __syncthreads();
+    const int n_above = sh.cnt_a;  // == k - k_rem when COLLECT
+    if (lo == hi) {
+        kth = lo;
         if (COLLECT)
-            for (int i = tid; i < k_rem; i += SEL_NT) sh.out[n_above + i] = flo;
+            for (int i = tid; i < k_rem; i += SEL_NT) sh.out[n_above + i] = lo;
     } else {
-        block_sort_desc(sh.gbuf, (int)n_range);
-        kth = sh.gbuf[k_rem - 1];
+        block_sort_desc(sh.sbuf, (int)n_range);
+        kth = sh.sbuf[k_rem - 1];
         if (COLLECT)
-            for (int i = tid; i < k_rem; i += SEL_NT) sh.out[n_above + i] = sh.gbuf[i];
+            for (int i = tid; i < k_rem; i += SEL_NT) sh.out[n_above + i] = sh.sbuf[i];
     }
     __syncthreads();
     return kth;
@@ -729,21 +787,39 @@ struct PieceSrc {
             }
             if (tid == SEL_NT - 1) ps->pref[MG_PB] = run;
             __syncthreads();
+            // Each thread walks one contiguous range of the batch's entries: one
+            // binary search for its first piece, then forward across piece ends.
             const int tot = ps->pref[MG_PB];
-            int pi = 0;
-            for (int e0 = tid; e0 < tot; e0 += SEL_NT * SEL_UNR) {
-                uint64_t kv[SEL_UNR];
-#pragma unroll
-                for (int q = 0; q < SEL_UNR; ++q) {
-                    const int e = e0 + q * SEL_NT;
-                    if (e < tot) {
-                        while (ps->pref[pi + 1] <= e) ++pi;
-                        kv[q] = keys[ps->base[pi] + (e - ps->pref[pi])];
-                    }
+            const int per = (tot + SEL_NT - 1) / SEL_NT;
+            const int e_beg = min(tid * per, tot), e_end = min(e_beg + per, tot);
+            if (e_beg < e_end) {
+                int lo_p = 0, hi_p = np - 1;  // last piece with pref <= e_beg
+                while (lo_p < hi_p) {
+                    const int mid = (lo_p + hi_p + 1) >> 1;
+                    if (ps->pref[mid] <= e_beg) lo_p = mid;
+                    else hi_p = mid - 1;
                 }
+                int pi = lo_p;
+                int next = ps->pref[pi + 1];
+                int64_t src = ps->base[pi] + (e_beg - ps->pref[pi]);
+                for (int e0 = e_beg; e0 < e_end; e0 += SEL_UNR) {
+                    uint64_t kv[SEL_UNR];
 #pragma unroll
-                for (int q = 0; q < SEL_UNR; ++q)
-                    if (e0 + q * SEL_NT < tot) f(kv[q]);
+                    for (int q = 0; q < SEL_UNR; ++q) {
+                        const int e = e0 + q;
+                        if (e < e_end) {
+                            while (e >= next) {  // crossed into the next non-empty piece
+                                ++pi;
+                                next = ps->pref[pi + 1];
+                                src = ps->base[pi] + (e - ps->pref[pi]);
+                            }
+                            kv[q] = keys[src++];
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < SEL_UNR; ++q)
+                        if (e0 + q < e_end) f(kv[q]);
+                }
             }
             __syncthreads();
         }
