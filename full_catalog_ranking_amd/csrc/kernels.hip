@@ -62,10 +62,10 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     };
 
     // ---- DMA (geometry in mfma_layout.hpp) --------------------------------
-    // buffer_load ... lds through a buffer resource per operand: the base
-    // (wave-uniform, SGPRs) moves with the tile and k-step; each op of a lane
-    // reads at a fixed 32-bit byte offset.  The resource's record count ends at
-    // the last row of the catalog (or of the batch), so rows past the end of a
+    // buffer_load ... lds through a buffer resource per operand (wave-uniform,
+    // SGPRs); each op of a lane reads at a fixed 32-bit byte offset plus the
+    // k-step's scalar offset.  The resource's record count ends at the last
+    // valid row of the tile (or of the batch), so rows past the end of a
     // partial tile read as zeros without any clamping; k-chunks past D read
     // the next row or zeros and meet zeroed user-side fragments.
     const int wsu = __builtin_amdgcn_readfirstlane(w);  // wave index, provably uniform
@@ -73,27 +73,28 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < MF_DMA; ++j) voff[j] = (uint32_t)mf_dma_voff(w, lane, j, D);
     const int64_t row_bytes = (int64_t)D * 2;
-    const int64_t tile_bytes = row_bytes * MF_TI;  // one operand tile, <= 32 MiB
-    const int64_t h_end = (int64_t)(a.B - u0) * row_bytes;  // bytes of H from the user tile on
+    // The user tile's resource is fixed; the catalog tile's is rebuilt when the
+    // DMA moves to a new tile.  k0 rides in the scalar offset, so rows past the
+    // end (and k-chunks past D on the last row) fall outside the record count.
+    const int h_rows = a.B - u0 < MF_TU ? a.B - u0 : MF_TU;
+    const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)a.H + (int64_t)u0 * row_bytes), (short)0, (int)(h_rows * row_bytes), 0x00020000);
+    __amdgpu_buffer_rsrc_t er;
+    auto e_rsrc = [&](int t) {
+        er = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.E + tile_item0(t) * row_bytes), (short)0,
+                                               (int)(tile_valid(t) * row_bytes), 0x00020000);
+    };
 
-    auto dma = [&](int stg, int t, int k0) {
-        const int64_t e0 = tile_item0(t) * row_bytes;  // byte offset of the tile in E
-        const int64_t e_left = a.M * row_bytes - e0 - (int64_t)k0 * 2;
-        const int64_t h_left = h_end - (int64_t)k0 * 2;
-        const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const char*)a.E + e0 + (int64_t)k0 * 2), (short)0,
-            (int)(e_left < tile_bytes ? e_left : tile_bytes), 0x00020000);
-        const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const char*)a.H + (int64_t)u0 * row_bytes + (int64_t)k0 * 2), (short)0,
-            (int)(h_left < tile_bytes ? h_left : tile_bytes), 0x00020000);
+    auto dma = [&](int stg, int k0) {
         uint8_t* sE = smem[stg] + mf_dma_lds_byte(wsu, 0, 0);
         uint8_t* sH = smem[stg] + MF_TI * MF_ROWB + mf_dma_lds_byte(wsu, 0, 0);
+        const int soff = k0 * 2;
 #pragma unroll
         for (int j = 0; j < MF_DMA; ++j) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)(sE + j * MF_NW * 1024),
-                                                     16, (int)voff[j], 0, 0, 0);
+                                                     16, (int)voff[j], soff, 0, 0);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (__attribute__((address_space(3))) void*)(sH + j * MF_NW * 1024),
-                                                     16, (int)voff[j], 0, 0, 0);
+                                                     16, (int)voff[j], soff, 0, 0);
         }
     };
 
@@ -234,10 +235,14 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     // retires all reads of the stage that the next DMA overwrites -- and reads
     // slice 0 of the next stage while slice 1 runs.
     int ls = 0, lt = 0, lk = 0;  // next DMA: stage, tile (chunk-relative), k-step
+    e_rsrc(tile0);
     auto issue_next = [&]() {
-        dma(ls, tile0 + min(lt, ntiles - 1), lk * MF_BK);
+        dma(ls, lk * MF_BK);
         ls = ls + 1 == MF_NS ? 0 : ls + 1;
-        if (++lk == nk) { lk = 0; ++lt; }
+        if (++lk == nk) {
+            lk = 0;
+            if (++lt < ntiles) e_rsrc(tile0 + lt);  // past the end: keep re-reading the last tile
+        }
     };
 #pragma unroll
     for (int q = 0; q < MF_NS - 1; ++q) issue_next();
