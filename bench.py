@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run plain device-to-device copies of MIB MiB (the reference "
+                         "kernel for scaling HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -46,6 +49,42 @@ def to_dev(a, dev, torch):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
     return torch.from_numpy(a).to(dev)
+
+
+def copy_calibration(mib, reps):
+    """Plain copies of a known size: FETCH_SIZE / WRITE_SIZE of this kernel against its
+    exact byte count give the scale of those counters."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
+def traffic_from_profile(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter summary,
+    or None when the summary is absent or was taken from other kernel sources."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.md" % (kernel, workload))
+    src = os.path.join(ROOT, "full_catalog_ranking_amd", "csrc", "kernels.hip")
+    if not os.path.exists(path):
+        return None
+    want = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernels.hip sha256") != want:
+        return None
+    try:
+        return float(fields["hbm bytes per launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(d, K, target_s, cand):
@@ -80,6 +119,9 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(1, args.steps))
+        return
     import torch
     from full_catalog_ranking_amd import genrec, synth
 
@@ -143,13 +185,13 @@ def main():
             alg_bytes = M * D * elem + B * D * elem
         achieved = alg_bytes / (main_ms * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=achieved / HBM_PEAK_GBS, traffic=None)
+                    frac=achieved / HBM_PEAK_GBS)
     else:
         peak = MFMA_BF16_PEAK_TFLOPS
         achieved = flops / (main_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s", frac=achieved / peak,
-                    traffic=None)
-    roof["kernel"] = "mfma_score_kernel<1>" if roof["bound"] == "mfma" else "stream_score_kernel"
+        roof = dict(bound="mfma", achieved=achieved, peak=peak, unit="TFLOP/s", frac=achieved / peak)
+    roof["kernel"] = "mfma_score_kernel" if roof["bound"] == "mfma" else "stream_score_kernel"
+    roof["traffic"] = traffic_from_profile(roof["kernel"], args.workload)
     roof["kernel_ms"] = main_ms
 
     res = {
