@@ -85,17 +85,15 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                                                (int)(tile_valid(t) * row_bytes), 0x00020000);
     };
 
-    auto dma = [&](int stg, int k0) {
+    // DMA op j of both operands for the stage at k0 (1 KiB per op per wave).
+    auto dma_op = [&](int stg, int k0, int j) {
         uint8_t* sE = smem[stg] + mf_dma_lds_byte(wsu, 0, 0);
         uint8_t* sH = smem[stg] + MF_TI * MF_ROWB + mf_dma_lds_byte(wsu, 0, 0);
         const int soff = k0 * 2;
-#pragma unroll
-        for (int j = 0; j < MF_DMA; ++j) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)(sE + j * MF_NW * 1024),
-                                                     16, (int)voff[j], soff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (__attribute__((address_space(3))) void*)(sH + j * MF_NW * 1024),
-                                                     16, (int)voff[j], soff, 0, 0);
-        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)(sE + j * MF_NW * 1024),
+                                                 16, (int)voff[j], soff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (__attribute__((address_space(3))) void*)(sH + j * MF_NW * 1024),
+                                                 16, (int)voff[j], soff, 0, 0);
     };
 
     f32x16_t acc[4][MF_UB];
@@ -226,18 +224,25 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 
     // ---- pipeline ------------------------------------------------------------
     // Steps run over the flat sequence (tile, k-step).  Each step issues the
-    // DMA of step+4 (past the end: the last tile again, into a stage nobody
-    // reads, so every step issues the same number of ops), reads slice 1 of
-    // its stage while slice 0 runs on the matrix cores, waits until its own
-    // DMA of step+1 has landed (vector-memory loads retire in order, so "at
-    // most the three youngest steps outstanding" suffices even with epilogue
-    // stores in between), meets the other waves at the barrier -- which also
-    // retires all reads of the stage that the next DMA overwrites -- and reads
-    // slice 0 of the next stage while slice 1 runs.
+    // DMA of step+4 -- op 0 of both operands among the MFMAs of its first
+    // half, op 1 among those of its second half, so that the CU's vector-
+    // memory path sees an even stream rather than a burst after every barrier
+    // (past the end: the last tile again, into a stage nobody reads, so every
+    // step issues the same number of ops).  It reads slice 1 of its stage
+    // while slice 0 runs on the matrix cores, waits until the DMA of step+1
+    // has landed (vector-memory ops retire in order, so "at most steps +2 and
+    // +3 and the first half of step +4 outstanding" suffices, epilogue stores
+    // in between only make the wait stricter), meets the other waves at the
+    // barrier -- which also retires all reads of the stage that the next DMA
+    // overwrites -- and reads slice 0 of the next stage while slice 1 runs.
+    // The DMA ring moves on after both halves (the stage the step's DMA
+    // writes was last read before the previous step's barrier).
+    static_assert(MF_DMA == 2, "one op per operand in each half of a step");
+    constexpr int kOpsPerStep = 2 * MF_DMA;
+    constexpr int kWaitOps = (MF_NS - 3) * kOpsPerStep + 2;
     int ls = 0, lt = 0, lk = 0;  // next DMA: stage, tile (chunk-relative), k-step
     e_rsrc(tile0);
-    auto issue_next = [&]() {
-        dma(ls, lk * MF_BK);
+    auto advance = [&]() {
         ls = ls + 1 == MF_NS ? 0 : ls + 1;
         if (++lk == nk) {
             lk = 0;
@@ -245,8 +250,12 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         }
     };
 #pragma unroll
-    for (int q = 0; q < MF_NS - 1; ++q) issue_next();
-    MF_WAIT_VMCNT((MF_NS - 2) * 2 * MF_DMA);
+    for (int q = 0; q < MF_NS - 1; ++q) {
+        dma_op(ls, lk * MF_BK, 0);
+        dma_op(ls, lk * MF_BK, 1);
+        advance();
+    }
+    MF_WAIT_VMCNT((MF_NS - 2) * kOpsPerStep);
     __builtin_amdgcn_s_barrier();
 
     Frag f0, f1;
@@ -259,34 +268,33 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             for (int ub = 0; ub < MF_UB; ++ub) acc[ib][ub] = f32x16_t{};
         int last = 0;
         for (int k = 0; k < nk; ++k) {
-            issue_next();
+            dma_op(ls, lk * MF_BK, 0);
             load_frag(f1, cs, 1, k * MF_BK);
             mma(f0);
-            // schedule: slice-1 reads between the first MFMAs, DMA ops between the rest
+            // schedule: slice-1 reads between the MFMAs, the two DMA ops after MFMAs 3 and 6
 #pragma unroll
-            for (int i = 0; i < 4 + MF_UB; ++i) {
+            for (int i = 0; i < 4 * MF_UB; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                if (i < 4 + MF_UB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                if (i == 2 || i == 5) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA)
             }
-#pragma unroll
-            for (int i = 0; i < 4 * MF_UB - 4 - MF_UB; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read (DMA)
-            }
-            MF_WAIT_VMCNT((MF_NS - 2) * 2 * MF_DMA);
+            MF_WAIT_VMCNT(kWaitOps);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             last = cs;
             cs = cs + 1 == MF_NS ? 0 : cs + 1;
+            dma_op(ls, lk * MF_BK, 1);
             // (on the very last step this reads a stage whose data is never used)
             load_frag(f0, cs, 0, (k + 1 < nk ? k + 1 : 0) * MF_BK);
             mma(f1);
 #pragma unroll
-            for (int i = 0; i < 4 + MF_UB; ++i) {
+            for (int i = 0; i < 4 * MF_UB; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+                if (i < 4 + MF_UB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+                if (i == 2 || i == 5) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4 * MF_UB - 4 - MF_UB, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            advance();
         }
         epilogue(tile0 + t, last);
     }

@@ -25,9 +25,13 @@ constexpr int MF_STAGE = (MF_TI + MF_TU) * MF_ROWB;  // 32 KiB per stage
 constexpr int MF_DMA = 2;    // 16-byte DMA ops per lane per operand per stage
 static_assert(MF_DMA * MF_NW * 64 * 16 == MF_TI * MF_ROWB, "DMA ops must cover one operand stage");
 
-// 16-byte chunk swizzle within a 64-byte staged row: conflict-free
-// ds_read_b128 of 32 consecutive rows at one k-chunk for 32- or 64-bank LDS.
-GENREC_HD inline int mf_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// 16-byte chunk swizzle within a 64-byte staged row.  The fragment read of a
+// wave takes 32 consecutive rows at k-chunk c (lanes 0-31) and c+1 (lanes
+// 32-63); on gfx950 that ds_read_b128 runs at the full 256 B/clk (no bank-
+// conflict cycles in the SQ_LDS_BANK_CONFLICT counter) with the chunk xor-ed
+// by bits 2-3 of the row, while e.g. bits 1-2 xor bits 3-4 cost a 2-way
+// conflict.
+GENREC_HD inline int mf_swz(int row) { return (row >> 2) & 3; }
 
 // DMA: wave w, op j writes the 1 KiB of staged rows (j*NW + w)*16 .. +16;
 // lane l writes 16 bytes at l*16, i.e. staged row (j*NW + w)*16 + l/4 at
