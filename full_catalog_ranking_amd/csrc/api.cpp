@@ -65,7 +65,7 @@ hipError_t timed(genrec_profiler* prof, int kind, hipStream_t s, F&& launch) {
     return hipSuccess;
 }
 
-enum { KIND_SAMPLE = 0, KIND_THRESHOLD = 1, KIND_MAIN = 2, KIND_MERGE = 3, KIND_PLAN = 4 };
+enum { KIND_SAMPLE = 0, KIND_THRESHOLD = 1, KIND_MAIN = 2, KIND_MERGE = 3, KIND_PLAN = 4, KIND_RESCUE = 5 };
 
 }  // namespace
 
@@ -155,10 +155,11 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
     if (!buf || len == 0) return GENREC_ERR_INVALID_ARG;
     const DensePlan p = plan_dense(B, D, M, K, dtype);
     snprintf(buf, len,
-             "{\"path\":\"%s\",\"sample\":%d,\"stride\":%lld,\"n_sample\":%lld,\"UT\":%d,\"P\":%d,"
-             "\"tiles_per_chunk\":%d,\"CH\":%lld,\"workspace\":%zu}",
+             "{\"path\":\"%s\",\"sample\":%d,\"stride\":%lld,\"n_sample\":%lld,\"fast\":%d,\"r_fast\":%d,"
+             "\"UT\":%d,\"P\":%d,\"tiles_per_chunk\":%d,\"CH\":%lld,\"workspace\":%zu}",
              p.mfma ? "mfma" : "stream", p.sample ? 1 : 0, (long long)p.stride, (long long)p.n_sample,
-             p.main.UT, p.main.P, p.main.base + (p.main.rem ? 1 : 0), (long long)p.main.CH, p.total);
+             p.fast ? 1 : 0, p.r_fast, p.main.UT, p.main.P, p.main.base + (p.main.rem ? 1 : 0),
+             (long long)p.main.CH, p.total);
     return GENREC_OK;
 }
 
@@ -179,7 +180,11 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
     if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
 
-    float* theta = at<float>(workspace, p.off_theta);
+    float* theta_fast = at<float>(workspace, p.off_theta);
+    float* theta_safe = at<float>(workspace, p.off_theta_safe);
+    int* uflag = at<int>(workspace, p.off_uflag);
+    int* tflag = at<int>(workspace, p.off_tflag);
+    int64_t* rescued = at<int64_t>(workspace, p.off_hdr + kHdrRescued);
     float* sample = at<float>(workspace, p.off_sample);
     float* pm = at<float>(workspace, p.off_pm);
     float* pl = at<float>(workspace, p.off_pl);
@@ -188,8 +193,22 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
     uint64_t* keys = at<uint64_t>(workspace, p.off_keys);
     const bool f32 = dtype == GENREC_F32;
 
+    ThresholdArgs th{};
+    th.sample = sample;
+    th.n_sample = p.n_sample;
+    th.B = B;
+    th.K = K;
+    th.r_fast = p.r_fast;
+    th.theta_safe = theta_safe;
+    th.theta_fast = p.fast ? theta_fast : nullptr;
+    th.user_flag = uflag;
+    th.tile_flag = tflag;
+    th.rescued = rescued;
+    // The rescue counter is cleared by the threshold kernel when it runs,
+    // else by the merge (see below).
+
+    MfmaArgs a{};
     if (p.mfma) {
-        MfmaArgs a{};
         a.H = (const uint16_t*)H;
         a.E = (const uint16_t*)E;
         a.B = B;
@@ -204,7 +223,7 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
             a.rem = p.pre.rem;
             a.sample_out = sample;
             if ((st = hip_status(timed(prof, KIND_SAMPLE, s, [&] { return launch_mfma(a, 0, s); }))) != GENREC_OK) return st;
-            if ((st = hip_status(timed(prof, KIND_THRESHOLD, s, [&] { return launch_threshold(sample, p.n_sample, K, theta, B, s); }))) != GENREC_OK) return st;
+            if ((st = hip_status(timed(prof, KIND_THRESHOLD, s, [&] { return launch_threshold(th, s); }))) != GENREC_OK) return st;
         }
         a.n_tiles = (int)ceil_div(M, kMfmaTileItems);
         a.tile_stride = 1;
@@ -213,7 +232,7 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
         a.base = p.main.base;
         a.rem = p.main.rem;
         a.sample_out = nullptr;
-        a.theta = p.sample ? theta : nullptr;
+        a.theta = p.sample ? (p.fast ? theta_fast : theta_safe) : nullptr;
         a.keys = keys;
         a.key_stride = p.key_stride;
         a.pm = pm;
@@ -235,14 +254,14 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
             a.P = p.pre.P;
             a.sample_out = sample;
             if ((st = hip_status(timed(prof, KIND_SAMPLE, s, [&] { return launch_stream(a, 0, f32, (int64_t)B * p.pre.P, s); }))) != GENREC_OK) return st;
-            if ((st = hip_status(timed(prof, KIND_THRESHOLD, s, [&] { return launch_threshold(sample, p.n_sample, K, theta, B, s); }))) != GENREC_OK) return st;
+            if ((st = hip_status(timed(prof, KIND_THRESHOLD, s, [&] { return launch_threshold(th, s); }))) != GENREC_OK) return st;
         }
         a.n_items = M;
         a.tile_stride = 1;
         a.CH = p.main.CH;
         a.P = p.main.P;
         a.sample_out = nullptr;
-        a.theta = p.sample ? theta : nullptr;
+        a.theta = p.sample ? theta_safe : nullptr;
         a.keys = keys;
         a.pm = pm;
         a.pl = pl;
@@ -263,8 +282,24 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
     m.out_idx = out_idx;
     m.out_scores = out_scores;
     m.out_lse = out_lse;
+    // clears the error words and, without a threshold pass, the rescue count
     m.clear_err = at<int64_t>(workspace, p.off_hdr);
-    return hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }));
+    m.mode = p.fast ? 1 : 0;
+    m.user_flag = uflag;
+    m.tile_flag = tflag;
+    m.rescued = rescued;
+    if ((st = hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }))) != GENREC_OK) return st;
+    if (!p.fast) return GENREC_OK;
+    // Rescue: users the fast threshold left short of K candidates are scored
+    // again (their whole user tile) with the K-th sampled score and merged;
+    // with no flagged user both launches exit at once.
+    a.theta = theta_safe;
+    a.tile_flag = tflag;
+    a.user_flag = uflag;
+    if ((st = hip_status(timed(prof, KIND_RESCUE, s, [&] { return launch_mfma(a, 1, s); }))) != GENREC_OK) return st;
+    m.mode = 2;
+    m.clear_err = nullptr;
+    return hip_status(timed(prof, KIND_RESCUE, s, [&] { return launch_merge(m, s); }));
 }
 
 size_t genrec_score_candidates_topk_workspace(int B, int D, int64_t M, int64_t nnz, int K, int dtype) {
@@ -349,6 +384,7 @@ int genrec_score_candidates_topk_profiled(const void* H, const void* E, int dtyp
     m.out_scores = out_scores;
     m.out_lse = out_lse;
     m.clear_err = nullptr;
+    m.mode = 0;
     return hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }));
 }
 
@@ -360,6 +396,17 @@ int genrec_get_device_errors(const void* workspace, void* stream, int64_t* n_bad
     if (hipStreamSynchronize(s) != hipSuccess) return GENREC_ERR_HIP;
     if (n_bad_ids) *n_bad_ids = h[0];
     if (n_bad_offsets) *n_bad_offsets = h[1];
+    return GENREC_OK;
+}
+
+int genrec_get_rescued_users(const void* workspace, void* stream, int64_t* n_rescued) {
+    if (!workspace || !n_rescued) return GENREC_ERR_INVALID_ARG;
+    int64_t h = 0;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(&h, (const uint8_t*)workspace + kHdrRescued, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return GENREC_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return GENREC_ERR_HIP;
+    *n_rescued = h;
     return GENREC_OK;
 }
 

@@ -13,9 +13,10 @@
 //                      lists: VALU dot products (v_dot2_f32_bf16 / fp32 FMA)
 //                      over gathered rows, one 16-byte load per lane per row
 //                      step, eight rows in flight per wave.
-//  threshold_kernel    per user, the K-th largest score of a sample of whole
-//                      catalog tiles: a lower bound of the K-th largest score,
-//                      used as the candidate threshold of the main pass.
+//  threshold_kernel    per user, the K-th (and a smaller rank's) largest score
+//                      of a sample of whole catalog tiles: lower bounds of the
+//                      catalog's order statistics, the candidate thresholds of
+//                      the main pass and of the rescue pass.
 //  merge_kernel        per user, lse from the per-piece (max, sum-exp) pairs
 //                      and the exact top-K of the candidates (range-narrowing
 //                      histogram select + bitonic sort), written sorted.
@@ -48,6 +49,8 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     int L = blockIdx.x;
     if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
     const int c = L / a.UT, ut = L - c * a.UT;
+    // rescue pass: user tiles without a flagged user have nothing to redo
+    if (MODE == 1 && a.tile_flag != nullptr && a.tile_flag[ut] == 0) return;
     const int tile0 = c * a.base + min(c, a.rem);  // first pass-tile of this chunk
     const int ntiles = a.base + (c < a.rem ? 1 : 0);
     const int u0 = ut * MF_TU;
@@ -145,7 +148,9 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         cnt_[ub] = 0;
         float t = -FLT_MAX;
         if (MODE == 1 && a.theta != nullptr && u < a.B) t = fmaxf(a.theta[u], -FLT_MAX);
-        th_[ub] = (u < a.B) ? t : INFINITY;  // users past B never append
+        // users past B never append, nor, in the rescue pass, unflagged users
+        const bool active = u < a.B && (a.user_flag == nullptr || a.user_flag[u] != 0);
+        th_[ub] = active ? t : INFINITY;
     }
 
     auto epilogue = [&](int t, int stg) {
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 #pragma unroll
         for (int ub = 0; ub < MF_UB; ++ub) {
             const int u = u0 + wu * MF_WU + ub * 32 + (lane & 31);
-            if (u < a.B) {
+            if (u < a.B && (a.user_flag == nullptr || a.user_flag[u] != 0)) {
                 const int64_t piece = ((int64_t)u * a.P + c) * 4 + g;
                 a.pm[piece] = m_[ub];
                 a.pl[piece] = l_[ub];
@@ -709,44 +714,154 @@ __device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
     return kth;
 }
 
-// Source: one dense fp32 score row (the catalog sample of one user).
-struct DenseRowSrc {
-    const float* row;
-    int64_t n;
-    __device__ int64_t total() const { return n; }
-    template <class F>
-    __device__ void for_each(F&& f) const {
-        for (int64_t e0 = threadIdx.x; e0 < n; e0 += (int64_t)SEL_NT * SEL_UNR) {
-            float v[SEL_UNR];
-#pragma unroll
-            for (int q = 0; q < SEL_UNR; ++q) {
-                const int64_t e = e0 + (int64_t)q * SEL_NT;
-                v[q] = e < n ? row[e] : 0.f;
-            }
-#pragma unroll
-            for (int q = 0; q < SEL_UNR; ++q) {
-                const int64_t e = e0 + (int64_t)q * SEL_NT;
-                if (e < n) f(rank_key(v[q], (uint32_t)e));
-            }
-        }
-    }
+// ---------------------------------------------------------------------------
+// Sampled thresholds: per user, the K-th (and the r_fast-th) largest score of
+// the catalog sample.  One block per user holds the whole sample in
+// registers as 32-bit order keys (32 per thread), so the row is read once;
+// selection narrows a key range with 256-bin histograms -- the first pass is
+// shared by both ranks, later passes only count keys inside the rank's bin.
+// ---------------------------------------------------------------------------
+constexpr int TH_NT = 1024;
+constexpr int TH_PER = 32;
+constexpr int TH_NW = TH_NT / kWave;
+static_assert(TH_NT * TH_PER == 32768, "one user's sample must fit the block");
+
+struct ThShared {
+    int hist[TH_NW][256];
+    unsigned red_lo[TH_NW], red_hi[TH_NW];
+    int bin[2], above[2];
 };
 
-__global__ __launch_bounds__(SEL_NT) void threshold_kernel(const float* sample, int64_t n_sample, int K,
-                                                           float* theta) {
-    __shared__ SelShared sh;
-    const int b = blockIdx.x;
-    if (n_sample < K) {
-        if (threadIdx.x == 0) theta[b] = -INFINITY;
+__device__ __forceinline__ int th_shift(unsigned span) { return max(0, 32 - __clz(span) - 8); }
+
+// Histogram of the keys in [lo, hi] into 256 bins of width 2^shift (summed
+// over waves into hist[0]); every thread calls it.
+__device__ void th_hist(const uint32_t (&key)[TH_PER], unsigned lo, unsigned hi, int shift, ThShared& sh) {
+    const int tid = threadIdx.x, w = tid >> 6;
+    for (int i = tid; i < TH_NW * 256; i += TH_NT) (&sh.hist[0][0])[i] = 0;
+    __syncthreads();
+    int* wh = sh.hist[w];
+#pragma unroll
+    for (int i = 0; i < TH_PER; ++i)
+        if (key[i] >= lo && key[i] <= hi) atomicAdd(&wh[(key[i] - lo) >> shift], 1);
+    __syncthreads();
+    if (tid < 256) {
+        int t = 0;
+#pragma unroll
+        for (int q = 0; q < TH_NW; ++q) t += sh.hist[q][tid];
+        sh.hist[0][tid] = t;
+    }
+    __syncthreads();
+}
+
+// Wave 0: the bin d holding the k-th largest key of the histogram
+// (above(d) < k <= above(d) + hist[d]); result in sh.bin[q], sh.above[q].
+__device__ void th_find(int k, int q, ThShared& sh) {
+    const int lane = threadIdx.x & 63;
+    if ((threadIdx.x >> 6) != 0) return;
+    int v[4], tsum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // lane owns 4 bins, highest bins first
+        v[i] = sh.hist[0][255 - (lane * 4 + i)];
+        tsum += v[i];
+    }
+    int incl = tsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    int run = incl - tsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (run < k && k <= run + v[i]) {
+            sh.bin[q] = 255 - (lane * 4 + i);
+            sh.above[q] = run;
+        }
+        run += v[i];
+    }
+}
+
+// A hair below the sampled score: still a lower bound of the catalog's
+// order statistic, robust to any rounding difference between passes.
+__device__ __forceinline__ float th_lower(float t) { return t - fabsf(t) * 0x1p-20f - FLT_MIN; }
+
+__global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
+    __shared__ ThShared sh;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid == 0) {
+        if (a.user_flag != nullptr) a.user_flag[b] = 0;
+        if (a.tile_flag != nullptr && b % MF_TU == 0) a.tile_flag[b / MF_TU] = 0;
+        if (a.rescued != nullptr && b == 0) *a.rescued = 0;
+    }
+    const int n = (int)a.n_sample;
+    if (n < a.K) {
+        if (tid == 0) {
+            a.theta_safe[b] = -INFINITY;
+            if (a.theta_fast != nullptr) a.theta_fast[b] = -INFINITY;
+        }
         return;
     }
-    DenseRowSrc src{sample + (int64_t)b * n_sample, n_sample};
-    const uint64_t kth = block_select<false>(src, K, sh);
-    if (threadIdx.x == 0) {
-        const float t = key_score(kth);
-        // A hair lower than the sampled K-th score: still a valid lower bound
-        // of the catalog's K-th score, and robust to any rounding difference.
-        theta[b] = t - fabsf(t) * 0x1p-20f - FLT_MIN;
+    const float* row = a.sample + (int64_t)b * a.n_sample;
+    uint32_t key[TH_PER];  // 0 = no key (every score's key is larger)
+    unsigned lo = ~0u, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < TH_PER; ++i) {
+        const int e = i * TH_NT + tid;
+        key[i] = e < n ? order_key(row[e]) : 0u;
+        if (e < n) {
+            lo = min(lo, key[i]);
+            hi = max(hi, key[i]);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        lo = min(lo, (unsigned)__shfl_xor((int)lo, o));
+        hi = max(hi, (unsigned)__shfl_xor((int)hi, o));
+    }
+    if (lane == 0) { sh.red_lo[w] = lo; sh.red_hi[w] = hi; }
+    __syncthreads();
+    lo = sh.red_lo[0];
+    hi = sh.red_hi[0];
+#pragma unroll
+    for (int q = 1; q < TH_NW; ++q) {
+        lo = min(lo, sh.red_lo[q]);
+        hi = max(hi, sh.red_hi[q]);
+    }
+    // ranks: q = 0 the K-th largest, q = 1 the r_fast-th largest
+    const int nq = a.theta_fast != nullptr ? 2 : 1;
+    unsigned qlo[2] = {lo, lo}, qhi[2] = {hi, hi};
+    int krem[2] = {a.K, max(1, min(a.r_fast, a.K))};
+    if (lo < hi) {  // first pass, shared by both ranks
+        const int shift = th_shift(hi - lo);
+        th_hist(key, lo, hi, shift, sh);
+        for (int q = 0; q < nq; ++q) th_find(krem[q], q, sh);
+        __syncthreads();
+        for (int q = 0; q < nq; ++q) {
+            krem[q] -= sh.above[q];
+            qlo[q] = lo + ((unsigned)sh.bin[q] << shift);
+            const unsigned top = qlo[q] + ((1u << shift) - 1u);
+            qhi[q] = top < hi ? top : hi;
+        }
+        __syncthreads();
+    }
+    for (int q = 0; q < nq; ++q) {
+        while (qlo[q] < qhi[q]) {  // at most three more passes: each narrows the span 256-fold
+            const int shift = th_shift(qhi[q] - qlo[q]);
+            th_hist(key, qlo[q], qhi[q], shift, sh);
+            th_find(krem[q], 0, sh);
+            __syncthreads();
+            krem[q] -= sh.above[0];
+            const unsigned nlo = qlo[q] + ((unsigned)sh.bin[0] << shift);
+            const unsigned top = nlo + ((1u << shift) - 1u);
+            qhi[q] = top < qhi[q] ? top : qhi[q];
+            qlo[q] = nlo;
+            __syncthreads();
+        }
+    }
+    if (tid == 0) {
+        a.theta_safe[b] = th_lower(key_to_score(qlo[0]));
+        if (a.theta_fast != nullptr) a.theta_fast[b] = th_lower(key_to_score(qlo[1]));
     }
 }
 
@@ -845,9 +960,12 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     __shared__ float2 s_ml[SEL_NT / kWave];
     __shared__ unsigned long long s_n[SEL_NT / kWave];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (a.mode == 2 && a.user_flag[b] == 0) return;  // rescue merge: flagged users only
     if (b == 0 && tid == 0 && a.clear_err != nullptr) {
         a.clear_err[0] = 0;
         a.clear_err[1] = 0;
+        // no threshold pass cleared the rescue count, and nothing adds to it
+        if (a.mode == 0 && a.rescued != nullptr) *a.rescued = 0;
     }
     int64_t p0, p1;
     if (a.piece_begin != nullptr) {
@@ -877,6 +995,16 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     tot.init();
     unsigned long long ntot = 0;
     for (int q = 0; q < SEL_NT / kWave; ++q) { tot.merge(s_ml[q].x, s_ml[q].y); ntot += s_n[q]; }
+    if (a.mode == 1 && ntot < (unsigned long long)a.K) {
+        // the fast threshold let fewer than K items through: the rescue pass
+        // recomputes this user with the K-th sampled score
+        if (tid == 0) {
+            a.user_flag[b] = 1;
+            a.tile_flag[b / MF_TU] = 1;
+            atomicAdd((unsigned long long*)a.rescued, 1ull);
+        }
+        return;
+    }
     if (tid == 0)
         a.out_lse[b] = tot.l > 0.f ? tot.m + __builtin_amdgcn_logf(tot.l) * kLn2 : -INFINITY;
 
@@ -1014,9 +1142,9 @@ hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, 
     return hipGetLastError();
 }
 
-hipError_t launch_threshold(const float* sample, int64_t n_sample, int K, float* theta, int B,
-                            hipStream_t s) {
-    hipLaunchKernelGGL(threshold_kernel, dim3(B), dim3(SEL_NT), 0, s, sample, n_sample, K, theta);
+hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s) {
+    if (a.n_sample > (int64_t)TH_NT * TH_PER) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(threshold_kernel, dim3(a.B), dim3(TH_NT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -25,6 +25,10 @@ struct MfmaArgs {
     float* pl;
     int* pcnt;
     int64_t* preg;
+    // rescue pass (mode 1): only user tiles with tile_flag[ut] != 0 run, and
+    // only users with user_flag[u] != 0 append candidates and write records
+    const int* tile_flag;
+    const int* user_flag;
 };
 
 struct CandPiece {
@@ -68,6 +72,24 @@ struct MergeArgs {
     float* out_scores;
     float* out_lse;
     int64_t* clear_err;  // zeroed by block 0 when non-null
+    // mode 0: every user; 1: a user with fewer than K candidates is flagged
+    // (user_flag, tile_flag of its 256-user tile, rescued count) and skipped;
+    // 2: only flagged users
+    int mode;
+    int* user_flag;
+    int* tile_flag;
+    int64_t* rescued;
+};
+
+struct ThresholdArgs {
+    const float* sample;  // [B][n_sample] sampled scores
+    int64_t n_sample;     // <= 32768
+    int B, K, r_fast;
+    float* theta_safe;    // [B] lower bound of the K-th largest sampled score
+    float* theta_fast;    // [B] lower bound of the r_fast-th largest (may be null)
+    int* user_flag;       // [B] cleared (may be null)
+    int* tile_flag;       // [ceil(B/256)] cleared (may be null)
+    int64_t* rescued;     // cleared by block 0 (may be null)
 };
 
 struct CandPlanArgs {
@@ -82,8 +104,7 @@ struct CandPlanArgs {
 
 hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s);
 hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, hipStream_t s);
-hipError_t launch_threshold(const float* sample, int64_t n_sample, int K, float* theta, int B,
-                            hipStream_t s);
+hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_cand_plan(const CandPlanArgs& a, hipStream_t s);
 

@@ -16,6 +16,8 @@ constexpr int kStreamMaxB = 8;         // bf16 batches up to this size use the V
 constexpr int64_t kSampleMinM = 65536; // smaller catalogs skip the threshold pre-pass
 constexpr int64_t kSampleMinStride = 32; // sample every G-th catalog tile, G >= 32
 constexpr int64_t kSampleMaxTiles = 128; // sampled items per user at most 128 * 256
+constexpr int64_t kSampleMaxItems = 32768;  // = kSampleMaxTiles * 256: one user's sample fits the threshold kernel
+constexpr int kFastOversample = 4;     // fast threshold: expected candidates ~ 4 K
 constexpr int64_t kStreamPieces = 2048;  // target work pieces of the VALU path
 constexpr int64_t kStreamChunkAlign = 32;
 constexpr int kCandPiece = 256;        // candidate entries per piece (matches the kernels)
@@ -34,12 +36,19 @@ struct DensePlan {
     int64_t stride = 1;        // G: the sample holds catalog tiles 0, G, 2G, ... (full tiles only)
     int64_t sample_tiles = 0;  // number of sampled 256-row tiles
     int64_t n_sample = 0;      // sampled items = 256 * sample_tiles
+    // Fast threshold (MFMA path): the r_fast-th largest sampled score instead
+    // of the K-th, r_fast ~ 4 K n_sample / M, so that about 4 K catalog items
+    // are expected to pass.  A user with fewer than K candidates is detected
+    // by the merge and recomputed by the rescue pass with the K-th sampled
+    // score, which at least K catalog items always reach.
+    int r_fast = 0;
+    bool fast = false;
     Chunking main, pre;
     int pieces_per_chunk = 1;  // MFMA: one piece per (user, chunk, lane group) = 4
     int64_t n_pieces = 0;
     int64_t key_stride = 0;    // candidate-region elements per user
-    size_t off_hdr = 0, off_theta = 0, off_sample = 0, off_pm = 0, off_pl = 0, off_pcnt = 0,
-           off_preg = 0, off_keys = 0, total = 0;
+    size_t off_hdr = 0, off_theta = 0, off_theta_safe = 0, off_uflag = 0, off_tflag = 0, off_sample = 0,
+           off_pm = 0, off_pl = 0, off_pcnt = 0, off_preg = 0, off_keys = 0, total = 0;
 };
 
 inline Chunking chunk_mfma(int B, int64_t n_tiles) {
@@ -72,6 +81,8 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
     p.sample_tiles = ceil_div(full_tiles, p.stride);
     p.n_sample = p.sample_tiles * kMfmaTileItems;
     p.sample = M >= kSampleMinM && p.n_sample >= 4 * (int64_t)K;
+    p.r_fast = (int)std::min<int64_t>(K, std::max<int64_t>(1, ceil_div((int64_t)kFastOversample * K * p.n_sample, M)));
+    p.fast = p.mfma && p.sample && p.r_fast < K;
     p.main = p.mfma ? chunk_mfma(B, ceil_div(M, kMfmaTileItems)) : chunk_stream(B, M);
     if (p.sample) p.pre = p.mfma ? chunk_mfma(B, p.sample_tiles) : chunk_stream(B, p.n_sample);
     p.pieces_per_chunk = p.mfma ? 4 : 1;
@@ -82,6 +93,12 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
     o += 256;
     p.off_theta = o;
     o = align_up(o + sizeof(float) * (size_t)B, 256);
+    p.off_theta_safe = o;
+    o = align_up(o + sizeof(float) * (size_t)B, 256);
+    p.off_uflag = o;
+    o = align_up(o + sizeof(int) * (size_t)B, 256);
+    p.off_tflag = o;
+    o = align_up(o + sizeof(int) * (size_t)ceil_div(B, kMfmaTileUsers), 256);
     p.off_sample = o;
     if (p.sample) o = align_up(o + sizeof(float) * (size_t)B * (size_t)p.n_sample, 256);
     p.off_pm = o;
@@ -105,8 +122,8 @@ struct CandPlan {
 };
 
 // Header of every workspace: int64 bad-id count, int64 bad-offset count,
-// int32 piece count.
-constexpr size_t kHdrErrIds = 0, kHdrErrOffsets = 8, kHdrPieces = 16;
+// int32 piece count (candidate calls); int64 rescued-user count (dense calls).
+constexpr size_t kHdrErrIds = 0, kHdrErrOffsets = 8, kHdrPieces = 16, kHdrRescued = 24;
 
 inline CandPlan plan_cand(int B, int64_t nnz) {
     CandPlan p;

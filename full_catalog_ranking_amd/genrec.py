@@ -24,6 +24,7 @@ EXPORTED = (
     "genrec_score_candidates_topk_workspace",
     "genrec_score_candidates_topk",
     "genrec_get_device_errors",
+    "genrec_get_rescued_users",
     "genrec_describe_plan",
     "genrec_status_string",
     "genrec_version",
@@ -34,7 +35,7 @@ EXPORTED = (
     "genrec_score_lse_topk_profiled",
     "genrec_score_candidates_topk_profiled",
 )
-KERNEL_KINDS = ("sample_score", "threshold", "main_score", "merge", "cand_plan")
+KERNEL_KINDS = ("sample_score", "threshold", "main_score", "merge", "cand_plan", "rescue")
 
 
 class GenrecError(RuntimeError):
@@ -64,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.genrec_score_candidates_topk.restype = I
         L.genrec_get_device_errors.argtypes = [P, P, P, P]
         L.genrec_get_device_errors.restype = I
+        L.genrec_get_rescued_users.argtypes = [P, P, P]
+        L.genrec_get_rescued_users.restype = I
         L.genrec_describe_plan.argtypes = [I, I, I64, I, I, ctypes.c_char_p, SZ]
         L.genrec_describe_plan.restype = I
         L.genrec_status_string.argtypes = [I]
@@ -234,3 +237,12 @@ def device_errors(workspace: torch.Tensor) -> tuple[int, int]:
     if st != 0:
         raise GenrecError(st, "genrec_get_device_errors")
     return a.value, b.value
+
+
+def rescued_users(workspace: torch.Tensor) -> int:
+    """Users of the last full-catalog call on this workspace that needed the rescue pass."""
+    n = ctypes.c_int64(0)
+    st = lib().genrec_get_rescued_users(_ptr(workspace), _stream_handle(workspace.device), ctypes.byref(n))
+    if st != 0:
+        raise GenrecError(st, "genrec_get_rescued_users")
+    return n.value

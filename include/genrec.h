@@ -114,6 +114,17 @@ int genrec_score_candidates_topk(const void* H, const void* E, int dtype,
 int genrec_get_device_errors(const void* workspace, void* stream, int64_t* n_bad_ids,
                              int64_t* n_bad_offsets);
 
+/*
+ * Number of users of the last genrec_score_lse_topk call on this workspace
+ * that needed the rescue pass.  On the MFMA path with a sampled threshold the
+ * main pass keeps only scores at or above a fast threshold (a high-ranked
+ * sampled score); a user for whom fewer than K catalog items reach it is
+ * scored again with the K-th largest sampled score, which at least K items
+ * always reach.  Results are exact either way; the count reports the extra
+ * work.  Synchronises `stream`.  GENREC_ERR_INVALID_ARG for null pointers.
+ */
+int genrec_get_rescued_users(const void* workspace, void* stream, int64_t* n_rescued);
+
 /* Introspection: writes into buf (at most len bytes, NUL-terminated) a JSON
  * object describing how genrec_score_lse_topk would run these sizes: the
  * scoring path ("mfma" or "stream"), whether the sampled-threshold pre-pass
@@ -129,11 +140,12 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
  * returns, per kernel kind, the number of launches and their summed duration
  * in milliseconds.  Kinds: 0 sampled-threshold scoring pass, 1 threshold
  * selection, 2 main scoring pass (MFMA or VALU), 3 top-K merge, 4 candidate
- * work-list plan.  One profiler holds up to `max_launches` launches; further
+ * work-list plan, 5 rescue (the scoring pass and merge that recompute users
+ * left short of K candidates; they exit at once when no user is).  One profiler holds up to `max_launches` launches; further
  * launches are not recorded.  A profiler may only be used by one stream at a
  * time.  create returns NULL on failure.
  */
-#define GENREC_NUM_KERNEL_KINDS 5
+#define GENREC_NUM_KERNEL_KINDS 6
 typedef struct genrec_profiler genrec_profiler;
 genrec_profiler* genrec_profiler_create(int max_launches);
 void genrec_profiler_destroy(genrec_profiler* prof);

@@ -79,6 +79,7 @@ def test_candidate_argument_errors(L):
     assert need > 0
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 4, 64, 100, 10, 5, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WORKSPACE
     assert L.genrec_get_device_errors(None, None, None, None) == INVALID
+    assert L.genrec_get_rescued_users(None, None, None) == INVALID
 
 
 def test_workspace_queries(L):
@@ -95,8 +96,14 @@ def test_plan_selection(L):
     import torch
     p = genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)
     assert p["path"] == "mfma" and p["sample"] == 1 and p["UT"] == 4 and p["P"] == 64
+    # every 32nd of the 3906 full catalog tiles is sampled; fast threshold rank ceil(4 K n_sample / M)
+    assert p["n_sample"] == 123 * 256 and p["fast"] == 1 and p["r_fast"] == -(-4 * 500 * 123 * 256 // 1_000_000)
     p = genrec.describe_plan(256, 2048, 100_000, 100, torch.bfloat16)
     assert p["path"] == "mfma" and p["sample"] == 1 and p["P"] == 256
+    assert p["fast"] == 1 and p["r_fast"] == -(-4 * 100 * p["n_sample"] // 100_000)
+    # the VALU path keeps the K-th sampled score (no rescue pass)
+    p = genrec.describe_plan(3, 96, 70_000, 50, torch.bfloat16)
+    assert p["path"] == "stream" and p["sample"] == 1 and p["fast"] == 0
     p = genrec.describe_plan(1, 2048, 5000, 100, torch.bfloat16)
     assert p["path"] == "stream" and p["sample"] == 0
     p = genrec.describe_plan(4, 256, 5000, 10, torch.float32)

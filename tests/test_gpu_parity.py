@@ -118,6 +118,38 @@ def test_mfma_ragged(dev, oracle_mod, B, D, M, K):
     parity.check_dense(g, ref, where="mfma %s" % ((B, D, M, K),))
 
 
+def test_fast_threshold_rescue(dev, oracle_mod):
+    """A user whose always-sampled catalog tile 0 holds 40 scaled copies of its
+    own vector: the fast threshold (a high-ranked sampled score) lets fewer
+    than K catalog items through for that user, the merge flags it, and the
+    rescue pass (the K-th sampled score) must still give the exact result;
+    every other user keeps its first-pass result."""
+    from full_catalog_ranking_amd import genrec
+    B, D, M, K = 16, 64, 131072, 100
+    d = synth.make_dense(B, D, M, seed=11)
+    plan = genrec.describe_plan(B, D, M, K, torch.bfloat16)
+    assert plan["path"] == "mfma" and plan["fast"] == 1 and plan["r_fast"] < 40 < K
+    h = synth.bf16_bits_to_f32(d["H"][3])
+    E = d["E"].copy()
+    for i in range(40):
+        E[i] = synth.f32_to_bf16_bits((h * np.float32(0.05 + 0.001 * i)).astype(np.float32))
+    H, Ed = to_dev(d["H"], dev), to_dev(E, dev)
+    ws = torch.empty(genrec.workspace_bytes(B, D, M, K, H.dtype), dtype=torch.uint8, device=dev)
+    print("  rescue B=%d D=%d M=%d K=%d plan=%s" % (B, D, M, K, plan), flush=True)
+    idx, sc, ls = genrec.score_lse_topk(H, Ed, K, workspace=ws)
+    n_rescued = genrec.rescued_users(ws)
+    g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
+    ref = oracle_mod.full(d["H"], E, K)
+    parity.check_dense(g, ref, where="rescue")
+    assert set(g[0][3, :40].tolist()) == set(range(40))
+    assert n_rescued == 1
+    # a second call on the same workspace without the planted rows: no rescue
+    idx, sc, ls = genrec.score_lse_topk(H, to_dev(d["E"], dev), K, workspace=ws)
+    assert genrec.rescued_users(ws) == 0
+    parity.check_dense((idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()),
+                       oracle_mod.full(d["H"], d["E"], K, users=[0, 3, 15]), where="no rescue")
+
+
 @pytest.mark.parametrize("B,D,M,K,bf16", [
     (3, 96, 70000, 50, True),    # VALU path with the sampled pre-pass
     (1, 8, 1, 5, True),          # M = 1, K > M
