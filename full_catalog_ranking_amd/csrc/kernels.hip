@@ -153,77 +153,75 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         th_[ub] = active ? t : INFINITY;
     }
 
-    auto epilogue = [&](int t, int stg) {
+    auto epilogue = [&](int t) {
         const int lim = tile_valid(t);  // valid tile rows
         const bool full = lim == MF_TI;
         const int64_t j0 = tile_item0(t);
-        // Scores go through LDS one quad at a time (it keeps the live register
-        // set small): quad q of a block sits in one of this wave's own four
-        // DMA chunks of the stage just consumed -- only this wave's next DMA
-        // rewrites them.
-        uint8_t* xs = smem[stg] + lane * 16;
-        auto xq = [&](int q) -> int {
-            return (q >> 1) * (MF_TI * MF_ROWB) + mf_dma_lds_byte(w, 0, q & 1);
-        };
+        // Rows past the end of a partial tile read as -inf: they add nothing
+        // to the sum and never pass a threshold.  Each 32 x 32 block (16
+        // scores per lane) is finished before the next is read, fenced by a
+        // scheduling barrier, which keeps the live register set small.
 #pragma unroll
         for (int ub = 0; ub < MF_UB; ++ub) {
-            const int ul = wu * MF_WU + ub * 32 + (lane & 31);
-            const int u = u0 + ul;
+            const int u = u0 + wu * MF_WU + ub * 32 + (lane & 31);
             if (MODE == 0) {
-                if (u < a.B) {
+                if (u < a.B) {  // rows jq .. jq+3 of the lane are consecutive items: one 16-byte store
                     float* orow = a.sample_out + (int64_t)u * n_pass + (int64_t)t * MF_TI;
 #pragma unroll
                     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int jl = lrow0 + ib * 32 + (r >> 2) * 8 + (r & 3);
-                            if (jl < lim) orow[jl] = acc[ib][ub][r];
+                        for (int q = 0; q < 4; ++q) {
+                            const int jq = lrow0 + ib * 32 + q * 8;
+                            if (jq + 3 < lim)
+                                *(float4*)(orow + jq) = make_float4(acc[ib][ub][4 * q], acc[ib][ub][4 * q + 1],
+                                                                    acc[ib][ub][4 * q + 2], acc[ib][ub][4 * q + 3]);
+                            else
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (jq + e < lim) orow[jq + e] = acc[ib][ub][4 * q + e];
                         }
                 }
                 continue;
             }
-            // Sum of exp(s - ref) against a reference: the running max (or, on
-            // the first tile, row 0 of the tile).  A score more than 64 nats
-            // above the reference moves the reference there first, so no term
-            // can overflow; terms far below it underflow harmlessly.
+            // exact running max per 32 x 32 block: the block's max, one rescale
+            // of the running sum and one exp per score against it
             const float th = th_[ub];
-            float ref = m_[ub] == -INFINITY ? acc[0][ub][0] : m_[ub];
-            float rb = ref * kLog2e, lsum = 0.f;
-            uint64_t* kreg = a.keys + (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles;
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
+                const int jb = lrow0 + ib * 32;  // rows jb + 8q + e
+                float v[16];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(float4*)(xs + xq(q)) =
-                        make_float4(acc[ib][ub][4 * q], acc[ib][ub][4 * q + 1], acc[ib][ub][4 * q + 2], acc[ib][ub][4 * q + 3]);
-#pragma unroll 1
-                for (int q = 0; q < 4; ++q) {
-                    const float4 v4 = *(const float4*)(xs + xq(q));
-                    float v[4] = {v4.x, v4.y, v4.z, v4.w};
-                    const int jq = lrow0 + ib * 32 + q * 8;  // rows jq .. jq+3
-                    if (!full) {  // rows past the end: -inf adds nothing and never passes
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[e] = jq + e < lim ? v[e] : -INFINITY;
-                    }
-                    const float qmax = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-                    if (qmax > ref + 64.f) {
-                        lsum *= fast_exp2((ref - qmax) * kLog2e);
-                        ref = qmax;
-                        rb = qmax * kLog2e;
-                    }
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) lsum += fast_exp2(fmaf(v[e], kLog2e, -rb));
-                    if (qmax >= th) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (v[e] >= th) kreg[cnt_[ub]++] = rank_key(v[e], (uint32_t)(j0 + jq + e));
+                for (int r = 0; r < 16; ++r) {
+                    v[r] = acc[ib][ub][r];
+                    if (!full) {
+                        const int m = (jb + (r >> 2) * 8 + (r & 3) - lim) >> 31;  // all ones iff the row is valid
+                        v[r] = __uint_as_float((__float_as_uint(v[r]) & (uint32_t)m) | (0xFF800000u & ~(uint32_t)m));
                     }
                 }
+                float bmax = v[0];
+#pragma unroll
+                for (int r = 1; r < 16; ++r) bmax = fmaxf(bmax, v[r]);
+                const float mnew = fmaxf(m_[ub], bmax);
+                if (mnew != -INFINITY) {
+                    const float mb = mnew * kLog2e;
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        s0 += fast_exp2(fmaf(v[r], kLog2e, -mb));
+                        s1 += fast_exp2(fmaf(v[r + 1], kLog2e, -mb));
+                    }
+                    l_[ub] = l_[ub] * fast_exp2(fmaf(m_[ub], kLog2e, -mb)) + (s0 + s1);
+                    m_[ub] = mnew;
+                }
+                if (bmax >= th) {
+                    uint64_t* kreg = a.keys + (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles;
+                    const uint32_t idb = (uint32_t)(j0 + jb);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (v[r] >= th) kreg[cnt_[ub]++] = rank_key(v[r], idb + (r >> 2) * 8 + (r & 3));
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            LseState st{m_[ub], l_[ub]};
-            st.merge(ref, lsum);
-            m_[ub] = st.m;
-            l_[ub] = st.l;
         }
     };
 
@@ -271,7 +269,6 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
             for (int ub = 0; ub < MF_UB; ++ub) acc[ib][ub] = f32x16_t{};
-        int last = 0;
         for (int k = 0; k < nk; ++k) {
             dma_op(ls, lk * MF_BK, 0);
             load_frag(f1, cs, 1, k * MF_BK);
@@ -286,7 +283,6 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             MF_WAIT_VMCNT(kWaitOps);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            last = cs;
             cs = cs + 1 == MF_NS ? 0 : cs + 1;
             dma_op(ls, lk * MF_BK, 1);
             // (on the very last step this reads a stage whose data is never used)
@@ -301,7 +297,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             advance();
         }
-        epilogue(tile0 + t, last);
+        epilogue(tile0 + t);
     }
     MF_WAIT_VMCNT(0);
 
@@ -718,8 +714,8 @@ __device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
 // Sampled thresholds: per user, the K-th (and the r_fast-th) largest score of
 // the catalog sample.  One block per user holds the whole sample in
 // registers as 32-bit order keys (32 per thread), so the row is read once;
-// selection narrows a key range with 256-bin histograms -- the first pass is
-// shared by both ranks, later passes only count keys inside the rank's bin.
+// selection narrows a key range with 256-bin histograms, after a subsample
+// histogram and an exact count have cut the range to a few k keys.
 // ---------------------------------------------------------------------------
 constexpr int TH_NT = 1024;
 constexpr int TH_PER = 32;
@@ -832,21 +828,58 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
     const int nq = a.theta_fast != nullptr ? 2 : 1;
     unsigned qlo[2] = {lo, lo}, qhi[2] = {hi, hi};
     int krem[2] = {a.K, max(1, min(a.r_fast, a.K))};
-    if (lo < hi) {  // first pass, shared by both ranks
+    if (lo < hi) {
+        // Cut the range from below before the full histograms: a histogram of
+        // every 8th key (register slots 0, 8, 16, 24) places the (2k/8 + 8)-th
+        // largest of that subsample; the lower edge c of its bin is checked
+        // exactly -- if at least k keys reach c, the k-th largest lies in
+        // [c, hi], which holds a few k keys instead of all of them, so the
+        // narrowing passes below count few keys.  Otherwise the full range.
+        int nsub = 0;
+#pragma unroll
+        for (int i = 0; i < TH_PER; i += 8) nsub += max(0, min(TH_NT, n - i * TH_NT));
         const int shift = th_shift(hi - lo);
-        th_hist(key, lo, hi, shift, sh);
-        for (int q = 0; q < nq; ++q) th_find(krem[q], q, sh);
+        for (int i = tid; i < TH_NW * 256; i += TH_NT) (&sh.hist[0][0])[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TH_PER; i += 8)
+            if (key[i] >= lo && key[i] <= hi) atomicAdd(&sh.hist[w][(key[i] - lo) >> shift], 1);
+        __syncthreads();
+        if (tid < 256) {
+            int t = 0;
+#pragma unroll
+            for (int q = 0; q < TH_NW; ++q) t += sh.hist[q][tid];
+            sh.hist[0][tid] = t;
+        }
+        __syncthreads();
+        for (int q = 0; q < nq; ++q) th_find(min(nsub, 2 * ((krem[q] + 7) / 8) + 8), q, sh);
+        __syncthreads();
+        unsigned cut[2];
+        int cnt[2] = {0, 0};
+        for (int q = 0; q < nq; ++q) cut[q] = lo + ((unsigned)sh.bin[q] << shift);
+#pragma unroll
+        for (int i = 0; i < TH_PER; ++i) {
+            cnt[0] += key[i] >= cut[0];
+            if (nq > 1) cnt[1] += key[i] >= cut[1];
+        }
         __syncthreads();
         for (int q = 0; q < nq; ++q) {
-            krem[q] -= sh.above[q];
-            qlo[q] = lo + ((unsigned)sh.bin[q] << shift);
-            const unsigned top = qlo[q] + ((1u << shift) - 1u);
-            qhi[q] = top < hi ? top : hi;
+            int v = cnt[q];
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+            if (lane == 0) sh.hist[q][w] = v;
+        }
+        __syncthreads();
+        for (int q = 0; q < nq; ++q) {
+            int tot = 0;
+#pragma unroll
+            for (int x = 0; x < TH_NW; ++x) tot += sh.hist[q][x];
+            if (tot >= krem[q]) qlo[q] = cut[q];
         }
         __syncthreads();
     }
     for (int q = 0; q < nq; ++q) {
-        while (qlo[q] < qhi[q]) {  // at most three more passes: each narrows the span 256-fold
+        while (qlo[q] < qhi[q]) {  // each pass narrows the span 256-fold: at most four
             const int shift = th_shift(qhi[q] - qlo[q]);
             th_hist(key, qlo[q], qhi[q], shift, sh);
             th_find(krem[q], 0, sh);
