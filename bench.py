@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="large", choices=["large", "batch", "gemv", "tiny", "cand"])
+    ap.add_argument("--workload", default="large", choices=["large", "batch", "gemv", "tiny", "cand", "gemv_big"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")

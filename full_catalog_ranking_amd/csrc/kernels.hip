@@ -494,8 +494,9 @@ __global__ __launch_bounds__(ST_NT) void stream_score_kernel(StreamArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int SEL_NT = 256;
 constexpr int SEL_NB = 256;     // histogram bins per narrowing pass
-constexpr int SEL_GCAP = 4096;  // range gathered into LDS once it holds at most this many keys
-constexpr int SEL_SMALL = 512;  // range sorted once it holds at most this many keys
+constexpr int SEL_GCAP = 6144;  // range gathered into LDS once it holds at most this many keys
+constexpr int SEL_SMALL = 256;  // range ranked once it holds at most this many keys
+static_assert(SEL_GCAP >= GENREC_KMAX, "the merge places the final K keys in the gather buffer");
 constexpr int SEL_UNR = 8;      // independent loads in flight per thread
 
 struct SelShared {
@@ -545,6 +546,23 @@ __device__ void block_sort_desc(uint64_t* buf, int n) {
             }
             __syncthreads();
         }
+    }
+}
+
+// Rank placement: key i of in[0..n) goes to out[r], r = the number of keys
+// that rank before it (larger, or equal with a lower index), i.e. out holds
+// the keys in descending order, a stable sort.  O(n^2 / threads) compares but
+// no barrier inside; used for the few hundred keys at the end of a selection.
+// With limit < n only the keys of rank < limit are written.
+__device__ void block_rank_place(const uint64_t* in, int n, uint64_t* out, int limit) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const uint64_t x = in[i];
+        int r = 0;
+        for (int j = 0; j < n; ++j) {
+            const uint64_t y = in[j];
+            r += (y > x) | ((y == x) & (j < i));
+        }
+        if (r < limit) out[r] = x;
     }
 }
 
@@ -620,17 +638,20 @@ __device__ int64_t narrow(const Src& src, unsigned long long& lo, unsigned long 
 
 // Finds the k-th largest key (1 <= k <= n) among the keys the source yields
 // and, with COLLECT, leaves the k largest keys in sh.out[0..k) (unsorted).
-// Returns the k-th largest key.  Passes over the source:
+// Returns the k-th largest key.  At most SEL_GCAP keys: one pass copies them
+// into LDS.  More: passes over the source --
 //   1. min / max of all keys;
 //   2. while the candidate range [lo, hi] holds more than SEL_GCAP keys, a
 //      narrowing pass (histogram of the range, keep the bin of the k-th);
 //   3. gather: the range into LDS and (COLLECT) every key above it into out.
 // Then, in LDS, narrowing continues until at most SEL_SMALL keys remain in
 // the range, which are sorted; keys above the final range join out.
-template <bool COLLECT, class Src>
-__device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    unsigned long long lo = ~0ull, hi = 0;
+// Block-wide min and max of the keys a source yields (every thread gets both).
+template <class Src>
+__device__ void block_minmax(const Src& src, unsigned long long& lo, unsigned long long& hi, SelShared& sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    lo = ~0ull;
+    hi = 0;
     src.for_each([&](uint64_t key) {
         lo = key < lo ? key : lo;
         hi = key > hi ? key : hi;
@@ -646,26 +667,43 @@ __device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
         hi = sh.red_hi[q] > hi ? sh.red_hi[q] : hi;
     }
     __syncthreads();
+}
 
+template <bool COLLECT, class Src>
+__device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
+    const int tid = threadIdx.x;
+    unsigned long long lo, hi;
     int64_t n_range = src.total();
     int k_rem = k;
-    while (lo != hi && n_range > SEL_GCAP) n_range = narrow(src, lo, hi, k_rem, sh);
-
-    // gather the range into LDS; keys above it are in the result for sure
-    if (tid == 0) { sh.cnt_a = 0; sh.cnt_b = 0; }
-    __syncthreads();
-    {
-        const unsigned long long flo = lo, fhi = hi;
-        const bool single = flo == fhi;
-        src.for_each([&](uint64_t key) {
-            if (key > fhi) {
-                if (COLLECT) sh.out[atomicAdd(&sh.cnt_a, 1)] = key;
-            } else if (key >= flo && !single) {
-                sh.gbuf[atomicAdd(&sh.cnt_b, 1)] = key;
-            }
-        });
+    int ng;
+    if (n_range <= SEL_GCAP) {
+        // few keys: one pass copies them all into LDS (each to its position in
+        // the source's order), and everything else happens there
+        src.gather(sh.gbuf);
+        if (tid == 0) sh.cnt_a = 0;
+        __syncthreads();
+        ng = (int)n_range;
+        block_minmax(LdsSrc{sh.gbuf, ng}, lo, hi, sh);
+    } else {
+        block_minmax(src, lo, hi, sh);
+        while (lo != hi && n_range > SEL_GCAP) n_range = narrow(src, lo, hi, k_rem, sh);
+        // gather the range into LDS; keys above it are in the result for sure
+        if (tid == 0) { sh.cnt_a = 0; sh.cnt_b = 0; }
+        __syncthreads();
+        {
+            const unsigned long long flo = lo, fhi = hi;
+            const bool single = flo == fhi;
+            src.for_each([&](uint64_t key) {
+                if (key > fhi) {
+                    if (COLLECT) sh.out[atomicAdd(&sh.cnt_a, 1)] = key;
+                } else if (key >= flo && !single) {
+                    sh.gbuf[atomicAdd(&sh.cnt_b, 1)] = key;
+                }
+            });
+        }
+        __syncthreads();
+        ng = sh.cnt_b;
     }
-    __syncthreads();
     uint64_t kth;
     if (lo == hi) {  // every key left in the range is the k-th (equal keys)
         kth = lo;
@@ -676,7 +714,6 @@ __device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
         __syncthreads();
         return kth;
     }
-    const int ng = sh.cnt_b;
     LdsSrc lsrc{sh.gbuf, ng};
     while (lo != hi && n_range > SEL_SMALL) n_range = narrow(lsrc, lo, hi, k_rem, sh);
     // keys of the gathered set above the final range join out; the range is sorted
@@ -701,10 +738,11 @@ __device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
         if (COLLECT)
             for (int i = tid; i < k_rem; i += SEL_NT) sh.out[n_above + i] = lo;
     } else {
-        block_sort_desc(sh.sbuf, (int)n_range);
-        kth = sh.sbuf[k_rem - 1];
-        if (COLLECT)
-            for (int i = tid; i < k_rem; i += SEL_NT) sh.out[n_above + i] = sh.sbuf[i];
+        // the k_rem largest keys of the range, in descending order, after the
+        // keys above it
+        block_rank_place(sh.sbuf, (int)n_range, sh.out + n_above, k_rem);
+        __syncthreads();
+        kth = sh.out[n_above + k_rem - 1];
     }
     __syncthreads();
     return kth;
@@ -915,9 +953,12 @@ struct PieceSrc {
     int64_t n;  // total keys
     PieceShared* ps;
     __device__ int64_t total() const { return n; }
+    // Calls f(key, e) for every key, e = its index in the concatenation of
+    // the pieces' regions.
     template <class F>
-    __device__ void for_each(F&& f) const {
+    __device__ void walk(F&& f) const {
         const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+        int ebase = 0;
         for (int64_t pb = p0; pb < p1; pb += MG_PB) {
             const int np = (int)min((int64_t)MG_PB, p1 - pb);
             // exclusive scan of the batch's counts (4 per thread)
@@ -979,11 +1020,20 @@ struct PieceSrc {
                     }
 #pragma unroll
                     for (int q = 0; q < SEL_UNR; ++q)
-                        if (e0 + q < e_end) f(kv[q]);
+                        if (e0 + q < e_end) f(kv[q], ebase + e0 + q);
                 }
             }
+            ebase += tot;
             __syncthreads();
         }
+    }
+    template <class F>
+    __device__ void for_each(F&& f) const {
+        walk([&](uint64_t key, int) { f(key); });
+    }
+    // Every key to dst[e] (needs total() entries of room).
+    __device__ void gather(uint64_t* dst) const {
+        walk([&](uint64_t key, int e) { dst[e] = key; });
     }
 };
 
@@ -1048,11 +1098,19 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     if (keff > 0) {
         PieceSrc src{a.keys, a.pcnt, a.preg, p0, p1, (int64_t)ntot, &ps};
         block_select<true>(src, keff, sh);
-        block_sort_desc(sh.out, keff);
+        // the K keys in ranking order: rank placement for a few hundred
+        // (quadratic compares, one barrier), a bitonic sort for more
+        if (keff <= 256) {
+            block_rank_place(sh.out, keff, sh.gbuf, keff);
+        } else {
+            block_sort_desc(sh.out, keff);
+            for (int i = tid; i < keff; i += SEL_NT) sh.gbuf[i] = sh.out[i];
+        }
+        __syncthreads();
     }
     for (int i = tid; i < K; i += SEL_NT) {
         if (i < keff) {
-            const uint64_t key = sh.out[i];
+            const uint64_t key = sh.gbuf[i];
             oidx[i] = (int32_t)key_id(key);
             osc[i] = key_score(key);
         } else {

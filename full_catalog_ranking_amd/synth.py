@@ -175,6 +175,8 @@ WORKLOADS = {
     "batch": dict(B=256, D=2048, M=100_000, K=100, dtype="bf16"),
     "large": dict(B=1024, D=4096, M=1_000_000, K=500, dtype="bf16"),
     "cand":  dict(B=4096, D=2048, M=1_000_000, K=100, dtype="bf16", lo=100, hi=3000),
+    # one user against an 8 GB catalog: sustained catalog streaming at B = 1
+    "gemv_big": dict(B=1, D=4096, M=1_000_000, K=100, dtype="bf16"),
 }
 
 TINY_PLANT_ITEM = 17
