@@ -65,7 +65,8 @@ hipError_t timed(genrec_profiler* prof, int kind, hipStream_t s, F&& launch) {
     return hipSuccess;
 }
 
-enum { KIND_SAMPLE = 0, KIND_THRESHOLD = 1, KIND_MAIN = 2, KIND_MERGE = 3, KIND_PLAN = 4, KIND_RESCUE = 5 };
+enum { KIND_SAMPLE = 0, KIND_THRESHOLD = 1, KIND_MAIN = 2, KIND_MERGE = 3, KIND_PLAN = 4, KIND_RESCUE = 5,
+       KIND_HOT_SELECT = 6, KIND_HOT_SCORE = 7 };
 
 }  // namespace
 
@@ -307,7 +308,7 @@ size_t genrec_score_candidates_topk_workspace(int B, int D, int64_t M, int64_t n
     if (check_common(dummy, dummy, dtype, B, D, M, K, (const int32_t*)dummy, dummy, dummy) != GENREC_OK)
         return 0;
     if (nnz < 0) return 0;
-    return plan_cand(B, nnz).total;
+    return plan_cand(B, D, M, nnz, dtype).total;
 }
 
 int genrec_score_candidates_topk(const void* H, const void* E, int dtype, const int64_t* cand_offsets,
@@ -326,7 +327,7 @@ int genrec_score_candidates_topk_profiled(const void* H, const void* E, int dtyp
     if (st != GENREC_OK) return st;
     if (nnz < 0 || !cand_offsets || (nnz > 0 && !cand_ids)) return GENREC_ERR_INVALID_ARG;
     if (!aligned(cand_offsets, 8) || !aligned(cand_ids, 4)) return GENREC_ERR_INVALID_ARG;
-    const CandPlan p = plan_cand(B, nnz);
+    const CandPlan p = plan_cand(B, D, M, nnz, dtype);
     if (!workspace || workspace_bytes < p.total) return GENREC_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
@@ -351,12 +352,53 @@ int genrec_score_candidates_topk_profiled(const void* H, const void* E, int dtyp
     c.err = err;
     if ((st = hip_status(timed(prof, KIND_PLAN, s, [&] { return launch_cand_plan(c, s); }))) != GENREC_OK) return st;
 
+    if (p.hot) {
+        // hot head: count, pick and gather the most-listed rows, then score
+        // them densely for every user
+        HotArgs h{};
+        h.ids = cand_ids;
+        h.nnz = nnz;
+        h.E = (const uint16_t*)E;
+        h.M = M;
+        h.D = D;
+        h.c_min = p.c_min;
+        h.t_max = p.t_max;
+        h.n_hblk = p.n_hblk;
+        h.cnt = at<int>(workspace, p.off_cnt);
+        h.hot_idx = at<int>(workspace, p.off_hot_idx);
+        h.hist = at<int>(workspace, p.off_hist);
+        h.meta = at<int>(workspace, p.off_meta);
+        h.hblk = at<int>(workspace, p.off_hblk);
+        h.hot_ids = at<int>(workspace, p.off_hot_ids);
+        h.e_hot = at<uint16_t>(workspace, p.off_ehot);
+        if ((st = hip_status(timed(prof, KIND_HOT_SELECT, s, [&] { return launch_hot_select(h, s); }))) != GENREC_OK)
+            return st;
+        MfmaArgs d{};
+        d.H = (const uint16_t*)H;
+        d.E = h.e_hot;
+        d.B = B;
+        d.D = D;
+        d.M = p.t_max;
+        d.n_tiles = p.t_max / kMfmaTileItems;
+        d.tile_stride = 1;
+        d.UT = p.hot_chunks.UT;
+        d.P = p.hot_chunks.P;
+        d.base = p.hot_chunks.base;
+        d.rem = p.hot_chunks.rem;
+        d.sample_out = at<float>(workspace, p.off_shot);
+        d.live_rows = h.meta + 1;
+        if ((st = hip_status(timed(prof, KIND_HOT_SCORE, s, [&] { return launch_mfma(d, 0, s); }))) != GENREC_OK) return st;
+    }
+
     StreamArgs a{};
     a.H = H;
     a.E = E;
     a.B = B;
     a.D = D;
     a.M = M;
+    a.hot_idx = p.hot ? at<int>(workspace, p.off_hot_idx) : nullptr;
+    a.s_hot = p.hot ? at<float>(workspace, p.off_shot) : nullptr;
+    a.t_hot = p.t_max;
     a.ids = cand_ids;
     a.n_pieces = n_pieces;
     a.table = table;

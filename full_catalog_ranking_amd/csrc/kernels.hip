@@ -26,6 +26,7 @@
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "mfma_layout.hpp"
+#include "plan.hpp"
 
 namespace genrec {
 
@@ -53,6 +54,8 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     if (MODE == 1 && a.tile_flag != nullptr && a.tile_flag[ut] == 0) return;
     const int tile0 = c * a.base + min(c, a.rem);  // first pass-tile of this chunk
     const int ntiles = a.base + (c < a.rem ? 1 : 0);
+    // dense pass over a partly filled catalog: chunks past its live rows are idle
+    if (MODE == 0 && a.live_rows != nullptr && (int64_t)tile0 * a.tile_stride * MF_TI >= *a.live_rows) return;
     const int u0 = ut * MF_TU;
     const int nk = (a.D + MF_BK - 1) / MF_BK;
     const int D = a.D;
@@ -375,10 +378,14 @@ __device__ __forceinline__ float reduce_scatter8(float (&v)[ST_U], int lane) {
     return s;
 }
 
+static_assert(ST_NT == CAND_PIECE, "one thread per list entry of a piece");
+
 template <typename T, int MODE>
 __global__ __launch_bounds__(ST_NT) void stream_score_kernel(StreamArgs a) {
     __shared__ int s_cnt;
     __shared__ float2 s_ml[ST_NT / kWave];
+    __shared__ int s_cold[MODE == 2 ? CAND_PIECE : 1];  // list mode: ids still to gather
+    __shared__ int s_wc[ST_NT / kWave];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     constexpr int VEC = Vec16<T>::N;
 
@@ -410,20 +417,55 @@ __global__ __launch_bounds__(ST_NT) void stream_score_kernel(StreamArgs a) {
     LseState st;
     st.init();
 
+    if (MODE == 2) {
+        // One thread per entry: ids outside [0, M) are counted and skipped; a
+        // hot id's score is looked up in the dense hot scores; the remaining
+        // ids go, in list order, to a block-wide list that the gather loop
+        // below works through.
+        const int e = tid;
+        int id = 0;
+        bool valid = false;
+        if (e < n) {
+            id = a.ids[e0 + e];
+            valid = id >= 0 && (int64_t)id < a.M;
+        }
+        const uint64_t badmask = __ballot(e < n && !valid);
+        if (lane == 0 && badmask) atomicAdd((unsigned long long*)a.err, (unsigned long long)__popcll(badmask));
+        bool cold = valid;
+        if (valid && a.hot_idx != nullptr) {
+            const int hi = a.hot_idx[id];
+            if (hi >= 0) {
+                cold = false;
+                const float s = a.s_hot[(int64_t)b * a.t_hot + hi];
+                st.add(s);
+                if (s >= th) {
+                    const int pos = atomicAdd(&s_cnt, 1);
+                    a.keys[region + pos] = rank_key(s, (uint32_t)id);
+                }
+            }
+        }
+        const uint64_t cm = __ballot(cold);
+        if (lane == 0) s_wc[w] = __popcll(cm);
+        __syncthreads();
+        int base = 0, tot = 0;
+#pragma unroll
+        for (int q = 0; q < ST_NT / kWave; ++q) {
+            base += q < w ? s_wc[q] : 0;
+            tot += s_wc[q];
+        }
+        if (cold) s_cold[base + __popcll(cm & ((1ull << lane) - 1ull))] = id;
+        n = tot;
+        __syncthreads();
+    }
+
     for (int64_t g0 = (int64_t)w * ST_U; g0 < n; g0 += (ST_NT / kWave) * ST_U) {
         int64_t item[ST_U];
         bool ok[ST_U];
         if (MODE == 2) {
-            int myid = -1;
-            if (lane < ST_U && g0 + lane < n) myid = a.ids[e0 + g0 + lane];
-            const bool bad = lane < ST_U && g0 + lane < n && (myid < 0 || (int64_t)myid >= a.M);
-            const uint64_t badmask = __ballot(bad);
-            if (lane == 0 && badmask) atomicAdd((unsigned long long*)a.err, (unsigned long long)__popcll(badmask));
 #pragma unroll
             for (int u = 0; u < ST_U; ++u) {
-                const int id = __shfl(myid, u);
-                ok[u] = g0 + u < n && id >= 0 && (int64_t)id < a.M;
-                item[u] = ok[u] ? id : 0;
+                ok[u] = g0 + u < n;
+                item[u] = ok[u] ? s_cold[g0 + u] : 0;
             }
         } else {
 #pragma unroll
@@ -1204,6 +1246,180 @@ __global__ __launch_bounds__(PL_NT) void cand_plan_kernel(CandPlanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Candidate lists, hot head: which catalog rows to score densely
+// ---------------------------------------------------------------------------
+constexpr int HOT_NT = 256;
+constexpr int HOT_PER = kHotBlock / HOT_NT;  // ids per thread in the compaction
+
+__global__ __launch_bounds__(HOT_NT) void hot_clear_kernel(HotArgs a) {
+    const int64_t stride = (int64_t)gridDim.x * HOT_NT;
+    for (int64_t i = (int64_t)blockIdx.x * HOT_NT + threadIdx.x; i < a.M; i += stride) a.cnt[i] = 0;
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < kHotBins; i += HOT_NT) a.hist[i] = 0;
+        if (threadIdx.x < 4) a.meta[threadIdx.x] = 0;
+    }
+}
+
+// How many list entries name each catalog id, estimated from every
+// kHotSample-th entry of the id array (all lists, in range ids): the hot set
+// only steers where scores are computed, never what they are, so an estimate
+// does; sampling cuts the device-wide atomics on popular ids 16-fold.
+__global__ __launch_bounds__(HOT_NT) void hot_count_kernel(HotArgs a) {
+    const int64_t n_samples = (a.nnz + kHotSample - 1) / kHotSample;
+    const int64_t stride = (int64_t)gridDim.x * HOT_NT;
+    for (int64_t t = (int64_t)blockIdx.x * HOT_NT + threadIdx.x; t < n_samples; t += stride) {
+        const int id = a.ids[t * kHotSample];
+        if (id >= 0 && (int64_t)id < a.M) atomicAdd(&a.cnt[id], 1);
+    }
+}
+
+// Histogram of the non-zero counts (bin = min(count, 4095)).
+__global__ __launch_bounds__(HOT_NT) void hot_hist_kernel(HotArgs a) {
+    __shared__ int h[kHotBins];
+    for (int i = threadIdx.x; i < kHotBins; i += HOT_NT) h[i] = 0;
+    __syncthreads();
+    const int64_t stride = (int64_t)gridDim.x * HOT_NT;
+    for (int64_t i = (int64_t)blockIdx.x * HOT_NT + threadIdx.x; i < a.M; i += stride) {
+        const int c = a.cnt[i];
+        if (c > 0) atomicAdd(&h[min(c, kHotBins - 1)], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kHotBins; i += HOT_NT)
+        if (h[i]) atomicAdd(&a.hist[i], h[i]);
+}
+
+// One block: the threshold c = the smallest count >= c_min whose suffix
+// (items with at least c entries) holds at most t_max items; none such: no
+// hot rows.  meta[0] = c, meta[1] = the number of hot rows.
+constexpr int HOT_PICK_NT = 1024;
+__global__ __launch_bounds__(HOT_PICK_NT) void hot_pick_kernel(HotArgs a) {
+    __shared__ int s_w[HOT_PICK_NT / kWave];
+    constexpr int PER = kHotBins / HOT_PICK_NT;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // thread t owns bins kHotBins-1-(PER t .. PER t + PER - 1): highest first
+    int v[PER], tsum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        v[i] = a.hist[kHotBins - 1 - (tid * PER + i)];
+        tsum += v[i];
+    }
+    int incl = tsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_w[w] = incl;
+    __syncthreads();
+    int run = incl - tsum;
+    for (int q = 0; q < w; ++q) run += s_w[q];
+    if (tid == 0) a.meta[0] = 0x7FFFFFFF;  // no hot rows unless a bin qualifies below
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int bin = kHotBins - 1 - (tid * PER + i);
+        run += v[i];  // now the suffix count of `bin`
+        // bins are visited from the top, so suffix(bin) only grows; the
+        // threshold is the lowest qualifying bin
+        const int below = bin - 1;  // suffix(below) = run + hist[below]
+        if (bin >= a.c_min && run <= a.t_max) {
+            const bool lowest = bin == a.c_min || run + a.hist[below] > a.t_max;
+            if (lowest) {
+                a.meta[0] = bin;
+                a.meta[1] = run;
+            }
+        }
+    }
+}
+
+// Hot ids per block of kHotBlock catalog ids.
+__global__ __launch_bounds__(HOT_NT) void hot_blockcount_kernel(HotArgs a) {
+    __shared__ int s_w[HOT_NT / kWave];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int c = a.meta[0];
+    const int64_t id0 = (int64_t)blockIdx.x * kHotBlock + (int64_t)tid * HOT_PER;
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < HOT_PER; ++i) n += (id0 + i < a.M && a.cnt[id0 + i] >= c) ? 1 : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
+    if (lane == 0) s_w[w] = n;
+    __syncthreads();
+    if (tid == 0) {
+        int t = 0;
+        for (int q = 0; q < HOT_NT / kWave; ++q) t += s_w[q];
+        a.hblk[blockIdx.x] = t;
+    }
+}
+
+// One block: exclusive scan of the per-block counts, in place.
+__global__ __launch_bounds__(HOT_PICK_NT) void hot_scan_kernel(HotArgs a) {
+    __shared__ int s_w[HOT_PICK_NT / kWave];
+    __shared__ int s_carry;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < a.n_hblk; base += HOT_PICK_NT) {
+        const int64_t i = base + tid;
+        const int v = i < a.n_hblk ? a.hblk[i] : 0;
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+        }
+        if (lane == 63) s_w[w] = incl;
+        __syncthreads();
+        int pre = s_carry;
+        for (int q = 0; q < w; ++q) pre += s_w[q];
+        if (i < a.n_hblk) a.hblk[i] = pre + incl - v;
+        __syncthreads();
+        if (tid == HOT_PICK_NT - 1) s_carry = pre + incl;
+        __syncthreads();
+    }
+}
+
+// Hot index of every catalog id (-1: not hot) and the hot ids in id order.
+__global__ __launch_bounds__(HOT_NT) void hot_assign_kernel(HotArgs a) {
+    __shared__ int s_w[HOT_NT / kWave];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int c = a.meta[0];
+    const int64_t id0 = (int64_t)blockIdx.x * kHotBlock + (int64_t)tid * HOT_PER;
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < HOT_PER; ++i) n += (id0 + i < a.M && a.cnt[id0 + i] >= c) ? 1 : 0;
+    int incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_w[w] = incl;
+    __syncthreads();
+    int pos = a.hblk[blockIdx.x] + incl - n;
+    for (int q = 0; q < w; ++q) pos += s_w[q];
+#pragma unroll
+    for (int i = 0; i < HOT_PER; ++i) {
+        const int64_t id = id0 + i;
+        if (id < a.M) {
+            const bool hotv = a.cnt[id] >= c;
+            a.hot_idx[id] = hotv ? pos : -1;
+            if (hotv) a.hot_ids[pos++] = (int)id;
+        }
+    }
+}
+
+// The hot catalog rows, gathered in hot-index order (rows past the hot count
+// are left as they are: their dense scores are never looked up).
+__global__ __launch_bounds__(HOT_NT) void hot_gather_kernel(HotArgs a) {
+    const int r = blockIdx.x;
+    if (r >= a.meta[1]) return;
+    const uint4* src = (const uint4*)(a.E + (int64_t)a.hot_ids[r] * a.D);
+    uint4* dst = (uint4*)(a.e_hot + (int64_t)r * a.D);
+    for (int i = threadIdx.x; i < a.D / 8; i += HOT_NT) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s) {
@@ -1241,6 +1457,23 @@ hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s) {
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(merge_kernel, dim3(a.B), dim3(SEL_NT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_hot_select(const HotArgs& a, hipStream_t s) {
+    const int fill_grid = (int)std::min<int64_t>(4096, ceil_div(a.M, HOT_NT));
+    hipLaunchKernelGGL(hot_clear_kernel, dim3(fill_grid), dim3(HOT_NT), 0, s, a);
+    const int64_t n_samples = (a.nnz + kHotSample - 1) / kHotSample;
+    if (n_samples > 0)
+        hipLaunchKernelGGL(hot_count_kernel, dim3((unsigned)std::min<int64_t>(4096, ceil_div(n_samples, HOT_NT))),
+                           dim3(HOT_NT), 0, s, a);
+    // few blocks: each adds its LDS histogram to the global one once
+    hipLaunchKernelGGL(hot_hist_kernel, dim3((unsigned)std::min<int64_t>(256, ceil_div(a.M, HOT_NT))), dim3(HOT_NT), 0, s, a);
+    hipLaunchKernelGGL(hot_pick_kernel, dim3(1), dim3(HOT_PICK_NT), 0, s, a);
+    hipLaunchKernelGGL(hot_blockcount_kernel, dim3((unsigned)a.n_hblk), dim3(HOT_NT), 0, s, a);
+    hipLaunchKernelGGL(hot_scan_kernel, dim3(1), dim3(HOT_PICK_NT), 0, s, a);
+    hipLaunchKernelGGL(hot_assign_kernel, dim3((unsigned)a.n_hblk), dim3(HOT_NT), 0, s, a);
+    hipLaunchKernelGGL(hot_gather_kernel, dim3((unsigned)a.t_max), dim3(HOT_NT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -29,6 +29,9 @@ struct MfmaArgs {
     // only users with user_flag[u] != 0 append candidates and write records
     const int* tile_flag;
     const int* user_flag;
+    // mode 0: when set, only the first *live_rows catalog rows matter; chunks
+    // that start past them exit at once
+    const int* live_rows;
 };
 
 struct CandPiece {
@@ -57,6 +60,30 @@ struct StreamArgs {
     int* pcnt;
     int64_t* preg;
     int64_t* err;
+    // candidate mode, hot head: hot_idx[id] >= 0 gives the entry's score as
+    // s_hot[user * t_hot + hot_idx[id]] (no gather); null = every row gathered
+    const int* hot_idx;
+    const float* s_hot;
+    int t_hot;
+};
+
+// Hot head of the candidate lists: per-item list counts, the count threshold,
+// the deterministic compaction of hot ids and the gathered hot catalog rows.
+struct HotArgs {
+    const int32_t* ids;
+    int64_t nnz;
+    const uint16_t* E;
+    int64_t M;
+    int D;
+    int c_min, t_max;  // c_min: minimum sampled count of a hot row
+    int64_t n_hblk;
+    int* cnt;        // [M] sampled list counts
+    int* hot_idx;    // [M]
+    int* hist;       // [4096]
+    int* meta;       // [0] = c, [1] = number of hot rows
+    int* hblk;       // [n_hblk] per-block counts, then their exclusive scan
+    int* hot_ids;    // [t_max]
+    uint16_t* e_hot; // [t_max][D]
 };
 
 struct MergeArgs {
@@ -107,5 +134,6 @@ hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, 
 hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_cand_plan(const CandPlanArgs& a, hipStream_t s);
+hipError_t launch_hot_select(const HotArgs& a, hipStream_t s);
 
 }  // namespace genrec

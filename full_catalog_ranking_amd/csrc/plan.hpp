@@ -117,17 +117,51 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
 
 struct CandPlan {
     int64_t n_pieces_max = 0;
+    // Hot head (bf16, B > 8): catalog items listed at least c times over all
+    // lists (in sampled counts; c >= c_min, raised until at most t_max items
+    // qualify) are scored
+    // densely for every user on the MFMA path into s_hot[B][t_max]; the list
+    // pass looks their scores up and gathers only the other rows.
+    bool hot = false;
+    int t_max = 0, c_min = 0;
+    int64_t n_hblk = 0;  // blocks of kHotBlock catalog ids
+    Chunking hot_chunks;
     size_t off_hdr = 0, off_begin = 0, off_table = 0, off_pm = 0, off_pl = 0, off_pcnt = 0,
-           off_preg = 0, off_keys = 0, total = 0;
+           off_preg = 0, off_keys = 0, off_cnt = 0, off_hot_idx = 0, off_hist = 0, off_meta = 0, off_hblk = 0,
+           off_hot_ids = 0, off_ehot = 0, off_shot = 0, total = 0;
 };
+
+constexpr int kHotMaxRows = 16384;           // hot rows at most
+constexpr int64_t kHotMaxEBytes = 256ll << 20;  // ... and at most this much gathered catalog
+constexpr int64_t kHotMaxSBytes = 1ll << 30;    // ... and this much of dense scores
+constexpr int kHotBins = 4096;               // histogram of per-item list counts
+constexpr int kHotBlock = 4096;              // catalog ids per block of the hot compaction
+constexpr int kHotSample = 16;               // list counts are estimated from every 16th entry
 
 // Header of every workspace: int64 bad-id count, int64 bad-offset count,
 // int32 piece count (candidate calls); int64 rescued-user count (dense calls).
 constexpr size_t kHdrErrIds = 0, kHdrErrOffsets = 8, kHdrPieces = 16, kHdrRescued = 24;
 
-inline CandPlan plan_cand(int B, int64_t nnz) {
+inline CandPlan plan_cand(int B, int D, int64_t M, int64_t nnz, int dtype) {
     CandPlan p;
     p.n_pieces_max = nnz / kCandPiece + B;
+    if (dtype == 0 && B > kStreamMaxB && nnz > 0) {
+        const int64_t bpad = ceil_div(B, kMfmaTileUsers) * kMfmaTileUsers;
+        int64_t t = std::min<int64_t>(kHotMaxRows, ceil_div(M, kMfmaTileItems) * kMfmaTileItems);
+        t = std::min<int64_t>(t, kHotMaxEBytes / (2 * (int64_t)D));
+        t = std::min<int64_t>(t, kHotMaxSBytes / (4 * (int64_t)B));
+        t = t / kMfmaTileItems * kMfmaTileItems;
+        if (t >= kMfmaTileItems) {
+            p.hot = true;
+            p.t_max = (int)t;
+            // break-even: scoring a row densely for B_pad users on the matrix
+            // cores costs about as much as gathering it ~B_pad / 128 times;
+            // in sampled counts (every kHotSample-th entry) that is / 16
+            p.c_min = (int)std::max<int64_t>(2, ceil_div(std::max<int64_t>(4, bpad / 128), kHotSample));
+            p.n_hblk = ceil_div(M, kHotBlock);
+            p.hot_chunks = chunk_mfma(B, t / kMfmaTileItems);
+        }
+    }
     size_t o = 0;
     p.off_hdr = o;
     o += 256;
@@ -145,6 +179,24 @@ inline CandPlan plan_cand(int B, int64_t nnz) {
     o = align_up(o + sizeof(int64_t) * (size_t)p.n_pieces_max, 256);
     p.off_keys = o;
     o = align_up(o + sizeof(uint64_t) * (size_t)std::max<int64_t>(nnz, 1), 256);
+    if (p.hot) {
+        p.off_cnt = o;
+        o = align_up(o + sizeof(int) * (size_t)M, 256);
+        p.off_hot_idx = o;
+        o = align_up(o + sizeof(int) * (size_t)M, 256);
+        p.off_hist = o;
+        o = align_up(o + sizeof(int) * (size_t)kHotBins, 256);
+        p.off_meta = o;
+        o = align_up(o + 256, 256);
+        p.off_hblk = o;
+        o = align_up(o + sizeof(int) * (size_t)p.n_hblk, 256);
+        p.off_hot_ids = o;
+        o = align_up(o + sizeof(int) * (size_t)p.t_max, 256);
+        p.off_ehot = o;
+        o = align_up(o + 2 * (size_t)p.t_max * (size_t)D, 256);
+        p.off_shot = o;
+        o = align_up(o + sizeof(float) * (size_t)B * (size_t)p.t_max, 256);
+    }
     p.total = o;
     return p;
 }

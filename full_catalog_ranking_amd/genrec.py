@@ -35,7 +35,8 @@ EXPORTED = (
     "genrec_score_lse_topk_profiled",
     "genrec_score_candidates_topk_profiled",
 )
-KERNEL_KINDS = ("sample_score", "threshold", "main_score", "merge", "cand_plan", "rescue")
+KERNEL_KINDS = ("sample_score", "threshold", "main_score", "merge", "cand_plan", "rescue", "hot_select",
+                "hot_score")
 
 
 class GenrecError(RuntimeError):

@@ -141,11 +141,14 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
  * in milliseconds.  Kinds: 0 sampled-threshold scoring pass, 1 threshold
  * selection, 2 main scoring pass (MFMA or VALU), 3 top-K merge, 4 candidate
  * work-list plan, 5 rescue (the scoring pass and merge that recompute users
- * left short of K candidates; they exit at once when no user is).  One profiler holds up to `max_launches` launches; further
+ * left short of K candidates; they exit at once when no user is), 6 hot-head
+ * selection of a candidate call (per-item list counts, the count threshold,
+ * the compaction and gather of the most-listed catalog rows), 7 dense scoring
+ * of those rows for every user.  One profiler holds up to `max_launches` launches; further
  * launches are not recorded.  A profiler may only be used by one stream at a
  * time.  create returns NULL on failure.
  */
-#define GENREC_NUM_KERNEL_KINDS 6
+#define GENREC_NUM_KERNEL_KINDS 8
 typedef struct genrec_profiler genrec_profiler;
 genrec_profiler* genrec_profiler_create(int max_launches);
 void genrec_profiler_destroy(genrec_profiler* prof);

@@ -88,8 +88,17 @@ def test_workspace_queries(L):
     big = L.genrec_score_lse_topk_workspace(1024, 4096, 1_000_000, 500, 0)
     # candidate regions dominate: 8 bytes per (user, item)
     assert 1024 * 1_000_000 * 8 <= big <= 1024 * 1_000_000 * 8 * 1.05
-    c = L.genrec_score_candidates_topk_workspace(4096, 2048, 1_000_000, 6_400_000, 100, 0)
+    # fp32: no hot head; 8 bytes per list entry dominate
+    c = L.genrec_score_candidates_topk_workspace(4096, 2048, 1_000_000, 6_400_000, 100, 1)
     assert 6_400_000 * 8 <= c <= 6_400_000 * 8 * 1.5
+    # bf16 adds the hot head: per-item counts and hot index (2 x 4 bytes per catalog item),
+    # 16,384 gathered rows of 2 D bytes and their dense scores for every user
+    hot = 2 * 4 * 1_000_000 + 16384 * 2048 * 2 + 4096 * 16384 * 4
+    cb = L.genrec_score_candidates_topk_workspace(4096, 2048, 1_000_000, 6_400_000, 100, 0)
+    assert c + hot <= cb <= c + hot * 1.01
+    # few users: no hot head
+    assert (L.genrec_score_candidates_topk_workspace(8, 2048, 1_000_000, 20_000, 100, 0)
+            == L.genrec_score_candidates_topk_workspace(8, 2048, 1_000_000, 20_000, 100, 1))
 
 
 def test_plan_selection(L):

@@ -235,6 +235,30 @@ def test_candidate_edge_cases(dev, oracle_mod):
     assert list(g[0][2][:4]) in ([12, 12, 12, 40], [40, 12, 12, 12], [12, 12, 40, 12], [12, 40, 12, 12])
 
 
+@pytest.mark.parametrize("B,M,lo,hi,seed", [
+    (600, 20_000, 400, 800, 21),   # more than 16,384 items reach the minimum count: the threshold rises
+    (300, 5_000, 50, 400, 22),     # every listed popular item is hot, the tail is gathered
+])
+def test_candidates_hot_head(dev, oracle_mod, B, M, lo, hi, seed):
+    """Zipf-weighted lists over a small catalog: the most-listed rows are scored
+    densely on the matrix cores and looked up, the rest gathered; duplicates
+    and out-of-range ids keep their meaning, and two runs agree bit for bit."""
+    d = synth.make_dense(B, 64, M, seed=seed)
+    off, ids = synth.gen_candidates(B, M, seed, lo, hi)
+    ids = ids.copy()
+    ids[5] = ids[4]        # a duplicate inside user 0's list
+    ids[17] = -3           # out of range, skipped and counted
+    ids[40] = M + 7
+    d["offsets"], d["ids"] = off, ids
+    g, errs = run_cand(d, 50, dev)
+    assert errs == (2, 0)
+    ref = oracle_mod.cand(d["H"], d["E"], off, ids, 50)
+    parity.check_cand(g, ref, off, ids, where="hot head %s" % ((B, M),))
+    g2, _ = run_cand(d, 50, dev)
+    for x, y in zip(g, g2):
+        assert np.array_equal(x, y)
+
+
 def test_candidate_malformed_offsets(dev):
     B, D, M, K = 4, 64, 100, 5
     d = synth.make_dense(B, D, M, seed=9)
