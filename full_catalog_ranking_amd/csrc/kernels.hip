@@ -793,52 +793,31 @@ __device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
 // ---------------------------------------------------------------------------
 // Sampled thresholds: per user, the K-th (and the r_fast-th) largest score of
 // the catalog sample.  One block per user holds the whole sample in
-// registers as 32-bit order keys (32 per thread), so the row is read once;
+// registers as 32-bit order keys (128 per thread), so the row is read once;
 // selection narrows a key range with 256-bin histograms, after a subsample
 // histogram and an exact count have cut the range to a few k keys.
 // ---------------------------------------------------------------------------
-constexpr int TH_NT = 1024;
-constexpr int TH_PER = 32;
-constexpr int TH_NW = TH_NT / kWave;
-static_assert(TH_NT * TH_PER == 32768, "one user's sample must fit the block");
+constexpr int TH_KEYS = 32768;  // one user's sample at most
 
+template <int NW>
 struct ThShared {
-    int hist[TH_NW][256];
-    unsigned red_lo[TH_NW], red_hi[TH_NW];
+    int hist[2][NW][256];  // per rank, per wave
+    unsigned red_lo[NW], red_hi[NW];
+    int cnt[2][NW];
     int bin[2], above[2];
 };
 
 __device__ __forceinline__ int th_shift(unsigned span) { return max(0, 32 - __clz(span) - 8); }
 
-// Histogram of the keys in [lo, hi] into 256 bins of width 2^shift (summed
-// over waves into hist[0]); every thread calls it.
-__device__ void th_hist(const uint32_t (&key)[TH_PER], unsigned lo, unsigned hi, int shift, ThShared& sh) {
-    const int tid = threadIdx.x, w = tid >> 6;
-    for (int i = tid; i < TH_NW * 256; i += TH_NT) (&sh.hist[0][0])[i] = 0;
-    __syncthreads();
-    int* wh = sh.hist[w];
-#pragma unroll
-    for (int i = 0; i < TH_PER; ++i)
-        if (key[i] >= lo && key[i] <= hi) atomicAdd(&wh[(key[i] - lo) >> shift], 1);
-    __syncthreads();
-    if (tid < 256) {
-        int t = 0;
-#pragma unroll
-        for (int q = 0; q < TH_NW; ++q) t += sh.hist[q][tid];
-        sh.hist[0][tid] = t;
-    }
-    __syncthreads();
-}
-
-// Wave 0: the bin d holding the k-th largest key of the histogram
-// (above(d) < k <= above(d) + hist[d]); result in sh.bin[q], sh.above[q].
-__device__ void th_find(int k, int q, ThShared& sh) {
+// Wave 0: the bin d of hist holding the k-th largest key (above(d) < k <=
+// above(d) + hist[d], bins scanned from the top); result in sh.bin[q], sh.above[q].
+template <class Sh>
+__device__ void th_find(const int* hist, int k, int q, Sh& sh) {
     const int lane = threadIdx.x & 63;
-    if ((threadIdx.x >> 6) != 0) return;
     int v[4], tsum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {  // lane owns 4 bins, highest bins first
-        v[i] = sh.hist[0][255 - (lane * 4 + i)];
+        v[i] = hist[255 - (lane * 4 + i)];
         tsum += v[i];
     }
     int incl = tsum;
@@ -862,8 +841,14 @@ __device__ void th_find(int k, int q, ThShared& sh) {
 // order statistic, robust to any rounding difference between passes.
 __device__ __forceinline__ float th_lower(float t) { return t - fabsf(t) * 0x1p-20f - FLT_MIN; }
 
+// TH_NT threads of TH_KEYS / TH_NT keys each: many threads for few users
+// (latency), fewer for many (throughput).
+template <int TH_NT>
 __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
-    __shared__ ThShared sh;
+    constexpr int TH_PER = TH_KEYS / TH_NT;
+    constexpr int TH_NW = TH_NT / kWave;
+    static_assert(TH_PER % 8 == 0 && TH_NT >= 256, "thread layout");
+    __shared__ ThShared<TH_NW> sh;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (tid == 0) {
         if (a.user_flag != nullptr) a.user_flag[b] = 0;
@@ -878,16 +863,26 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
         }
         return;
     }
+    // key e of thread t: e = 1024 i + 4 t + j (i < 32, j < 4): 16-byte loads,
+    // contiguous across the block
     const float* row = a.sample + (int64_t)b * a.n_sample;
     uint32_t key[TH_PER];  // 0 = no key (every score's key is larger)
     unsigned lo = ~0u, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < TH_PER; ++i) {
-        const int e = i * TH_NT + tid;
-        key[i] = e < n ? order_key(row[e]) : 0u;
-        if (e < n) {
-            lo = min(lo, key[i]);
-            hi = max(hi, key[i]);
+    for (int i = 0; i < TH_PER / 4; ++i) {
+        const int e = i * (TH_NT * 4) + tid * 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (e + 3 < n) v = *(const float4*)(row + e);
+        const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool in = e + 3 < n ? true : (e + j < n);
+            const float x = (e + 3 < n) ? f[j] : (e + j < n ? row[e + j] : 0.f);
+            key[4 * i + j] = in ? order_key(x) : 0u;
+            if (in) {
+                lo = min(lo, key[4 * i + j]);
+                hi = max(hi, key[4 * i + j]);
+            }
         }
     }
 #pragma unroll
@@ -909,30 +904,28 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
     unsigned qlo[2] = {lo, lo}, qhi[2] = {hi, hi};
     int krem[2] = {a.K, max(1, min(a.r_fast, a.K))};
     if (lo < hi) {
-        // Cut the range from below before the full histograms: a histogram of
-        // every 8th key (register slots 0, 8, 16, 24) places the (2k/8 + 8)-th
-        // largest of that subsample; the lower edge c of its bin is checked
-        // exactly -- if at least k keys reach c, the k-th largest lies in
-        // [c, hi], which holds a few k keys instead of all of them, so the
-        // narrowing passes below count few keys.  Otherwise the full range.
-        int nsub = 0;
-#pragma unroll
-        for (int i = 0; i < TH_PER; i += 8) nsub += max(0, min(TH_NT, n - i * TH_NT));
+        // Cut the range from below first: a histogram of every 8th key places
+        // the (2k/8 + 8)-th largest of that subsample; the lower edge c of its
+        // bin is checked exactly -- if at least k keys reach c, the k-th
+        // largest lies in [c, hi], which holds a few k keys instead of all of
+        // them.  Otherwise the full range.
+        const int nsub = (n + 7) / 8;
         const int shift = th_shift(hi - lo);
-        for (int i = tid; i < TH_NW * 256; i += TH_NT) (&sh.hist[0][0])[i] = 0;
+        for (int i = tid; i < TH_NW * 256; i += TH_NT) (&sh.hist[0][0][0])[i] = 0;
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < TH_PER; i += 8)
-            if (key[i] >= lo && key[i] <= hi) atomicAdd(&sh.hist[w][(key[i] - lo) >> shift], 1);
+            if (key[i] >= lo && key[i] <= hi) atomicAdd(&sh.hist[0][w][(key[i] - lo) >> shift], 1);
         __syncthreads();
         if (tid < 256) {
             int t = 0;
 #pragma unroll
-            for (int q = 0; q < TH_NW; ++q) t += sh.hist[q][tid];
-            sh.hist[0][tid] = t;
+            for (int q = 0; q < TH_NW; ++q) t += sh.hist[0][q][tid];
+            sh.hist[1][0][tid] = t;
         }
         __syncthreads();
-        for (int q = 0; q < nq; ++q) th_find(min(nsub, 2 * ((krem[q] + 7) / 8) + 8), q, sh);
+        if (w == 0)
+            for (int q = 0; q < nq; ++q) th_find(sh.hist[1][0], min(nsub, 2 * ((krem[q] + 7) / 8) + 8), q, sh);
         __syncthreads();
         unsigned cut[2];
         int cnt[2] = {0, 0};
@@ -942,35 +935,70 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
             cnt[0] += key[i] >= cut[0];
             if (nq > 1) cnt[1] += key[i] >= cut[1];
         }
-        __syncthreads();
         for (int q = 0; q < nq; ++q) {
             int v = cnt[q];
 #pragma unroll
             for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-            if (lane == 0) sh.hist[q][w] = v;
+            if (lane == 0) sh.cnt[q][w] = v;
         }
         __syncthreads();
         for (int q = 0; q < nq; ++q) {
             int tot = 0;
 #pragma unroll
-            for (int x = 0; x < TH_NW; ++x) tot += sh.hist[q][x];
+            for (int x = 0; x < TH_NW; ++x) tot += sh.cnt[q][x];
             if (tot >= krem[q]) qlo[q] = cut[q];
         }
-        __syncthreads();
     }
-    for (int q = 0; q < nq; ++q) {
-        while (qlo[q] < qhi[q]) {  // each pass narrows the span 256-fold: at most four
-            const int shift = th_shift(qhi[q] - qlo[q]);
-            th_hist(key, qlo[q], qhi[q], shift, sh);
-            th_find(krem[q], 0, sh);
-            __syncthreads();
-            krem[q] -= sh.above[0];
-            const unsigned nlo = qlo[q] + ((unsigned)sh.bin[0] << shift);
-            const unsigned top = nlo + ((1u << shift) - 1u);
-            qhi[q] = top < qhi[q] ? top : qhi[q];
-            qlo[q] = nlo;
-            __syncthreads();
+    // Narrowing, both ranks in the same passes: each pass histograms the keys
+    // of each open range into 256 bins of width 2^shift and keeps the bin of
+    // the rank; a span shrinks 256-fold per pass, so at most four passes.
+    for (int pass = 0; pass < 4; ++pass) {
+        const bool open0 = qlo[0] < qhi[0], open1 = nq > 1 && qlo[1] < qhi[1];
+        if (!open0 && !open1) break;  // block-uniform
+        const int sh0 = open0 ? th_shift(qhi[0] - qlo[0]) : 0;
+        const int sh1 = open1 ? th_shift(qhi[1] - qlo[1]) : 0;
+        for (int i = tid; i < 2 * TH_NW * 256; i += TH_NT) (&sh.hist[0][0][0])[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TH_PER; ++i) {
+            if (open0 && key[i] >= qlo[0] && key[i] <= qhi[0]) atomicAdd(&sh.hist[0][w][(key[i] - qlo[0]) >> sh0], 1);
+            if (open1 && key[i] >= qlo[1] && key[i] <= qhi[1]) atomicAdd(&sh.hist[1][w][(key[i] - qlo[1]) >> sh1], 1);
         }
+        __syncthreads();
+        {  // per-wave histograms summed into wave slot 0 (thread t < 256 sums bin t of both ranks)
+            int t0 = 0, t1 = 0;
+            if (tid < 256) {
+#pragma unroll
+                for (int q = 0; q < TH_NW; ++q) {
+                    t0 += sh.hist[0][q][tid];
+                    t1 += sh.hist[1][q][tid];
+                }
+            }
+            __syncthreads();
+            if (tid < 256) {
+                sh.hist[0][0][tid] = t0;
+                sh.hist[1][0][tid] = t1;
+            }
+        }
+        __syncthreads();
+        if (w == 0 && open0) th_find(sh.hist[0][0], krem[0], 0, sh);
+        if (w == 1 && open1) th_find(sh.hist[1][0], krem[1], 1, sh);
+        __syncthreads();
+        if (open0) {
+            krem[0] -= sh.above[0];
+            const unsigned nlo = qlo[0] + ((unsigned)sh.bin[0] << sh0);
+            const unsigned top = nlo + ((1u << sh0) - 1u);
+            qhi[0] = top < qhi[0] ? top : qhi[0];
+            qlo[0] = nlo;
+        }
+        if (open1) {
+            krem[1] -= sh.above[1];
+            const unsigned nlo = qlo[1] + ((unsigned)sh.bin[1] << sh1);
+            const unsigned top = nlo + ((1u << sh1) - 1u);
+            qhi[1] = top < qhi[1] ? top : qhi[1];
+            qlo[1] = nlo;
+        }
+        __syncthreads();
     }
     if (tid == 0) {
         a.theta_safe[b] = th_lower(key_to_score(qlo[0]));
@@ -1450,8 +1478,9 @@ hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, 
 }
 
 hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s) {
-    if (a.n_sample > (int64_t)TH_NT * TH_PER) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(threshold_kernel, dim3(a.B), dim3(TH_NT), 0, s, a);
+    if (a.n_sample > (int64_t)TH_KEYS) return hipErrorInvalidValue;
+    if (a.B <= 512) hipLaunchKernelGGL(threshold_kernel<1024>, dim3(a.B), dim3(1024), 0, s, a);
+    else hipLaunchKernelGGL(threshold_kernel<256>, dim3(a.B), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
