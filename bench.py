@@ -39,6 +39,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 1 GiB scratch buffer before every step (flushes the 256 MB Infinity "
+                         "Cache and the L2s) and time each step on its own, the flush outside")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure library reference rates on this GPU (device copy GB/s, "
+                         "hipBLASLt bf16 GEMM TFLOP/s) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (the reference "
                          "kernel for scaling HBM byte counters) and exit")
@@ -63,6 +69,43 @@ def copy_calibration(mib, reps):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
+def peaks():
+    """Reference rates of this GPU from library code: a 4 GiB device-to-device copy
+    (bytes read + written / time) and torch.matmul (hipBLASLt) of bf16 8192^3 with
+    the second operand transposed (both operands K-contiguous, like H and E)."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = {}
+    n = 4 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["device_copy_GBps"] = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    bt = b.t()
+    for _ in range(3):
+        c = a @ bt
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        c = a @ bt
+    e1.record()
+    torch.cuda.synchronize()
+    out["hipblaslt_bf16_8192_NT_TFLOPs"] = 2 * 8192 ** 3 * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del c
+    print(json.dumps({"peaks": out, "kind": "library reference rates on this GPU (not the spec peaks)"}), flush=True)
 
 
 def traffic_from_profile(kernel, workload):
@@ -122,6 +165,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, max(1, args.steps))
         return
+    if args.peaks:
+        peaks()
+        return
     import torch
     from full_catalog_ranking_amd import genrec, synth
 
@@ -163,12 +209,26 @@ def main():
     # stream the kernels run on); the events add no synchronisation
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step(prof)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    if args.cold:
+        # each step after a 1 GiB scratch write; only the steps are timed
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        ms = 0.0
+        for _ in range(args.steps):
+            scratch.fill_(1)
+            start.record()
+            step(prof)
+            end.record()
+            torch.cuda.synchronize()
+            ms += start.elapsed_time(end)
+        ms /= args.steps
+        del scratch
+    else:
+        start.record()
+        for _ in range(args.steps):
+            step(prof)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
     kern = prof.summary()
     log("step %.3f ms; kernels %s" % (ms, {k: "%.3f ms x%d" % (v[1] / v[0], v[0]) for k, v in kern.items()}))
 
@@ -208,7 +268,7 @@ def main():
         "dtype": "bf16" if H.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "D": D, "M": M, "K": K,
-                   **({"nnz": units} if cand else {})},
+                   **({"nnz": units} if cand else {}), **({"cache": "cold"} if args.cold else {})},
         "tflops": flops / (ms * 1e-3) / 1e12,
         "kernels_ms": {k: v[1] / v[0] for k, v in kern.items()},
         "roofline": roof,
