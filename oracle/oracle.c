@@ -28,6 +28,16 @@
  *           the lower catalog id first.  Fewer than K items: the tail is
  *           padded with (id -1, score -inf).
  *
+ *  masked   the same three steps over the items a bitmask allows: item i
+ *           takes part for user b only when bit i % 32 of word
+ *           mask[b * stride + i / 32] is set (stride 0: one mask for every
+ *           user).  Items left out add nothing to the normaliser and never
+ *           rank; fewer than K allowed items pad as above.  (Reading of the
+ *           pages' item filtering: the GenRec explainer page, on why plain
+ *           LLM rankers fall short, lists ignored business constraints and
+ *           items outside the catalog; the xGR explainer page, xBeam, filters
+ *           invalid candidates with masks.)
+ *
  *  candidates: the same three steps over user b's list
  *           ids[offsets[b] .. offsets[b+1]) only (GenRec explainer page, top-K
  *           ranking over a separately given candidate set).  Entries are
@@ -167,6 +177,33 @@ void oracle_full(const void* H, const void* E, int dtype, int64_t D, int64_t M, 
     for (int64_t r = 0; r < nu; ++r) {
         out_lse[r] = oracle_lse(S + r * M, M);
         oracle_topk_row(S + r * M, M, K, out_idx + r * K, out_score + r * K);
+    }
+}
+
+/* Masked full-catalog head for the listed users: the items of user b are
+ * those whose mask bit is set (see the header).  S (nu x M) receives every
+ * score, allowed or not. */
+void oracle_full_masked(const void* H, const void* E, int dtype, int64_t D, int64_t M, int64_t K,
+                        const uint32_t* mask, int64_t stride, const int64_t* users, int64_t nu, double* S,
+                        int64_t* out_idx, double* out_score, double* out_lse) {
+    oracle_scores(H, E, dtype, D, M, users, nu, S);
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nu; ++r) {
+        const uint32_t* mrow = mask + users[r] * stride;
+        double* s = (double*)malloc((size_t)(M > 0 ? M : 1) * sizeof(double));
+        int64_t* id = (int64_t*)malloc((size_t)(M > 0 ? M : 1) * sizeof(int64_t));
+        int64_t kept = 0;
+        for (int64_t i = 0; i < M; ++i) {
+            if ((mrow[i / 32] >> (i % 32)) & 1u) {
+                s[kept] = S[r * M + i];
+                id[kept] = i;
+                ++kept;
+            }
+        }
+        out_lse[r] = oracle_lse(s, kept);
+        rank_topk(s, id, kept, K, out_idx + r * K, out_score + r * K);
+        free(s);
+        free(id);
     }
 }
 

@@ -48,6 +48,7 @@ def _load():
         lib.oracle_lse.restype = ctypes.c_double
         lib.oracle_topk_row.argtypes = [P, I64, I64, P, P]
         lib.oracle_full.argtypes = [P, P, I32, I64, I64, I64, P, I64, P, P, P, P]
+        lib.oracle_full_masked.argtypes = [P, P, I32, I64, I64, I64, P, I64, P, I64, P, P, P, P]
         lib.oracle_cand.argtypes = [P, P, I32, I64, I64, I64, P, P, P, I64, P, P, P, P]
         lib.oracle_cand.restype = I64
         _lib = lib
@@ -127,6 +128,32 @@ def full(H: np.ndarray, E: np.ndarray, K: int, users=None):
     ls = np.empty(u.size, dtype=np.float64)
     _load().oracle_full(_ptr(H), _ptr(E), dt, D, M, K, _ptr(u), u.size, _ptr(S),
                         _ptr(idx), _ptr(sc), _ptr(ls))
+    return dict(idx=idx, score=sc, lse=ls, S=S, users=u)
+
+
+def full_masked(H: np.ndarray, E: np.ndarray, K: int, mask: np.ndarray, users=None):
+    """Masked full-catalog head: item i takes part for user b only when bit i % 32
+    of mask word [b][i // 32] (mask of shape (B, W)) or [i // 32] (shape (W,),
+    one mask for all users) is set.  Same return value as full()."""
+    H, E = np.ascontiguousarray(H), np.ascontiguousarray(E)
+    dt = _dtype_code(H)
+    assert _dtype_code(E) == dt and H.shape[1] == E.shape[1]
+    u = _users(users, H.shape[0])
+    M, D = E.shape
+    mask = np.ascontiguousarray(mask, dtype=np.uint32)
+    W = (M + 31) // 32
+    if mask.ndim == 1:
+        assert mask.size >= W
+        stride = 0
+    else:
+        assert mask.shape[0] == H.shape[0] and mask.shape[1] >= W
+        stride = mask.shape[1]
+    S = np.empty((u.size, M), dtype=np.float64)
+    idx = np.empty((u.size, K), dtype=np.int64)
+    sc = np.empty((u.size, K), dtype=np.float64)
+    ls = np.empty(u.size, dtype=np.float64)
+    _load().oracle_full_masked(_ptr(H), _ptr(E), dt, D, M, K, _ptr(mask), stride, _ptr(u), u.size, _ptr(S),
+                               _ptr(idx), _ptr(sc), _ptr(ls))
     return dict(idx=idx, score=sc, lse=ls, S=S, users=u)
 
 

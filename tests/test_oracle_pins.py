@@ -215,3 +215,73 @@ def test_tiny_golden_regression(oracle_mod):
     assert r["idx"].tolist() == g["idx"]
     assert np.allclose(r["score"], g["score"], rtol=0, atol=1e-12)
     assert np.allclose(r["lse"], g["lse"], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Masked full-catalog head
+# ---------------------------------------------------------------------------
+def _pack_mask(allowed: np.ndarray) -> np.ndarray:
+    """bool array (..., M) -> uint32 words, bit i % 32 of word i // 32 (LSB first)."""
+    M = allowed.shape[-1]
+    W = (M + 31) // 32
+    pad = np.zeros(allowed.shape[:-1] + (W * 32,), dtype=bool)
+    pad[..., :M] = allowed
+    bits = pad.reshape(allowed.shape[:-1] + (W, 32)).astype(np.uint64)
+    return (bits << np.arange(32, dtype=np.uint64)).sum(axis=-1).astype(np.uint32)
+
+
+def test_mask_packing_reads_back():
+    rng = np.random.default_rng(1)
+    a = rng.random(77) < 0.4
+    w = _pack_mask(a)
+    back = np.array([(w[i // 32] >> np.uint32(i % 32)) & 1 for i in range(77)], dtype=bool)
+    assert (back == a).all() and w.size == 3
+
+
+def test_masked_all_allowed_equals_unmasked(oracle_mod):
+    d = synth.make_dense(5, 32, 700, seed=31)
+    full = oracle_mod.full(d["H"], d["E"], 20)
+    m = oracle_mod.full_masked(d["H"], d["E"], 20, _pack_mask(np.ones(700, dtype=bool)))
+    for k in ("idx", "score", "lse"):
+        assert np.array_equal(full[k], m[k])
+
+
+def test_masked_equals_full_on_allowed_subcatalog(oracle_mod):
+    """Masking = the plain head on the catalog of allowed rows, ids mapped back."""
+    d = synth.make_dense(6, 40, 900, seed=32)
+    rng = np.random.default_rng(32)
+    allowed = rng.random((6, 900)) < 0.3
+    m = oracle_mod.full_masked(d["H"], d["E"], 25, _pack_mask(allowed))
+    for b in range(6):
+        keep = np.flatnonzero(allowed[b])
+        sub = oracle_mod.full(d["H"][b:b + 1], d["E"][keep], 25)
+        mapped = np.where(sub["idx"][0] >= 0, keep[np.maximum(sub["idx"][0], 0)], -1)
+        assert (m["idx"][b] == mapped).all()
+        assert np.array_equal(m["score"][b], sub["score"][0])
+        assert m["lse"][b] == pytest.approx(sub["lse"][0], abs=1e-13)
+
+
+def test_masked_brute_force_and_edge_cases(oracle_mod):
+    """numpy dot, scipy logsumexp and a lexsort over the allowed items; a global
+    mask; no allowed item (lse -inf, full padding); fewer allowed than K."""
+    d = synth.make_dense(3, 16, 200, seed=33, bf16=False)
+    H, E = d["H"].astype(np.float64), d["E"].astype(np.float64)
+    rng = np.random.default_rng(33)
+    allowed = rng.random(200) < 0.05          # ~10 allowed, K = 15 > allowed count
+    g = oracle_mod.full_masked(d["H"], d["E"], 15, _pack_mask(allowed))
+    for b in range(3):
+        keep = np.flatnonzero(allowed)
+        s = E[keep] @ H[b]
+        order = keep[np.lexsort((keep, -s))]
+        n = keep.size
+        assert n < 15
+        assert list(g["idx"][b][:n]) == list(order) and (g["idx"][b][n:] == -1).all()
+        assert np.isneginf(g["score"][b][n:]).all()
+        assert g["lse"][b] == pytest.approx(scipy.special.logsumexp(s), abs=1e-12)
+    none = oracle_mod.full_masked(d["H"], d["E"], 4, _pack_mask(np.zeros(200, dtype=bool)))
+    assert np.isneginf(none["lse"]).all() and (none["idx"] == -1).all() and np.isneginf(none["score"]).all()
+    # bits past M in the last word are ignored
+    w = _pack_mask(allowed)
+    w[-1] |= np.uint32(0xFFFFFFFF) << np.uint32(200 % 32)
+    g2 = oracle_mod.full_masked(d["H"], d["E"], 15, w)
+    assert np.array_equal(g2["idx"], g["idx"]) and np.array_equal(g2["lse"], g["lse"])
