@@ -171,9 +171,14 @@ int genrec_score_lse_topk(const void* H, const void* E, int dtype, int B, int D,
                                           workspace_bytes, stream, nullptr);
 }
 
-int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K,
-                                   int32_t* out_idx, float* out_scores, float* out_lse, void* workspace,
-                                   size_t workspace_bytes, void* stream, genrec_profiler* prof) {
+}  // extern "C"
+
+namespace {
+
+// The full-catalog head, with an optional item mask (null: every item).
+int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K, const uint32_t* mask,
+                int64_t mask_stride, int32_t* out_idx, float* out_scores, float* out_lse, void* workspace,
+                size_t workspace_bytes, void* stream, genrec_profiler* prof) {
     int st = check_common(H, E, dtype, B, D, M, K, out_idx, out_scores, out_lse);
     if (st != GENREC_OK) return st;
     const DensePlan p = plan_dense(B, D, M, K, dtype);
@@ -215,6 +220,8 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
         a.B = B;
         a.D = D;
         a.M = M;
+        a.mask = mask;
+        a.mask_stride = mask_stride;
         if (p.sample) {
             a.n_tiles = (int)p.sample_tiles;
             a.tile_stride = (int)p.stride;
@@ -248,6 +255,8 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
         a.B = B;
         a.D = D;
         a.M = M;
+        a.mask = mask;
+        a.mask_stride = mask_stride;
         if (p.sample) {
             a.n_items = p.n_sample;
             a.tile_stride = (int)p.stride;
@@ -289,6 +298,8 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
     m.user_flag = uflag;
     m.tile_flag = tflag;
     m.rescued = rescued;
+    m.theta_fast = theta_fast;
+    m.theta_safe = theta_safe;
     if ((st = hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }))) != GENREC_OK) return st;
     if (!p.fast) return GENREC_OK;
     // Rescue: users the fast threshold left short of K candidates are scored
@@ -301,6 +312,36 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
     m.mode = 2;
     m.clear_err = nullptr;
     return hip_status(timed(prof, KIND_RESCUE, s, [&] { return launch_merge(m, s); }));
+}
+
+}  // namespace
+
+extern "C" {
+
+int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K,
+                                   int32_t* out_idx, float* out_scores, float* out_lse, void* workspace,
+                                   size_t workspace_bytes, void* stream, genrec_profiler* prof) {
+    return score_dense(H, E, dtype, B, D, M, K, nullptr, 0, out_idx, out_scores, out_lse, workspace,
+                       workspace_bytes, stream, prof);
+}
+
+int genrec_score_lse_topk_masked_profiled(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K,
+                                          const uint32_t* item_mask, int64_t mask_stride_words, int32_t* out_idx,
+                                          float* out_scores, float* out_lse, void* workspace, size_t workspace_bytes,
+                                          void* stream, genrec_profiler* prof) {
+    if (!item_mask || !aligned(item_mask, 4)) return GENREC_ERR_INVALID_ARG;
+    if (M > 0 && mask_stride_words != 0 && mask_stride_words < (M + 31) / 32) return GENREC_ERR_INVALID_ARG;
+    if (mask_stride_words < 0) return GENREC_ERR_INVALID_ARG;
+    return score_dense(H, E, dtype, B, D, M, K, item_mask, mask_stride_words, out_idx, out_scores, out_lse,
+                       workspace, workspace_bytes, stream, prof);
+}
+
+int genrec_score_lse_topk_masked(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K,
+                                 const uint32_t* item_mask, int64_t mask_stride_words, int32_t* out_idx,
+                                 float* out_scores, float* out_lse, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    return genrec_score_lse_topk_masked_profiled(H, E, dtype, B, D, M, K, item_mask, mask_stride_words, out_idx,
+                                                 out_scores, out_lse, workspace, workspace_bytes, stream, nullptr);
 }
 
 size_t genrec_score_candidates_topk_workspace(int B, int D, int64_t M, int64_t nnz, int K, int dtype) {

@@ -37,7 +37,7 @@ namespace genrec {
 // s_waitcnt vmcnt(n) with expcnt / lgkmcnt left alone (gfx9 encoding).
 #define MF_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
 
-template <int MODE, bool KTAIL>
+template <int MODE, bool KTAIL, bool MASKED>
 __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[MF_NS][MF_STAGE];
 
@@ -167,22 +167,37 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 #pragma unroll
         for (int ub = 0; ub < MF_UB; ++ub) {
             const int u = u0 + wu * MF_WU + ub * 32 + (lane & 31);
+            // Item mask: the 32 rows of block ib that this lane group covers
+            // (rows wi*128 + ib*32 + 4*(lane/32) + 8q + e) lie in one mask word;
+            // masked items score -inf (nothing to the sum, never a candidate).
+            auto mask_word = [&](int ib) -> uint32_t {
+                if (!MASKED || u >= a.B) return 0xFFFFFFFFu;
+                const int64_t w0 = j0 + wi * 128 + ib * 32;  // multiple of 32
+                if (w0 >= a.M) return 0u;
+                return a.mask[(int64_t)u * a.mask_stride + (w0 >> 5)];
+            };
+            const int mbit0 = (lane >> 5) * 4;
             if (MODE == 0) {
                 if (u < a.B) {  // rows jq .. jq+3 of the lane are consecutive items: one 16-byte store
                     float* orow = a.sample_out + (int64_t)u * n_pass + (int64_t)t * MF_TI;
 #pragma unroll
-                    for (int ib = 0; ib < 4; ++ib)
+                    for (int ib = 0; ib < 4; ++ib) {
+                        const uint32_t mw = mask_word(ib);
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int jq = lrow0 + ib * 32 + q * 8;
+                            float v4[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                v4[e] = (!MASKED || ((mw >> (mbit0 + 8 * q + e)) & 1u)) ? acc[ib][ub][4 * q + e] : -INFINITY;
                             if (jq + 3 < lim)
-                                *(float4*)(orow + jq) = make_float4(acc[ib][ub][4 * q], acc[ib][ub][4 * q + 1],
-                                                                    acc[ib][ub][4 * q + 2], acc[ib][ub][4 * q + 3]);
+                                *(float4*)(orow + jq) = make_float4(v4[0], v4[1], v4[2], v4[3]);
                             else
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)
-                                    if (jq + e < lim) orow[jq + e] = acc[ib][ub][4 * q + e];
+                                    if (jq + e < lim) orow[jq + e] = v4[e];
                         }
+                    }
                 }
                 continue;
             }
@@ -193,9 +208,11 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             for (int ib = 0; ib < 4; ++ib) {
                 const int jb = lrow0 + ib * 32;  // rows jb + 8q + e
                 float v[16];
+                const uint32_t mw = mask_word(ib);
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     v[r] = acc[ib][ub][r];
+                    if (MASKED && !((mw >> (mbit0 + (r >> 2) * 8 + (r & 3))) & 1u)) v[r] = -INFINITY;
                     if (!full) {
                         const int m = (jb + (r >> 2) * 8 + (r & 3) - lim) >> 31;  // all ones iff the row is valid
                         v[r] = __uint_as_float((__float_as_uint(v[r]) & (uint32_t)m) | (0xFF800000u & ~(uint32_t)m));
@@ -499,9 +516,13 @@ __global__ __launch_bounds__(ST_NT) void stream_score_kernel(StreamArgs a) {
 #pragma unroll
             for (int q = 0; q < ST_U; ++q)
                 if (q == u) it = item[q];
+            float sv = s;
+            if (MODE != 2 && a.mask != nullptr && !((a.mask[(int64_t)b * a.mask_stride + (it >> 5)] >> (it & 31)) & 1u))
+                sv = -INFINITY;  // masked item: nothing to the sum, never a candidate
             if (MODE == 0) {
-                a.sample_out[(int64_t)b * a.n_items + jbeg + g0 + u] = s;
-            } else {
+                a.sample_out[(int64_t)b * a.n_items + jbeg + g0 + u] = sv;
+            } else if (sv != -INFINITY) {
+                const float s = sv;
                 st.add(s);
                 if (s >= th) {
                     const int pos = atomicAdd(&s_cnt, 1);
@@ -1148,9 +1169,11 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     tot.init();
     unsigned long long ntot = 0;
     for (int q = 0; q < SEL_NT / kWave; ++q) { tot.merge(s_ml[q].x, s_ml[q].y); ntot += s_n[q]; }
-    if (a.mode == 1 && ntot < (unsigned long long)a.K) {
+    if (a.mode == 1 && ntot < (unsigned long long)a.K && a.theta_fast[b] > a.theta_safe[b]) {
         // the fast threshold let fewer than K items through: the rescue pass
-        // recomputes this user with the K-th sampled score
+        // recomputes this user with the K-th sampled score (when that is
+        // lower: else every item it would keep was kept, e.g. a user with
+        // fewer than K allowed items)
         if (tid == 0) {
             a.user_flag[b] = 1;
             a.tile_flag[b / MF_TU] = 1;
@@ -1453,13 +1476,22 @@ __global__ __launch_bounds__(HOT_NT) void hot_gather_kernel(HotArgs a) {
 hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s) {
     const int grid = a.UT * a.P;
     const bool ktail = (a.D % MF_BK) != 0;
+    const bool masked = a.mask != nullptr;
+#define GENREC_MFMA(MO, KT, MK) hipLaunchKernelGGL((mfma_score_kernel<MO, KT, MK>), dim3(grid), dim3(MF_NT), 0, s, a)
     if (mode == 0) {
-        if (ktail) hipLaunchKernelGGL((mfma_score_kernel<0, true>), dim3(grid), dim3(MF_NT), 0, s, a);
-        else hipLaunchKernelGGL((mfma_score_kernel<0, false>), dim3(grid), dim3(MF_NT), 0, s, a);
+        if (masked) {
+            if (ktail) GENREC_MFMA(0, true, true); else GENREC_MFMA(0, false, true);
+        } else {
+            if (ktail) GENREC_MFMA(0, true, false); else GENREC_MFMA(0, false, false);
+        }
     } else {
-        if (ktail) hipLaunchKernelGGL((mfma_score_kernel<1, true>), dim3(grid), dim3(MF_NT), 0, s, a);
-        else hipLaunchKernelGGL((mfma_score_kernel<1, false>), dim3(grid), dim3(MF_NT), 0, s, a);
+        if (masked) {
+            if (ktail) GENREC_MFMA(1, true, true); else GENREC_MFMA(1, false, true);
+        } else {
+            if (ktail) GENREC_MFMA(1, true, false); else GENREC_MFMA(1, false, false);
+        }
     }
+#undef GENREC_MFMA
     return hipGetLastError();
 }
 

@@ -32,6 +32,10 @@ struct MfmaArgs {
     // mode 0: when set, only the first *live_rows catalog rows matter; chunks
     // that start past them exit at once
     const int* live_rows;
+    // item mask (null: every item): item i takes part for user u only when bit
+    // i % 32 of mask[u * mask_stride + i / 32] is set (stride 0: one mask)
+    const uint32_t* mask;
+    int64_t mask_stride;
 };
 
 struct CandPiece {
@@ -65,6 +69,9 @@ struct StreamArgs {
     const int* hot_idx;
     const float* s_hot;
     int t_hot;
+    // dense modes: item mask as in MfmaArgs (null: every item)
+    const uint32_t* mask;
+    int64_t mask_stride;
 };
 
 // Hot head of the candidate lists: per-item list counts, the count threshold,
@@ -106,6 +113,10 @@ struct MergeArgs {
     int* user_flag;
     int* tile_flag;
     int64_t* rescued;
+    // mode 1: a user is flagged only when the rescue threshold is lower than
+    // the fast one (else the first pass already kept every item it would)
+    const float* theta_fast;
+    const float* theta_safe;
 };
 
 struct ThresholdArgs {

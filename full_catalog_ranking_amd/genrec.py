@@ -21,6 +21,8 @@ KMAX = 1024
 EXPORTED = (
     "genrec_score_lse_topk_workspace",
     "genrec_score_lse_topk",
+    "genrec_score_lse_topk_masked",
+    "genrec_score_lse_topk_masked_profiled",
     "genrec_score_candidates_topk_workspace",
     "genrec_score_candidates_topk",
     "genrec_get_device_errors",
@@ -82,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.genrec_profiler_summary.restype = I
         L.genrec_score_lse_topk_profiled.argtypes = L.genrec_score_lse_topk.argtypes + [P]
         L.genrec_score_lse_topk_profiled.restype = I
+        L.genrec_score_lse_topk_masked.argtypes = [P, P, I, I, I, I64, I, P, I64, P, P, P, P, SZ, P]
+        L.genrec_score_lse_topk_masked.restype = I
+        L.genrec_score_lse_topk_masked_profiled.argtypes = L.genrec_score_lse_topk_masked.argtypes + [P]
+        L.genrec_score_lse_topk_masked_profiled.restype = I
         L.genrec_score_candidates_topk_profiled.argtypes = L.genrec_score_candidates_topk.argtypes + [P]
         L.genrec_score_candidates_topk_profiled.restype = I
         _lib = L
@@ -172,11 +178,27 @@ class Profiler:
 
 
 def score_lse_topk(H: torch.Tensor, E: torch.Tensor, K: int, workspace: torch.Tensor | None = None,
-                   out=None, profiler: Profiler | None = None):
-    """Full-catalog ranking head: returns (idx int32 [B,K], scores f32 [B,K], lse f32 [B])."""
+                   out=None, profiler: Profiler | None = None, mask: torch.Tensor | None = None):
+    """Full-catalog ranking head: returns (idx int32 [B,K], scores f32 [B,K], lse f32 [B]).
+
+    mask (optional): int32/uint32 device tensor of item-mask words, shape (W,) for one
+    mask shared by all users or (B, W) per user, W >= ceil(M/32); bit i % 32 of word
+    i // 32 set = item i takes part."""
     _check_inputs(H, E)
     B, D = H.shape
     M = E.shape[0]
+    if mask is not None:
+        if mask.dtype not in (torch.int32, torch.uint32) or not (mask.is_cuda and mask.is_contiguous()):
+            raise TypeError("mask must be a contiguous int32/uint32 device tensor")
+        W = (M + 31) // 32
+        if mask.dim() == 1:
+            if mask.numel() < W:
+                raise ValueError("mask needs ceil(M/32) words")
+            stride = 0
+        elif mask.dim() == 2 and mask.shape[0] == B and mask.shape[1] >= W:
+            stride = mask.shape[1]
+        else:
+            raise ValueError("mask must be (W,) or (B, W) with W >= ceil(M/32)")
     need = workspace_bytes(B, D, M, K, H.dtype)
     if need == 0:
         raise GenrecError(lib().genrec_score_lse_topk(None, None, dtype_code(H.dtype), B, D, M, K,
@@ -185,14 +207,21 @@ def score_lse_topk(H: torch.Tensor, E: torch.Tensor, K: int, workspace: torch.Te
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=H.device)
     idx, sc, ls = out if out is not None else _outputs(B, K, H.device)
-    args = (_ptr(H), _ptr(E), dtype_code(H.dtype), B, D, M, K, _ptr(idx), _ptr(sc), _ptr(ls),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(H.device))
-    if profiler is None:
-        st = lib().genrec_score_lse_topk(*args)
+    tail = (_ptr(idx), _ptr(sc), _ptr(ls), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream_handle(H.device))
+    head = (_ptr(H), _ptr(E), dtype_code(H.dtype), B, D, M, K)
+    if mask is None:
+        name = "genrec_score_lse_topk"
+        args = head + tail
     else:
-        st = lib().genrec_score_lse_topk_profiled(*args, profiler.h)
+        name = "genrec_score_lse_topk_masked"
+        args = head + (_ptr(mask), stride) + tail
+    if profiler is None:
+        st = getattr(lib(), name)(*args)
+    else:
+        st = getattr(lib(), name + "_profiled")(*args, profiler.h)
     if st != 0:
-        raise GenrecError(st, "genrec_score_lse_topk")
+        raise GenrecError(st, name)
     return idx, sc, ls
 
 

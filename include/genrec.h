@@ -84,6 +84,28 @@ int genrec_score_lse_topk(const void* H, const void* E, int dtype,
                           int32_t* out_idx, float* out_scores, float* out_lse,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Masked full-catalog head: as genrec_score_lse_topk, over the items a
+ * bitmask allows.  Item i takes part for user b only when bit (i % 32) of
+ * item_mask[b * mask_stride_words + i / 32] is set (least significant bit
+ * first); mask_stride_words == 0 means one mask of ceil(M/32) words for every
+ * user, else each user's row has mask_stride_words >= ceil(M/32) words.
+ * Items left out add nothing to lse and never rank; with fewer than K allowed
+ * items the tail is padded (id -1, score -inf), with none lse = -inf.  Bits
+ * past M are ignored.  item_mask: device memory, 4-byte aligned, caller-owned.
+ * The workspace is the one genrec_score_lse_topk_workspace() gives.  Source:
+ * the pages' item filtering -- the GenRec explainer page lists ignored
+ * business constraints and out-of-catalog items among the failings of plain
+ * LLM rankers; the xGR explainer page's xBeam filters invalid candidates with
+ * masks.  Errors: GENREC_ERR_INVALID_ARG for a null or misaligned mask or a
+ * stride below ceil(M/32); otherwise as genrec_score_lse_topk.
+ */
+int genrec_score_lse_topk_masked(const void* H, const void* E, int dtype,
+                                 int B, int D, int64_t M, int K,
+                                 const uint32_t* item_mask, int64_t mask_stride_words,
+                                 int32_t* out_idx, float* out_scores, float* out_lse,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes needed by genrec_score_candidates_topk (0 if unsupported). */
 size_t genrec_score_candidates_topk_workspace(int B, int D, int64_t M, int64_t nnz, int K,
                                               int dtype);
@@ -155,13 +177,20 @@ void genrec_profiler_destroy(genrec_profiler* prof);
 int genrec_profiler_reset(genrec_profiler* prof);
 int genrec_profiler_summary(genrec_profiler* prof, int* counts, double* total_ms);
 
-/* Same as genrec_score_lse_topk / genrec_score_candidates_topk, recording
- * every launch into `prof` (which may be NULL). */
+/* Same as genrec_score_lse_topk / genrec_score_lse_topk_masked /
+ * genrec_score_candidates_topk, recording every launch into `prof` (which may
+ * be NULL). */
 int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype,
                                    int B, int D, int64_t M, int K,
                                    int32_t* out_idx, float* out_scores, float* out_lse,
                                    void* workspace, size_t workspace_bytes, void* stream,
                                    genrec_profiler* prof);
+int genrec_score_lse_topk_masked_profiled(const void* H, const void* E, int dtype,
+                                          int B, int D, int64_t M, int K,
+                                          const uint32_t* item_mask, int64_t mask_stride_words,
+                                          int32_t* out_idx, float* out_scores, float* out_lse,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          genrec_profiler* prof);
 int genrec_score_candidates_topk_profiled(const void* H, const void* E, int dtype,
                                           const int64_t* cand_offsets, const int32_t* cand_ids,
                                           int B, int D, int64_t M, int64_t nnz, int K,

@@ -80,6 +80,11 @@ def test_candidate_argument_errors(L):
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 4, 64, 100, 10, 5, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WORKSPACE
     assert L.genrec_get_device_errors(None, None, None, None) == INVALID
     assert L.genrec_get_rescued_users(None, None, None) == INVALID
+    m = L.genrec_score_lse_topk_masked
+    ws = L.genrec_score_lse_topk_workspace(4, 64, 100, 10, 0)
+    assert m(FAKE, FAKE, 0, 4, 64, 100, 10, None, 0, FAKE, FAKE, FAKE, FAKE, ws, None) == INVALID   # no mask
+    assert m(FAKE, FAKE, 0, 4, 64, 100, 10, FAKE, 3, FAKE, FAKE, FAKE, FAKE, ws, None) == INVALID   # stride < 4 words
+    assert m(FAKE, FAKE, 0, 4, 64, 100, 10, FAKE, -1, FAKE, FAKE, FAKE, FAKE, ws, None) == INVALID
 
 
 def test_workspace_queries(L):

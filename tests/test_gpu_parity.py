@@ -150,6 +150,59 @@ def test_fast_threshold_rescue(dev, oracle_mod):
                        oracle_mod.full(d["H"], d["E"], K, users=[0, 3, 15]), where="no rescue")
 
 
+def _pack_mask(allowed):
+    M = allowed.shape[-1]
+    W = (M + 31) // 32
+    pad = np.zeros(allowed.shape[:-1] + (W * 32,), dtype=bool)
+    pad[..., :M] = allowed
+    bits = pad.reshape(allowed.shape[:-1] + (W, 32)).astype(np.uint64)
+    return (bits << np.arange(32, dtype=np.uint64)).sum(axis=-1).astype(np.uint32)
+
+
+@pytest.mark.parametrize("case,B,D,M,K,per_user", [
+    ("global 90%, sampled fast path", 256, 512, 100_000, 100, False),
+    ("per-user densities incl. none and < K, ragged, k tail", 300, 200, 70_001, 37, True),
+    ("per-user, VALU path with sample", 3, 96, 70_000, 50, True),
+    ("global 2% (< K allowed), unsampled MFMA", 17, 128, 3000, 64, False),
+])
+def test_masked_head(dev, oracle_mod, case, B, D, M, K, per_user):
+    from full_catalog_ranking_amd import genrec
+    d = synth.make_dense(B, D, M, seed=B + D)
+    rng = np.random.default_rng(B * 31 + M)
+    if per_user:
+        dens = np.concatenate([[0.0, 1e-4, 1.0], rng.uniform(0.005, 1.0, B - 3)])[:B]
+        allowed = rng.random((B, M)) < dens[:, None]
+    else:
+        allowed = np.broadcast_to(rng.random(M) < (0.9 if M > 10_000 else 0.02), (B, M))
+    words = _pack_mask(allowed if per_user else allowed[0])
+    mask = torch.from_numpy(words.view(np.int32)).to(dev)
+    H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
+    print("  masked %s B=%d D=%d M=%d K=%d" % (case, B, D, M, K), flush=True)
+    ws = torch.empty(genrec.workspace_bytes(B, D, M, K, H.dtype), dtype=torch.uint8, device=dev)
+    idx, sc, ls = genrec.score_lse_topk(H, E, K, workspace=ws, mask=mask)
+    g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
+    users = sorted(set([0, 1, 2, B - 1] + list(range(0, B, max(1, B // 10)))))
+    ref = oracle_mod.full_masked(d["H"], d["E"], K, words, users=users)
+    parity.check_dense(g, ref, where="masked %s" % case)
+    for b in range(B):  # every returned item is allowed, every padded slot is (-1, -inf)
+        ids = g[0][b]
+        assert allowed[b][ids[ids >= 0]].all()
+        assert (np.isneginf(g[1][b][ids < 0])).all()
+    if not per_user and M > 10_000:
+        assert genrec.rescued_users(ws) == 0
+
+
+def test_masked_all_allowed_equals_unmasked(dev):
+    from full_catalog_ranking_amd import genrec
+    d = synth.make_dense(40, 256, 70_000, seed=8)
+    H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
+    words = _pack_mask(np.ones(70_000, dtype=bool))
+    a = genrec.score_lse_topk(H, E, 30)
+    b = genrec.score_lse_topk(H, E, 30, mask=torch.from_numpy(words.view(np.int32)).to(dev))
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
 @pytest.mark.parametrize("B,D,M,K,bf16", [
     (3, 96, 70000, 50, True),    # VALU path with the sampled pre-pass
     (1, 8, 1, 5, True),          # M = 1, K > M
