@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mask-density", type=float, default=None, metavar="P",
+                    help="full-catalog workloads: score through the masked head with one seeded "
+                         "item mask that allows a fraction P of the catalog")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scratch buffer before every step (flushes the 256 MB Infinity "
                          "Cache and the L2s) and time each step on its own, the flush outside")
@@ -130,17 +133,24 @@ def traffic_from_profile(kernel, workload):
         return None
 
 
-def cpu_baseline(d, K, target_s, cand):
+def cpu_baseline(d, K, target_s, cand, mask_words=None):
     """The oracle on a bounded sample of the same workload: whole users."""
     from oracle import oracle
     oracle.build()
     B = d["B"]
     users = [0]
+
+    def dense(us):
+        if mask_words is None:
+            oracle.full(d["H"], d["E"], K, users=us)
+        else:
+            oracle.full_masked(d["H"], d["E"], K, mask_words, users=us)
+
     t0 = time.perf_counter()
     if cand:
         oracle.cand(d["H"], d["E"], d["offsets"], d["ids"], K, users=users)
     else:
-        oracle.full(d["H"], d["E"], K, users=users)
+        dense(users)
     t1 = time.perf_counter() - t0
     n = int(max(1, min(B, target_s / max(t1, 1e-3))))
     users = list(np.linspace(0, B - 1, n).astype(np.int64))
@@ -149,7 +159,7 @@ def cpu_baseline(d, K, target_s, cand):
         oracle.cand(d["H"], d["E"], d["offsets"], d["ids"], K, users=users)
         units = int(sum(d["offsets"][u + 1] - d["offsets"][u] for u in users))
     else:
-        oracle.full(d["H"], d["E"], K, users=users)
+        dense(users)
         units = n * d["M"]
     t = time.perf_counter() - t0
     return dict(value=units / t, unit="scores/s", cores=oracle.threads(), kind="oracle",
@@ -195,11 +205,23 @@ def main():
            torch.empty((B,), dtype=torch.float32, device=dev))
     prof = genrec.Profiler(max_launches=8 * (args.steps + 1))
 
+    mask = None
+    words = None
+    if args.mask_density is not None:
+        if cand:
+            raise SystemExit("--mask-density applies to the full-catalog workloads")
+        allowed = np.random.default_rng(12345).random(M) < args.mask_density
+        W = (M + 31) // 32
+        pad = np.zeros(W * 32, dtype=bool)
+        pad[:M] = allowed
+        words = (pad.reshape(W, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(axis=1).astype(np.uint32)
+        mask = torch.from_numpy(words.view(np.int32)).to(dev)
+
     def step(p=None):
         if cand:
             genrec.score_candidates_topk(H, E, off, ids, K, workspace=ws, out=out, profiler=p)
         else:
-            genrec.score_lse_topk(H, E, K, workspace=ws, out=out, profiler=p)
+            genrec.score_lse_topk(H, E, K, workspace=ws, out=out, profiler=p, mask=mask)
 
     for _ in range(args.warmup):
         step()
@@ -268,7 +290,8 @@ def main():
         "dtype": "bf16" if H.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "D": D, "M": M, "K": K,
-                   **({"nnz": units} if cand else {}), **({"cache": "cold"} if args.cold else {})},
+                   **({"nnz": units} if cand else {}), **({"cache": "cold"} if args.cold else {}),
+                   **({"mask_density": args.mask_density} if args.mask_density is not None else {})},
         "tflops": flops / (ms * 1e-3) / 1e12,
         "kernels_ms": {k: v[1] / v[0] for k, v in kern.items()},
         "roofline": roof,
@@ -276,7 +299,7 @@ def main():
     if not args.no_cpu_baseline:
         del H, E, ws
         torch.cuda.empty_cache()
-        res["cpu_baseline"] = cpu_baseline(d, K, args.cpu_seconds, cand)
+        res["cpu_baseline"] = cpu_baseline(d, K, args.cpu_seconds, cand, words)
     print(json.dumps(res), flush=True)
 
 
