@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="large", choices=["large", "batch", "gemv", "tiny", "cand", "gemv_big"])
+    ap.add_argument("--workload", default="large", choices=["large", "batch", "gemv", "tiny", "cand", "gemv_big", "beam128", "beam512"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -166,6 +166,53 @@ def cpu_baseline(d, K, target_s, cand, mask_words=None):
                 sample="%d of %d users, %d scores with lse and full sort, %.1f s" % (n, B, units, t))
 
 
+def bench_beam(args):
+    """Beam step: batched top-K of R dense score rows of N entries (one kernel)."""
+    import torch
+    from full_catalog_ranking_amd import genrec, synth
+    dev = torch.device("cuda:0")
+    genrec.lib()
+    d = synth.make_workload(args.workload)
+    R, N, K = d["R"], d["N"], d["K"]
+    S = torch.from_numpy(d["scores"]).to(dev)
+    out = (torch.empty((R, K), dtype=torch.int32, device=dev), torch.empty((R, K), dtype=torch.float32, device=dev))
+    for _ in range(args.warmup):
+        genrec.topk_rows(S, K, out=out)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        genrec.topk_rows(S, K, out=out)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    alg_bytes = R * N * 4 + R * K * 8
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": R * N / (ms * 1e-3), "unit": "scores/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "R": R, "N": N, "K": K},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "kernel": "topk_rows_kernel", "kernel_ms": ms,
+                     "traffic": traffic_from_profile("topk_rows_kernel", args.workload)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        oracle.build()
+        t0 = time.perf_counter()
+        oracle.topk_row(d["scores"][0].astype(np.float64), K)
+        t1 = max(time.perf_counter() - t0, 1e-4)
+        n = int(max(1, min(R, args.cpu_seconds / t1)))
+        t0 = time.perf_counter()
+        for r in np.linspace(0, R - 1, n).astype(np.int64):
+            oracle.topk_row(d["scores"][r].astype(np.float64), K)
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = dict(value=n * N / t, unit="scores/s", cores=1, kind="oracle",
+                                   sample="%d of %d rows, full stable sort each, %.1f s" % (n, R, t))
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -177,6 +224,9 @@ def main():
         return
     if args.peaks:
         peaks()
+        return
+    if args.workload.startswith("beam"):
+        bench_beam(args)
         return
     import torch
     from full_catalog_ranking_amd import genrec, synth

@@ -482,6 +482,35 @@ int genrec_get_device_errors(const void* workspace, void* stream, int64_t* n_bad
     return GENREC_OK;
 }
 
+size_t genrec_topk_rows_workspace(int R, int64_t N, int K) {
+    if (R <= 0 || N <= 0 || K <= 0 || K > GENREC_KMAX || N >= ((int64_t)1 << 31)) return 0;
+    return plan_topk(R, N, K).workspace;
+}
+
+int genrec_topk_rows(const float* scores, int R, int64_t N, int64_t ld, int K, int32_t* out_idx,
+                     float* out_scores, void* workspace, size_t workspace_bytes, void* stream) {
+    if (R <= 0 || N <= 0 || K <= 0 || ld < N) return GENREC_ERR_INVALID_ARG;
+    if (!scores || !out_idx || !out_scores) return GENREC_ERR_INVALID_ARG;
+    if (!aligned(scores, 4) || !aligned(out_idx, 4) || !aligned(out_scores, 4)) return GENREC_ERR_INVALID_ARG;
+    if (K > GENREC_KMAX) return GENREC_ERR_UNSUPPORTED;
+    if (N >= ((int64_t)1 << 31)) return GENREC_ERR_UNSUPPORTED;
+    const TopkPlan p = plan_topk(R, N, K);
+    if (p.workspace > 0 && (!workspace || workspace_bytes < p.workspace)) return GENREC_ERR_WORKSPACE;
+    if (p.workspace > 0 && !aligned(workspace, 8)) return GENREC_ERR_INVALID_ARG;
+    TopkRowsArgs a{};
+    a.scores = scores;
+    a.R = R;
+    a.N = N;
+    a.ld = ld;
+    a.K = K;
+    a.out_idx = out_idx;
+    a.out_scores = out_scores;
+    a.C = p.C;
+    a.nchunk = p.nchunk;
+    a.part = (uint64_t*)workspace;
+    return hip_status(launch_topk_rows(a, (hipStream_t)stream));
+}
+
 int genrec_get_rescued_users(const void* workspace, void* stream, int64_t* n_rescued) {
     if (!workspace || !n_rescued) return GENREC_ERR_INVALID_ARG;
     int64_t h = 0;

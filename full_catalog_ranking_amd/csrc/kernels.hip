@@ -21,6 +21,8 @@
 //                      and the exact top-K of the candidates (range-narrowing
 //                      histogram select + bitonic sort), written sorted.
 //  cand_plan_kernel    CSR offsets -> work list of fixed-size list pieces.
+//  hot_*_kernel        candidate lists: the most-listed rows, scored densely.
+//  topk_rows_kernel    batched top-K of dense score rows (a beam step).
 #include <float.h>
 
 #include "device_common.hpp"
@@ -1214,6 +1216,122 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Batched top-K of dense score rows (beam step)
+// ---------------------------------------------------------------------------
+// Source: a segment of one fp32 score row; the key of column base + e is
+// rank_key(score, base + e).
+struct DenseRowSrc {
+    const float* row;  // the segment's first score
+    int64_t n;
+    int64_t base;      // column of row[0]
+    __device__ int64_t total() const { return n; }
+    template <class F>
+    __device__ void for_each(F&& f) const {
+        for (int64_t e0 = threadIdx.x; e0 < n; e0 += (int64_t)SEL_NT * SEL_UNR) {
+            float v[SEL_UNR];
+#pragma unroll
+            for (int q = 0; q < SEL_UNR; ++q) {
+                const int64_t e = e0 + (int64_t)q * SEL_NT;
+                v[q] = e < n ? row[e] : 0.f;
+            }
+#pragma unroll
+            for (int q = 0; q < SEL_UNR; ++q) {
+                const int64_t e = e0 + (int64_t)q * SEL_NT;
+                if (e < n) f(rank_key(v[q], (uint32_t)(base + e)));
+            }
+        }
+    }
+    __device__ void gather(uint64_t* dst) const {
+        for (int64_t e = threadIdx.x; e < n; e += SEL_NT) dst[e] = rank_key(row[e], (uint32_t)(base + e));
+    }
+};
+
+// Source: the per-chunk partial results of one row, chunk c holding
+// min(K, its length) keys at part + c * K.
+struct PartialSrc {
+    const uint64_t* part;
+    int nchunk, K;
+    int64_t N, C;
+    __device__ int cnt(int c) const { return (int)min((int64_t)K, min(C, N - (int64_t)c * C)); }
+    __device__ int64_t total() const {
+        int64_t t = 0;
+        for (int c = 0; c < nchunk; ++c) t += cnt(c);
+        return t;
+    }
+    template <class F>
+    __device__ void walk(F&& f) const {
+        int e = 0;
+        for (int c = 0; c < nchunk; ++c) {
+            const int n = cnt(c);
+            for (int i = threadIdx.x; i < n; i += SEL_NT) f(part[(int64_t)c * K + i], e + i);
+            e += n;
+        }
+    }
+    template <class F>
+    __device__ void for_each(F&& f) const {
+        walk([&](uint64_t key, int) { f(key); });
+    }
+    __device__ void gather(uint64_t* dst) const {
+        walk([&](uint64_t key, int e) { dst[e] = key; });
+    }
+};
+
+// The k largest keys of a source in ranking order, written out (or, for an
+// intermediate chunk, as raw keys).
+template <class Src>
+__device__ void topk_emit(const Src& src, int k, int K, SelShared& sh, int32_t* oidx, float* osc, uint64_t* okeys) {
+    const int tid = threadIdx.x;
+    if (k > 0) {
+        block_select<true>(src, k, sh);
+        if (okeys != nullptr) {  // partial result: any order
+            for (int i = tid; i < k; i += SEL_NT) okeys[i] = sh.out[i];
+            return;
+        }
+        if (k <= 256) {
+            block_rank_place(sh.out, k, sh.gbuf, k);
+        } else {
+            block_sort_desc(sh.out, k);
+            for (int i = tid; i < k; i += SEL_NT) sh.gbuf[i] = sh.out[i];
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < K; i += SEL_NT) {
+        if (i < k) {
+            const uint64_t key = sh.gbuf[i];
+            oidx[i] = (int32_t)key_id(key);
+            osc[i] = key_score(key);
+        } else {
+            oidx[i] = -1;
+            osc[i] = -INFINITY;
+        }
+    }
+}
+
+// Block (r, c): the top-K of chunk c of row r -- the final result when the row
+// is one chunk, else its keys for the merge.
+__global__ __launch_bounds__(SEL_NT) void topk_chunk_kernel(TopkRowsArgs a) {
+    __shared__ SelShared sh;
+    const int r = blockIdx.x / a.nchunk, c = blockIdx.x - r * a.nchunk;
+    const int64_t c0 = (int64_t)c * a.C;
+    const int64_t n = min(a.C, a.N - c0);
+    DenseRowSrc src{a.scores + (int64_t)r * a.ld + c0, n, c0};
+    const int k = (int)min((int64_t)a.K, n);
+    if (a.nchunk == 1)
+        topk_emit(src, k, a.K, sh, a.out_idx + (int64_t)r * a.K, a.out_scores + (int64_t)r * a.K, nullptr);
+    else
+        topk_emit(src, k, a.K, sh, nullptr, nullptr, a.part + ((int64_t)r * a.nchunk + c) * a.K);
+}
+
+// Block r: the top-K of the row's chunk results.
+__global__ __launch_bounds__(SEL_NT) void topk_merge_rows_kernel(TopkRowsArgs a) {
+    __shared__ SelShared sh;
+    const int r = blockIdx.x;
+    PartialSrc src{a.part + (int64_t)r * a.nchunk * a.K, a.nchunk, a.K, a.N, a.C};
+    const int k = (int)min((int64_t)a.K, a.N);
+    topk_emit(src, k, a.K, sh, a.out_idx + (int64_t)r * a.K, a.out_scores + (int64_t)r * a.K, nullptr);
+}
+
+// ---------------------------------------------------------------------------
 // Candidate lists: CSR offsets -> pieces of at most CAND_PIECE entries
 // ---------------------------------------------------------------------------
 constexpr int PL_NT = 1024;
@@ -1513,6 +1631,13 @@ hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s) {
     if (a.n_sample > (int64_t)TH_KEYS) return hipErrorInvalidValue;
     if (a.B <= 512) hipLaunchKernelGGL(threshold_kernel<1024>, dim3(a.B), dim3(1024), 0, s, a);
     else hipLaunchKernelGGL(threshold_kernel<256>, dim3(a.B), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s) {
+    if (a.R <= 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)((int64_t)a.R * a.nchunk)), dim3(SEL_NT), 0, s, a);
+    if (a.nchunk > 1) hipLaunchKernelGGL(topk_merge_rows_kernel, dim3(a.R), dim3(SEL_NT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -140,7 +140,20 @@ struct CandPlanArgs {
     int64_t* err;
 };
 
+struct TopkRowsArgs {
+    const float* scores;  // [R][ld], the first N of each row used
+    int R;
+    int64_t N, ld;
+    int K;
+    int32_t* out_idx;     // [R][K]
+    float* out_scores;    // [R][K]
+    int64_t C;            // columns per chunk
+    int nchunk;           // chunks per row (1: no merge pass)
+    uint64_t* part;       // nchunk > 1: [R][nchunk][K] chunk results
+};
+
 hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s);
+hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s);
 hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, hipStream_t s);
 hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);

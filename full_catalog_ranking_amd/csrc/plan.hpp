@@ -201,4 +201,27 @@ inline CandPlan plan_cand(int B, int D, int64_t M, int64_t nnz, int dtype) {
     return p;
 }
 
+// Batched top-K of dense rows: rows longer than one block handles well are
+// split into chunks whose top-K keys a second pass merges; the chunk count is
+// kept so that the merged keys (chunks x K) fit the merge's LDS gather.
+constexpr int64_t kTopkChunkMin = 4096;
+constexpr int64_t kTopkGather = 6144;  // the merge kernel's LDS gather capacity (keys)
+
+struct TopkPlan {
+    int64_t C = 0;
+    int nchunk = 1;
+    size_t workspace = 0;
+};
+
+inline TopkPlan plan_topk(int R, int64_t N, int K) {
+    TopkPlan p;
+    const int64_t max_chunks = std::max<int64_t>(1, kTopkGather / std::max(1, K));
+    int64_t C = std::max(kTopkChunkMin, ceil_div(N, max_chunks));
+    C = ceil_div(C, 4096) * 4096;
+    p.C = C;
+    p.nchunk = (int)ceil_div(N, C);
+    if (p.nchunk > 1) p.workspace = sizeof(uint64_t) * (size_t)R * (size_t)p.nchunk * (size_t)K;
+    return p;
+}
+
 }  // namespace genrec

@@ -27,6 +27,8 @@ EXPORTED = (
     "genrec_score_candidates_topk",
     "genrec_get_device_errors",
     "genrec_get_rescued_users",
+    "genrec_topk_rows",
+    "genrec_topk_rows_workspace",
     "genrec_describe_plan",
     "genrec_status_string",
     "genrec_version",
@@ -68,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.genrec_score_candidates_topk.restype = I
         L.genrec_get_device_errors.argtypes = [P, P, P, P]
         L.genrec_get_device_errors.restype = I
+        L.genrec_topk_rows.argtypes = [P, I, I64, I64, I, P, P, P, SZ, P]
+        L.genrec_topk_rows.restype = I
+        L.genrec_topk_rows_workspace.argtypes = [I, I64, I]
+        L.genrec_topk_rows_workspace.restype = SZ
         L.genrec_get_rescued_users.argtypes = [P, P, P]
         L.genrec_get_rescued_users.restype = I
         L.genrec_describe_plan.argtypes = [I, I, I64, I, I, ctypes.c_char_p, SZ]
@@ -276,3 +282,25 @@ def rescued_users(workspace: torch.Tensor) -> int:
     if st != 0:
         raise GenrecError(st, "genrec_get_rescued_users")
     return n.value
+
+
+def topk_rows(scores: torch.Tensor, K: int, out=None, workspace: torch.Tensor | None = None):
+    """Batched top-K of fp32 score rows [R, N] (row stride may exceed N):
+    returns (idx int32 [R, K], values f32 [R, K]), score descending, ties by column."""
+    if scores.dtype != torch.float32 or not scores.is_cuda or scores.dim() != 2 or scores.stride(1) != 1:
+        raise TypeError("scores must be a float32 device tensor [R, N] with unit column stride")
+    R, N = scores.shape
+    if out is None:
+        idx = torch.empty((R, K), dtype=torch.int32, device=scores.device)
+        val = torch.empty((R, K), dtype=torch.float32, device=scores.device)
+    else:
+        idx, val = out
+    need = int(lib().genrec_topk_rows_workspace(R, N, K))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().genrec_topk_rows(_ptr(scores), R, N, scores.stride(0), K, _ptr(idx), _ptr(val),
+                                _ptr(workspace), wsb, _stream_handle(scores.device))
+    if st != 0:
+        raise GenrecError(st, "genrec_topk_rows")
+    return idx, val

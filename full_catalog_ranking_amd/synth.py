@@ -177,6 +177,9 @@ WORKLOADS = {
     "cand":  dict(B=4096, D=2048, M=1_000_000, K=100, dtype="bf16", lo=100, hi=3000),
     # one user against an 8 GB catalog: sustained catalog streaming at B = 1
     "gemv_big": dict(B=1, D=4096, M=1_000_000, K=100, dtype="bf16"),
+    # beam steps: R requests of width x width continuation scores -> the best `width`
+    "beam128": dict(R=256, N=128 * 128, K=128, kind="beam"),
+    "beam512": dict(R=64, N=512 * 512, K=512, kind="beam"),
 }
 
 TINY_PLANT_ITEM = 17
@@ -204,9 +207,22 @@ def make_dense(B: int, D: int, M: int, seed: int = 0, permute: bool = False,
     return dict(H=H, E=E, B=B, D=D, M=M, dtype="bf16" if bf16 else "f32")
 
 
+def gen_scores(R: int, N: int, seed: int, decimals: int | None = None) -> np.ndarray:
+    """Beam-step scores (R x N float32): a per-row offset (the beam's running
+    log-probability) plus N(0, 1) continuation scores; with `decimals` the
+    values are rounded, which makes exact ties frequent."""
+    z = _rng(seed, 4).standard_normal((R, N), dtype=np.float32)
+    z += _rng(seed, 5).standard_normal((R, 1), dtype=np.float32) * np.float32(3.0)
+    if decimals is not None:
+        z = np.round(z, decimals).astype(np.float32)
+    return z
+
+
 def make_workload(name: str, seed: int = 0, **over) -> dict:
     cfg = dict(WORKLOADS[name])
     cfg.update(over)
+    if cfg.get("kind") == "beam":
+        return dict(scores=gen_scores(cfg["R"], cfg["N"], seed), R=cfg["R"], N=cfg["N"], K=cfg["K"], kind="beam")
     if name == "tiny":
         d = make_tiny(seed, B=cfg["B"], D=cfg["D"], M=cfg["M"])
     else:

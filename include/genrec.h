@@ -147,6 +147,26 @@ int genrec_get_device_errors(const void* workspace, void* stream, int64_t* n_bad
  */
 int genrec_get_rescued_users(const void* workspace, void* stream, int64_t* n_rescued);
 
+/*
+ * Batched top-K of dense score rows -- the selection step of a beam search
+ * (xGR explainer page, xBeam: beam widths of 128 to 512, e.g. 128 beams x 128
+ * continuations = 16,384 candidates ranked down to the best 128, without a
+ * full sort).  For each row r < R of scores (fp32, row r at scores + r * ld,
+ * its first N entries used, ld >= N), the K largest entries ranked by score
+ * descending, ties by the lower column: out_idx [R][K] int32 column indices,
+ * out_scores [R][K] the scores.  K > N pads with (-1, -inf).  Long rows are
+ * split into chunks merged by a second pass, which needs `workspace` of
+ * genrec_topk_rows_workspace(R, N, K) bytes (8-byte aligned; 0 bytes --
+ * workspace may be NULL -- when one pass suffices).  Asynchronous on
+ * `stream`.  1 <= K <= GENREC_KMAX, 1 <= N < 2^31, R >= 1, 4-byte aligned
+ * pointers; GENREC_ERR_INVALID_ARG / GENREC_ERR_UNSUPPORTED /
+ * GENREC_ERR_WORKSPACE otherwise.  Non-finite scores are not supported.
+ */
+size_t genrec_topk_rows_workspace(int R, int64_t N, int K);
+int genrec_topk_rows(const float* scores, int R, int64_t N, int64_t ld, int K,
+                     int32_t* out_idx, float* out_scores,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /* Introspection: writes into buf (at most len bytes, NUL-terminated) a JSON
  * object describing how genrec_score_lse_topk would run these sizes: the
  * scoring path ("mfma" or "stream"), whether the sampled-threshold pre-pass

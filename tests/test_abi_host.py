@@ -80,6 +80,18 @@ def test_candidate_argument_errors(L):
     assert f(FAKE, FAKE, 0, FAKE, FAKE, 4, 64, 100, 10, 5, FAKE, FAKE, FAKE, FAKE, need - 1, None) == WORKSPACE
     assert L.genrec_get_device_errors(None, None, None, None) == INVALID
     assert L.genrec_get_rescued_users(None, None, None) == INVALID
+    t = L.genrec_topk_rows
+    assert t(None, 2, 100, 100, 5, FAKE, FAKE, None, 0, None) == INVALID       # no scores
+    assert t(FAKE, 0, 100, 100, 5, FAKE, FAKE, None, 0, None) == INVALID       # R = 0
+    assert t(FAKE, 2, 100, 99, 5, FAKE, FAKE, None, 0, None) == INVALID        # ld < N
+    assert t(FAKE, 2, 100, 100, 0, FAKE, FAKE, None, 0, None) == INVALID       # K = 0
+    assert t(FAKE, 2, 100, 100, 2000, FAKE, FAKE, None, 0, None) == UNSUPPORTED  # K > KMAX
+    # one pass up to 4,096 columns; longer rows need the chunk results' workspace
+    assert L.genrec_topk_rows_workspace(8, 4096, 128) == 0
+    assert L.genrec_topk_rows_workspace(8, 16384, 128) == 8 * 4 * 128 * 8
+    need = L.genrec_topk_rows_workspace(8, 512 * 512, 512)
+    assert need > 0 and need % (8 * 8 * 512) == 0 and need // (8 * 8 * 512) * 512 <= 6144
+    assert t(FAKE, 8, 512 * 512, 512 * 512, 512, FAKE, FAKE, None, 0, None) == WORKSPACE
     m = L.genrec_score_lse_topk_masked
     ws = L.genrec_score_lse_topk_workspace(4, 64, 100, 10, 0)
     assert m(FAKE, FAKE, 0, 4, 64, 100, 10, None, 0, FAKE, FAKE, FAKE, FAKE, ws, None) == INVALID   # no mask

@@ -334,3 +334,31 @@ def test_candidates_equal_full_catalog(dev):
     assert errs == (0, 0)
     assert np.array_equal(gc[0], gd[0]) and np.array_equal(gc[1], gd[1])
     assert np.allclose(gc[2], gd[2], atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# Batched top-K of dense score rows (beam step)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("R,N,K,decimals,ld_pad", [
+    (7, 128 * 128, 128, None, 0),     # width-128 beam step
+    (3, 512 * 512, 512, None, 0),     # width-512 beam step (bitonic final sort)
+    (4, 5000, 1024, 1, 3),            # many exact ties, K = KMAX, padded row stride
+    (5, 100, 128, None, 0),           # K > N: padding
+    (2, 6144, 200, 2, 0),             # exactly the LDS gather size, ties
+    (1, 1, 1, None, 0),
+    (2, 100_000, 50, 2, 5),           # seven chunks merged, ties across chunks
+    (3, 16_385, 100, None, 0),        # a one-column last chunk
+])
+def test_topk_rows(dev, oracle_mod, R, N, K, decimals, ld_pad):
+    from full_catalog_ranking_amd import genrec
+    s = synth.gen_scores(R, N, seed=R * 7 + N, decimals=decimals)
+    full = np.zeros((R, N + ld_pad), dtype=np.float32)
+    full[:, :N] = s
+    t = torch.from_numpy(full).to(dev)[:, :N]
+    print("  topk_rows R=%d N=%d K=%d ties=%s" % (R, N, K, decimals), flush=True)
+    idx, val = genrec.topk_rows(t, K)
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    for r in range(R):
+        ri, rv = oracle_mod.topk_row(s[r].astype(np.float64), K)
+        assert np.array_equal(idx[r], ri), r   # exact: same fp32 values, same (score, column) order
+        assert np.array_equal(val[r], rv.astype(np.float32)), r

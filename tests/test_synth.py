@@ -66,3 +66,13 @@ def test_tiny_workload_recipe():
     for u in range(4):
         assert np.array_equal(d["E"][17 + u], 2 * d["H"][u])
     assert abs(d["E"][1000:].std() * math.sqrt(256) - 1) < 0.01
+
+
+def test_beam_scores_seeded_and_shaped():
+    a = synth.gen_scores(3, 1000, seed=4)
+    b = synth.gen_scores(3, 1000, seed=4)
+    assert a.dtype == np.float32 and a.shape == (3, 1000) and np.array_equal(a, b)
+    t = synth.gen_scores(2, 5000, seed=4, decimals=1)
+    assert np.unique(t[0]).size < 500   # rounding makes ties common
+    w = synth.make_workload("beam128")
+    assert w["scores"].shape == (256, 16384) and w["K"] == 128
