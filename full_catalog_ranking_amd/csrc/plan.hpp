@@ -12,7 +12,7 @@ namespace genrec {
 constexpr int kNumCU = 256;            // MI355X compute units
 constexpr int kMfmaTileItems = 256;    // items per MFMA tile
 constexpr int kMfmaTileUsers = 256;    // users per MFMA tile
-constexpr int kStreamMaxB = 8;         // bf16 batches up to this size use the VALU path
+constexpr int kStreamMaxB = 1;         // bf16 batches up to this size use the VALU path (a half-empty MFMA tile still beats re-reading E per user)
 constexpr int64_t kSampleMinM = 65536; // smaller catalogs skip the threshold pre-pass
 constexpr int64_t kSampleMinStride = 32; // sample every G-th catalog tile, G >= 32
 constexpr int64_t kSampleMaxTiles = 128; // sampled items per user at most 128 * 256
@@ -117,7 +117,7 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
 
 struct CandPlan {
     int64_t n_pieces_max = 0;
-    // Hot head (bf16, B > 8): catalog items listed at least c times over all
+    // Hot head (bf16, B >= 64): catalog items listed at least c times over all
     // lists (in sampled counts; c >= c_min, raised until at most t_max items
     // qualify) are scored
     // densely for every user on the MFMA path into s_hot[B][t_max]; the list
@@ -131,6 +131,7 @@ struct CandPlan {
            off_hot_ids = 0, off_ehot = 0, off_shot = 0, total = 0;
 };
 
+constexpr int kHotMinUsers = 64;             // fewer users: no item can reach the break-even count
 constexpr int kHotMaxRows = 16384;           // hot rows at most
 constexpr int64_t kHotMaxEBytes = 256ll << 20;  // ... and at most this much gathered catalog
 constexpr int64_t kHotMaxSBytes = 1ll << 30;    // ... and this much of dense scores
@@ -145,7 +146,7 @@ constexpr size_t kHdrErrIds = 0, kHdrErrOffsets = 8, kHdrPieces = 16, kHdrRescue
 inline CandPlan plan_cand(int B, int D, int64_t M, int64_t nnz, int dtype) {
     CandPlan p;
     p.n_pieces_max = nnz / kCandPiece + B;
-    if (dtype == 0 && B > kStreamMaxB && nnz > 0) {
+    if (dtype == 0 && B >= kHotMinUsers && nnz > 0) {
         const int64_t bpad = ceil_div(B, kMfmaTileUsers) * kMfmaTileUsers;
         int64_t t = std::min<int64_t>(kHotMaxRows, ceil_div(M, kMfmaTileItems) * kMfmaTileItems);
         t = std::min<int64_t>(t, kHotMaxEBytes / (2 * (int64_t)D));

@@ -128,8 +128,11 @@ def test_plan_selection(L):
     assert p["path"] == "mfma" and p["sample"] == 1 and p["P"] == 256
     assert p["fast"] == 1 and p["r_fast"] == -(-4 * 100 * p["n_sample"] // 100_000)
     # the VALU path keeps the K-th sampled score (no rescue pass)
-    p = genrec.describe_plan(3, 96, 70_000, 50, torch.bfloat16)
+    p = genrec.describe_plan(1, 96, 70_000, 50, torch.bfloat16)
     assert p["path"] == "stream" and p["sample"] == 1 and p["fast"] == 0
+    # small bf16 batches go to the matrix cores (E read once, not once per user)
+    assert genrec.describe_plan(2, 96, 70_000, 50, torch.bfloat16)["path"] == "mfma"
+    assert genrec.describe_plan(8, 4096, 1_000_000, 100, torch.float32)["path"] == "stream"
     p = genrec.describe_plan(1, 2048, 5000, 100, torch.bfloat16)
     assert p["path"] == "stream" and p["sample"] == 0
     p = genrec.describe_plan(4, 256, 5000, 10, torch.float32)
