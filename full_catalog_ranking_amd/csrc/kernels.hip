@@ -159,11 +159,10 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     }
 
     auto epilogue = [&](int t) {
-        const int lim = tile_valid(t);  // valid tile rows
-        const bool full = lim == MF_TI;
+        const int lim = tile_valid(t);  // valid tile rows (mode 0 stores only these)
         const int64_t j0 = tile_item0(t);
-        // Rows past the end of a partial tile read as -inf: they add nothing
-        // to the sum and never pass a threshold.  Each 32 x 32 block (16
+        // Rows past the end of a partial tile hold -inf (set before the call):
+        // they add nothing to the sum and never pass a threshold.  Each 32 x 32 block (16
         // scores per lane) is finished before the next is read, fenced by a
         // scheduling barrier, which keeps the live register set small.
 #pragma unroll
@@ -215,10 +214,6 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                 for (int r = 0; r < 16; ++r) {
                     v[r] = acc[ib][ub][r];
                     if (MASKED && !((mw >> (mbit0 + (r >> 2) * 8 + (r & 3))) & 1u)) v[r] = -INFINITY;
-                    if (!full) {
-                        const int m = (jb + (r >> 2) * 8 + (r & 3) - lim) >> 31;  // all ones iff the row is valid
-                        v[r] = __uint_as_float((__float_as_uint(v[r]) & (uint32_t)m) | (0xFF800000u & ~(uint32_t)m));
-                    }
                 }
                 float bmax = v[0];
 #pragma unroll
@@ -318,6 +313,20 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             }
             __builtin_amdgcn_sched_barrier(0);
             advance();
+        }
+        // Partial tile (the catalog's last): rows past the end score -inf,
+        // set once here under a uniform branch.  Folding this test into every
+        // block's epilogue made the compiler keep 16 row masks per block in
+        // scalar registers and spill them on every tile.
+        if (MODE == 1 && tile_valid(tile0 + t) < MF_TI) {
+            const int lim = tile_valid(tile0 + t);
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+                for (int ub = 0; ub < MF_UB; ++ub)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (lrow0 + ib * 32 + (r >> 2) * 8 + (r & 3) >= lim) acc[ib][ub][r] = -INFINITY;
         }
         epilogue(tile0 + t);
     }

@@ -18,6 +18,12 @@ constexpr int64_t kSampleMinStride = 32; // sample every G-th catalog tile, G >=
 constexpr int64_t kSampleMaxTiles = 128; // sampled items per user at most 128 * 256
 constexpr int64_t kSampleMaxItems = 32768;  // = kSampleMaxTiles * 256: one user's sample fits the threshold kernel
 constexpr int kFastOversample = 4;     // fast threshold: expected candidates ~ 4 K
+// MFMA path: the sample only has to place the fast threshold at rank >= 32 of
+// the sampled scores.  The number of catalog items above the r-th largest of
+// n sampled scores is about M r / n with a Gamma(r)-shaped spread, so at
+// r = 32 and 4 K expected the chance of fewer than K (a rescue) is ~1e-9 per
+// user.  A larger sample buys nothing there and costs a pass over more tiles.
+constexpr int64_t kFastMinRank = 32;
 constexpr int64_t kStreamPieces = 2048;  // target work pieces of the VALU path
 constexpr int64_t kStreamChunkAlign = 32;
 constexpr int kCandPiece = 256;        // candidate entries per piece (matches the kernels)
@@ -77,7 +83,12 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
     DensePlan p;
     p.mfma = dtype == 0 && B > kStreamMaxB;
     const int64_t full_tiles = M / kMfmaTileItems;
-    p.stride = std::max<int64_t>(kSampleMinStride, ceil_div(full_tiles, kSampleMaxTiles));
+    int64_t want_tiles = kSampleMaxTiles;
+    if (p.mfma && K > 0)
+        want_tiles = std::min<int64_t>(
+            kSampleMaxTiles,
+            std::max<int64_t>(1, ceil_div(ceil_div(kFastMinRank * M, (int64_t)kFastOversample * K), kMfmaTileItems)));
+    p.stride = std::max<int64_t>(kSampleMinStride, ceil_div(full_tiles, want_tiles));
     p.sample_tiles = ceil_div(full_tiles, p.stride);
     p.n_sample = p.sample_tiles * kMfmaTileItems;
     p.sample = M >= kSampleMinM && p.n_sample >= 4 * (int64_t)K;

@@ -122,14 +122,20 @@ def test_plan_selection(L):
     import torch
     p = genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)
     assert p["path"] == "mfma" and p["sample"] == 1 and p["UT"] == 4 and p["P"] == 64
-    # every 32nd of the 3906 full catalog tiles is sampled; fast threshold rank ceil(4 K n_sample / M)
-    assert p["n_sample"] == 123 * 256 and p["fast"] == 1 and p["r_fast"] == -(-4 * 500 * 123 * 256 // 1_000_000)
+    # MFMA path: ~32 M / (4 K) = 16,000 sampled items suffice for a fast
+    # threshold of rank >= 32: every 62nd of the 3906 full tiles (63 tiles);
+    # fast threshold rank ceil(4 K n_sample / M)
+    assert p["stride"] == 62 and p["n_sample"] == 63 * 256
+    assert p["fast"] == 1 and p["r_fast"] == -(-4 * 500 * 63 * 256 // 1_000_000) >= 32
     p = genrec.describe_plan(256, 2048, 100_000, 100, torch.bfloat16)
     assert p["path"] == "mfma" and p["sample"] == 1 and p["P"] == 256
     assert p["fast"] == 1 and p["r_fast"] == -(-4 * 100 * p["n_sample"] // 100_000)
     # the VALU path keeps the K-th sampled score (no rescue pass)
     p = genrec.describe_plan(1, 96, 70_000, 50, torch.bfloat16)
     assert p["path"] == "stream" and p["sample"] == 1 and p["fast"] == 0
+    # ... and the largest sample: every 32nd full tile, at most 128 tiles
+    p = genrec.describe_plan(1, 4096, 1_000_000, 100, torch.bfloat16)
+    assert p["stride"] == 32 and p["n_sample"] == 123 * 256
     # small bf16 batches go to the matrix cores (E read once, not once per user)
     assert genrec.describe_plan(2, 96, 70_000, 50, torch.bfloat16)["path"] == "mfma"
     assert genrec.describe_plan(8, 4096, 1_000_000, 100, torch.float32)["path"] == "stream"
