@@ -829,7 +829,7 @@ __device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
 // selection narrows a key range with 256-bin histograms, after a subsample
 // histogram and an exact count have cut the range to a few k keys.
 // ---------------------------------------------------------------------------
-constexpr int TH_KEYS = 32768;  // one user's sample at most
+constexpr int TH_KEYS = 32768;  // one user's sample at most (a 16,384-key build serves smaller samples)
 
 template <int NW>
 struct ThShared {
@@ -873,11 +873,11 @@ __device__ void th_find(const int* hist, int k, int q, Sh& sh) {
 // order statistic, robust to any rounding difference between passes.
 __device__ __forceinline__ float th_lower(float t) { return t - fabsf(t) * 0x1p-20f - FLT_MIN; }
 
-// TH_NT threads of TH_KEYS / TH_NT keys each: many threads for few users
-// (latency), fewer for many (throughput).
-template <int TH_NT>
+// TH_NT threads of TH_CAP / TH_NT keys each (TH_CAP >= the sample size):
+// many threads for few users (latency), fewer for many (throughput).
+template <int TH_NT, int TH_CAP>
 __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
-    constexpr int TH_PER = TH_KEYS / TH_NT;
+    constexpr int TH_PER = TH_CAP / TH_NT;
     constexpr int TH_NW = TH_NT / kWave;
     static_assert(TH_PER % 8 == 0 && TH_NT >= 256, "thread layout");
     __shared__ ThShared<TH_NW> sh;
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
         }
         return;
     }
-    // key e of thread t: e = 1024 i + 4 t + j (i < 32, j < 4): 16-byte loads,
+    // key e of thread t: e = 4 TH_NT i + 4 t + j (j < 4): 16-byte loads,
     // contiguous across the block
     const float* row = a.sample + (int64_t)b * a.n_sample;
     uint32_t key[TH_PER];  // 0 = no key (every score's key is larger)
@@ -1638,8 +1638,15 @@ hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, 
 
 hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s) {
     if (a.n_sample > (int64_t)TH_KEYS) return hipErrorInvalidValue;
-    if (a.B <= 512) hipLaunchKernelGGL(threshold_kernel<1024>, dim3(a.B), dim3(1024), 0, s, a);
-    else hipLaunchKernelGGL(threshold_kernel<256>, dim3(a.B), dim3(256), 0, s, a);
+    // many threads for few users; keys per thread sized to the sample
+    const bool half = a.n_sample <= (int64_t)(TH_KEYS / 2);
+    if (a.B <= 512) {
+        if (half) hipLaunchKernelGGL((threshold_kernel<1024, TH_KEYS / 2>), dim3(a.B), dim3(1024), 0, s, a);
+        else hipLaunchKernelGGL((threshold_kernel<1024, TH_KEYS>), dim3(a.B), dim3(1024), 0, s, a);
+    } else {
+        if (half) hipLaunchKernelGGL((threshold_kernel<256, TH_KEYS / 2>), dim3(a.B), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((threshold_kernel<256, TH_KEYS>), dim3(a.B), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -70,7 +70,10 @@ def _dtype_code(X: np.ndarray) -> int:
 def _users(users, B: int) -> np.ndarray:
     if users is None:
         users = np.arange(B)
-    return np.ascontiguousarray(users, dtype=np.int64)
+    u = np.ascontiguousarray(users, dtype=np.int64)
+    if u.size and (u.min() < 0 or u.max() >= B):
+        raise ValueError("user index out of range [0, %d)" % B)
+    return u
 
 
 def threads() -> int:

@@ -92,6 +92,22 @@ def test_large_b1024_sampled_users(dev, oracle_mod):
     assert all(np.unique(r).size == d["K"] for r in idx[::37])
 
 
+@pytest.mark.parametrize("B,D,M,K", [
+    (600, 64, 700_000, 10),   # MFMA path, > 512 users: 256-thread threshold, 22,016-item sample
+    (1, 64, 700_000, 50),     # VALU path, one user: 1024-thread threshold, same sample size
+])
+def test_threshold_full_capacity(dev, oracle_mod, B, D, M, K):
+    """Samples above 16,384 items take the threshold kernel's 32,768-key build."""
+    from full_catalog_ranking_amd import genrec
+    plan = genrec.describe_plan(B, D, M, K, torch.bfloat16)
+    assert plan["sample"] == 1 and 16384 < plan["n_sample"] <= 32768
+    d = synth.make_dense(B, D, M, seed=B + K)
+    g = run_dense(d, K, dev)
+    users = sorted({0, min(1, B - 1), B // 2, B - 1})
+    ref = oracle_mod.full(d["H"], d["E"], K, users=users)
+    parity.check_dense(g, ref, where="threshold capacity %s" % ((B, D, M, K),))
+
+
 def test_candidates_b4096(dev, oracle_mod):
     d = synth.make_workload("cand")
     g, errs = run_cand(d, d["K"], dev)

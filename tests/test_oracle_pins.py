@@ -285,3 +285,13 @@ def test_masked_brute_force_and_edge_cases(oracle_mod):
     w[-1] |= np.uint32(0xFFFFFFFF) << np.uint32(200 % 32)
     g2 = oracle_mod.full_masked(d["H"], d["E"], 15, w)
     assert np.array_equal(g2["idx"], g["idx"]) and np.array_equal(g2["lse"], g["lse"])
+
+
+def test_users_out_of_range_rejected(oracle_mod):
+    """A user index past the batch is an error, not a read past H."""
+    H = np.zeros((2, 4), dtype=np.float32)
+    E = np.zeros((3, 4), dtype=np.float32)
+    with pytest.raises(ValueError):
+        oracle_mod.full(H, E, 1, users=[0, 2])
+    with pytest.raises(ValueError):
+        oracle_mod.full(H, E, 1, users=[-1])
