@@ -297,8 +297,13 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                 if (i < 4 + MF_UB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
                 if (i == 2 || i == 5) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA)
             }
+            // raised wave priority across the wait and the barrier: the wave
+            // that gets through first issues its next reads and MFMAs ahead of
+            // its SIMD partner (measured ~1% faster than without)
+            __builtin_amdgcn_s_setprio(1);
             MF_WAIT_VMCNT(kWaitOps);
             __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
             cs = cs + 1 == MF_NS ? 0 : cs + 1;
             dma_op(ls, lk * MF_BK, 1);
