@@ -66,7 +66,8 @@ hipError_t timed(genrec_profiler* prof, int kind, hipStream_t s, F&& launch) {
 }
 
 enum { KIND_SAMPLE = 0, KIND_THRESHOLD = 1, KIND_MAIN = 2, KIND_MERGE = 3, KIND_PLAN = 4, KIND_RESCUE = 5,
-       KIND_HOT_SELECT = 6, KIND_HOT_SCORE = 7 };
+       KIND_HOT_SELECT = 6, KIND_HOT_SCORE = 7, KIND_CE_SMALL = 8, KIND_TRANSPOSE = 9, KIND_GRAD_TILES = 10,
+       KIND_GRAD_E = 11, KIND_GRAD_H = 12 };
 
 }  // namespace
 
@@ -509,6 +510,221 @@ int genrec_topk_rows(const float* scores, int R, int64_t N, int64_t ld, int K, i
     a.nchunk = p.nchunk;
     a.part = (uint64_t*)workspace;
     return hip_status(launch_topk_rows(a, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// Cross-entropy over the catalog
+// ---------------------------------------------------------------------------
+namespace {
+
+int check_ce(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels, const float* weights) {
+    if (B <= 0 || D <= 0 || M <= 0) return GENREC_ERR_INVALID_ARG;
+    if (!H || !E || !labels) return GENREC_ERR_INVALID_ARG;
+    if (!aligned(H, 16) || !aligned(E, 16) || !aligned(labels, 4) || (weights && !aligned(weights, 4)))
+        return GENREC_ERR_INVALID_ARG;
+    if (M >= ((int64_t)1 << 31)) return GENREC_ERR_UNSUPPORTED;
+    if (D % 8 != 0 || D > GENREC_DMAX) return GENREC_ERR_UNSUPPORTED;
+    return GENREC_OK;
+}
+
+CeArgs ce_args(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels, const float* weights,
+               void* workspace, const CePlan& p) {
+    CeArgs c{};
+    c.H = (const uint16_t*)H;
+    c.E = (const uint16_t*)E;
+    c.B = B;
+    c.D = D;
+    c.M = M;
+    c.labels = labels;
+    c.weights = weights;
+    c.w_eff = at<float>(workspace, p.off_w);
+    c.err = at<int64_t>(workspace, p.off_hdr);
+    return c;
+}
+
+}  // namespace
+
+size_t genrec_ce_forward_workspace(int B, int D, int64_t M) {
+    if (B <= 0 || D <= 0 || M <= 0 || M >= ((int64_t)1 << 31)) return 0;
+    return plan_ce(B, D, M).fwd_total;
+}
+
+size_t genrec_ce_backward_workspace(int B, int D, int64_t M) {
+    if (B <= 0 || D <= 0 || M <= 0 || M >= ((int64_t)1 << 31)) return 0;
+    return plan_ce(B, D, M).bwd_total;
+}
+
+int genrec_ce_forward_profiled(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels,
+                               const float* weights, float* out_loss, float* out_lse, void* workspace,
+                               size_t workspace_bytes, void* stream, genrec_profiler* prof) {
+    int st = check_ce(H, E, B, D, M, labels, weights);
+    if (st != GENREC_OK) return st;
+    if (!out_loss || !out_lse || !aligned(out_loss, 4) || !aligned(out_lse, 4)) return GENREC_ERR_INVALID_ARG;
+    const CePlan p = plan_ce(B, D, M);
+    if (!workspace || workspace_bytes < p.fwd_total) return GENREC_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    CeArgs c = ce_args(H, E, B, D, M, labels, weights, workspace, p);
+    if ((st = hip_status(timed(prof, KIND_CE_SMALL, s, [&] { return launch_ce_prep(c, s); }))) != GENREC_OK) return st;
+    // logsumexp pieces of every (user, catalog chunk, lane group); no candidates
+    MfmaArgs a{};
+    a.H = (const uint16_t*)H;
+    a.E = (const uint16_t*)E;
+    a.B = B;
+    a.D = D;
+    a.M = M;
+    a.n_tiles = (int)ceil_div(M, kMfmaTileItems);
+    a.tile_stride = 1;
+    a.UT = p.main.UT;
+    a.P = p.main.P;
+    a.base = p.main.base;
+    a.rem = p.main.rem;
+    a.no_cand = 1;
+    a.pm = at<float>(workspace, p.off_pm);
+    a.pl = at<float>(workspace, p.off_pl);
+    a.pcnt = at<int>(workspace, p.off_pcnt);
+    a.preg = at<int64_t>(workspace, p.off_preg);
+    if ((st = hip_status(timed(prof, KIND_MAIN, s, [&] { return launch_mfma(a, 1, s); }))) != GENREC_OK) return st;
+    c.pm = a.pm;
+    c.pl = a.pl;
+    c.P = p.main.P * 4;
+    c.out_loss = out_loss;
+    c.out_lse = out_lse;
+    return hip_status(timed(prof, KIND_CE_SMALL, s, [&] { return launch_ce_finish(c, s); }));
+}
+
+int genrec_ce_forward(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels,
+                      const float* weights, float* out_loss, float* out_lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+    return genrec_ce_forward_profiled(H, E, B, D, M, labels, weights, out_loss, out_lse, workspace, workspace_bytes,
+                                      stream, nullptr);
+}
+
+int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels,
+                                const float* weights, const float* lse, float* out_dH, float* out_dE,
+                                void* workspace, size_t workspace_bytes, void* stream, genrec_profiler* prof) {
+    int st = check_ce(H, E, B, D, M, labels, weights);
+    if (st != GENREC_OK) return st;
+    if (!lse || !out_dH || !out_dE || !aligned(lse, 4) || !aligned(out_dH, 4) || !aligned(out_dE, 4))
+        return GENREC_ERR_INVALID_ARG;
+    const CePlan p = plan_ce(B, D, M);
+    if (!workspace || workspace_bytes < p.bwd_total) return GENREC_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    CeArgs c = ce_args(H, E, B, D, M, labels, weights, workspace, p);
+    if ((st = hip_status(timed(prof, KIND_CE_SMALL, s, [&] { return launch_ce_prep(c, s); }))) != GENREC_OK) return st;
+    uint16_t* ht = at<uint16_t>(workspace, p.off_ht);
+    uint16_t* et = at<uint16_t>(workspace, p.off_et);
+    uint16_t* grows = at<uint16_t>(workspace, p.off_grows);
+    uint16_t* gcols = at<uint16_t>(workspace, p.off_gcols);
+    float* dhp = at<float>(workspace, p.off_dhp);
+    // H^T [D][Bp], users past B zero: the user side of the dE product
+    TransposeArgs th{};
+    th.in = (const uint16_t*)H;
+    th.R = B;
+    th.C = D;
+    th.ld_in = D;
+    th.out = ht;
+    th.ld_out = p.Bp;
+    if ((st = hip_status(timed(prof, KIND_TRANSPOSE, s, [&] { return launch_transpose(th, s); }))) != GENREC_OK)
+        return st;
+    for (int64_t ci = 0; ci < p.n_chunks; ++ci) {
+        const int64_t r0 = ci * p.chunk;
+        const int64_t rows = std::min<int64_t>(p.chunk, M - r0);
+        const int64_t mcp = ceil_div(rows, kMfmaTileItems) * kMfmaTileItems;
+        const int ntl = (int)(mcp / kMfmaTileItems);
+        const uint16_t* Ec = (const uint16_t*)E + r0 * D;
+        // E chunk^T [D][mcp], rows past the chunk zero: the item side of dH
+        TransposeArgs te{};
+        te.in = Ec;
+        te.R = rows;
+        te.C = D;
+        te.ld_in = D;
+        te.out = et;
+        te.ld_out = mcp;
+        if ((st = hip_status(timed(prof, KIND_TRANSPOSE, s, [&] { return launch_transpose(te, s); }))) != GENREC_OK)
+            return st;
+        // G = w (softmax - target) of the chunk, [B][mcp] and [mcp][Bp]
+        MfmaArgs g{};
+        g.H = (const uint16_t*)H;
+        g.E = Ec;
+        g.B = B;
+        g.D = D;
+        g.M = rows;
+        g.n_tiles = ntl;
+        g.tile_stride = 1;
+        const Chunking cg = chunk_mfma(B, ntl);
+        g.UT = cg.UT;
+        g.P = cg.P;
+        g.base = cg.base;
+        g.rem = cg.rem;
+        g.lse = lse;
+        g.wgt = c.w_eff;
+        g.labels = labels;
+        g.item0 = r0;
+        g.g_rows = grows;
+        g.g_cols = gcols;
+        g.ld_g = mcp;
+        g.ld_gt = p.Bp;
+        g.gt_users = (int)p.Bp;
+        if ((st = hip_status(timed(prof, KIND_GRAD_TILES, s, [&] { return launch_mfma_split(g, 3, 1, s); }))) !=
+            GENREC_OK)
+            return st;
+        // dE rows of the chunk = G^T H: rows = items, columns = D, reduction = Bp users
+        MfmaArgs de{};
+        de.E = gcols;
+        de.H = ht;
+        de.M = rows;
+        de.B = D;
+        de.D = (int)p.Bp;
+        de.n_tiles = ntl;
+        de.tile_stride = 1;
+        const Chunking ce = chunk_mfma(D, ntl);
+        de.UT = ce.UT;
+        de.P = ce.P;
+        de.base = ce.base;
+        de.rem = ce.rem;
+        de.c_out = out_dE + r0 * D;
+        de.ldc = D;
+        if ((st = hip_status(timed(prof, KIND_GRAD_E, s, [&] { return launch_mfma_split(de, 4, 1, s); }))) !=
+            GENREC_OK)
+            return st;
+        // dH += G E_chunk: rows = D, columns = users, reduction = the chunk's
+        // items in `splits` parts, each into its own partial sum
+        MfmaArgs dh{};
+        dh.E = et;
+        dh.H = grows;
+        dh.M = D;
+        dh.B = B;
+        dh.D = (int)(mcp / p.splits);
+        dh.ld = mcp;
+        dh.k_split = mcp / p.splits;
+        dh.n_tiles = (int)ceil_div(D, kMfmaTileItems);
+        dh.tile_stride = 1;
+        const Chunking chh = chunk_mfma(B, dh.n_tiles);
+        dh.UT = chh.UT;
+        dh.P = chh.P;
+        dh.base = chh.base;
+        dh.rem = chh.rem;
+        dh.c_out = dhp;
+        dh.ldc = D;
+        dh.c_split = (int64_t)B * D;
+        dh.c_trans = 1;
+        dh.c_accum = ci > 0 ? 1 : 0;
+        if ((st = hip_status(timed(prof, KIND_GRAD_H, s, [&] { return launch_mfma_split(dh, 4, p.splits, s); }))) !=
+            GENREC_OK)
+            return st;
+    }
+    return hip_status(timed(prof, KIND_CE_SMALL, s, [&] {
+        return launch_sum_splits(dhp, p.splits, (int64_t)B * D, (int64_t)B * D, out_dH, s);
+    }));
+}
+
+int genrec_ce_backward(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels,
+                       const float* weights, const float* lse, float* out_dH, float* out_dE, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return genrec_ce_backward_profiled(H, E, B, D, M, labels, weights, lse, out_dH, out_dE, workspace,
+                                       workspace_bytes, stream, nullptr);
 }
 
 int genrec_get_rescued_users(const void* workspace, void* stream, int64_t* n_rescued) {

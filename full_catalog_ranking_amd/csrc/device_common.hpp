@@ -37,6 +37,9 @@ __device__ __forceinline__ float key_score(uint64_t k) { return key_to_score((ui
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// fp32 -> bf16 bits, round to nearest even (the conversion of the __bf16 type).
+__device__ __forceinline__ uint16_t bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
 // Online log-sum-exp state: sum_i exp(s_i) = l * exp(m).
 struct LseState {
     float m, l;

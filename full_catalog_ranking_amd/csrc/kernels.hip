@@ -61,6 +61,10 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     const int u0 = ut * MF_TU;
     const int nk = (a.D + MF_BK - 1) / MF_BK;
     const int D = a.D;
+    // row stride of both operands, and where this block's share of the
+    // reduction starts in every row (grid y splits it)
+    const int64_t ldr = a.ld != 0 ? a.ld : (int64_t)D;
+    const int64_t kofs = (int64_t)blockIdx.y * a.k_split;
 
     // Pass-tile t holds catalog rows [t*G*256, t*G*256 + 256) clipped to M.
     auto tile_item0 = [&](int t) -> int64_t { return (int64_t)t * a.tile_stride * MF_TI; };
@@ -79,17 +83,17 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     const int wsu = __builtin_amdgcn_readfirstlane(w);  // wave index, provably uniform
     uint32_t voff[MF_DMA];
 #pragma unroll
-    for (int j = 0; j < MF_DMA; ++j) voff[j] = (uint32_t)mf_dma_voff(w, lane, j, D);
-    const int64_t row_bytes = (int64_t)D * 2;
+    for (int j = 0; j < MF_DMA; ++j) voff[j] = (uint32_t)mf_dma_voff(w, lane, j, (int)ldr);
+    const int64_t row_bytes = ldr * 2;
     // The user tile's resource is fixed; the catalog tile's is rebuilt when the
     // DMA moves to a new tile.  k0 rides in the scalar offset, so rows past the
     // end (and k-chunks past D on the last row) fall outside the record count.
     const int h_rows = a.B - u0 < MF_TU ? a.B - u0 : MF_TU;
     const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const char*)a.H + (int64_t)u0 * row_bytes), (short)0, (int)(h_rows * row_bytes), 0x00020000);
+        (void*)((const char*)a.H + (int64_t)u0 * row_bytes + kofs * 2), (short)0, (int)(h_rows * row_bytes), 0x00020000);
     __amdgpu_buffer_rsrc_t er;
     auto e_rsrc = [&](int t) {
-        er = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.E + tile_item0(t) * row_bytes), (short)0,
+        er = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.E + tile_item0(t) * row_bytes + kofs * 2), (short)0,
                                                (int)(tile_valid(t) * row_bytes), 0x00020000);
     };
 
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         if (MODE == 1 && a.theta != nullptr && u < a.B) t = fmaxf(a.theta[u], -FLT_MAX);
         // users past B never append, nor, in the rescue pass, unflagged users
         const bool active = u < a.B && (a.user_flag == nullptr || a.user_flag[u] != 0);
-        th_[ub] = active ? t : INFINITY;
+        th_[ub] = active && !a.no_cand ? t : INFINITY;
     }
 
     auto epilogue = [&](int t) {
@@ -178,6 +182,77 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                 return a.mask[(int64_t)u * a.mask_stride + (w0 >> 5)];
             };
             const int mbit0 = (lane >> 5) * 4;
+            if (MODE == 3) {
+                // g = w (softmax - target) of the scores, rounded to bf16, into
+                // both layouts; zeros past the valid rows and past the users
+                if (u < a.gt_users) {
+                    const bool real = u < a.B;
+                    const float lse_u = real ? a.lse[u] : 0.f;
+                    const float w_u = real ? a.wgt[u] : 0.f;
+                    // row of the user's label within this tile (outside [0, 256): none)
+                    const int64_t y_row = real ? (int64_t)a.labels[u] - a.item0 - j0 : -1;
+#pragma unroll
+                    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int jq = lrow0 + ib * 32 + q * 8;
+                            uint16_t gb[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float p = fast_exp2((acc[ib][ub][4 * q + e] - lse_u) * kLog2e);
+                                const float gv = w_u * (p - (jq + e == y_row ? 1.f : 0.f));
+                                gb[e] = bf16_bits(real && jq + e < lim ? gv : 0.f);
+                            }
+                            if (real)
+                                *(uint2*)(a.g_rows + (int64_t)u * a.ld_g + j0 + jq) =
+                                    make_uint2(gb[0] | ((uint32_t)gb[1] << 16), gb[2] | ((uint32_t)gb[3] << 16));
+                            uint16_t* gc = a.g_cols + (j0 + jq) * a.ld_gt + u;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) gc[e * a.ld_gt] = gb[e];
+                        }
+                }
+                continue;
+            }
+            if (MODE == 4) {
+                // plain product: the tile's valid rows of column u, fp32
+                if (u < a.B) {
+                    float* cz = a.c_out + (int64_t)blockIdx.y * a.c_split;
+#pragma unroll
+                    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int jq = lrow0 + ib * 32 + q * 8;
+                            const int64_t row = j0 + jq;
+                            if (a.c_trans) {  // [u][row .. row + 3]: consecutive
+                                float* o = cz + (int64_t)u * a.ldc + row;
+                                if (jq + 3 < lim) {
+                                    float4 v = make_float4(acc[ib][ub][4 * q], acc[ib][ub][4 * q + 1],
+                                                           acc[ib][ub][4 * q + 2], acc[ib][ub][4 * q + 3]);
+                                    if (a.c_accum) {
+                                        const float4 o4 = *(const float4*)o;
+                                        v.x += o4.x;
+                                        v.y += o4.y;
+                                        v.z += o4.z;
+                                        v.w += o4.w;
+                                    }
+                                    *(float4*)o = v;
+                                } else {
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e)
+                                        if (jq + e < lim) o[e] = acc[ib][ub][4 * q + e] + (a.c_accum ? o[e] : 0.f);
+                                }
+                            } else {  // [row + e][u]: a row segment across the lanes
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (jq + e < lim) {
+                                        float* o = cz + (row + e) * a.ldc + u;
+                                        *o = acc[ib][ub][4 * q + e] + (a.c_accum ? *o : 0.f);
+                                    }
+                            }
+                        }
+                }
+                continue;
+            }
             if (MODE == 0) {
                 if (u < a.B) {  // rows jq .. jq+3 of the lane are consecutive items: one 16-byte store
                     float* orow = a.sample_out + (int64_t)u * n_pass + (int64_t)t * MF_TI;
@@ -1605,6 +1680,170 @@ __global__ __launch_bounds__(HOT_NT) void hot_gather_kernel(HotArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Cross-entropy over the catalog: bookkeeping kernels around the MFMA passes
+// ---------------------------------------------------------------------------
+constexpr int CE_NT = 256;
+
+// Effective weight per example: the caller's weight (1 when none), 0 for a
+// label outside [0, M); err[0] = the number of such labels, err[1] = 0.
+// One block.
+__global__ __launch_bounds__(1024) void ce_prep_kernel(CeArgs a) {
+    __shared__ int s_bad;
+    if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
+    int bad = 0;
+    for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
+        const int32_t y = a.labels[b];
+        const bool ok = y >= 0 && (int64_t)y < a.M;
+        a.w_eff[b] = ok ? (a.weights != nullptr ? a.weights[b] : 1.f) : 0.f;
+        bad += ok ? 0 : 1;
+    }
+    if (bad) atomicAdd(&s_bad, bad);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        a.err[0] = s_bad;
+        a.err[1] = 0;
+    }
+}
+
+// Per example b: lse_b from the logsumexp pieces of the MFMA pass, the
+// label's score s_y = h_b . e_y (fp32 sum of exact bf16 products) and
+// loss_b = w_b (lse_b - s_y); an example whose label is out of range has
+// weight 0 and loss 0.
+__global__ __launch_bounds__(CE_NT) void ce_finish_kernel(CeArgs a) {
+    __shared__ float s_m[CE_NT / kWave], s_l[CE_NT / kWave], s_d[CE_NT / kWave];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    LseState st;
+    st.init();
+    for (int p = tid; p < a.P; p += CE_NT) st.merge(a.pm[(int64_t)b * a.P + p], a.pl[(int64_t)b * a.P + p]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) st.merge(__shfl_xor(st.m, o), __shfl_xor(st.l, o));
+    const int32_t y = a.labels[b];
+    const bool ok = y >= 0 && (int64_t)y < a.M;
+    float dot = 0.f;
+    if (ok) {
+        const uint16_t* h = a.H + (int64_t)b * a.D;
+        const uint16_t* e = a.E + (int64_t)y * a.D;
+        for (int d = tid * 8; d < a.D; d += CE_NT * 8) {
+            const uint4 hv = *(const uint4*)(h + d), ev = *(const uint4*)(e + d);
+            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.x), __builtin_bit_cast(bf16x2_t, ev.x), dot, false);
+            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.y), __builtin_bit_cast(bf16x2_t, ev.y), dot, false);
+            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.z), __builtin_bit_cast(bf16x2_t, ev.z), dot, false);
+            dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.w), __builtin_bit_cast(bf16x2_t, ev.w), dot, false);
+        }
+    }
+    dot = wave_sum(dot);
+    if (lane == 0) { s_m[w] = st.m; s_l[w] = st.l; s_d[w] = dot; }
+    __syncthreads();
+    if (tid == 0) {
+        LseState t;
+        t.init();
+        float sy = 0.f;
+        for (int q = 0; q < CE_NT / kWave; ++q) { t.merge(s_m[q], s_l[q]); sy += s_d[q]; }
+        const float lse = t.l > 0.f ? t.m + __builtin_amdgcn_logf(t.l) * kLn2 : -INFINITY;
+        a.out_lse[b] = lse;
+        a.out_loss[b] = ok ? a.w_eff[b] * (lse - sy) : 0.f;
+    }
+}
+
+// out[c][r] = in[r][c] through a 64 x 64 LDS tile; rows r in [R, ld_out) of
+// the output are zero.
+constexpr int TR_T = 64;
+__global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
+    __shared__ uint16_t tile[TR_T][TR_T + 2];
+    const int64_t c0 = (int64_t)blockIdx.x * TR_T, r0 = (int64_t)blockIdx.y * TR_T;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < TR_T * (TR_T / 8); i += 256) {
+        const int rr = i >> 3, cc = (i & 7) * 8;
+        const int64_t r = r0 + rr, cb = c0 + cc;
+        uint16_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (r < a.R) {
+            const uint16_t* src = a.in + r * a.ld_in + cb;
+            if (cb + 7 < a.C) {
+                const uint4 q = *(const uint4*)src;
+                const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = (uint16_t)w4[e];
+                    v[2 * e + 1] = (uint16_t)(w4[e] >> 16);
+                }
+            } else {
+                for (int e = 0; e < 8; ++e)
+                    if (cb + e < a.C) v[e] = src[e];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tile[rr][cc + e] = v[e];
+    }
+    __syncthreads();
+    for (int i = tid; i < TR_T * (TR_T / 8); i += 256) {
+        const int cc = i >> 3, rr = (i & 7) * 8;
+        const int64_t c = c0 + cc, r = r0 + rr;
+        if (c >= a.C || r >= a.ld_out) continue;
+        uint16_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = tile[rr + e][cc];
+        uint16_t* dst = a.out + c * a.ld_out + r;
+        if (r + 7 < a.ld_out) {
+            *(uint4*)dst = make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
+                                      v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
+        } else {
+            for (int e = 0; e < 8; ++e)
+                if (r + e < a.ld_out) dst[e] = v[e];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* in, int n, int64_t stride, int64_t count,
+                                                         float* out) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+        float t = 0.f;
+        for (int z = 0; z < n; ++z) t += in[z * stride + i];
+        out[i] = t;
+    }
+}
+
+hipError_t launch_ce_prep(const CeArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(ce_prep_kernel, dim3(1), dim3(1024), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_ce_finish(const CeArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(ce_finish_kernel, dim3(a.B), dim3(CE_NT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s) {
+    const int64_t gx = (a.C + TR_T - 1) / TR_T, gy = (a.ld_out + TR_T - 1) / TR_T;
+    if (gx <= 0 || gy <= 0) return hipSuccess;
+    if (gy > 65535 || gx > 2147483647) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_splits(const float* in, int n, int64_t stride, int64_t count, float* out, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    const int64_t g = std::min<int64_t>((count + 255) / 256, 4096);
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)g), dim3(256), 0, s, in, n, stride, count, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_split(const MfmaArgs& a, int mode, int splits, hipStream_t s) {
+    const dim3 grid(a.UT * a.P, splits);
+    const bool ktail = (a.D % MF_BK) != 0;
+    if (mode == 3) {
+        if (ktail) hipLaunchKernelGGL((mfma_score_kernel<3, true, false>), grid, dim3(MF_NT), 0, s, a);
+        else hipLaunchKernelGGL((mfma_score_kernel<3, false, false>), grid, dim3(MF_NT), 0, s, a);
+    } else if (mode == 4) {
+        if (ktail) return hipErrorInvalidValue;  // the products run over zero-padded reductions
+        hipLaunchKernelGGL((mfma_score_kernel<4, false, false>), grid, dim3(MF_NT), 0, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s) {
     const int grid = a.UT * a.P;
     const bool ktail = (a.D % MF_BK) != 0;

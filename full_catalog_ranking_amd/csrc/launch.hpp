@@ -36,6 +36,58 @@ struct MfmaArgs {
     // i % 32 of mask[u * mask_stride + i / 32] is set (stride 0: one mask)
     const uint32_t* mask;
     int64_t mask_stride;
+    // Row stride, in elements, of both operands (0: D).  D is the reduction
+    // length of this launch; grid y > 1 splits it: split z reads the operands
+    // from element z * k_split of each row (D = k_split).
+    int64_t ld;
+    int64_t k_split;
+    // mode 1: no candidate is kept at all (logsumexp pieces only)
+    int no_cand;
+    // mode 3 -- softmax-minus-target tiles of the cross-entropy gradient:
+    // rows are catalog items item0 + j (j < M valid), columns users;
+    // g = w[u] (exp(s - lse[u]) - [item0 + j == labels[u]]) goes to
+    // g_rows[u * ld_g + j] and g_cols[j * ld_gt + u] as bf16, with zeros in
+    // invalid rows (j < n_tiles * 256) and in columns B .. gt_users - 1.
+    const float* lse;
+    const float* wgt;
+    const int32_t* labels;
+    int64_t item0;
+    uint16_t* g_rows;
+    uint16_t* g_cols;
+    int64_t ld_g, ld_gt;
+    int gt_users;
+    // mode 4 -- plain product C[row][col] = sum_k A[row][k] B[col][k] (rows
+    // from the E-side operand, M valid; columns from the H-side operand, B
+    // valid) stored fp32 at c_out[row * ldc + col], or [col * ldc + row] when
+    // c_trans, added to what is there when c_accum; split z writes from
+    // c_out + z * c_split.
+    float* c_out;
+    int64_t ldc, c_split;
+    int c_trans, c_accum;
+};
+
+// Cross-entropy bookkeeping kernels.
+struct CeArgs {
+    const uint16_t* H;
+    const uint16_t* E;
+    int B, D;
+    int64_t M;
+    const int32_t* labels;
+    const float* weights;  // null: 1
+    float* w_eff;          // [B] weight, 0 for a label outside [0, M)
+    int64_t* err;          // [0] += labels outside [0, M)
+    const float* pm;       // forward: P pieces per user (logsumexp partials)
+    const float* pl;
+    int P;
+    float* out_loss;
+    float* out_lse;
+};
+
+struct TransposeArgs {
+    const uint16_t* in;  // [R][ld_in]
+    int64_t R, C, ld_in;
+    uint16_t* out;       // [C][ld_out]: out[c][r] = in[r][c], zero for R <= r < ld_out
+    int64_t ld_out;
 };
 
 struct CandPiece {
@@ -159,5 +211,12 @@ hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_cand_plan(const CandPlanArgs& a, hipStream_t s);
 hipError_t launch_hot_select(const HotArgs& a, hipStream_t s);
+// mode 3 / 4 of launch_mfma take grid y = splits of the reduction
+hipError_t launch_mfma_split(const MfmaArgs& a, int mode, int splits, hipStream_t s);
+hipError_t launch_ce_prep(const CeArgs& a, hipStream_t s);
+hipError_t launch_ce_finish(const CeArgs& a, hipStream_t s);
+hipError_t launch_transpose(const TransposeArgs& a, hipStream_t s);
+// out[i] = sum_{z < n} in[z * stride + i], i < count
+hipError_t launch_sum_splits(const float* in, int n, int64_t stride, int64_t count, float* out, hipStream_t s);
 
 }  // namespace genrec

@@ -236,4 +236,62 @@ inline TopkPlan plan_topk(int R, int64_t N, int K) {
     return p;
 }
 
+// ---------------------------------------------------------------------------
+// Cross-entropy over the catalog (bf16 only)
+// ---------------------------------------------------------------------------
+constexpr int64_t kCeChunk = 65536;  // catalog rows per backward chunk (G held for one chunk)
+constexpr int kCeMaxSplits = 8;      // reduction splits of the dH product (powers of two)
+
+struct CePlan {
+    Chunking main;  // forward logsumexp pass over the catalog
+    int64_t n_pieces = 0;
+    int64_t Bp = 0;        // users padded to 32 (reduction of the dE product)
+    int64_t chunk = 0;     // catalog rows per backward chunk
+    int64_t Mcp = 0;       // chunk rounded up to 256 (reduction of the dH product)
+    int64_t n_chunks = 0;
+    int splits = 1;
+    size_t off_hdr = 0, off_w = 0, off_pm = 0, off_pl = 0, off_pcnt = 0, off_preg = 0, fwd_total = 0;
+    size_t off_ht = 0, off_et = 0, off_grows = 0, off_gcols = 0, off_dhp = 0, bwd_total = 0;
+};
+
+inline CePlan plan_ce(int B, int D, int64_t M) {
+    CePlan p;
+    p.main = chunk_mfma(B, ceil_div(M, kMfmaTileItems));
+    p.n_pieces = (int64_t)B * p.main.P * 4;
+    p.Bp = ceil_div(B, 32) * 32;
+    p.chunk = std::min<int64_t>(M, kCeChunk);
+    p.Mcp = ceil_div(p.chunk, kMfmaTileItems) * kMfmaTileItems;
+    p.n_chunks = ceil_div(M, p.chunk);
+    const int64_t tiles = ceil_div(B, kMfmaTileUsers) * ceil_div(D, kMfmaTileItems);
+    while (p.splits < kCeMaxSplits && tiles * p.splits < kNumCU) p.splits *= 2;
+    size_t o = 0;
+    p.off_hdr = o;
+    o += 256;
+    p.off_w = o;
+    o = align_up(o + sizeof(float) * (size_t)B, 256);
+    const size_t common = o;
+    p.off_pm = o;
+    o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
+    p.off_pl = o;
+    o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
+    p.off_pcnt = o;
+    o = align_up(o + sizeof(int) * (size_t)p.n_pieces, 256);
+    p.off_preg = o;
+    o = align_up(o + sizeof(int64_t) * (size_t)p.n_pieces, 256);
+    p.fwd_total = o;
+    o = common;
+    p.off_ht = o;
+    o = align_up(o + 2 * (size_t)D * (size_t)p.Bp, 256);
+    p.off_et = o;
+    o = align_up(o + 2 * (size_t)D * (size_t)p.Mcp, 256);
+    p.off_grows = o;
+    o = align_up(o + 2 * (size_t)B * (size_t)p.Mcp, 256);
+    p.off_gcols = o;
+    o = align_up(o + 2 * (size_t)p.Mcp * (size_t)p.Bp, 256);
+    p.off_dhp = o;
+    o = align_up(o + sizeof(float) * (size_t)p.splits * (size_t)B * (size_t)D, 256);
+    p.bwd_total = o;
+    return p;
+}
+
 }  // namespace genrec

@@ -38,9 +38,16 @@ EXPORTED = (
     "genrec_profiler_summary",
     "genrec_score_lse_topk_profiled",
     "genrec_score_candidates_topk_profiled",
+    "genrec_ce_forward_workspace",
+    "genrec_ce_forward",
+    "genrec_ce_forward_profiled",
+    "genrec_ce_backward_workspace",
+    "genrec_ce_backward",
+    "genrec_ce_backward_profiled",
 )
+# must list GENREC_NUM_KERNEL_KINDS names: the summary fills that many slots
 KERNEL_KINDS = ("sample_score", "threshold", "main_score", "merge", "cand_plan", "rescue", "hot_select",
-                "hot_score")
+                "hot_score", "ce_small", "transpose", "grad_tiles", "grad_E", "grad_H")
 
 
 class GenrecError(RuntimeError):
@@ -96,6 +103,18 @@ def lib() -> ctypes.CDLL:
         L.genrec_score_lse_topk_masked_profiled.restype = I
         L.genrec_score_candidates_topk_profiled.argtypes = L.genrec_score_candidates_topk.argtypes + [P]
         L.genrec_score_candidates_topk_profiled.restype = I
+        L.genrec_ce_forward_workspace.argtypes = [I, I, I64]
+        L.genrec_ce_forward_workspace.restype = SZ
+        L.genrec_ce_backward_workspace.argtypes = [I, I, I64]
+        L.genrec_ce_backward_workspace.restype = SZ
+        L.genrec_ce_forward.argtypes = [P, P, I, I, I64, P, P, P, P, P, SZ, P]
+        L.genrec_ce_forward.restype = I
+        L.genrec_ce_forward_profiled.argtypes = L.genrec_ce_forward.argtypes + [P]
+        L.genrec_ce_forward_profiled.restype = I
+        L.genrec_ce_backward.argtypes = [P, P, I, I, I64, P, P, P, P, P, P, SZ, P]
+        L.genrec_ce_backward.restype = I
+        L.genrec_ce_backward_profiled.argtypes = L.genrec_ce_backward.argtypes + [P]
+        L.genrec_ce_backward_profiled.restype = I
         _lib = L
     return _lib
 
@@ -263,6 +282,71 @@ def score_candidates_topk(H: torch.Tensor, E: torch.Tensor, offsets: torch.Tenso
     if st != 0:
         raise GenrecError(st, "genrec_score_candidates_topk")
     return idx, sc, ls, workspace
+
+
+def _check_ce(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, weights):
+    _check_inputs(H, E)
+    if H.dtype != torch.bfloat16:
+        raise TypeError("the cross-entropy entry points take bfloat16 H and E")
+    B = H.shape[0]
+    if labels.dtype != torch.int32 or labels.shape != (B,) or not (labels.is_cuda and labels.is_contiguous()):
+        raise ValueError("labels must be a contiguous int32 device tensor of shape (B,)")
+    if weights is not None and (weights.dtype != torch.float32 or weights.shape != (B,)
+                                or not (weights.is_cuda and weights.is_contiguous())):
+        raise ValueError("weights must be a contiguous float32 device tensor of shape (B,)")
+
+
+def ce_forward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, weights: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, profiler: Profiler | None = None):
+    """Catalog cross-entropy forward: (loss f32 [B], lse f32 [B], workspace).
+
+    loss_b = w_b (lse_b - h_b . e_{y_b}); an out-of-range label gives loss 0
+    and is counted (device_errors(workspace)[0])."""
+    _check_ce(H, E, labels, weights)
+    B, D = H.shape
+    M = E.shape[0]
+    need = lib().genrec_ce_forward_workspace(B, D, M)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    loss = torch.empty((B,), dtype=torch.float32, device=H.device)
+    lse = torch.empty((B,), dtype=torch.float32, device=H.device)
+    args = (_ptr(H), _ptr(E), B, D, M, _ptr(labels), _ptr(weights), _ptr(loss), _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream_handle(H.device))
+    if profiler is None:
+        st = lib().genrec_ce_forward(*args)
+    else:
+        st = lib().genrec_ce_forward_profiled(*args, profiler.h)
+    if st != 0:
+        raise GenrecError(st, "genrec_ce_forward")
+    return loss, lse, workspace
+
+
+def ce_backward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, lse: torch.Tensor,
+                weights: torch.Tensor | None = None, workspace: torch.Tensor | None = None, out=None,
+                profiler: Profiler | None = None):
+    """Gradients of sum_b loss_b: (dH f32 [B, D], dE f32 [M, D]); lse from ce_forward."""
+    _check_ce(H, E, labels, weights)
+    B, D = H.shape
+    M = E.shape[0]
+    if lse.dtype != torch.float32 or lse.shape != (B,) or not (lse.is_cuda and lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 device tensor of shape (B,)")
+    need = lib().genrec_ce_backward_workspace(B, D, M)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    if out is None:
+        dH = torch.empty((B, D), dtype=torch.float32, device=H.device)
+        dE = torch.empty((M, D), dtype=torch.float32, device=H.device)
+    else:
+        dH, dE = out
+    args = (_ptr(H), _ptr(E), B, D, M, _ptr(labels), _ptr(weights), _ptr(lse), _ptr(dH), _ptr(dE),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(H.device))
+    if profiler is None:
+        st = lib().genrec_ce_backward(*args)
+    else:
+        st = lib().genrec_ce_backward_profiled(*args, profiler.h)
+    if st != 0:
+        raise GenrecError(st, "genrec_ce_backward")
+    return dH, dE
 
 
 def device_errors(workspace: torch.Tensor) -> tuple[int, int]:

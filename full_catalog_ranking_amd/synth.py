@@ -31,6 +31,9 @@ that chunked / threaded generation is bit-identical to serial generation):
   the same stream.  Keeping first occurrences of an i.i.d. weighted sequence is
   exactly successive weighted sampling without replacement, and the list keeps
   that sampled order.
+* Cross-entropy examples: user b's label (the engaged item) is one draw with
+  probability proportional to the Zipf weights, from stream (seed, 3); its
+  reward weight is uniform on [0.25, 2], from stream (seed, 4).
 """
 from __future__ import annotations
 
@@ -163,6 +166,19 @@ def gen_candidates(B: int, M: int, seed: int, lo: int, hi: int,
     return offsets, ids.astype(np.int32)
 
 
+def gen_labels(B: int, M: int, seed: int) -> np.ndarray:
+    """One engaged item per example (int32 [B]), Zipf-weighted by popularity rank."""
+    cdf = np.cumsum(zipf_weights(M))
+    cdf /= cdf[-1]
+    y = np.searchsorted(cdf, _rng(seed, 3).random(B), side="right")
+    return np.minimum(y, M - 1).astype(np.int32)
+
+
+def gen_weights(B: int, seed: int) -> np.ndarray:
+    """Per-example reward weights (float32 [B]), uniform on [0.25, 2]."""
+    return _rng(seed, 4).uniform(0.25, 2.0, B).astype(np.float32)
+
+
 # ---------------------------------------------------------------------------
 # Named workloads.  Sizes follow the five benchmark shapes of this project:
 # a 4-user fp32 toy with planted items, a single-user GEMV, a 256-user batch,
@@ -180,6 +196,8 @@ WORKLOADS = {
     # beam steps: R requests of width x width continuation scores -> the best `width`
     "beam128": dict(R=256, N=128 * 128, K=128, kind="beam"),
     "beam512": dict(R=64, N=512 * 512, K=512, kind="beam"),
+    # reward-weighted catalog cross-entropy, forward + backward, at the large shape
+    "ce": dict(B=1024, D=4096, M=1_000_000, K=0, dtype="bf16", kind="ce"),
 }
 
 TINY_PLANT_ITEM = 17
@@ -230,4 +248,8 @@ def make_workload(name: str, seed: int = 0, **over) -> dict:
     d["K"] = cfg["K"]
     if name == "cand":
         d["offsets"], d["ids"] = gen_candidates(cfg["B"], cfg["M"], seed, cfg["lo"], cfg["hi"])
+    if cfg.get("kind") == "ce":
+        d["labels"] = gen_labels(cfg["B"], cfg["M"], seed)
+        d["weights"] = gen_weights(cfg["B"], seed)
+        d["kind"] = "ce"
     return d

@@ -167,6 +167,43 @@ int genrec_topk_rows(const float* scores, int R, int64_t N, int64_t ld, int K,
                      int32_t* out_idx, float* out_scores,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Cross-entropy over the whole catalog, forward and backward, without a
+ * B x M score matrix in memory (GenRec explainer page, "two objectives and
+ * reward-weighted ranking" section: the ranking objective is a cross-entropy
+ * over the catalog, each example's loss multiplied by a scalar weight built
+ * from reward signals; its "start from the ranking head" step: an
+ * inner-product head trained with the full-catalog softmax).
+ *
+ * bf16 only.  H [B][D], E [M][D] as above (16-byte aligned, D % 8 == 0);
+ * labels [B] int32 catalog ids; weights [B] float32, or NULL for all ones.
+ * With s_bi = h_b . e_i and lse_b = ln sum_i exp(s_bi):
+ *   forward:   out_loss[b] = w_b (lse_b - s_{b,y_b}),  out_lse[b] = lse_b;
+ *   backward:  with G[b][i] = w_b (exp(s_bi - lse_b) - [i == y_b]),
+ *              out_dH = G E  ([B][D] float32),  out_dE = G^T H  ([M][D] float32),
+ *              the gradients of sum_b out_loss[b]; `lse` is the forward's out_lse.
+ * An example whose label lies outside [0, M) is ignored (loss 0, no
+ * gradient) and counted: genrec_get_device_errors on the same workspace
+ * reports the count as *n_bad_ids (and 0 as *n_bad_offsets).
+ * The backward recomputes the scores chunk by chunk (65,536 catalog rows at a
+ * time), holds G of one chunk in bf16 (rounded to nearest even) and computes
+ * both products on the matrix cores with fp32 accumulation; only the
+ * workspace of genrec_ce_backward_workspace() bytes is used.  Asynchronous on
+ * `stream`; out_dH and out_dE are overwritten.  Outputs 4-byte aligned,
+ * workspace 256-byte aligned.  GENREC_ERR_INVALID_ARG / _UNSUPPORTED /
+ * _WORKSPACE as for the other entry points.
+ */
+size_t genrec_ce_forward_workspace(int B, int D, int64_t M);
+int genrec_ce_forward(const void* H, const void* E, int B, int D, int64_t M,
+                      const int32_t* labels, const float* weights,
+                      float* out_loss, float* out_lse,
+                      void* workspace, size_t workspace_bytes, void* stream);
+size_t genrec_ce_backward_workspace(int B, int D, int64_t M);
+int genrec_ce_backward(const void* H, const void* E, int B, int D, int64_t M,
+                       const int32_t* labels, const float* weights, const float* lse,
+                       float* out_dH, float* out_dE,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Introspection: writes into buf (at most len bytes, NUL-terminated) a JSON
  * object describing how genrec_score_lse_topk would run these sizes: the
  * scoring path ("mfma" or "stream"), whether the sampled-threshold pre-pass
@@ -186,11 +223,13 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
  * left short of K candidates; they exit at once when no user is), 6 hot-head
  * selection of a candidate call (per-item list counts, the count threshold,
  * the compaction and gather of the most-listed catalog rows), 7 dense scoring
- * of those rows for every user.  One profiler holds up to `max_launches` launches; further
+ * of those rows for every user, 8 small cross-entropy kernels (label check,
+ * loss, sum of the dH partials), 9 transposes (H, catalog chunks), 10 softmax-
+ * minus-target tiles G, 11 dE product, 12 dH product.  One profiler holds up to `max_launches` launches; further
  * launches are not recorded.  A profiler may only be used by one stream at a
  * time.  create returns NULL on failure.
  */
-#define GENREC_NUM_KERNEL_KINDS 8
+#define GENREC_NUM_KERNEL_KINDS 13
 typedef struct genrec_profiler genrec_profiler;
 genrec_profiler* genrec_profiler_create(int max_launches);
 void genrec_profiler_destroy(genrec_profiler* prof);
@@ -198,8 +237,8 @@ int genrec_profiler_reset(genrec_profiler* prof);
 int genrec_profiler_summary(genrec_profiler* prof, int* counts, double* total_ms);
 
 /* Same as genrec_score_lse_topk / genrec_score_lse_topk_masked /
- * genrec_score_candidates_topk, recording every launch into `prof` (which may
- * be NULL). */
+ * genrec_score_candidates_topk / genrec_ce_forward / genrec_ce_backward,
+ * recording every launch into `prof` (which may be NULL). */
 int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype,
                                    int B, int D, int64_t M, int K,
                                    int32_t* out_idx, float* out_scores, float* out_lse,
@@ -217,6 +256,16 @@ int genrec_score_candidates_topk_profiled(const void* H, const void* E, int dtyp
                                           int32_t* out_idx, float* out_scores, float* out_lse,
                                           void* workspace, size_t workspace_bytes, void* stream,
                                           genrec_profiler* prof);
+int genrec_ce_forward_profiled(const void* H, const void* E, int B, int D, int64_t M,
+                               const int32_t* labels, const float* weights,
+                               float* out_loss, float* out_lse,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               genrec_profiler* prof);
+int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int64_t M,
+                                const int32_t* labels, const float* weights, const float* lse,
+                                float* out_dH, float* out_dE,
+                                void* workspace, size_t workspace_bytes, void* stream,
+                                genrec_profiler* prof);
 
 /* Human-readable name of a genrec_status value (static storage). */
 const char* genrec_status_string(int status);

@@ -180,3 +180,56 @@ def cand(H: np.ndarray, E: np.ndarray, offsets: np.ndarray, ids: np.ndarray, K: 
     bad = _load().oracle_cand(_ptr(H), _ptr(E), dt, D, M, K, _ptr(off), _ptr(idv), _ptr(u), u.size,
                               _ptr(es), _ptr(idx), _ptr(sc), _ptr(ls))
     return dict(idx=idx, score=sc, lse=ls, entry_scores=es, n_bad=int(bad), users=u)
+
+
+def widen(X: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of bf16 bit patterns (uint16) or float32 inputs."""
+    if X.dtype == np.uint16:
+        return (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if X.dtype == np.float32:
+        return X.astype(np.float64)
+    raise TypeError("oracle inputs are uint16 (bf16 bits) or float32, got %s" % X.dtype)
+
+
+def ce(H: np.ndarray, E: np.ndarray, labels: np.ndarray, weights=None, users=None, grads: bool = True):
+    """Cross-entropy of the catalog softmax, reward-weighted per example.
+
+    Follows the GenRec explainer page, "two objectives and reward-weighted
+    ranking" section: the ranking objective is the cross-entropy of the
+    softmax over the catalog, each example's loss multiplied by its scalar
+    weight.  With s_bi = h_b . e_i (fp64, as scores()) and lse_b = ln sum_i
+    exp(s_bi) (as lse()):
+        loss_b = w_b (lse_b - s_{b, y_b})
+        G[b][i] = w_b (exp(s_bi - lse_b) - [i == y_b])   (d loss_b / d s_bi)
+        dH = G E,  dE = G^T H                               (chain rule through s = H E^T)
+    An example whose label lies outside [0, M) is ignored: weight 0.
+    users: rows to evaluate (default all); dE needs every user, so it is
+    returned only when users is None.  Returns dict(loss, lse, users, S (the
+    score rows), w (effective weights), and with grads: P (softmax rows), G,
+    dH, and dE when users is None).
+    """
+    u = _users(users, H.shape[0])
+    M = E.shape[0]
+    S = scores(H, E, u)
+    y = np.asarray(labels, dtype=np.int64)[u]
+    w = np.ones(u.size) if weights is None else np.asarray(weights, dtype=np.float64)[u]
+    valid = (y >= 0) & (y < M)
+    w = np.where(valid, w, 0.0)
+    lse_v = np.array([lse(S[r]) for r in range(u.size)])
+    rows = np.arange(u.size)
+    s_y = np.where(valid, S[rows, np.where(valid, y, 0)], 0.0)
+    out = dict(loss=w * (lse_v - s_y), lse=lse_v, users=u, S=S, w=w)
+    if grads:
+        P = np.exp(S - lse_v[:, None])
+        G = w[:, None] * P
+        G[rows[valid], y[valid]] -= w[valid]
+        out["P"] = P
+        out["G"] = G
+        # dH = G E, with E widened a block of rows at a time (memory only)
+        dH = np.zeros((u.size, E.shape[1]))
+        for i0 in range(0, M, 65536):
+            dH += G[:, i0:i0 + 65536] @ widen(E[i0:i0 + 65536])
+        out["dH"] = dH
+        if users is None:
+            out["dE"] = G.T @ widen(H)
+    return out

@@ -77,3 +77,40 @@ def check_cand(gpu, ref, offsets, ids, tau=None, where=""):
         check_row(g_idx[b], g_sc[b], g_lse[b], ref["idx"][r], ref["score"][r], ref["lse"][r],
                   lambda q, t=table: np.array([t[int(x)] for x in q]), tau, where="%s user %d" % (where, b))
     return tau
+
+
+# ---------------------------------------------------------------------------
+# Catalog cross-entropy
+# ---------------------------------------------------------------------------
+# The GPU keeps G = w (softmax - target) in bf16 (rounded to nearest even,
+# relative error <= 2^-9) and forms the softmax from fp32 scores and lse, each
+# within the score tolerance tau of the exact value, so every entry of G is
+# within c |A| of the exact one with c = 2^-9 + 2 tau and A = |G| + w P (the
+# second term covers the label entry, whose G is w (p - 1)).  The products
+# add at most depth * 2^-24 relative fp32 rounding on top (depth = the longest
+# chain of fp32 additions into one output).  So, entrywise,
+#   |dH_gpu - dH| <= (c + depth_H 2^-24) (A |E|)   and
+#   |dE_gpu - dE| <= (c + depth_E 2^-24) (A^T |H|),
+# loss and lse within the lse rule (loss scaled by w).
+def check_ce(gpu, ref, E, H, widen, depth_h=1, depth_e=1, where=""):
+    """gpu = (loss, lse, dH, dE or None) host arrays for the users in ref['users']
+    (dE for the whole catalog); ref = oracle.ce(...); E, H = the raw inputs and
+    widen = their exact fp64 conversion."""
+    loss, lse_g, dH, dE = gpu
+    tau = SCORE_REL * np.abs(ref["S"]).max()
+    w = ref["w"]
+    assert np.abs(lse_g - ref["lse"]).max() <= LSE_ABS, (where, "lse", np.abs(lse_g - ref["lse"]).max())
+    assert (np.abs(loss - ref["loss"]) <= w * 2 * LSE_ABS + 1e-6).all(), (where, "loss",
+                                                                        np.abs(loss - ref["loss"]).max())
+    c = 2.0 ** -9 + 2 * tau
+    A = np.abs(ref["G"]) + w[:, None] * ref["P"]
+    AE = np.zeros(dH.shape)
+    for i0 in range(0, E.shape[0], 65536):  # A |E|, a block of catalog rows at a time
+        AE += A[:, i0:i0 + 65536] @ np.abs(widen(E[i0:i0 + 65536]))
+    tol_h = (c + depth_h * 2.0 ** -24) * AE + 1e-30
+    err_h = np.abs(dH - ref["dH"])
+    assert (err_h <= tol_h).all(), (where, "dH", err_h.max(), (err_h / tol_h).max())
+    if dE is not None:
+        tol_e = (c + depth_e * 2.0 ** -24) * (A.T @ np.abs(widen(H))) + 1e-30
+        err_e = np.abs(dE - ref["dE"])
+        assert (err_e <= tol_e).all(), (where, "dE", err_e.max(), (err_e / tol_e).max())

@@ -295,3 +295,75 @@ def test_users_out_of_range_rejected(oracle_mod):
         oracle_mod.full(H, E, 1, users=[0, 2])
     with pytest.raises(ValueError):
         oracle_mod.full(H, E, 1, users=[-1])
+
+
+# ---------------------------------------------------------------------------
+# Catalog cross-entropy (forward and gradients)
+# ---------------------------------------------------------------------------
+def _ce_case(seed, B=3, D=5, M=7, step=2.0 ** -12):
+    """Small fp32 inputs on a grid of `step`, so that x +- step stays exact."""
+    rng = np.random.default_rng(seed)
+    H = (np.round(rng.standard_normal((B, D)) / step) * step).astype(np.float32)
+    E = (np.round(rng.standard_normal((M, D)) / step) * step).astype(np.float32)
+    y = rng.integers(0, M, B).astype(np.int32)
+    w = rng.uniform(0.25, 2.0, B)
+    return H, E, y, w
+
+
+def test_ce_gradients_match_central_differences(oracle_mod):
+    """dH and dE are the derivatives of sum_b loss_b: checked against central
+    differences of the oracle's own forward (no use of the gradient formula)."""
+    step = 2.0 ** -12
+    H, E, y, w = _ce_case(3, step=step)
+    r = oracle_mod.ce(H, E, y, w)
+    total = lambda H_, E_: oracle_mod.ce(H_, E_, y, w, grads=False)["loss"].sum()
+    for X, g, name in ((H, r["dH"], "dH"), (E, r["dE"], "dE")):
+        num = np.zeros_like(g)
+        for idx in np.ndindex(*X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += step
+            Xm[idx] -= step
+            args_p = (Xp, E) if name == "dH" else (H, Xp)
+            args_m = (Xm, E) if name == "dH" else (H, Xm)
+            num[idx] = (total(*args_p) - total(*args_m)) / (2 * step)
+        assert np.abs(num - g).max() <= 1e-6 * max(1.0, np.abs(g).max()), (name, np.abs(num - g).max())
+
+
+def test_ce_closed_form_zero_catalog(oracle_mod):
+    """E = 0: every score is 0, so lse = ln M, loss_b = w_b ln M, dH = 0 and
+    dE_i = sum_b w_b (1/M - [i == y_b]) h_b."""
+    H, E, y, w = _ce_case(4, B=4, M=9)
+    E = np.zeros_like(E)
+    r = oracle_mod.ce(H, E, y, w)
+    M = E.shape[0]
+    assert np.allclose(r["lse"], math.log(M), rtol=0, atol=1e-14)
+    assert np.allclose(r["loss"], w * math.log(M), rtol=1e-14, atol=0)
+    assert np.abs(r["dH"]).max() == 0.0
+    expect = np.zeros((M, H.shape[1]))
+    for b in range(H.shape[0]):
+        for i in range(M):
+            expect[i] += w[b] * ((1.0 / M) - (1.0 if i == y[b] else 0.0)) * H[b].astype(np.float64)
+    assert np.allclose(r["dE"], expect, rtol=1e-13, atol=1e-15)
+
+
+def test_ce_invariants_and_library(oracle_mod):
+    """Softmax rows agree with scipy, G rows sum to zero so dE's columns sum
+    to zero, the loss is non-negative, and an out-of-range label is ignored."""
+    H, E, y, w = _ce_case(5, B=6, D=8, M=50)
+    y = y.copy()
+    y[2], y[4] = -1, 50  # outside [0, M)
+    r = oracle_mod.ce(H, E, y, w)
+    S = oracle_mod.scores(H, E)
+    assert np.allclose(r["lse"], scipy.special.logsumexp(S, axis=1), rtol=1e-14, atol=1e-14)
+    assert np.allclose(r["P"], scipy.special.softmax(S, axis=1), rtol=1e-12, atol=1e-15)
+    assert np.abs(r["G"].sum(axis=1)).max() < 1e-14
+    assert np.abs(r["dE"].sum(axis=0)).max() < 1e-12
+    assert (r["loss"] >= 0).all()
+    assert r["loss"][2] == 0.0 and r["loss"][4] == 0.0
+    assert np.abs(r["G"][[2, 4]]).max() == 0.0 and np.abs(r["dH"][[2, 4]]).max() == 0.0
+    # a valid example's loss is the negative log-probability of its label, weighted
+    b = 0
+    assert abs(r["loss"][b] - w[b] * -math.log(r["P"][b, y[b]])) < 1e-12
+    # a subset of users gives the same rows
+    rs = oracle_mod.ce(H, E, y, w, users=[5, 0])
+    assert np.allclose(rs["dH"], r["dH"][[5, 0]], rtol=0, atol=0) and "dE" not in rs
