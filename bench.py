@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="large", choices=["large", "batch", "gemv", "tiny", "cand", "gemv_big", "beam128", "beam512"])
+    ap.add_argument("--workload", default="large",
+                    choices=["large", "batch", "gemv", "tiny", "cand", "gemv_big", "beam128", "beam512", "ce"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -213,6 +214,80 @@ def bench_beam(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_ce(args):
+    """Reward-weighted catalog cross-entropy: one step = forward + backward."""
+    import torch
+    from full_catalog_ranking_amd import genrec, synth
+    dev = torch.device("cuda:0")
+    genrec.lib()
+    t0 = time.perf_counter()
+    d = synth.make_workload(args.workload)
+    log("inputs generated in %.1f s" % (time.perf_counter() - t0))
+    B, D, M = d["B"], d["D"], d["M"]
+    H, E = to_dev(d["H"], dev, torch), to_dev(d["E"], dev, torch)
+    lab = torch.from_numpy(d["labels"]).to(dev)
+    w = torch.from_numpy(d["weights"]).to(dev)
+    wsf = torch.empty(genrec.lib().genrec_ce_forward_workspace(B, D, M), dtype=torch.uint8, device=dev)
+    wsb = torch.empty(genrec.lib().genrec_ce_backward_workspace(B, D, M), dtype=torch.uint8, device=dev)
+    dH = torch.empty((B, D), dtype=torch.float32, device=dev)
+    dE = torch.empty((M, D), dtype=torch.float32, device=dev)
+    prof = genrec.Profiler(max_launches=80 * (args.steps + 1))
+
+    def step(p=None):
+        loss, lse, _ = genrec.ce_forward(H, E, lab, w, workspace=wsf, profiler=p)
+        genrec.ce_backward(H, E, lab, lse, w, workspace=wsb, out=(dH, dE), profiler=p)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step(prof)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    kern = prof.summary()
+    per_step = {k: v[1] / args.steps for k, v in kern.items()}
+    log("step %.3f ms; kernels per step %s" % (ms, {k: "%.3f ms" % v for k, v in per_step.items()}))
+    # each MFMA kind computes one B x M x D product per step: 2 B M D flops
+    prod = 2.0 * B * M * D
+    tf = {k: prod / (per_step[k] * 1e-3) / 1e12 for k in ("main_score", "grad_tiles", "grad_E", "grad_H")
+          if k in per_step}
+    dom = max(tf, key=lambda k: per_step[k])
+    kname = {"main_score": "mfma_score_kernel<1>", "grad_tiles": "mfma_score_kernel<3>",
+             "grad_E": "mfma_score_kernel<4> (dE)", "grad_H": "mfma_score_kernel<4> (dH)"}[dom]
+    res = {
+        "metric": METRIC, "value": B * M / (ms * 1e-3), "unit": "scores/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "ce", "B": B, "D": D, "M": M, "step": "forward+backward"},
+        "tflops": 4 * prod / (ms * 1e-3) / 1e12,
+        "kernels_ms": per_step,
+        "kernel_tflops": tf,
+        "roofline": {"bound": "mfma", "achieved": tf[dom], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf[dom] / MFMA_BF16_PEAK_TFLOPS, "kernel": kname, "kernel_ms": per_step[dom],
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        del H, E, dE, wsb
+        torch.cuda.empty_cache()
+        from oracle import oracle
+        oracle.build()
+        t0 = time.perf_counter()
+        oracle.ce(d["H"], d["E"], d["labels"], d["weights"], users=[0])
+        t1 = time.perf_counter() - t0
+        n = int(max(1, min(B, args.cpu_seconds / max(t1, 1e-3))))
+        users = np.linspace(0, B - 1, n).astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.ce(d["H"], d["E"], d["labels"], d["weights"], users=users)
+        t = time.perf_counter() - t0
+        res["cpu_baseline"] = dict(value=n * M / t, unit="scores/s", cores=oracle.threads(), kind="oracle",
+                                   sample="%d of %d users: loss, lse and dH rows (fp64; dE needs every user), "
+                                          "%.1f s" % (n, B, t))
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -227,6 +302,9 @@ def main():
         return
     if args.workload.startswith("beam"):
         bench_beam(args)
+        return
+    if args.workload == "ce":
+        bench_ce(args)
         return
     import torch
     from full_catalog_ranking_amd import genrec, synth

@@ -634,7 +634,7 @@ int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int6
         const int64_t mcp = ceil_div(rows, kMfmaTileItems) * kMfmaTileItems;
         const int ntl = (int)(mcp / kMfmaTileItems);
         const uint16_t* Ec = (const uint16_t*)E + r0 * D;
-        // E chunk^T [D][mcp], rows past the chunk zero: the item side of dH
+        // E chunk^T [D][mcp] k-blocked, rows past the chunk zero: the item side of dH
         TransposeArgs te{};
         te.in = Ec;
         te.R = rows;
@@ -642,9 +642,10 @@ int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int6
         te.ld_in = D;
         te.out = et;
         te.ld_out = mcp;
+        te.blocked = 1;
         if ((st = hip_status(timed(prof, KIND_TRANSPOSE, s, [&] { return launch_transpose(te, s); }))) != GENREC_OK)
             return st;
-        // G = w (softmax - target) of the chunk, [B][mcp] and [mcp][Bp]
+        // G = w (softmax - target) of the chunk: [Bp][mcp] k-blocked and [mcp][Bp]
         MfmaArgs g{};
         g.H = (const uint16_t*)H;
         g.E = Ec;
@@ -664,7 +665,7 @@ int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int6
         g.item0 = r0;
         g.g_rows = grows;
         g.g_cols = gcols;
-        g.ld_g = mcp;
+        g.ld_g = p.Bp * kMfmaBlockK;
         g.ld_gt = p.Bp;
         g.gt_users = (int)p.Bp;
         if ((st = hip_status(timed(prof, KIND_GRAD_TILES, s, [&] { return launch_mfma_split(g, 3, 1, s); }))) !=
@@ -690,15 +691,19 @@ int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int6
             GENREC_OK)
             return st;
         // dH += G E_chunk: rows = D, columns = users, reduction = the chunk's
-        // items in `splits` parts, each into its own partial sum
+        // items in `splits` parts, each into its own partial sum; both
+        // operands k-blocked
         MfmaArgs dh{};
         dh.E = et;
         dh.H = grows;
         dh.M = D;
         dh.B = B;
         dh.D = (int)(mcp / p.splits);
-        dh.ld = mcp;
         dh.k_split = mcp / p.splits;
+        dh.blk_e = (int64_t)D * kMfmaBlockK;
+        dh.blk_h = p.Bp * kMfmaBlockK;
+        dh.e_elems = mcp * D;
+        dh.h_elems = mcp * p.Bp;
         dh.n_tiles = (int)ceil_div(D, kMfmaTileItems);
         dh.tile_stride = 1;
         const Chunking chh = chunk_mfma(B, dh.n_tiles);
@@ -711,7 +716,7 @@ int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int6
         dh.c_split = (int64_t)B * D;
         dh.c_trans = 1;
         dh.c_accum = ci > 0 ? 1 : 0;
-        if ((st = hip_status(timed(prof, KIND_GRAD_H, s, [&] { return launch_mfma_split(dh, 4, p.splits, s); }))) !=
+        if ((st = hip_status(timed(prof, KIND_GRAD_H, s, [&] { return launch_mfma_split(dh, 5, p.splits, s); }))) !=
             GENREC_OK)
             return st;
     }

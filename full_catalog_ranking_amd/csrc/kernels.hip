@@ -63,8 +63,12 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     const int D = a.D;
     // row stride of both operands, and where this block's share of the
     // reduction starts in every row (grid y splits it)
-    const int64_t ldr = a.ld != 0 ? a.ld : (int64_t)D;
+    // mode 5: k-blocked operands, rows of 32 reduction elements
+    constexpr bool BLKD = MODE == 5;
+    const int64_t ldr = BLKD ? (int64_t)MF_BK : (a.ld != 0 ? a.ld : (int64_t)D);
     const int64_t kofs = (int64_t)blockIdx.y * a.k_split;
+    const int64_t kofs_e = BLKD ? kofs / MF_BK * a.blk_e : kofs;  // element offsets of the split
+    const int64_t kofs_h = BLKD ? kofs / MF_BK * a.blk_h : kofs;
 
     // Pass-tile t holds catalog rows [t*G*256, t*G*256 + 256) clipped to M.
     auto tile_item0 = [&](int t) -> int64_t { return (int64_t)t * a.tile_stride * MF_TI; };
@@ -89,23 +93,27 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     // DMA moves to a new tile.  k0 rides in the scalar offset, so rows past the
     // end (and k-chunks past D on the last row) fall outside the record count.
     const int h_rows = a.B - u0 < MF_TU ? a.B - u0 : MF_TU;
+    const int64_t h_off = (int64_t)u0 * (BLKD ? MF_BK : ldr) + kofs_h;  // elements
     const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const char*)a.H + (int64_t)u0 * row_bytes + kofs * 2), (short)0, (int)(h_rows * row_bytes), 0x00020000);
+        (void*)(a.H + h_off), (short)0, (int)(BLKD ? (a.h_elems - h_off) * 2 : h_rows * row_bytes), 0x00020000);
     __amdgpu_buffer_rsrc_t er;
     auto e_rsrc = [&](int t) {
-        er = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.E + tile_item0(t) * row_bytes + kofs * 2), (short)0,
-                                               (int)(tile_valid(t) * row_bytes), 0x00020000);
+        const int64_t e_off = tile_item0(t) * (BLKD ? MF_BK : ldr) + kofs_e;
+        er = __builtin_amdgcn_make_buffer_rsrc((void*)(a.E + e_off), (short)0,
+                                               (int)(BLKD ? (a.e_elems - e_off) * 2 : tile_valid(t) * row_bytes),
+                                               0x00020000);
     };
 
     // DMA op j of both operands for the stage at k0 (1 KiB per op per wave).
     auto dma_op = [&](int stg, int k0, int j) {
         uint8_t* sE = smem[stg] + mf_dma_lds_byte(wsu, 0, 0);
         uint8_t* sH = smem[stg] + MF_TI * MF_ROWB + mf_dma_lds_byte(wsu, 0, 0);
-        const int soff = k0 * 2;
+        const int soff_e = BLKD ? (int)(k0 / MF_BK * a.blk_e * 2) : k0 * 2;
+        const int soff_h = BLKD ? (int)(k0 / MF_BK * a.blk_h * 2) : k0 * 2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)(sE + j * MF_NW * 1024),
-                                                 16, (int)voff[j], soff, 0, 0);
+                                                 16, (int)voff[j], soff_e, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (__attribute__((address_space(3))) void*)(sH + j * MF_NW * 1024),
-                                                 16, (int)voff[j], soff, 0, 0);
+                                                 16, (int)voff[j], soff_h, 0, 0);
     };
 
     f32x16_t acc[4][MF_UB];
@@ -184,7 +192,13 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             const int mbit0 = (lane >> 5) * 4;
             if (MODE == 3) {
                 // g = w (softmax - target) of the scores, rounded to bf16, into
-                // both layouts; zeros past the valid rows and past the users
+                // both layouts; zeros past the valid rows and past the users.
+                // The user index is made opaque so that the compiler rebuilds
+                // the store addresses per tile instead of keeping 32 of them
+                // live (and spilled) across the whole tile loop.
+                int uo = u;
+                asm volatile("" : "+v"(uo));
+                const int u = uo;
                 if (u < a.gt_users) {
                     const bool real = u < a.B;
                     const float lse_u = real ? a.lse[u] : 0.f;
@@ -203,9 +217,9 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                                 const float gv = w_u * (p - (jq + e == y_row ? 1.f : 0.f));
                                 gb[e] = bf16_bits(real && jq + e < lim ? gv : 0.f);
                             }
-                            if (real)
-                                *(uint2*)(a.g_rows + (int64_t)u * a.ld_g + j0 + jq) =
-                                    make_uint2(gb[0] | ((uint32_t)gb[1] << 16), gb[2] | ((uint32_t)gb[3] << 16));
+                            const int64_t jl = j0 + jq;  // k-blocked: 32 items of 32 users' rows per 2 KiB
+                            *(uint2*)(a.g_rows + (jl >> 5) * a.ld_g + (int64_t)u * MF_BK + (jl & 31)) =
+                                make_uint2(gb[0] | ((uint32_t)gb[1] << 16), gb[2] | ((uint32_t)gb[3] << 16));
                             uint16_t* gc = a.g_cols + (j0 + jq) * a.ld_gt + u;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) gc[e * a.ld_gt] = gb[e];
@@ -213,7 +227,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                 }
                 continue;
             }
-            if (MODE == 4) {
+            if (MODE == 4 || MODE == 5) {
                 // plain product: the tile's valid rows of column u, fp32
                 if (u < a.B) {
                     float* cz = a.c_out + (int64_t)blockIdx.y * a.c_split;
@@ -1784,7 +1798,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
         uint16_t v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = tile[rr + e][cc];
-        uint16_t* dst = a.out + c * a.ld_out + r;
+        uint16_t* dst = a.out + (a.blocked ? (r >> 5) * a.C * 32 + c * 32 + (r & 31) : c * a.ld_out + r);
         if (r + 7 < a.ld_out) {
             *(uint4*)dst = make_uint4(v[0] | ((uint32_t)v[1] << 16), v[2] | ((uint32_t)v[3] << 16),
                                       v[4] | ((uint32_t)v[5] << 16), v[6] | ((uint32_t)v[7] << 16));
@@ -1838,6 +1852,9 @@ hipError_t launch_mfma_split(const MfmaArgs& a, int mode, int splits, hipStream_
     } else if (mode == 4) {
         if (ktail) return hipErrorInvalidValue;  // the products run over zero-padded reductions
         hipLaunchKernelGGL((mfma_score_kernel<4, false, false>), grid, dim3(MF_NT), 0, s, a);
+    } else if (mode == 5) {
+        if (ktail || a.k_split % MF_BK != 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((mfma_score_kernel<5, false, false>), grid, dim3(MF_NT), 0, s, a);
     } else {
         return hipErrorInvalidValue;
     }

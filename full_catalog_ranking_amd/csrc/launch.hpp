@@ -47,7 +47,8 @@ struct MfmaArgs {
     // rows are catalog items item0 + j (j < M valid), columns users;
     // g = w[u] (exp(s - lse[u]) - [item0 + j == labels[u]]) goes to
     // g_rows[u * ld_g + j] and g_cols[j * ld_gt + u] as bf16, with zeros in
-    // invalid rows (j < n_tiles * 256) and in columns B .. gt_users - 1.
+    // invalid rows (j < n_tiles * 256) and in columns B .. gt_users - 1;
+    // g_rows is k-blocked: G[u][j] at (j / 32) * ld_g + u * 32 + j % 32.
     const float* lse;
     const float* wgt;
     const int32_t* labels;
@@ -64,6 +65,12 @@ struct MfmaArgs {
     float* c_out;
     int64_t ldc, c_split;
     int c_trans, c_accum;
+    // mode 5 -- mode 4 over k-blocked operands: element (r, k) of an operand
+    // at (k / 32) * blk + r * 32 + k % 32 (blk_e / blk_h elements per block of
+    // 32 reduction steps); e_elems / h_elems = the operands' sizes in elements
+    // (reads past them give zeros; rows past the valid ones read neighbouring
+    // data, which only reaches outputs that are not stored)
+    int64_t blk_e, blk_h, e_elems, h_elems;
 };
 
 // Cross-entropy bookkeeping kernels.
@@ -88,6 +95,8 @@ struct TransposeArgs {
     int64_t R, C, ld_in;
     uint16_t* out;       // [C][ld_out]: out[c][r] = in[r][c], zero for R <= r < ld_out
     int64_t ld_out;
+    // blocked != 0: out[c][r] at (r / 32) * C * 32 + c * 32 + r % 32 instead
+    int blocked;
 };
 
 struct CandPiece {

@@ -12,6 +12,7 @@ namespace genrec {
 constexpr int kNumCU = 256;            // MI355X compute units
 constexpr int kMfmaTileItems = 256;    // items per MFMA tile
 constexpr int kMfmaTileUsers = 256;    // users per MFMA tile
+constexpr int kMfmaBlockK = 32;        // reduction elements per k-step (and per k-block of a blocked operand)
 constexpr int kStreamMaxB = 1;         // bf16 batches up to this size use the VALU path (a half-empty MFMA tile still beats re-reading E per user)
 constexpr int64_t kSampleMinM = 65536; // smaller catalogs skip the threshold pre-pass
 constexpr int64_t kSampleMinStride = 32; // sample every G-th catalog tile, G >= 32
@@ -263,7 +264,8 @@ inline CePlan plan_ce(int B, int D, int64_t M) {
     p.Mcp = ceil_div(p.chunk, kMfmaTileItems) * kMfmaTileItems;
     p.n_chunks = ceil_div(M, p.chunk);
     const int64_t tiles = ceil_div(B, kMfmaTileUsers) * ceil_div(D, kMfmaTileItems);
-    while (p.splits < kCeMaxSplits && tiles * p.splits < kNumCU) p.splits *= 2;
+    // two rounds of blocks measured faster than one round of twice the work
+    while (p.splits < kCeMaxSplits && tiles * p.splits < 2 * kNumCU) p.splits *= 2;
     size_t o = 0;
     p.off_hdr = o;
     o += 256;
@@ -284,8 +286,8 @@ inline CePlan plan_ce(int B, int D, int64_t M) {
     o = align_up(o + 2 * (size_t)D * (size_t)p.Bp, 256);
     p.off_et = o;
     o = align_up(o + 2 * (size_t)D * (size_t)p.Mcp, 256);
-    p.off_grows = o;
-    o = align_up(o + 2 * (size_t)B * (size_t)p.Mcp, 256);
+    p.off_grows = o;  // k-blocked, Bp rows per block of 32 catalog rows
+    o = align_up(o + 2 * (size_t)p.Bp * (size_t)p.Mcp, 256);
     p.off_gcols = o;
     o = align_up(o + 2 * (size_t)p.Mcp * (size_t)p.Bp, 256);
     p.off_dhp = o;
