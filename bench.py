@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--de-dtype", default="f32", choices=["f32", "bf16"],
+                    help="ce workload: dtype of the catalog gradient dE")
     ap.add_argument("--mask-density", type=float, default=None, metavar="P",
                     help="full-catalog workloads: score through the masked head with one seeded "
                          "item mask that allows a fraction P of the catalog")
@@ -230,12 +232,13 @@ def bench_ce(args):
     wsf = torch.empty(genrec.lib().genrec_ce_forward_workspace(B, D, M), dtype=torch.uint8, device=dev)
     wsb = torch.empty(genrec.lib().genrec_ce_backward_workspace(B, D, M), dtype=torch.uint8, device=dev)
     dH = torch.empty((B, D), dtype=torch.float32, device=dev)
-    dE = torch.empty((M, D), dtype=torch.float32, device=dev)
+    de_dtype = torch.bfloat16 if args.de_dtype == "bf16" else torch.float32
+    dE = torch.empty((M, D), dtype=de_dtype, device=dev)
     prof = genrec.Profiler(max_launches=80 * (args.steps + 1))
 
     def step(p=None):
         loss, lse, _ = genrec.ce_forward(H, E, lab, w, workspace=wsf, profiler=p)
-        genrec.ce_backward(H, E, lab, lse, w, workspace=wsb, out=(dH, dE), profiler=p)
+        genrec.ce_backward(H, E, lab, lse, w, workspace=wsb, out=(dH, dE), profiler=p, de_dtype=de_dtype)
 
     for _ in range(args.warmup):
         step()
@@ -261,7 +264,8 @@ def bench_ce(args):
         "metric": METRIC, "value": B * M / (ms * 1e-3), "unit": "scores/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "ce", "B": B, "D": D, "M": M, "step": "forward+backward"},
+        "config": {"workload": "ce", "B": B, "D": D, "M": M, "step": "forward+backward",
+                   "dE": args.de_dtype},
         "tflops": 4 * prod / (ms * 1e-3) / 1e12,
         "kernels_ms": per_step,
         "kernel_tflops": tf,

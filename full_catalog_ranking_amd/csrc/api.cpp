@@ -601,12 +601,13 @@ int genrec_ce_forward(const void* H, const void* E, int B, int D, int64_t M, con
 }
 
 int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels,
-                                const float* weights, const float* lse, float* out_dH, float* out_dE,
+                                const float* weights, const float* lse, float* out_dH, void* out_dE, int de_dtype,
                                 void* workspace, size_t workspace_bytes, void* stream, genrec_profiler* prof) {
     int st = check_ce(H, E, B, D, M, labels, weights);
     if (st != GENREC_OK) return st;
     if (!lse || !out_dH || !out_dE || !aligned(lse, 4) || !aligned(out_dH, 4) || !aligned(out_dE, 4))
         return GENREC_ERR_INVALID_ARG;
+    if (de_dtype != GENREC_F32 && de_dtype != GENREC_BF16) return GENREC_ERR_INVALID_ARG;
     const CePlan p = plan_ce(B, D, M);
     if (!workspace || workspace_bytes < p.bwd_total) return GENREC_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
@@ -685,7 +686,8 @@ int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int6
         de.P = ce.P;
         de.base = ce.base;
         de.rem = ce.rem;
-        de.c_out = out_dE + r0 * D;
+        de.c_bf16 = de_dtype == GENREC_BF16 ? 1 : 0;
+        de.c_out = de.c_bf16 ? (float*)((uint16_t*)out_dE + r0 * D) : (float*)out_dE + r0 * D;
         de.ldc = D;
         if ((st = hip_status(timed(prof, KIND_GRAD_E, s, [&] { return launch_mfma_split(de, 4, 1, s); }))) !=
             GENREC_OK)
@@ -726,9 +728,9 @@ int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int6
 }
 
 int genrec_ce_backward(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels,
-                       const float* weights, const float* lse, float* out_dH, float* out_dE, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-    return genrec_ce_backward_profiled(H, E, B, D, M, labels, weights, lse, out_dH, out_dE, workspace,
+                       const float* weights, const float* lse, float* out_dH, void* out_dE, int de_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return genrec_ce_backward_profiled(H, E, B, D, M, labels, weights, lse, out_dH, out_dE, de_dtype, workspace,
                                        workspace_bytes, stream, nullptr);
 }
 

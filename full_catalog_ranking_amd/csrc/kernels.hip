@@ -255,6 +255,11 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                                     for (int e = 0; e < 4; ++e)
                                         if (jq + e < lim) o[e] = acc[ib][ub][4 * q + e] + (a.c_accum ? o[e] : 0.f);
                                 }
+                            } else if (a.c_bf16) {  // [row + e][u], bf16
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    if (jq + e < lim)
+                                        ((uint16_t*)a.c_out)[(row + e) * a.ldc + u] = bf16_bits(acc[ib][ub][4 * q + e]);
                             } else {  // [row + e][u]: a row segment across the lanes
 #pragma unroll
                                 for (int e = 0; e < 4; ++e)

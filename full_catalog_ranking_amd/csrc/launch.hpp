@@ -65,6 +65,7 @@ struct MfmaArgs {
     float* c_out;
     int64_t ldc, c_split;
     int c_trans, c_accum;
+    int c_bf16;  // stores bf16 (round to nearest even) at ((uint16_t*)c_out)[same index]; no c_accum
     // mode 5 -- mode 4 over k-blocked operands: element (r, k) of an operand
     // at (k / 32) * blk + r * 32 + k % 32 (blk_e / blk_h elements per block of
     // 32 reduction steps); e_elems / h_elems = the operands' sizes in elements

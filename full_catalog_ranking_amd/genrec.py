@@ -111,7 +111,7 @@ def lib() -> ctypes.CDLL:
         L.genrec_ce_forward.restype = I
         L.genrec_ce_forward_profiled.argtypes = L.genrec_ce_forward.argtypes + [P]
         L.genrec_ce_forward_profiled.restype = I
-        L.genrec_ce_backward.argtypes = [P, P, I, I, I64, P, P, P, P, P, P, SZ, P]
+        L.genrec_ce_backward.argtypes = [P, P, I, I, I64, P, P, P, P, P, I, P, SZ, P]
         L.genrec_ce_backward.restype = I
         L.genrec_ce_backward_profiled.argtypes = L.genrec_ce_backward.argtypes + [P]
         L.genrec_ce_backward_profiled.restype = I
@@ -323,8 +323,9 @@ def ce_forward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, weights: 
 
 def ce_backward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, lse: torch.Tensor,
                 weights: torch.Tensor | None = None, workspace: torch.Tensor | None = None, out=None,
-                profiler: Profiler | None = None):
-    """Gradients of sum_b loss_b: (dH f32 [B, D], dE f32 [M, D]); lse from ce_forward."""
+                profiler: Profiler | None = None, de_dtype: torch.dtype = torch.float32):
+    """Gradients of sum_b loss_b: (dH f32 [B, D], dE [M, D] in de_dtype (float32 or
+    bfloat16)); lse from ce_forward."""
     _check_ce(H, E, labels, weights)
     B, D = H.shape
     M = E.shape[0]
@@ -333,13 +334,18 @@ def ce_backward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, lse: tor
     need = lib().genrec_ce_backward_workspace(B, D, M)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    if de_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("de_dtype must be float32 or bfloat16")
     if out is None:
         dH = torch.empty((B, D), dtype=torch.float32, device=H.device)
-        dE = torch.empty((M, D), dtype=torch.float32, device=H.device)
+        dE = torch.empty((M, D), dtype=de_dtype, device=H.device)
     else:
         dH, dE = out
+        if dE.dtype != de_dtype or dH.dtype != torch.float32 or dH.shape != (B, D) or dE.shape != (M, D):
+            raise ValueError("out = (dH float32 [B, D], dE de_dtype [M, D])")
     args = (_ptr(H), _ptr(E), B, D, M, _ptr(labels), _ptr(weights), _ptr(lse), _ptr(dH), _ptr(dE),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(H.device))
+            dtype_code(de_dtype), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream_handle(H.device))
     if profiler is None:
         st = lib().genrec_ce_backward(*args)
     else:

@@ -180,7 +180,9 @@ int genrec_topk_rows(const float* scores, int R, int64_t N, int64_t ld, int K,
  * With s_bi = h_b . e_i and lse_b = ln sum_i exp(s_bi):
  *   forward:   out_loss[b] = w_b (lse_b - s_{b,y_b}),  out_lse[b] = lse_b;
  *   backward:  with G[b][i] = w_b (exp(s_bi - lse_b) - [i == y_b]),
- *              out_dH = G E  ([B][D] float32),  out_dE = G^T H  ([M][D] float32),
+ *              out_dH = G E  ([B][D] float32),  out_dE = G^T H  ([M][D], float32 when
+ *              de_dtype is GENREC_F32, bfloat16 rounded to nearest even when it is
+ *              GENREC_BF16 -- half the bytes of the largest output),
  *              the gradients of sum_b out_loss[b]; `lse` is the forward's out_lse.
  * An example whose label lies outside [0, M) is ignored (loss 0, no
  * gradient) and counted: genrec_get_device_errors on the same workspace
@@ -201,7 +203,7 @@ int genrec_ce_forward(const void* H, const void* E, int B, int D, int64_t M,
 size_t genrec_ce_backward_workspace(int B, int D, int64_t M);
 int genrec_ce_backward(const void* H, const void* E, int B, int D, int64_t M,
                        const int32_t* labels, const float* weights, const float* lse,
-                       float* out_dH, float* out_dE,
+                       float* out_dH, void* out_dE, int de_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* Introspection: writes into buf (at most len bytes, NUL-terminated) a JSON
@@ -263,7 +265,7 @@ int genrec_ce_forward_profiled(const void* H, const void* E, int B, int D, int64
                                genrec_profiler* prof);
 int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int64_t M,
                                 const int32_t* labels, const float* weights, const float* lse,
-                                float* out_dH, float* out_dE,
+                                float* out_dH, void* out_dE, int de_dtype,
                                 void* workspace, size_t workspace_bytes, void* stream,
                                 genrec_profiler* prof);
 

@@ -147,3 +147,24 @@ def test_plan_selection(L):
     assert p["path"] == "mfma" and p["sample"] == 0
     with pytest.raises(genrec.GenrecError):
         genrec.describe_plan(4, 12, 100, 10, torch.bfloat16)
+
+
+def test_ce_validation_and_workspace(L):
+    """Cross-entropy entry points: argument errors come back before any launch."""
+    f, b = L.genrec_ce_forward, L.genrec_ce_backward
+    wf = L.genrec_ce_forward_workspace(300, 64, 5000)
+    wb = L.genrec_ce_backward_workspace(300, 64, 5000)
+    assert wf > 0 and wb > 0
+    assert L.genrec_ce_forward_workspace(0, 64, 5000) == 0
+    assert f(FAKE, FAKE, 0, 64, 5000, FAKE, None, FAKE, FAKE, FAKE, wf, None) == INVALID        # B = 0
+    assert f(FAKE, FAKE, 300, 60, 5000, FAKE, None, FAKE, FAKE, FAKE, wf, None) == UNSUPPORTED  # D % 8
+    assert f(FAKE, FAKE, 300, 64, 5000, None, None, FAKE, FAKE, FAKE, wf, None) == INVALID      # no labels
+    assert f(FAKE, FAKE, 300, 64, 5000, FAKE, None, FAKE, FAKE, FAKE, wf - 1, None) == WORKSPACE
+    assert b(FAKE, FAKE, 300, 64, 5000, FAKE, None, FAKE, FAKE, FAKE, 0, FAKE, wb - 1, None) == WORKSPACE
+    assert b(FAKE, FAKE, 300, 64, 5000, FAKE, None, FAKE, FAKE, FAKE, 7, FAKE, wb, None) == INVALID  # dE dtype
+    assert b(FAKE, FAKE, 300, 64, 5000, FAKE, None, None, FAKE, FAKE, 1, FAKE, wb, None) == INVALID  # no lse
+    # backward workspace at the benchmark shape: H^T, one chunk's E^T and G in two
+    # layouts (65,536 rows), 8 partial dH buffers
+    big = L.genrec_ce_backward_workspace(1024, 4096, 1_000_000)
+    parts = 2 * 4096 * 1024 + 2 * 4096 * 65536 + 2 * 2 * 1024 * 65536 + 4 * 8 * 1024 * 4096
+    assert parts <= big <= parts + 1_000_000

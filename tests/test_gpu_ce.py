@@ -24,7 +24,7 @@ def _bf16(a, dev):
     return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def run_ce(d, labels, weights, dev, backward=True):
+def run_ce(d, labels, weights, dev, backward=True, de_dtype=None):
     from full_catalog_ranking_amd import genrec
     B, D, M = d["B"], d["D"], d["M"]
     print("  ce B=%d D=%d M=%d weights=%s" % (B, D, M, weights is not None), flush=True)
@@ -35,10 +35,10 @@ def run_ce(d, labels, weights, dev, backward=True):
     errs = genrec.device_errors(ws)
     out = [loss.cpu().numpy(), lse.cpu().numpy(), None, None]
     if backward:
-        dH, dE = genrec.ce_backward(H, E, lab, lse, w)
+        dH, dE = genrec.ce_backward(H, E, lab, lse, w, de_dtype=de_dtype or torch.float32)
         torch.cuda.synchronize()
         out[2] = dH.cpu().numpy()
-        out[3] = dE.cpu().numpy() if dE is not None else None
+        out[3] = dE.float().cpu().numpy()
         del dH, dE
     del H, E
     return out, errs
@@ -78,6 +78,20 @@ def test_ce_parity(dev, oracle_mod, B, D, M, seed, bad, weighted):
     if bad:
         assert g[0][1] == 0.0 and g[0][-1] == 0.0
         assert np.abs(g[2][1]).max() == 0.0 and np.abs(g[2][-1]).max() == 0.0
+
+
+def test_ce_bf16_grad_catalog(dev, oracle_mod):
+    """dE stored in bf16: the same bound plus the rounding of the stored value."""
+    B, D, M = 300, 200, 5000
+    d = synth.make_dense(B, D, M, seed=11)
+    labels = synth.gen_labels(B, M, 11)
+    w = synth.gen_weights(B, 11)
+    g, errs = run_ce(d, labels, w, dev, de_dtype=torch.bfloat16)
+    assert errs == (0, 0)
+    ref = oracle_mod.ce(d["H"], d["E"], labels, w)
+    dh_depth, de_depth = _depths(B, D, M)
+    parity.check_ce(g, ref, d["E"], d["H"], oracle_mod.widen, dh_depth, de_depth, de_round=2.0 ** -8,
+                    where="ce bf16 dE")
 
 
 def test_ce_wide_rows(dev, oracle_mod):
