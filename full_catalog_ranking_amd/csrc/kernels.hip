@@ -698,28 +698,97 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
-// Bitonic sort, descending, of buf[0..n) padded to a power of two with zeros.
-__device__ void block_sort_desc(uint64_t* buf, int n) {
-    int p2 = 1;
-    while (p2 < n) p2 <<= 1;
-    for (int i = n + threadIdx.x; i < p2; i += blockDim.x) buf[i] = 0;
-    __syncthreads();
-    for (int k = 2; k <= p2; k <<= 1) {
+// Bitonic sort, descending, of one wave's 64 * C keys held in registers:
+// element t * 64 + lane is v[t]; partners in other lanes are exchanged with
+// shuffles, partners in the same lane directly.  No barrier.
+template <int C>
+__device__ void wave_sort_desc(uint64_t (&v)[C]) {
+    const int lane = threadIdx.x & 63;
+    constexpr int N = 64 * C;
+#pragma unroll
+    for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < p2; i += blockDim.x) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint64_t x = buf[i], y = buf[ixj];
-                    const bool desc = (i & k) == 0;
-                    if (desc ? (x < y) : (x > y)) {
-                        buf[i] = y;
-                        buf[ixj] = x;
+            if (j >= 64) {
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    const int tp = t ^ (j >> 6);
+                    if (tp > t) {
+                        const bool desc = ((t * 64 + lane) & k) == 0;
+                        const uint64_t x = v[t], y = v[tp];
+                        if (desc ? (x < y) : (x > y)) {
+                            v[t] = y;
+                            v[tp] = x;
+                        }
                     }
                 }
+            } else {
+#pragma unroll
+                for (int t = 0; t < C; ++t) {
+                    const uint64_t x = v[t];
+                    const uint64_t y = __shfl_xor(x, j);
+                    const bool desc = ((t * 64 + lane) & k) == 0;
+                    const bool lower = (lane & j) == 0;  // the smaller index of the pair
+                    const bool take_max = desc == lower;
+                    v[t] = take_max ? (x > y ? x : y) : (x < y ? x : y);
+                }
             }
-            __syncthreads();
         }
     }
+}
+
+// Count of keys in run[0..R) (descending) greater than x, or not below x
+// when `ge`.
+__device__ __forceinline__ int run_count_above(const uint64_t* run, int R, uint64_t x, bool ge) {
+    int lo = 0, hi = R;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const uint64_t y = run[mid];
+        if (ge ? (y >= x) : (y > x)) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+template <int C>
+__device__ void block_sort_runs(uint64_t* in, int n, uint64_t* out, int R) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    uint64_t v[C];
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        const int e = w * R + t * 64 + lane;
+        v[t] = e < n ? in[e] : 0ull;  // 0: below every key
+    }
+    wave_sort_desc<C>(v);
+    __syncthreads();  // every key of `in` is read before the runs overwrite it
+#pragma unroll
+    for (int t = 0; t < C; ++t) in[w * R + t * 64 + lane] = v[t];
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        const uint64_t x = v[t];
+        if (x == 0ull) continue;
+        int r = t * 64 + lane;
+        for (int q = 0; q < SEL_NT / kWave; ++q)
+            if (q != w) r += run_count_above(in + q * R, R, x, q < w);  // earlier runs first among equal keys
+        out[r] = x;
+    }
+}
+
+// Sort, descending, of in[0..n) into out[0..n), n <= 4 * 256 (`in` needs room
+// for 4 runs of R keys and is overwritten): each wave sorts a run of R keys
+// (a power of two >= n / 4) in registers, then every key's rank is its place
+// in its run plus the larger keys of the other three runs (binary searches);
+// equal keys keep their run order.  Two barriers instead of a bitonic
+// network's one per stage.
+__device__ void block_sort_into(uint64_t* in, int n, uint64_t* out) {
+    static_assert(SEL_NT == 4 * kWave, "four runs, one per wave");
+    static_assert(GENREC_KMAX <= 4 * 256, "runs of at most 256 keys fill the 1,024-key output buffer");
+    int R = 64;
+    while (R * (SEL_NT / kWave) < n) R <<= 1;
+    if (R == 64) block_sort_runs<1>(in, n, out, R);
+    else if (R == 128) block_sort_runs<2>(in, n, out, R);
+    else block_sort_runs<4>(in, n, out, R);
 }
 
 // Rank placement: key i of in[0..n) goes to out[r], r = the number of keys
@@ -1302,12 +1371,11 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
         PieceSrc src{a.keys, a.pcnt, a.preg, p0, p1, (int64_t)ntot, &ps};
         block_select<true>(src, keff, sh);
         // the K keys in ranking order: rank placement for a few hundred
-        // (quadratic compares, one barrier), a bitonic sort for more
+        // (quadratic compares, one barrier), wave sorts and a rank merge for more
         if (keff <= 256) {
             block_rank_place(sh.out, keff, sh.gbuf, keff);
         } else {
-            block_sort_desc(sh.out, keff);
-            for (int i = tid; i < keff; i += SEL_NT) sh.gbuf[i] = sh.out[i];
+            block_sort_into(sh.out, keff, sh.gbuf);
         }
         __syncthreads();
     }
@@ -1398,8 +1466,7 @@ __device__ void topk_emit(const Src& src, int k, int K, SelShared& sh, int32_t* 
         if (k <= 256) {
             block_rank_place(sh.out, k, sh.gbuf, k);
         } else {
-            block_sort_desc(sh.out, k);
-            for (int i = tid; i < k; i += SEL_NT) sh.gbuf[i] = sh.out[i];
+            block_sort_into(sh.out, k, sh.gbuf);
         }
         __syncthreads();
     }
