@@ -545,13 +545,14 @@ CeArgs ce_args(const void* H, const void* E, int B, int D, int64_t M, const int3
 }  // namespace
 
 size_t genrec_ce_forward_workspace(int B, int D, int64_t M) {
-    if (B <= 0 || D <= 0 || M <= 0 || M >= ((int64_t)1 << 31)) return 0;
+    if (B <= 0 || D <= 0 || M <= 0 || M >= ((int64_t)1 << 31) || D > GENREC_DMAX) return 0;
     return plan_ce(B, D, M).fwd_total;
 }
 
 size_t genrec_ce_backward_workspace(int B, int D, int64_t M) {
-    if (B <= 0 || D <= 0 || M <= 0 || M >= ((int64_t)1 << 31)) return 0;
-    return plan_ce(B, D, M).bwd_total;
+    if (B <= 0 || D <= 0 || M <= 0 || M >= ((int64_t)1 << 31) || D > GENREC_DMAX) return 0;
+    const CePlan p = plan_ce(B, D, M);
+    return p.ok ? p.bwd_total : 0;
 }
 
 int genrec_ce_forward_profiled(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels,
@@ -609,6 +610,7 @@ int genrec_ce_backward_profiled(const void* H, const void* E, int B, int D, int6
         return GENREC_ERR_INVALID_ARG;
     if (de_dtype != GENREC_F32 && de_dtype != GENREC_BF16) return GENREC_ERR_INVALID_ARG;
     const CePlan p = plan_ce(B, D, M);
+    if (!p.ok) return GENREC_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < p.bwd_total) return GENREC_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;

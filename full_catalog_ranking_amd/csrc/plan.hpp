@@ -240,10 +240,15 @@ inline TopkPlan plan_topk(int R, int64_t N, int K) {
 // ---------------------------------------------------------------------------
 // Cross-entropy over the catalog (bf16 only)
 // ---------------------------------------------------------------------------
-constexpr int64_t kCeChunk = 65536;  // catalog rows per backward chunk (G held for one chunk)
+constexpr int64_t kCeChunk = 65536;  // catalog rows per backward chunk at most (G held for one chunk)
+// The k-blocked operands of the dH product are addressed through buffer
+// resources (32-bit record counts and offsets): each stays under 1 GiB, which
+// shrinks the chunk for D or B beyond 8,192, and bounds both by 2^21.
+constexpr int64_t kCeBlockedMaxBytes = (int64_t)1 << 30;
 constexpr int kCeMaxSplits = 8;      // reduction splits of the dH product (powers of two)
 
 struct CePlan {
+    bool ok = true;  // false: a blocked operand cannot fit 256 catalog rows (B or D > 2^21)
     Chunking main;  // forward logsumexp pass over the catalog
     int64_t n_pieces = 0;
     int64_t Bp = 0;        // users padded to 32 (reduction of the dE product)
@@ -260,7 +265,10 @@ inline CePlan plan_ce(int B, int D, int64_t M) {
     p.main = chunk_mfma(B, ceil_div(M, kMfmaTileItems));
     p.n_pieces = (int64_t)B * p.main.P * 4;
     p.Bp = ceil_div(B, 32) * 32;
-    p.chunk = std::min<int64_t>(M, kCeChunk);
+    const int64_t wide = std::max<int64_t>(D, p.Bp);  // rows of the wider blocked operand
+    const int64_t cap = kCeBlockedMaxBytes / 2 / wide / kMfmaTileItems * kMfmaTileItems;
+    if (cap < kMfmaTileItems) p.ok = false;
+    p.chunk = std::max<int64_t>(1, std::min<int64_t>({M, kCeChunk, cap}));
     p.Mcp = ceil_div(p.chunk, kMfmaTileItems) * kMfmaTileItems;
     p.n_chunks = ceil_div(M, p.chunk);
     const int64_t tiles = ceil_div(B, kMfmaTileUsers) * ceil_div(D, kMfmaTileItems);

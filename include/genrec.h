@@ -188,7 +188,9 @@ int genrec_topk_rows(const float* scores, int R, int64_t N, int64_t ld, int K,
  * gradient) and counted: genrec_get_device_errors on the same workspace
  * reports the count as *n_bad_ids (and 0 as *n_bad_offsets).
  * The backward recomputes the scores chunk by chunk (65,536 catalog rows at a
- * time), holds G of one chunk in bf16 (rounded to nearest even) and computes
+ * time, fewer when D or B exceeds 8,192 so that each chunk operand stays under
+ * 1 GiB; B or D above 2^21 is GENREC_ERR_UNSUPPORTED for the backward),
+ * holds G of one chunk in bf16 (rounded to nearest even) and computes
  * both products on the matrix cores with fp32 accumulation; only the
  * workspace of genrec_ce_backward_workspace() bytes is used.  Asynchronous on
  * `stream`; out_dH and out_dE are overwritten.  Outputs 4-byte aligned,

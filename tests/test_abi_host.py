@@ -168,3 +168,15 @@ def test_ce_validation_and_workspace(L):
     big = L.genrec_ce_backward_workspace(1024, 4096, 1_000_000)
     parts = 2 * 4096 * 1024 + 2 * 4096 * 65536 + 2 * 2 * 1024 * 65536 + 4 * 8 * 1024 * 4096
     assert parts <= big <= parts + 1_000_000
+
+
+def test_ce_chunk_bounds(L):
+    """Wide rows shrink the backward's catalog chunk; past 2^21 users it is refused."""
+    w_small = L.genrec_ce_backward_workspace(8, 65536, 100_000)
+    # one chunk of 8,192 rows: E^T 65,536 x 8,192 bf16 = 1 GiB dominates
+    assert (1 << 30) <= w_small <= (1 << 30) + (64 << 20)
+    assert L.genrec_ce_backward_workspace(3_000_000, 8, 1000) == 0
+    assert L.genrec_ce_forward_workspace(3_000_000, 8, 1000) > 0
+    FAKE = 1 << 20
+    assert L.genrec_ce_backward(FAKE, FAKE, 3_000_000, 8, 1000, FAKE, None, FAKE, FAKE, FAKE, 1, FAKE,
+                                1 << 40, None) == UNSUPPORTED

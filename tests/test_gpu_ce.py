@@ -46,8 +46,9 @@ def run_ce(d, labels, weights, dev, backward=True, de_dtype=None):
 
 def _depths(B, D, M):
     """Longest fp32 addition chains of the two products (see parity.check_ce)."""
-    from full_catalog_ranking_amd import genrec
-    chunk = min(M, 65536)
+    bp = -(-B // 32) * 32
+    cap = (1 << 30) // 2 // max(D, bp) // 256 * 256  # blocked operands stay under 1 GiB
+    chunk = min(M, 65536, cap)
     mcp = -(-chunk // 256) * 256
     tiles = -(-B // 256) * -(-D // 256)
     splits = 1
@@ -106,6 +107,22 @@ def test_ce_wide_rows(dev, oracle_mod):
     ref = oracle_mod.ce(d["H"], d["E"], labels, w)
     dh_depth, de_depth = _depths(B, D, M)
     parity.check_ce(g, ref, d["E"], d["H"], oracle_mod.widen, dh_depth, de_depth, where="ce wide")
+
+
+def test_ce_wide_d_smaller_chunks(dev, oracle_mod):
+    """D = 16,384: the backward's chunk shrinks to 32,768 catalog rows (each
+    blocked operand under 1 GiB), two chunks here."""
+    from full_catalog_ranking_amd import genrec
+    B, D, M = 8, 16384, 36_000
+    assert genrec.lib().genrec_ce_backward_workspace(B, D, M) < (1 << 30) + (64 << 20)
+    d = synth.make_dense(B, D, M, seed=13)
+    labels = synth.gen_labels(B, M, 13)
+    w = synth.gen_weights(B, 13)
+    g, errs = run_ce(d, labels, w, dev)
+    assert errs == (0, 0)
+    ref = oracle_mod.ce(d["H"], d["E"], labels, w)
+    dh_depth, de_depth = _depths(B, D, M)
+    parity.check_ce(g, ref, d["E"], d["H"], oracle_mod.widen, dh_depth, de_depth, where="ce wide D")
 
 
 def test_ce_full_size_sampled_users(dev, oracle_mod):
