@@ -19,10 +19,18 @@
 //                      the main pass and of the rescue pass.
 //  merge_kernel        per user, lse from the per-piece (max, sum-exp) pairs
 //                      and the exact top-K of the candidates (range-narrowing
-//                      histogram select + bitonic sort), written sorted.
+//                      histogram select, then rank placement or wave sorts and
+//                      a rank merge), written sorted.
 //  cand_plan_kernel    CSR offsets -> work list of fixed-size list pieces.
 //  hot_*_kernel        candidate lists: the most-listed rows, scored densely.
-//  topk_rows_kernel    batched top-K of dense score rows (a beam step).
+//  topk_chunk_kernel,  batched top-K of dense score rows (a beam step).
+//  topk_merge_rows_kernel
+//  mfma_score_kernel   modes 3-5 and ce_*, transpose, sum_splits kernels: the
+//                      catalog cross-entropy (GenRec explainer page, "two
+//                      objectives and reward-weighted ranking"): forward = the
+//                      logsumexp pass plus the label's score; backward = per
+//                      catalog chunk the softmax-minus-target tiles G and the
+//                      products dE = G^T H and dH = G E.
 #include <float.h>
 
 #include "device_common.hpp"
