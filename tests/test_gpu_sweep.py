@@ -1,0 +1,136 @@
+"""Seeded sweep of random shapes through every entry point against the CPU
+oracle (under the rules in parity.py): dense bf16 / fp32, masked, candidate
+lists, batched top-K rows and the cross-entropy.  Each case draws its kind
+and sizes from one seeded generator, within the supported shapes and sizes
+the oracle finishes in about a second."""
+import numpy as np
+import pytest
+
+from full_catalog_ranking_amd import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from full_catalog_ranking_amd import genrec
+    genrec.lib()  # fails loudly if the HIP library is missing
+    return torch.device("cuda:0")
+
+
+def _td(a, dev):
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev) if a.dtype == np.uint16 \
+        else torch.from_numpy(a).to(dev)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_shapes(dev, oracle_mod, case):
+    from full_catalog_ranking_amd import genrec
+    oracle = oracle_mod
+    rng = np.random.default_rng([20261203, case])
+    td = lambda a: _td(a, dev)
+
+    def pick_users(B):
+        return sorted(set([0, B - 1] + list(rng.integers(0, B, min(B, 6)))))
+
+    kind = rng.choice(["dense", "dense", "masked", "cand", "topk", "ce"])
+    if kind in ("dense", "masked"):
+        bf16 = bool(rng.random() < 0.8)
+        B = int(rng.choice([1, 2, 3, 8, 40, 256, 300, 513]))
+        D = int(rng.integers(1, 65)) * 8
+        M = int(rng.choice([1, 7, 300, 4097, 20000, 70001]))
+        if B * M * D > 3e9:  # keep the oracle's work to about a second
+            M = max(1, int(3e9 // (B * D)))
+        K = int(min(1024, rng.choice([1, 10, 64, 100, 257, 500, 1024])))
+        seed = int(rng.integers(0, 1 << 30))
+        print("case %d %s B=%d D=%d M=%d K=%d bf16=%s seed=%d" % (case, kind, B, D, M, K, bf16, seed), flush=True)
+        d = synth.make_dense(B, D, M, seed=seed, bf16=bf16)
+        H, E = td(d["H"]), td(d["E"])
+        users = pick_users(B)
+        if kind == "masked":
+            per_user = bool(rng.random() < 0.5)
+            dens = rng.uniform(0.0, 1.0, B if per_user else 1)
+            allowed = rng.random((B if per_user else 1, M)) < dens[:, None]
+            W = (M + 31) // 32
+            pad = np.zeros((allowed.shape[0], W * 32), dtype=bool)
+            pad[:, :M] = allowed
+            bits = pad.reshape(allowed.shape[0], W, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)
+            words = bits.sum(axis=-1).astype(np.uint32)
+            words = words if per_user else words[0]
+            mask = torch.from_numpy(np.ascontiguousarray(words).view(np.int32)).to(dev)
+            idx, sc, ls = genrec.score_lse_topk(H, E, K, mask=mask)
+            ref = oracle.full_masked(d["H"], d["E"], K, words, users=users)
+        else:
+            idx, sc, ls = genrec.score_lse_topk(H, E, K)
+            ref = oracle.full(d["H"], d["E"], K, users=users)
+        g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
+        parity.check_dense(g, ref, where="sweep %d" % case)
+    elif kind == "cand":
+        B = int(rng.choice([1, 5, 64, 100, 300]))
+        D = int(rng.integers(1, 65)) * 8
+        M = int(rng.choice([50, 3000, 50000]))
+        lo = int(rng.integers(0, 50))
+        hi = int(lo + rng.integers(0, 600))
+        hi = min(hi, M)
+        lo = min(lo, hi)
+        K = int(min(1024, rng.choice([1, 10, 100, 300])))
+        seed = int(rng.integers(0, 1 << 30))
+        print("case %d cand B=%d D=%d M=%d lists=[%d,%d] K=%d seed=%d" % (case, B, D, M, lo, hi, K, seed), flush=True)
+        d = synth.make_dense(B, D, M, seed=seed)
+        off, ids = synth.gen_candidates(B, M, seed, lo, hi)
+        H, E = td(d["H"]), td(d["E"])
+        idx, sc, ls, ws = genrec.score_candidates_topk(H, E, torch.from_numpy(off).to(dev),
+                                                       torch.from_numpy(ids).to(dev), K)
+        assert genrec.device_errors(ws) == (0, 0)
+        g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
+        ref = oracle.cand(d["H"], d["E"], off, ids, K)
+        parity.check_cand(g, ref, off, ids, where="sweep %d" % case)
+    elif kind == "topk":
+        R = int(rng.choice([1, 3, 64, 100]))
+        N = int(rng.choice([1, 5, 4096, 4097, 30000, 300000]))
+        K = int(min(1024, rng.choice([1, 8, 128, 257, 512, 1024])))
+        dec = [None, 2][int(rng.integers(0, 2))]
+        seed = int(rng.integers(0, 1 << 30))
+        print("case %d topk R=%d N=%d K=%d dec=%s seed=%d" % (case, R, N, K, dec, seed), flush=True)
+        s = synth.gen_scores(R, N, seed=seed, decimals=dec)
+        idx, val = genrec.topk_rows(torch.from_numpy(s).to(dev), K)
+        idx, val = idx.cpu().numpy(), val.cpu().numpy()
+        for r in range(R):
+            ri, rv = oracle.topk_row(s[r].astype(np.float64), K)
+            assert np.array_equal(idx[r], ri), ("topk idx", r)
+            assert np.array_equal(val[r], rv.astype(np.float32)), ("topk val", r)
+    else:
+        B = int(rng.choice([1, 7, 64, 300]))
+        D = int(rng.integers(1, 65)) * 8
+        M = int(rng.choice([1, 70, 5000, 70000]))
+        if B * M * D > 2e9:
+            M = max(1, int(2e9 // (B * D)))
+        seed = int(rng.integers(0, 1 << 30))
+        weighted = bool(rng.random() < 0.7)
+        print("case %d ce B=%d D=%d M=%d weighted=%s seed=%d" % (case, B, D, M, weighted, seed), flush=True)
+        d = synth.make_dense(B, D, M, seed=seed)
+        labels = synth.gen_labels(B, M, seed)
+        w = synth.gen_weights(B, seed) if weighted else None
+        H, E = td(d["H"]), td(d["E"])
+        lab = torch.from_numpy(labels).to(dev)
+        wt = torch.from_numpy(w).to(dev) if weighted else None
+        loss, lse, _ = genrec.ce_forward(H, E, lab, wt)
+        dH, dE = genrec.ce_backward(H, E, lab, lse, wt)
+        torch.cuda.synchronize()
+        g = (loss.cpu().numpy(), lse.cpu().numpy(), dH.cpu().numpy(), dE.cpu().numpy())
+        ref = oracle.ce(d["H"], d["E"], labels, w)
+        bp = -(-B // 32) * 32
+        cap = (1 << 30) // 2 // max(D, bp) // 256 * 256
+        chunk = min(M, 65536, cap)
+        mcp = -(-chunk // 256) * 256
+        tiles = -(-B // 256) * -(-D // 256)
+        sp = 1  # the dH product's reduction splits
+        while sp < 8 and tiles * sp < 512:
+            sp *= 2
+        parity.check_ce(g, ref, d["E"], d["H"], oracle.widen, mcp // sp + -(-M // chunk) + sp, bp,
+                        where="sweep %d" % case)
