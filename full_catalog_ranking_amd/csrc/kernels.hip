@@ -44,8 +44,10 @@ namespace genrec {
 // Dense MFMA path
 // ---------------------------------------------------------------------------
 
-// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left alone (gfx9 encoding).
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt left alone (gfx9 encoding), and
+// the same with lgkmcnt(0) as well (every LDS read of the wave completed).
 #define MF_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
+#define MF_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0070 | ((n) & 15))
 
 template <int MODE, bool KTAIL, bool MASKED>
 __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
@@ -346,19 +348,20 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 
     // ---- pipeline ------------------------------------------------------------
     // Steps run over the flat sequence (tile, k-step).  Each step issues the
-    // DMA of step+4 -- op 0 of both operands among the MFMAs of its first
-    // half, op 1 among those of its second half, so that the CU's vector-
-    // memory path sees an even stream rather than a burst after every barrier
-    // (past the end: the last tile again, into a stage nobody reads, so every
-    // step issues the same number of ops).  It reads slice 1 of its stage
-    // while slice 0 runs on the matrix cores, waits until the DMA of step+1
-    // has landed (vector-memory ops retire in order, so "at most steps +2 and
-    // +3 and the first half of step +4 outstanding" suffices, epilogue stores
-    // in between only make the wait stricter), meets the other waves at the
-    // barrier -- which also retires all reads of the stage that the next DMA
-    // overwrites -- and reads slice 0 of the next stage while slice 1 runs.
-    // The DMA ring moves on after both halves (the stage the step's DMA
-    // writes was last read before the previous step's barrier).
+    // DMA of step + (NS - 1) -- op 0 of both operands among the MFMAs of its
+    // first half, op 1 among those of its second half, so that the CU's
+    // vector-memory path sees an even stream rather than a burst after every
+    // barrier (past the end: the last tile again, into a stage nobody reads,
+    // so every step issues the same number of ops).  It reads slice 1 of its
+    // stage while slice 0 runs on the matrix cores, waits until the DMA of
+    // step+1 has landed (loads retire in order, so "at most the ops of the
+    // later steps and the first half of the newest outstanding" suffices;
+    // epilogue stores in between only make the wait stricter) and until its
+    // own LDS reads have completed, then meets the other waves at the
+    // barrier: past it every read of this step's stage is done, and that
+    // stage is the one the next step's DMA overwrites.  It reads slice 0 of
+    // the next stage while slice 1 runs.  The DMA ring moves on after both
+    // halves.
     static_assert(MF_DMA == 2, "one op per operand in each half of a step");
     constexpr int kOpsPerStep = 2 * MF_DMA;
     constexpr int kWaitOps = (MF_NS - 3) * kOpsPerStep + 2;
@@ -399,13 +402,8 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                 if (i < 4 + MF_UB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
                 if (i == 2 || i == 5) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA)
             }
-            // raised wave priority across the wait and the barrier: the wave
-            // that gets through first issues its next reads and MFMAs ahead of
-            // its SIMD partner (measured ~1% faster than without)
-            __builtin_amdgcn_s_setprio(1);
-            MF_WAIT_VMCNT(kWaitOps);
+            MF_WAIT_VMCNT_LDS(kWaitOps);
             __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
             cs = cs + 1 == MF_NS ? 0 : cs + 1;
             dma_op(ls, lk * MF_BK, 1);

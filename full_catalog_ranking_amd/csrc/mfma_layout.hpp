@@ -15,7 +15,7 @@ namespace genrec {
 constexpr int MF_TI = 256;   // items per tile (MFMA rows)
 constexpr int MF_TU = 256;   // users per tile (MFMA columns)
 constexpr int MF_BK = 32;    // reduction depth per LDS stage
-constexpr int MF_NS = 5;     // LDS ring stages (4 in flight while one is read): 160 KiB
+constexpr int MF_NS = 4;     // LDS ring stages (3 in flight while one is read): 128 KiB; 5 stages time the same
 constexpr int MF_NT = 512;   // threads: 8 waves (2 per SIMD) in a 2 x 4 layout of 128 x 64 wave tiles
 constexpr int MF_NW = MF_NT / 64;
 constexpr int MF_WU = 64;    // users per wave tile
