@@ -30,10 +30,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def timed_steps(torch, step, steps):
+    """Times `steps` calls of step() back to back: the mean over the whole
+    bracketed region (synchronised before and after), and the median and
+    minimum of the per-step intervals between events recorded on the stream
+    in between (no synchronisation inside the region)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mean = ev[0].elapsed_time(ev[steps]) / steps
+    med = per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
+    return mean, med, per[0]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large",
                     choices=["large", "batch", "gemv", "tiny", "cand", "gemv_big", "beam128", "beam512", "ce"])
@@ -182,18 +200,13 @@ def bench_beam(args):
     for _ in range(args.warmup):
         genrec.topk_rows(S, K, out=out)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        genrec.topk_rows(S, K, out=out)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, med, mn = timed_steps(torch, lambda: genrec.topk_rows(S, K, out=out), args.steps)
     alg_bytes = R * N * 4 + R * K * 8
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": R * N / (ms * 1e-3), "unit": "scores/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": med,
+        "ms_per_step_min": mn, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload, "R": R, "N": N, "K": K},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -243,13 +256,7 @@ def bench_ce(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        step(prof)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, med, mn = timed_steps(torch, lambda: step(prof), args.steps)
     kern = prof.summary()
     per_step = {k: v[1] / args.steps for k, v in kern.items()}
     log("step %.3f ms; kernels per step %s" % (ms, {k: "%.3f ms" % v for k, v in per_step.items()}))
@@ -262,7 +269,8 @@ def bench_ce(args):
              "grad_E": "mfma_score_kernel<4> (dE)", "grad_H": "mfma_score_kernel<4> (dH)"}[dom]
     res = {
         "metric": METRIC, "value": B * M / (ms * 1e-3), "unit": "scores/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": med,
+        "ms_per_step_min": mn, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "ce", "B": B, "D": D, "M": M, "step": "forward+backward",
                    "dE": args.de_dtype},
@@ -366,23 +374,21 @@ def main():
     if args.cold:
         # each step after a 1 GiB scratch write; only the steps are timed
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        ms = 0.0
+        per = []
         for _ in range(args.steps):
             scratch.fill_(1)
             start.record()
             step(prof)
             end.record()
             torch.cuda.synchronize()
-            ms += start.elapsed_time(end)
-        ms /= args.steps
+            per.append(start.elapsed_time(end))
+        ms = sum(per) / args.steps
+        per.sort()
+        med = per[args.steps // 2] if args.steps % 2 else 0.5 * (per[args.steps // 2 - 1] + per[args.steps // 2])
+        mn = per[0]
         del scratch
     else:
-        start.record()
-        for _ in range(args.steps):
-            step(prof)
-        end.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / args.steps
+        ms, med, mn = timed_steps(torch, lambda: step(prof), args.steps)
     kern = prof.summary()
     log("step %.3f ms; kernels %s" % (ms, {k: "%.3f ms x%d" % (v[1] / v[0], v[0]) for k, v in kern.items()}))
 
@@ -416,6 +422,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_median": med,
+        "ms_per_step_min": mn,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
