@@ -158,12 +158,41 @@ def _stream_handle(device: torch.device) -> int:
 def _check_inputs(H: torch.Tensor, E: torch.Tensor):
     if not (H.is_cuda and E.is_cuda):
         raise ValueError("H and E must be device tensors")
+    if E.device != H.device:
+        raise ValueError("H and E must be on one device")
     if H.dim() != 2 or E.dim() != 2 or H.shape[1] != E.shape[1]:
         raise ValueError("H must be (B, D) and E (M, D), got %s and %s" % (tuple(H.shape), tuple(E.shape)))
     if H.dtype != E.dtype:
         raise ValueError("H and E must share a dtype")
     if not (H.is_contiguous() and E.is_contiguous()):
         raise ValueError("H and E must be contiguous")
+
+
+def _check_tensor(t: torch.Tensor, name: str, device, dtype=None, shape=None):
+    """A caller-provided tensor the kernels read or write: on `device`,
+    contiguous, and of the given dtype and shape when those are given."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device:
+        raise ValueError("%s must be a tensor on %s" % (name, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+def _check_workspace(ws: torch.Tensor, device, need: int):
+    _check_tensor(ws, "workspace", device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError("workspace holds %d bytes, %d needed" % (ws.numel() * ws.element_size(), need))
+
+
+def _check_outs(out, B: int, K: int, device):
+    if len(out) != 3:
+        raise ValueError("out = (idx int32 [B, K], scores float32 [B, K], lse float32 [B])")
+    _check_tensor(out[0], "out idx", device, torch.int32, (B, K))
+    _check_tensor(out[1], "out scores", device, torch.float32, (B, K))
+    _check_tensor(out[2], "out lse", device, torch.float32, (B,))
 
 
 def _outputs(B: int, K: int, device):
@@ -213,8 +242,9 @@ def score_lse_topk(H: torch.Tensor, E: torch.Tensor, K: int, workspace: torch.Te
     B, D = H.shape
     M = E.shape[0]
     if mask is not None:
-        if mask.dtype not in (torch.int32, torch.uint32) or not (mask.is_cuda and mask.is_contiguous()):
+        if mask.dtype not in (torch.int32, torch.uint32):
             raise TypeError("mask must be a contiguous int32/uint32 device tensor")
+        _check_tensor(mask, "mask", H.device)
         W = (M + 31) // 32
         if mask.dim() == 1:
             if mask.numel() < W:
@@ -231,6 +261,9 @@ def score_lse_topk(H: torch.Tensor, E: torch.Tensor, K: int, workspace: torch.Te
                           "genrec_score_lse_topk")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=H.device)
+    _check_workspace(workspace, H.device, need)
+    if out is not None:
+        _check_outs(out, B, K, H.device)
     idx, sc, ls = out if out is not None else _outputs(B, K, H.device)
     tail = (_ptr(idx), _ptr(sc), _ptr(ls), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream_handle(H.device))
@@ -241,10 +274,11 @@ def score_lse_topk(H: torch.Tensor, E: torch.Tensor, K: int, workspace: torch.Te
     else:
         name = "genrec_score_lse_topk_masked"
         args = head + (_ptr(mask), stride) + tail
-    if profiler is None:
-        st = getattr(lib(), name)(*args)
-    else:
-        st = getattr(lib(), name + "_profiled")(*args, profiler.h)
+    with torch.cuda.device(H.device):
+        if profiler is None:
+            st = getattr(lib(), name)(*args)
+        else:
+            st = getattr(lib(), name + "_profiled")(*args, profiler.h)
     if st != 0:
         raise GenrecError(st, name)
     return idx, sc, ls
@@ -257,8 +291,8 @@ def score_candidates_topk(H: torch.Tensor, E: torch.Tensor, offsets: torch.Tenso
     _check_inputs(H, E)
     if offsets.dtype != torch.int64 or ids.dtype != torch.int32:
         raise TypeError("offsets must be int64 and ids int32")
-    if not (offsets.is_cuda and ids.is_cuda and offsets.is_contiguous() and ids.is_contiguous()):
-        raise ValueError("offsets and ids must be contiguous device tensors")
+    _check_tensor(offsets, "offsets", H.device)
+    _check_tensor(ids, "ids", H.device)
     B, D = H.shape
     M = E.shape[0]
     if offsets.numel() != B + 1:
@@ -271,14 +305,18 @@ def score_candidates_topk(H: torch.Tensor, E: torch.Tensor, offsets: torch.Tenso
                           "genrec_score_candidates_topk")
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=H.device)
+    _check_workspace(workspace, H.device, need)
+    if out is not None:
+        _check_outs(out, B, K, H.device)
     idx, sc, ls = out if out is not None else _outputs(B, K, H.device)
     args = (_ptr(H), _ptr(E), dtype_code(H.dtype), _ptr(offsets), _ptr(ids) if nnz else None, B, D, M, nnz, K,
             _ptr(idx), _ptr(sc), _ptr(ls), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream_handle(H.device))
-    if profiler is None:
-        st = lib().genrec_score_candidates_topk(*args)
-    else:
-        st = lib().genrec_score_candidates_topk_profiled(*args, profiler.h)
+    with torch.cuda.device(H.device):
+        if profiler is None:
+            st = lib().genrec_score_candidates_topk(*args)
+        else:
+            st = lib().genrec_score_candidates_topk_profiled(*args, profiler.h)
     if st != 0:
         raise GenrecError(st, "genrec_score_candidates_topk")
     return idx, sc, ls, workspace
@@ -289,11 +327,9 @@ def _check_ce(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, weights):
     if H.dtype != torch.bfloat16:
         raise TypeError("the cross-entropy entry points take bfloat16 H and E")
     B = H.shape[0]
-    if labels.dtype != torch.int32 or labels.shape != (B,) or not (labels.is_cuda and labels.is_contiguous()):
-        raise ValueError("labels must be a contiguous int32 device tensor of shape (B,)")
-    if weights is not None and (weights.dtype != torch.float32 or weights.shape != (B,)
-                                or not (weights.is_cuda and weights.is_contiguous())):
-        raise ValueError("weights must be a contiguous float32 device tensor of shape (B,)")
+    _check_tensor(labels, "labels", H.device, torch.int32, (B,))
+    if weights is not None:
+        _check_tensor(weights, "weights", H.device, torch.float32, (B,))
 
 
 def ce_forward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, weights: torch.Tensor | None = None,
@@ -308,14 +344,16 @@ def ce_forward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, weights: 
     need = lib().genrec_ce_forward_workspace(B, D, M)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    _check_workspace(workspace, H.device, need)
     loss = torch.empty((B,), dtype=torch.float32, device=H.device)
     lse = torch.empty((B,), dtype=torch.float32, device=H.device)
     args = (_ptr(H), _ptr(E), B, D, M, _ptr(labels), _ptr(weights), _ptr(loss), _ptr(lse), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_handle(H.device))
-    if profiler is None:
-        st = lib().genrec_ce_forward(*args)
-    else:
-        st = lib().genrec_ce_forward_profiled(*args, profiler.h)
+    with torch.cuda.device(H.device):
+        if profiler is None:
+            st = lib().genrec_ce_forward(*args)
+        else:
+            st = lib().genrec_ce_forward_profiled(*args, profiler.h)
     if st != 0:
         raise GenrecError(st, "genrec_ce_forward")
     return loss, lse, workspace
@@ -329,11 +367,11 @@ def ce_backward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, lse: tor
     _check_ce(H, E, labels, weights)
     B, D = H.shape
     M = E.shape[0]
-    if lse.dtype != torch.float32 or lse.shape != (B,) or not (lse.is_cuda and lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 device tensor of shape (B,)")
+    _check_tensor(lse, "lse", H.device, torch.float32, (B,))
     need = lib().genrec_ce_backward_workspace(B, D, M)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    _check_workspace(workspace, H.device, need)
     if de_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("de_dtype must be float32 or bfloat16")
     if out is None:
@@ -341,15 +379,16 @@ def ce_backward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, lse: tor
         dE = torch.empty((M, D), dtype=de_dtype, device=H.device)
     else:
         dH, dE = out
-        if dE.dtype != de_dtype or dH.dtype != torch.float32 or dH.shape != (B, D) or dE.shape != (M, D):
-            raise ValueError("out = (dH float32 [B, D], dE de_dtype [M, D])")
+        _check_tensor(dH, "out dH", H.device, torch.float32, (B, D))
+        _check_tensor(dE, "out dE", H.device, de_dtype, (M, D))
     args = (_ptr(H), _ptr(E), B, D, M, _ptr(labels), _ptr(weights), _ptr(lse), _ptr(dH), _ptr(dE),
             dtype_code(de_dtype), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream_handle(H.device))
-    if profiler is None:
-        st = lib().genrec_ce_backward(*args)
-    else:
-        st = lib().genrec_ce_backward_profiled(*args, profiler.h)
+    with torch.cuda.device(H.device):
+        if profiler is None:
+            st = lib().genrec_ce_backward(*args)
+        else:
+            st = lib().genrec_ce_backward_profiled(*args, profiler.h)
     if st != 0:
         raise GenrecError(st, "genrec_ce_backward")
     return dH, dE
@@ -357,6 +396,7 @@ def ce_backward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, lse: tor
 
 def device_errors(workspace: torch.Tensor) -> tuple[int, int]:
     """(skipped out-of-range ids, users with malformed offsets) of the last candidate call."""
+    _check_tensor(workspace, "workspace", workspace.device)
     a, b = ctypes.c_int64(0), ctypes.c_int64(0)
     st = lib().genrec_get_device_errors(_ptr(workspace), _stream_handle(workspace.device),
                                         ctypes.byref(a), ctypes.byref(b))
@@ -367,6 +407,7 @@ def device_errors(workspace: torch.Tensor) -> tuple[int, int]:
 
 def rescued_users(workspace: torch.Tensor) -> int:
     """Users of the last full-catalog call on this workspace that needed the rescue pass."""
+    _check_tensor(workspace, "workspace", workspace.device)
     n = ctypes.c_int64(0)
     st = lib().genrec_get_rescued_users(_ptr(workspace), _stream_handle(workspace.device), ctypes.byref(n))
     if st != 0:
@@ -380,17 +421,24 @@ def topk_rows(scores: torch.Tensor, K: int, out=None, workspace: torch.Tensor | 
     if scores.dtype != torch.float32 or not scores.is_cuda or scores.dim() != 2 or scores.stride(1) != 1:
         raise TypeError("scores must be a float32 device tensor [R, N] with unit column stride")
     R, N = scores.shape
+    if scores.stride(0) < N:
+        raise ValueError("scores rows must not overlap (row stride >= N)")
     if out is None:
         idx = torch.empty((R, K), dtype=torch.int32, device=scores.device)
         val = torch.empty((R, K), dtype=torch.float32, device=scores.device)
     else:
         idx, val = out
+        _check_tensor(idx, "out idx", scores.device, torch.int32, (R, K))
+        _check_tensor(val, "out values", scores.device, torch.float32, (R, K))
     need = int(lib().genrec_topk_rows_workspace(R, N, K))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    if workspace is not None:
+        _check_workspace(workspace, scores.device, need)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().genrec_topk_rows(_ptr(scores), R, N, scores.stride(0), K, _ptr(idx), _ptr(val),
-                                _ptr(workspace), wsb, _stream_handle(scores.device))
+    with torch.cuda.device(scores.device):
+        st = lib().genrec_topk_rows(_ptr(scores), R, N, scores.stride(0), K, _ptr(idx), _ptr(val),
+                                    _ptr(workspace), wsb, _stream_handle(scores.device))
     if st != 0:
         raise GenrecError(st, "genrec_topk_rows")
     return idx, val

@@ -386,3 +386,40 @@ def test_topk_rows(dev, oracle_mod, R, N, K, decimals, ld_pad):
         ri, rv = oracle_mod.topk_row(s[r].astype(np.float64), K)
         assert np.array_equal(idx[r], ri), r   # exact: same fp32 values, same (score, column) order
         assert np.array_equal(val[r], rv.astype(np.float32)), r
+
+
+def test_binding_rejects_bad_buffers(dev, oracle_mod):
+    """Caller-provided outputs, workspaces and inputs of the wrong shape, dtype,
+    device or layout are refused before anything is launched; a valid call
+    afterwards is unaffected."""
+    from full_catalog_ranking_amd import genrec
+    B, D, M, K = 3, 64, 500, 7
+    d = synth.make_dense(B, D, M, seed=41)
+    H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
+    i32, f32 = torch.int32, torch.float32
+    good = (torch.empty((B, K), dtype=i32, device=dev), torch.empty((B, K), dtype=f32, device=dev),
+            torch.empty((B,), dtype=f32, device=dev))
+    with pytest.raises(ValueError):
+        genrec.score_lse_topk(H, E, K, out=(good[0][:, :K - 1], good[1], good[2]))
+    with pytest.raises(TypeError):
+        genrec.score_lse_topk(H, E, K, out=(good[1], good[1], good[2]))
+    with pytest.raises(ValueError):
+        genrec.score_lse_topk(H, E, K, out=(torch.empty((K, B), dtype=i32, device=dev).t(), good[1], good[2]))
+    with pytest.raises(ValueError):
+        genrec.score_lse_topk(H, E, K, out=(good[0], good[1], torch.empty((B,), dtype=f32)))
+    need = genrec.workspace_bytes(B, D, M, K, H.dtype)
+    with pytest.raises(ValueError):
+        genrec.score_lse_topk(H, E, K, workspace=torch.empty(need - 1, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError):
+        genrec.score_lse_topk(H, E.cpu(), K)
+    scores = torch.randn(4, 100, device=dev)
+    with pytest.raises(ValueError):
+        genrec.topk_rows(scores, 5, out=(torch.empty((4, 4), dtype=i32, device=dev),
+                                         torch.empty((4, 5), dtype=f32, device=dev)))
+    labels = torch.zeros(B, dtype=torch.int64, device=dev)
+    with pytest.raises(TypeError):
+        genrec.ce_forward(H, E, labels)
+    idx, sc, ls = genrec.score_lse_topk(H, E, K, out=good)
+    torch.cuda.synchronize()
+    ref = oracle_mod.full(d["H"], d["E"], K)
+    parity.check_dense((idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()), ref, where="after refusals")
