@@ -158,10 +158,10 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
     const DensePlan p = plan_dense(B, D, M, K, dtype);
     snprintf(buf, len,
              "{\"path\":\"%s\",\"sample\":%d,\"stride\":%lld,\"n_sample\":%lld,\"fast\":%d,\"r_fast\":%d,"
-             "\"UT\":%d,\"P\":%d,\"tiles_per_chunk\":%d,\"CH\":%lld,\"workspace\":%zu}",
+             "\"UT\":%d,\"P\":%d,\"tiles_per_chunk\":%d,\"CH\":%lld,\"merge_small\":%d,\"workspace\":%zu}",
              p.mfma ? "mfma" : "stream", p.sample ? 1 : 0, (long long)p.stride, (long long)p.n_sample,
              p.fast ? 1 : 0, p.r_fast, p.main.UT, p.main.P, p.main.base + (p.main.rem ? 1 : 0),
-             (long long)p.main.CH, p.total);
+             (long long)p.main.CH, p.merge_small ? 1 : 0, p.total);
     return GENREC_OK;
 }
 
@@ -301,6 +301,7 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     m.rescued = rescued;
     m.theta_fast = theta_fast;
     m.theta_safe = theta_safe;
+    m.small = p.merge_small ? 1 : 0;
     if ((st = hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }))) != GENREC_OK) return st;
     if (!p.fast) return GENREC_OK;
     // Rescue: users the fast threshold left short of K candidates are scored
@@ -311,6 +312,7 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     a.user_flag = uflag;
     if ((st = hip_status(timed(prof, KIND_RESCUE, s, [&] { return launch_mfma(a, 1, s); }))) != GENREC_OK) return st;
     m.mode = 2;
+    m.small = 0;  // users past the K-th sampled score: many candidates
     m.clear_err = nullptr;
     return hip_status(timed(prof, KIND_RESCUE, s, [&] { return launch_merge(m, s); }));
 }
@@ -469,6 +471,7 @@ int genrec_score_candidates_topk_profiled(const void* H, const void* E, int dtyp
     m.out_lse = out_lse;
     m.clear_err = nullptr;
     m.mode = 0;
+    m.small = nnz <= (int64_t)kMergeSmallGather * B ? 1 : 0;  // lists of up to ~2,048 entries on average
     return hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }));
 }
 

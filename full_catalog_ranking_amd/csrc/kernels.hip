@@ -680,17 +680,22 @@ constexpr int SEL_NT = 256;
 constexpr int SEL_NB = 256;     // histogram bins per narrowing pass
 constexpr int SEL_GCAP = 6144;  // range gathered into LDS once it holds at most this many keys
 constexpr int SEL_SMALL = 256;  // range ranked once it holds at most this many keys
-static_assert(SEL_GCAP >= GENREC_KMAX, "the merge places the final K keys in the gather buffer");
 constexpr int SEL_UNR = 8;      // independent loads in flight per thread
 
-struct SelShared {
+// Block-shared state of a selection; GCAP = keys the LDS gather holds (the
+// merge also uses a smaller build, which fits twice the blocks on a CU).
+template <int GCAP>
+struct SelSharedT {
+    static_assert(GCAP >= GENREC_KMAX, "the merge places the final K keys in the gather buffer");
+    static constexpr int kGcap = GCAP;
     unsigned long long red_lo[SEL_NT / kWave], red_hi[SEL_NT / kWave];
     int hist[SEL_NT / kWave][SEL_NB];  // one histogram per wave: less atomic contention
     int cnt_a, cnt_b, bin, above;
-    uint64_t gbuf[SEL_GCAP];
+    uint64_t gbuf[GCAP];
     uint64_t sbuf[SEL_SMALL];
     uint64_t out[GENREC_KMAX];
 };
+using SelShared = SelSharedT<SEL_GCAP>;
 
 __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
 #pragma unroll
@@ -832,9 +837,8 @@ struct LdsSrc {
 // One narrowing pass: histogram the keys of [lo, hi] into 256 power-of-two-
 // wide bins and move [lo, hi] to the bin holding the k_rem-th largest key.
 // k_rem drops by the keys of the bins above it; returns the keys in the bin.
-template <class Src>
-__device__ int64_t narrow(const Src& src, unsigned long long& lo, unsigned long long& hi, int& k_rem,
-                          SelShared& sh) {
+template <class Src, class Sh>
+__device__ int64_t narrow(const Src& src, unsigned long long& lo, unsigned long long& hi, int& k_rem, Sh& sh) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const unsigned long long span = hi - lo;
     const int shift = max(0, 64 - __clzll(span) - 8);  // (hi - lo) >> shift < 256
@@ -891,17 +895,17 @@ __device__ int64_t narrow(const Src& src, unsigned long long& lo, unsigned long 
 
 // Finds the k-th largest key (1 <= k <= n) among the keys the source yields
 // and, with COLLECT, leaves the k largest keys in sh.out[0..k) (unsorted).
-// Returns the k-th largest key.  At most SEL_GCAP keys: one pass copies them
-// into LDS.  More: passes over the source --
+// Returns the k-th largest key.  At most GCAP keys (the shared state's gather
+// capacity): one pass copies them into LDS.  More: passes over the source --
 //   1. min / max of all keys;
-//   2. while the candidate range [lo, hi] holds more than SEL_GCAP keys, a
+//   2. while the candidate range [lo, hi] holds more than GCAP keys, a
 //      narrowing pass (histogram of the range, keep the bin of the k-th);
 //   3. gather: the range into LDS and (COLLECT) every key above it into out.
 // Then, in LDS, narrowing continues until at most SEL_SMALL keys remain in
 // the range, which are sorted; keys above the final range join out.
 // Block-wide min and max of the keys a source yields (every thread gets both).
-template <class Src>
-__device__ void block_minmax(const Src& src, unsigned long long& lo, unsigned long long& hi, SelShared& sh) {
+template <class Src, class Sh>
+__device__ void block_minmax(const Src& src, unsigned long long& lo, unsigned long long& hi, Sh& sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     lo = ~0ull;
     hi = 0;
@@ -922,14 +926,15 @@ __device__ void block_minmax(const Src& src, unsigned long long& lo, unsigned lo
     __syncthreads();
 }
 
-template <bool COLLECT, class Src>
-__device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
+template <bool COLLECT, class Src, class Sh>
+__device__ uint64_t block_select(const Src& src, int k, Sh& sh) {
+    constexpr int GCAP = Sh::kGcap;
     const int tid = threadIdx.x;
     unsigned long long lo, hi;
     int64_t n_range = src.total();
     int k_rem = k;
     int ng;
-    if (n_range <= SEL_GCAP) {
+    if (n_range <= GCAP) {
         // few keys: one pass copies them all into LDS (each to its position in
         // the source's order), and everything else happens there
         src.gather(sh.gbuf);
@@ -939,7 +944,7 @@ __device__ uint64_t block_select(const Src& src, int k, SelShared& sh) {
         block_minmax(LdsSrc{sh.gbuf, ng}, lo, hi, sh);
     } else {
         block_minmax(src, lo, hi, sh);
-        while (lo != hi && n_range > SEL_GCAP) n_range = narrow(src, lo, hi, k_rem, sh);
+        while (lo != hi && n_range > GCAP) n_range = narrow(src, lo, hi, k_rem, sh);
         // gather the range into LDS; keys above it are in the result for sure
         if (tid == 0) { sh.cnt_a = 0; sh.cnt_b = 0; }
         __syncthreads();
@@ -1217,22 +1222,23 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
     }
 }
 
-// Source: the candidate regions of one user's pieces.
-constexpr int MG_PB = 1024;  // pieces staged in LDS per batch
-
+// Source: the candidate regions of one user's pieces, staged MG_PB pieces
+// per batch in LDS.
+template <int MG_PB>
 struct PieceShared {
     int64_t base[MG_PB];
     int pref[MG_PB + 1];
     int wsum[SEL_NT / kWave];
 };
 
+template <int MG_PB>
 struct PieceSrc {
     const uint64_t* keys;
     const int* pcnt;
     const int64_t* preg;
     int64_t p0, p1;
     int64_t n;  // total keys
-    PieceShared* ps;
+    PieceShared<MG_PB>* ps;
     __device__ int64_t total() const { return n; }
     // Calls f(key, e) for every key, e = its index in the concatenation of
     // the pieces' regions.
@@ -1318,9 +1324,16 @@ struct PieceSrc {
     }
 };
 
+// Merge builds: the default, and a smaller one (a 2,048-key gather and
+// 512-piece batches: 37 instead of 76 KB of LDS, four blocks on a CU instead of
+// two) for users expected to hold few pieces and candidates.  Either is exact
+// for any input; the size only decides how fast.
+constexpr int MG_GCAP_SMALL = kMergeSmallGather, MG_PB_SMALL = kMergeSmallPieces, MG_PB_LARGE = 1024;
+
+template <int GCAP, int MG_PB>
 __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
-    __shared__ SelShared sh;
-    __shared__ PieceShared ps;
+    __shared__ SelSharedT<GCAP> sh;
+    __shared__ PieceShared<MG_PB> ps;
     __shared__ float2 s_ml[SEL_NT / kWave];
     __shared__ unsigned long long s_n[SEL_NT / kWave];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1379,7 +1392,7 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     int32_t* oidx = a.out_idx + (int64_t)b * K;
     float* osc = a.out_scores + (int64_t)b * K;
     if (keff > 0) {
-        PieceSrc src{a.keys, a.pcnt, a.preg, p0, p1, (int64_t)ntot, &ps};
+        PieceSrc<MG_PB> src{a.keys, a.pcnt, a.preg, p0, p1, (int64_t)ntot, &ps};
         block_select<true>(src, keff, sh);
         // the K keys in ranking order: rank placement for a few hundred
         // (quadratic compares, one barrier), wave sorts and a rank merge for more
@@ -2006,7 +2019,10 @@ hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(merge_kernel, dim3(a.B), dim3(SEL_NT), 0, s, a);
+    if (a.small)
+        hipLaunchKernelGGL((merge_kernel<MG_GCAP_SMALL, MG_PB_SMALL>), dim3(a.B), dim3(SEL_NT), 0, s, a);
+    else
+        hipLaunchKernelGGL((merge_kernel<SEL_GCAP, MG_PB_LARGE>), dim3(a.B), dim3(SEL_NT), 0, s, a);
     return hipGetLastError();
 }
 

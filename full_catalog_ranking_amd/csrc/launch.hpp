@@ -179,6 +179,9 @@ struct MergeArgs {
     // the fast one (else the first pass already kept every item it would)
     const float* theta_fast;
     const float* theta_safe;
+    // 1: the smaller merge build (users with at most ~512 pieces and ~2,048
+    // candidates expected); any value gives the same result
+    int small;
 };
 
 struct ThresholdArgs {

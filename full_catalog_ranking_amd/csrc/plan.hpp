@@ -37,6 +37,11 @@ struct Chunking {
     int64_t CH = 0;                        // VALU: items per chunk (P chunks)
 };
 
+// The merge's smaller build (LDS gather of 2,048 keys, 512-piece batches)
+// serves users expected to hold at most that many candidates and pieces.
+constexpr int kMergeSmallGather = 2048;
+constexpr int kMergeSmallPieces = 512;
+
 struct DensePlan {
     bool mfma = false;
     bool sample = false;
@@ -54,6 +59,7 @@ struct DensePlan {
     int pieces_per_chunk = 1;  // MFMA: one piece per (user, chunk, lane group) = 4
     int64_t n_pieces = 0;
     int64_t key_stride = 0;    // candidate-region elements per user
+    bool merge_small = false;  // the merge's smaller build serves this shape (a speed choice)
     size_t off_hdr = 0, off_theta = 0, off_theta_safe = 0, off_uflag = 0, off_tflag = 0, off_sample = 0,
            off_pm = 0, off_pl = 0, off_pcnt = 0, off_preg = 0, off_keys = 0, total = 0;
 };
@@ -100,6 +106,13 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
     p.pieces_per_chunk = p.mfma ? 4 : 1;
     p.n_pieces = (int64_t)B * p.main.P * p.pieces_per_chunk;
     p.key_stride = p.mfma ? ceil_div(M, kMfmaTileItems) * kMfmaTileItems : M;
+    {
+        // expected candidates per user: ~4K past the fast threshold, ~K M / n
+        // past the K-th sampled score, every item without a sample
+        const int64_t expect = p.fast ? (int64_t)kFastOversample * K
+                                      : (p.sample ? ceil_div((int64_t)K * M, p.n_sample) : M);
+        p.merge_small = (int64_t)p.main.P * p.pieces_per_chunk <= kMergeSmallPieces && expect <= kMergeSmallGather;
+    }
     size_t o = 0;
     p.off_hdr = o;
     o += 256;

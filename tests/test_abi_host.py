@@ -149,6 +149,19 @@ def test_plan_selection(L):
         genrec.describe_plan(4, 12, 100, 10, torch.bfloat16)
 
 
+def test_merge_build_selection(L):
+    import torch
+    # 4 K = 2,000 expected candidates and 64 x 4 pieces per user: the small build
+    assert genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)["merge_small"] == 1
+    # K = 1,024: ~4,096 candidates expected
+    assert genrec.describe_plan(1024, 4096, 1_000_000, 1024, torch.bfloat16)["merge_small"] == 0
+    # 256 chunks x 4 lane groups = 1,024 pieces per user
+    assert genrec.describe_plan(256, 2048, 100_000, 100, torch.bfloat16)["merge_small"] == 0
+    # no sample: every item is a candidate
+    assert genrec.describe_plan(1, 2048, 5000, 100, torch.bfloat16)["merge_small"] == 0
+    assert genrec.describe_plan(9, 64, 1500, 64, torch.bfloat16)["merge_small"] == 1
+
+
 def test_ce_validation_and_workspace(L):
     """Cross-entropy entry points: argument errors come back before any launch."""
     f, b = L.genrec_ce_forward, L.genrec_ce_backward
