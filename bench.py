@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scratch buffer before every step (flushes the 256 MB Infinity "
                          "Cache and the L2s) and time each step on its own, the flush outside")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured as a HIP graph (the same launches without the "
+                         "host call's cost); per-kernel times still come from eager steps")
     ap.add_argument("--peaks", action="store_true",
                     help="only measure library reference rates on this GPU (device copy GB/s, "
                          "hipBLASLt bf16 GEMM TFLOP/s) and exit")
@@ -391,6 +394,18 @@ def main():
         med = per[args.steps // 2] if args.steps % 2 else 0.5 * (per[args.steps // 2 - 1] + per[args.steps // 2])
         mn = per[0]
         del scratch
+    elif args.graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ms, med, mn = timed_steps(torch, g.replay, args.steps)
+        del g
+        for _ in range(args.steps):  # per-kernel durations: eager steps
+            step(prof)
+        torch.cuda.synchronize()
     else:
         ms, med, mn = timed_steps(torch, lambda: step(prof), args.steps)
     kern = prof.summary()
@@ -435,6 +450,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "D": D, "M": M, "K": K,
                    **({"nnz": units} if cand else {}), **({"cache": "cold"} if args.cold else {}),
+                   **({"timing": "graph replay"} if args.graph and not args.cold else {}),
                    **({"mask_density": args.mask_density} if args.mask_density is not None else {})},
         "tflops": flops / (ms * 1e-3) / 1e12,
         "kernels_ms": {k: v[1] / v[0] for k, v in kern.items()},

@@ -6,6 +6,7 @@ or cannot be loaded this module raises -- there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import json
 import os
@@ -155,6 +156,14 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _on_device(device: torch.device):
+    """The library launches on the current device: make it the inputs' device
+    for the call (a no-op when it already is)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
 def _check_inputs(H: torch.Tensor, E: torch.Tensor):
     if not (H.is_cuda and E.is_cuda):
         raise ValueError("H and E must be device tensors")
@@ -274,7 +283,7 @@ def score_lse_topk(H: torch.Tensor, E: torch.Tensor, K: int, workspace: torch.Te
     else:
         name = "genrec_score_lse_topk_masked"
         args = head + (_ptr(mask), stride) + tail
-    with torch.cuda.device(H.device):
+    with _on_device(H.device):
         if profiler is None:
             st = getattr(lib(), name)(*args)
         else:
@@ -312,7 +321,7 @@ def score_candidates_topk(H: torch.Tensor, E: torch.Tensor, offsets: torch.Tenso
     args = (_ptr(H), _ptr(E), dtype_code(H.dtype), _ptr(offsets), _ptr(ids) if nnz else None, B, D, M, nnz, K,
             _ptr(idx), _ptr(sc), _ptr(ls), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream_handle(H.device))
-    with torch.cuda.device(H.device):
+    with _on_device(H.device):
         if profiler is None:
             st = lib().genrec_score_candidates_topk(*args)
         else:
@@ -349,7 +358,7 @@ def ce_forward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, weights: 
     lse = torch.empty((B,), dtype=torch.float32, device=H.device)
     args = (_ptr(H), _ptr(E), B, D, M, _ptr(labels), _ptr(weights), _ptr(loss), _ptr(lse), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_handle(H.device))
-    with torch.cuda.device(H.device):
+    with _on_device(H.device):
         if profiler is None:
             st = lib().genrec_ce_forward(*args)
         else:
@@ -384,7 +393,7 @@ def ce_backward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, lse: tor
     args = (_ptr(H), _ptr(E), B, D, M, _ptr(labels), _ptr(weights), _ptr(lse), _ptr(dH), _ptr(dE),
             dtype_code(de_dtype), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream_handle(H.device))
-    with torch.cuda.device(H.device):
+    with _on_device(H.device):
         if profiler is None:
             st = lib().genrec_ce_backward(*args)
         else:
@@ -436,7 +445,7 @@ def topk_rows(scores: torch.Tensor, K: int, out=None, workspace: torch.Tensor | 
     if workspace is not None:
         _check_workspace(workspace, scores.device, need)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    with torch.cuda.device(scores.device):
+    with _on_device(scores.device):
         st = lib().genrec_topk_rows(_ptr(scores), R, N, scores.stride(0), K, _ptr(idx), _ptr(val),
                                     _ptr(workspace), wsb, _stream_handle(scores.device))
     if st != 0:
