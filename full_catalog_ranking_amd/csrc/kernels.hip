@@ -93,7 +93,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     // k-step's scalar offset.  The resource's record count ends at the last
     // valid row of the tile (or of the batch), so rows past the end of a
     // partial tile read as zeros without any clamping; k-chunks past D read
-    // the next row or zeros and meet zeroed user-side fragments.
+    // the next row or zeros, and the fragment reads replace them by zeros.
     const int wsu = __builtin_amdgcn_readfirstlane(w);  // wave index, provably uniform
     uint32_t voff[MF_DMA];
 #pragma unroll
@@ -136,10 +136,16 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         const uint8_t* sE = smem[stg];
         const uint8_t* sH = smem[stg] + MF_TI * MF_ROWB;
         const int chunk = ks * 2 + (lane >> 5);
-        const bool kin = !KTAIL || k0 + chunk * 8 < D;  // k past D: zero the user side
+        // k past D: both fragments zero.  The staged chunks there hold the next
+        // row's first elements (or zeros), which need not be finite: the hot
+        // rows of a candidate call are gathered into a workspace whose rows
+        // past the live ones are stale, and NaN times zero is NaN.
+        const bool kin = !KTAIL || k0 + chunk * 8 < D;
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
+        for (int ib = 0; ib < 4; ++ib) {
             f.a[ib] = *(const bf16x8_t*)(sE + mf_frag_lds_byte(wi * 128 + ib * 32 + (lane & 31), chunk));
+            if (!kin) f.a[ib] = bf16x8_t{};
+        }
 #pragma unroll
         for (int ub = 0; ub < MF_UB; ++ub) {
             f.b[ub] = *(const bf16x8_t*)(sH + mf_frag_lds_byte(wu * MF_WU + ub * 32 + (lane & 31), chunk));

@@ -331,6 +331,32 @@ def test_candidates_hot_head(dev, oracle_mod, B, M, lo, hi, seed):
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("B,D,M,lo,hi,seed", [
+    (100, 264, 50, 42, 50, 54098347),  # every item hot; D % 32 = 8
+    (300, 72, 3000, 50, 400, 61),      # part of the catalog hot; D % 32 = 8
+])
+def test_candidates_hot_rows_k_tail_stale_workspace(dev, oracle_mod, B, D, M, lo, hi, seed):
+    """The hot rows are gathered into the workspace; with D not a multiple of
+    the 32-deep k-step the last k-step of a row reaches into the next staged
+    row, which past the live rows is whatever the workspace held.  Filled with
+    0xFF bytes (NaN as bf16 and as fp32) before the call, it must not reach any
+    score (found by the randomized sweep: a stale NaN row poisoned the last
+    hot row's scores)."""
+    from full_catalog_ranking_amd import genrec
+    K = 100
+    d = synth.make_dense(B, D, M, seed=seed)
+    off, ids = synth.gen_candidates(B, M, seed, lo, hi)
+    H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
+    ws = torch.full((genrec.cand_workspace_bytes(B, D, M, ids.size, K, H.dtype),), 255, dtype=torch.uint8, device=dev)
+    print("  cand stale workspace B=%d D=%d M=%d nnz=%d" % (B, D, M, ids.size), flush=True)
+    idx, sc, ls, ws = genrec.score_candidates_topk(H, E, torch.from_numpy(off).to(dev), torch.from_numpy(ids).to(dev),
+                                                   K, workspace=ws)
+    assert genrec.device_errors(ws) == (0, 0)
+    g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
+    ref = oracle_mod.cand(d["H"], d["E"], off, ids, K)
+    parity.check_cand(g, ref, off, ids, where="stale workspace %s" % ((B, D, M),))
+
+
 def test_candidate_malformed_offsets(dev):
     B, D, M, K = 4, 64, 100, 5
     d = synth.make_dense(B, D, M, seed=9)
