@@ -204,10 +204,24 @@ def _check_outs(out, B: int, K: int, device):
     _check_tensor(out[2], "out lse", device, torch.float32, (B,))
 
 
+# Testing aid: with GENREC_POISON=1 in the environment, every workspace and
+# output this module allocates starts filled with 0xFF bytes (NaN as bf16 and
+# fp32, -1 as int32) instead of whatever the allocator hands back, so that a
+# kernel reading memory the call has not written shows up as a wrong result.
+_POISON = os.environ.get("GENREC_POISON") == "1"
+
+
+def _empty(shape, dtype, device):
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if _POISON and t.numel():
+        t.view(torch.uint8).fill_(255)
+    return t
+
+
 def _outputs(B: int, K: int, device):
-    idx = torch.empty((B, K), dtype=torch.int32, device=device)
-    sc = torch.empty((B, K), dtype=torch.float32, device=device)
-    ls = torch.empty((B,), dtype=torch.float32, device=device)
+    idx = _empty((B, K), torch.int32, device)
+    sc = _empty((B, K), torch.float32, device)
+    ls = _empty((B,), torch.float32, device)
     return idx, sc, ls
 
 
@@ -269,7 +283,7 @@ def score_lse_topk(H: torch.Tensor, E: torch.Tensor, K: int, workspace: torch.Te
                                                       None, None, None, None, 0, None),
                           "genrec_score_lse_topk")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=H.device)
+        workspace = _empty(need, torch.uint8, H.device)
     _check_workspace(workspace, H.device, need)
     if out is not None:
         _check_outs(out, B, K, H.device)
@@ -313,7 +327,7 @@ def score_candidates_topk(H: torch.Tensor, E: torch.Tensor, offsets: torch.Tenso
                                                              M, nnz, K, None, None, None, None, 0, None),
                           "genrec_score_candidates_topk")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=H.device)
+        workspace = _empty(need, torch.uint8, H.device)
     _check_workspace(workspace, H.device, need)
     if out is not None:
         _check_outs(out, B, K, H.device)
@@ -352,10 +366,10 @@ def ce_forward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, weights: 
     M = E.shape[0]
     need = lib().genrec_ce_forward_workspace(B, D, M)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+        workspace = _empty(max(need, 1), torch.uint8, H.device)
     _check_workspace(workspace, H.device, need)
-    loss = torch.empty((B,), dtype=torch.float32, device=H.device)
-    lse = torch.empty((B,), dtype=torch.float32, device=H.device)
+    loss = _empty((B,), torch.float32, H.device)
+    lse = _empty((B,), torch.float32, H.device)
     args = (_ptr(H), _ptr(E), B, D, M, _ptr(labels), _ptr(weights), _ptr(loss), _ptr(lse), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_handle(H.device))
     with _on_device(H.device):
@@ -379,13 +393,13 @@ def ce_backward(H: torch.Tensor, E: torch.Tensor, labels: torch.Tensor, lse: tor
     _check_tensor(lse, "lse", H.device, torch.float32, (B,))
     need = lib().genrec_ce_backward_workspace(B, D, M)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+        workspace = _empty(max(need, 1), torch.uint8, H.device)
     _check_workspace(workspace, H.device, need)
     if de_dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("de_dtype must be float32 or bfloat16")
     if out is None:
-        dH = torch.empty((B, D), dtype=torch.float32, device=H.device)
-        dE = torch.empty((M, D), dtype=de_dtype, device=H.device)
+        dH = _empty((B, D), torch.float32, H.device)
+        dE = _empty((M, D), de_dtype, H.device)
     else:
         dH, dE = out
         _check_tensor(dH, "out dH", H.device, torch.float32, (B, D))
@@ -433,15 +447,15 @@ def topk_rows(scores: torch.Tensor, K: int, out=None, workspace: torch.Tensor | 
     if scores.stride(0) < N:
         raise ValueError("scores rows must not overlap (row stride >= N)")
     if out is None:
-        idx = torch.empty((R, K), dtype=torch.int32, device=scores.device)
-        val = torch.empty((R, K), dtype=torch.float32, device=scores.device)
+        idx = _empty((R, K), torch.int32, scores.device)
+        val = _empty((R, K), torch.float32, scores.device)
     else:
         idx, val = out
         _check_tensor(idx, "out idx", scores.device, torch.int32, (R, K))
         _check_tensor(val, "out values", scores.device, torch.float32, (R, K))
     need = int(lib().genrec_topk_rows_workspace(R, N, K))
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+        workspace = _empty(need, torch.uint8, scores.device)
     if workspace is not None:
         _check_workspace(workspace, scores.device, need)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -155,3 +155,29 @@ def test_ce_full_size_sampled_users(dev, oracle_mod):
     c = 2.0 ** -9 + 2 * tau + (-(-B // 32) * 32) * 2.0 ** -24
     bound = 3 * c * (d["weights"].astype(np.float64)[:, None] * np.abs(oracle_mod.widen(d["H"]))).sum(axis=0)
     assert (np.abs(col) <= bound).all(), (np.abs(col).max(), bound.min())
+
+
+def test_ce_poisoned_workspaces_and_outputs(dev, oracle_mod):
+    """Forward and backward on workspaces and outputs filled with 0xFF bytes
+    (NaN) before the calls; two catalog chunks and a k tail (D % 32 = 8)."""
+    from full_catalog_ranking_amd import genrec
+    B, D, M = 70, 40, 70_000
+    d = synth.make_dense(B, D, M, seed=19)
+    labels = synth.gen_labels(B, M, 19)
+    w = synth.gen_weights(B, 19)
+    H, E = _bf16(d["H"], dev), _bf16(d["E"], dev)
+    lab, wt = torch.from_numpy(labels).to(dev), torch.from_numpy(w).to(dev)
+    L = genrec.lib()
+    wsf = torch.full((L.genrec_ce_forward_workspace(B, D, M),), 255, dtype=torch.uint8, device=dev)
+    wsb = torch.full((L.genrec_ce_backward_workspace(B, D, M),), 255, dtype=torch.uint8, device=dev)
+    dH = torch.full((B, D), float("nan"), dtype=torch.float32, device=dev)
+    dE = torch.full((M, D), float("nan"), dtype=torch.float32, device=dev)
+    print("  ce poisoned B=%d D=%d M=%d" % (B, D, M), flush=True)
+    loss, lse, _ = genrec.ce_forward(H, E, lab, wt, workspace=wsf)
+    genrec.ce_backward(H, E, lab, lse, wt, workspace=wsb, out=(dH, dE))
+    torch.cuda.synchronize()
+    assert genrec.device_errors(wsf) == (0, 0)
+    g = (loss.cpu().numpy(), lse.cpu().numpy(), dH.cpu().numpy(), dE.cpu().numpy())
+    ref = oracle_mod.ce(d["H"], d["E"], labels, w)
+    dh_depth, de_depth = _depths(B, D, M)
+    parity.check_ce(g, ref, d["E"], d["H"], oracle_mod.widen, dh_depth, de_depth, where="ce poisoned")

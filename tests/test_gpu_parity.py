@@ -485,3 +485,63 @@ def test_concurrent_calls_on_two_streams(dev, oracle_mod):
         for a, b in zip(rep, outs[0]):
             for x, y in zip(a, b):
                 assert np.array_equal(x, y)
+
+
+def test_poisoned_workspaces_and_outputs(dev, oracle_mod):
+    """Every entry point on workspaces and outputs filled with 0xFF bytes (NaN
+    as bf16 / fp32, -1 as int32) before the call: no result may depend on
+    memory the call has not written.  Shapes with a k tail (D % 32 != 0),
+    ragged tiles and the sample / rescue passes."""
+    from full_catalog_ranking_amd import genrec
+
+    def poison(n):
+        return torch.full((n,), 255, dtype=torch.uint8, device=dev)
+
+    def outs(B, K):
+        o = (torch.empty((B, K), dtype=torch.int32, device=dev), torch.empty((B, K), dtype=torch.float32, device=dev),
+             torch.empty((B,), dtype=torch.float32, device=dev))
+        for t in o:
+            t.view(torch.uint8).fill_(255)
+        return o
+
+    # dense: MFMA with sample, fast threshold and rescue; VALU (B = 1); masked
+    for B, D, M, K, mask in [(70, 200, 70_000, 40, False), (1, 136, 40_000, 30, False), (33, 72, 9_000, 25, True)]:
+        d = synth.make_dense(B, D, M, seed=B + D)
+        H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
+        ws = poison(genrec.workspace_bytes(B, D, M, K, H.dtype))
+        print("  poisoned dense B=%d D=%d M=%d K=%d mask=%s" % (B, D, M, K, mask), flush=True)
+        if mask:
+            allowed = np.random.default_rng(D).random(M) < 0.5
+            W = (M + 31) // 32
+            pad = np.zeros(W * 32, dtype=bool)
+            pad[:M] = allowed
+            words = (pad.reshape(W, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(axis=1).astype(np.uint32)
+            g = genrec.score_lse_topk(H, E, K, workspace=ws, out=outs(B, K),
+                                      mask=torch.from_numpy(words.view(np.int32)).to(dev))
+            ref = oracle_mod.full_masked(d["H"], d["E"], K, words)
+        else:
+            g = genrec.score_lse_topk(H, E, K, workspace=ws, out=outs(B, K))
+            ref = oracle_mod.full(d["H"], d["E"], K)
+        parity.check_dense(tuple(x.cpu().numpy() for x in g), ref, where="poisoned dense %s" % ((B, D, M),))
+    # candidate lists with a hot head and gathered rows
+    B, D, M, K = 150, 104, 4000, 30
+    d = synth.make_dense(B, D, M, seed=77)
+    off, ids = synth.gen_candidates(B, M, 77, 20, 300)
+    H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
+    print("  poisoned cand B=%d D=%d M=%d nnz=%d" % (B, D, M, ids.size), flush=True)
+    ws = poison(genrec.cand_workspace_bytes(B, D, M, ids.size, K, H.dtype))
+    g = genrec.score_candidates_topk(H, E, torch.from_numpy(off).to(dev), torch.from_numpy(ids).to(dev), K,
+                                     workspace=ws, out=outs(B, K))[:3]
+    parity.check_cand(tuple(x.cpu().numpy() for x in g), oracle_mod.cand(d["H"], d["E"], off, ids, K), off, ids,
+                      where="poisoned cand")
+    # batched top-K rows of several chunks
+    R, N, K = 5, 50_000, 200
+    S = synth.gen_scores(R, N, seed=78, decimals=3)
+    need = genrec.lib().genrec_topk_rows_workspace(R, N, K)
+    o = outs(R, K)[:2]
+    print("  poisoned topk_rows R=%d N=%d K=%d" % (R, N, K), flush=True)
+    idx, val = genrec.topk_rows(torch.from_numpy(S).to(dev), K, out=o, workspace=poison(max(need, 1)))
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    for r in range(R):
+        ri, rv = oracle_mod.topk_row(S[r].astype(np.float64), K)
+        assert np.array_equal(idx[r], ri) and np.array_equal(val[r], rv.astype(np.float32))
