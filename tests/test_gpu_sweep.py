@@ -28,11 +28,36 @@ def _td(a, dev):
         else torch.from_numpy(a).to(dev)
 
 
-@pytest.mark.parametrize("case", range(16))
-def test_random_shapes(dev, oracle_mod, case):
+# Size distributions of the two families: "common" shapes, and "edge" shapes
+# at tile, chunk and capacity boundaries (M = 256k +- 1, 65,536 +- 1, K = 255 /
+# 256 / 257 / 1,024, lists longer than the small merge build's 2,048-key gather,
+# cross-entropy catalogs at the 65,536-row chunk boundary).
+SIZES = {
+    "common": dict(
+        dense_B=[1, 2, 3, 8, 40, 256, 300, 513], dense_D=lambda rng: int(rng.integers(1, 65)) * 8,
+        dense_M=[1, 7, 300, 4097, 20000, 70001], dense_K=[1, 10, 64, 100, 257, 500, 1024],
+        cand_B=[1, 5, 64, 100, 300], cand_D=lambda rng: int(rng.integers(1, 65)) * 8, cand_M=[50, 3000, 50000],
+        cand_lo=lambda rng: int(rng.integers(0, 50)), cand_span=lambda rng: int(rng.integers(0, 600)),
+        cand_K=[1, 10, 100, 300],
+        topk_R=[1, 3, 64, 100], topk_N=[1, 5, 4096, 4097, 30000, 300000],
+        ce_B=[1, 7, 64, 300], ce_D=lambda rng: int(rng.integers(1, 65)) * 8, ce_M=[1, 70, 5000, 70000]),
+    "edge": dict(
+        dense_B=[1, 2, 255, 256, 257, 511, 1025], dense_D=lambda rng: int(rng.choice([8, 16, 24, 32, 40, 264, 520])),
+        dense_M=[255, 256, 257, 8191, 8193, 65535, 65537, 131073, 262147], dense_K=[1, 255, 256, 257, 1000, 1024],
+        cand_B=[1, 63, 64, 65, 257], cand_D=lambda rng: int(rng.choice([8, 24, 72, 264])), cand_M=[300, 20000, 300000],
+        cand_lo=lambda rng: int(rng.choice([0, 1000, 2000])), cand_span=lambda rng: int(rng.choice([0, 100, 3000, 9000])),
+        cand_K=[1, 100, 1000, 1024],
+        topk_R=[1, 7, 65], topk_N=[1, 1023, 1024, 1025, 4095, 4096, 4097, 12289, 65537, 200000],
+        ce_B=[1, 33, 257], ce_D=lambda rng: int(rng.choice([8, 40, 264])), ce_M=[1, 255, 65535, 65536, 65537, 131073]),
+}
+
+
+@pytest.mark.parametrize("family,case", [("common", c) for c in range(16)] + [("edge", c) for c in range(12)])
+def test_random_shapes(dev, oracle_mod, family, case):
     from full_catalog_ranking_amd import genrec
     oracle = oracle_mod
-    rng = np.random.default_rng([20261203, case])
+    sz = SIZES[family]
+    rng = np.random.default_rng([20261203, case] + ([7] if family == "edge" else []))
     td = lambda a: _td(a, dev)
 
     def pick_users(B):
@@ -41,14 +66,14 @@ def test_random_shapes(dev, oracle_mod, case):
     kind = rng.choice(["dense", "dense", "masked", "cand", "topk", "ce"])
     if kind in ("dense", "masked"):
         bf16 = bool(rng.random() < 0.8)
-        B = int(rng.choice([1, 2, 3, 8, 40, 256, 300, 513]))
-        D = int(rng.integers(1, 65)) * 8
-        M = int(rng.choice([1, 7, 300, 4097, 20000, 70001]))
+        B = int(rng.choice(sz["dense_B"]))
+        D = sz["dense_D"](rng)
+        M = int(rng.choice(sz["dense_M"]))
         if B * M * D > 3e9:  # keep the oracle's work to about a second
             M = max(1, int(3e9 // (B * D)))
-        K = int(min(1024, rng.choice([1, 10, 64, 100, 257, 500, 1024])))
+        K = int(min(1024, rng.choice(sz["dense_K"])))
         seed = int(rng.integers(0, 1 << 30))
-        print("case %d %s B=%d D=%d M=%d K=%d bf16=%s seed=%d" % (case, kind, B, D, M, K, bf16, seed), flush=True)
+        print("case %s %d %s B=%d D=%d M=%d K=%d bf16=%s seed=%d" % (family, case, kind, B, D, M, K, bf16, seed), flush=True)
         d = synth.make_dense(B, D, M, seed=seed, bf16=bf16)
         H, E = td(d["H"]), td(d["E"])
         users = pick_users(B)
@@ -69,18 +94,18 @@ def test_random_shapes(dev, oracle_mod, case):
             idx, sc, ls = genrec.score_lse_topk(H, E, K)
             ref = oracle.full(d["H"], d["E"], K, users=users)
         g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
-        parity.check_dense(g, ref, where="sweep %d" % case)
+        parity.check_dense(g, ref, where="sweep %s %d" % (family, case))
     elif kind == "cand":
-        B = int(rng.choice([1, 5, 64, 100, 300]))
-        D = int(rng.integers(1, 65)) * 8
-        M = int(rng.choice([50, 3000, 50000]))
-        lo = int(rng.integers(0, 50))
-        hi = int(lo + rng.integers(0, 600))
+        B = int(rng.choice(sz["cand_B"]))
+        D = sz["cand_D"](rng)
+        M = int(rng.choice(sz["cand_M"]))
+        lo = sz["cand_lo"](rng)
+        hi = lo + sz["cand_span"](rng)
         hi = min(hi, M)
         lo = min(lo, hi)
-        K = int(min(1024, rng.choice([1, 10, 100, 300])))
+        K = int(min(1024, rng.choice(sz["cand_K"])))
         seed = int(rng.integers(0, 1 << 30))
-        print("case %d cand B=%d D=%d M=%d lists=[%d,%d] K=%d seed=%d" % (case, B, D, M, lo, hi, K, seed), flush=True)
+        print("case %s %d cand B=%d D=%d M=%d lists=[%d,%d] K=%d seed=%d" % (family, case, B, D, M, lo, hi, K, seed), flush=True)
         d = synth.make_dense(B, D, M, seed=seed)
         off, ids = synth.gen_candidates(B, M, seed, lo, hi)
         H, E = td(d["H"]), td(d["E"])
@@ -89,14 +114,14 @@ def test_random_shapes(dev, oracle_mod, case):
         assert genrec.device_errors(ws) == (0, 0)
         g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
         ref = oracle.cand(d["H"], d["E"], off, ids, K)
-        parity.check_cand(g, ref, off, ids, where="sweep %d" % case)
+        parity.check_cand(g, ref, off, ids, where="sweep %s %d" % (family, case))
     elif kind == "topk":
-        R = int(rng.choice([1, 3, 64, 100]))
-        N = int(rng.choice([1, 5, 4096, 4097, 30000, 300000]))
+        R = int(rng.choice(sz["topk_R"]))
+        N = int(rng.choice(sz["topk_N"]))
         K = int(min(1024, rng.choice([1, 8, 128, 257, 512, 1024])))
         dec = [None, 2][int(rng.integers(0, 2))]
         seed = int(rng.integers(0, 1 << 30))
-        print("case %d topk R=%d N=%d K=%d dec=%s seed=%d" % (case, R, N, K, dec, seed), flush=True)
+        print("case %s %d topk R=%d N=%d K=%d dec=%s seed=%d" % (family, case, R, N, K, dec, seed), flush=True)
         s = synth.gen_scores(R, N, seed=seed, decimals=dec)
         idx, val = genrec.topk_rows(torch.from_numpy(s).to(dev), K)
         idx, val = idx.cpu().numpy(), val.cpu().numpy()
@@ -105,14 +130,14 @@ def test_random_shapes(dev, oracle_mod, case):
             assert np.array_equal(idx[r], ri), ("topk idx", r)
             assert np.array_equal(val[r], rv.astype(np.float32)), ("topk val", r)
     else:
-        B = int(rng.choice([1, 7, 64, 300]))
-        D = int(rng.integers(1, 65)) * 8
-        M = int(rng.choice([1, 70, 5000, 70000]))
+        B = int(rng.choice(sz["ce_B"]))
+        D = sz["ce_D"](rng)
+        M = int(rng.choice(sz["ce_M"]))
         if B * M * D > 2e9:
             M = max(1, int(2e9 // (B * D)))
         seed = int(rng.integers(0, 1 << 30))
         weighted = bool(rng.random() < 0.7)
-        print("case %d ce B=%d D=%d M=%d weighted=%s seed=%d" % (case, B, D, M, weighted, seed), flush=True)
+        print("case %s %d ce B=%d D=%d M=%d weighted=%s seed=%d" % (family, case, B, D, M, weighted, seed), flush=True)
         d = synth.make_dense(B, D, M, seed=seed)
         labels = synth.gen_labels(B, M, seed)
         w = synth.gen_weights(B, seed) if weighted else None
@@ -133,4 +158,4 @@ def test_random_shapes(dev, oracle_mod, case):
         while sp < 8 and tiles * sp < 512:
             sp *= 2
         parity.check_ce(g, ref, d["E"], d["H"], oracle.widen, mcp // sp + -(-M // chunk) + sp, bp,
-                        where="sweep %d" % case)
+                        where="sweep %s %d" % (family, case))
