@@ -211,7 +211,9 @@ int genrec_ce_backward(const void* H, const void* E, int B, int D, int64_t M,
 /* Introspection: writes into buf (at most len bytes, NUL-terminated) a JSON
  * object describing how genrec_score_lse_topk would run these sizes: the
  * scoring path ("mfma" or "stream"), whether the sampled-threshold pre-pass
- * runs, the work split and the workspace size.  Host-only, touches no device.
+ * runs, the work split, which build of the top-K merge runs ("merge_small":
+ * the one with the smaller LDS gather, for few expected candidates per user)
+ * and the workspace size.  Host-only, touches no device.
  * Returns GENREC_OK or the status the compute call would return for the
  * shape. */
 int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, size_t len);
