@@ -193,3 +193,25 @@ def test_ce_chunk_bounds(L):
     FAKE = 1 << 20
     assert L.genrec_ce_backward(FAKE, FAKE, 3_000_000, 8, 1000, FAKE, None, FAKE, FAKE, FAKE, 1, FAKE,
                                 1 << 40, None) == UNSUPPORTED
+
+
+def test_plans_at_the_largest_supported_sizes(L):
+    """Workspace and plan arithmetic at the edge of the supported shapes stays
+    in 64-bit range and consistent (no launch)."""
+    import torch
+    M = (1 << 31) - 1
+    # dense: the candidate regions alone are B x 256 ceil(M / 256) keys of 8 bytes
+    w = L.genrec_score_lse_topk_workspace(4, 8, M, 1024, 0)
+    assert w >= 4 * ((M + 255) // 256 * 256) * 8
+    p = genrec.describe_plan(4, 8, M, 1024, torch.bfloat16)
+    assert p["workspace"] == w and p["path"] == "mfma" and p["sample"] == 1
+    assert L.genrec_score_lse_topk_workspace(1, 16384, M, 1, 1) >= M * 8   # fp32, VALU path
+    assert L.genrec_score_lse_topk_workspace(4, 65536, 100, 10, 0) > 0     # GENREC_DMAX
+    assert L.genrec_score_lse_topk_workspace(4, 65544, 100, 10, 0) == 0    # D past the maximum
+    # candidates: 8 bytes per entry plus the hot head's per-item arrays
+    nnz = (1 << 33) + 5
+    c = L.genrec_score_candidates_topk_workspace(4096, 2048, M, nnz, 100, 0)
+    assert c >= nnz * 8 + 2 * 4 * M
+    # cross-entropy: the chunk shrinks so that each blocked operand stays under 1 GiB
+    assert L.genrec_ce_backward_workspace(1 << 21, 8, M) > 0
+    assert L.genrec_ce_backward_workspace((1 << 21) + 1, 8, M) == 0
