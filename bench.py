@@ -285,8 +285,14 @@ def bench_ce(args):
         "kernels_ms": per_step,
         "kernel_tflops": tf,
         "roofline": {"bound": "mfma", "achieved": tf[dom], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf[dom] / MFMA_BF16_PEAK_TFLOPS, "kernel": kname, "kernel_ms": per_step[dom],
-                     "traffic": None},
+                     "frac": tf[dom] / MFMA_BF16_PEAK_TFLOPS, "kernel": kname,
+                     # one launch per catalog chunk: the mean launch, as the traffic figure
+                     "kernel_ms": per_step[dom] * args.steps / kern[dom][0],
+                     "launches_per_step": kern[dom][0] / args.steps,
+                     # counters taken with the default fp32 dE
+                     "traffic": traffic_from_profile({"grad_tiles": "mfma_score_kernel_3",
+                                                      "grad_E": "mfma_score_kernel_4"}.get(dom, "none"), "ce")
+                     if args.de_dtype == "f32" else None},
     }
     if not args.no_cpu_baseline:
         del H, E, dE, wsb
