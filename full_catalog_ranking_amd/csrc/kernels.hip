@@ -23,8 +23,10 @@
 //                      a rank merge), written sorted.
 //  cand_plan_kernel    CSR offsets -> work list of fixed-size list pieces.
 //  hot_*_kernel        candidate lists: the most-listed rows, scored densely.
-//  topk_chunk_kernel,  batched top-K of dense score rows (a beam step).
-//  topk_merge_rows_kernel
+//  topk_chunk_kernel,  batched top-K of dense score rows (a beam step) by
+//  topk_merge_rows_kernel  histogram narrowing per chunk, then per row.
+//  topk_seg_kernel,    the same for long rows with many segments: register-
+//  topk_rowmerge_kernel  resident radix selection per segment, then per row.
 //  mfma_score_kernel   modes 3-5 and ce_*, transpose, sum_splits kernels: the
 //                      catalog cross-entropy (GenRec explainer page, "two
 //                      objectives and reward-weighted ranking"): forward = the
@@ -1537,6 +1539,224 @@ __global__ __launch_bounds__(SEL_NT) void topk_merge_rows_kernel(TopkRowsArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Batched top-K by register-resident radix selection
+// ---------------------------------------------------------------------------
+// A block of TK_NT threads holds up to TK_NT * V keys in registers (V per
+// thread; slot j of thread t is key j * TK_NT + t) and narrows down the k-th
+// largest by deciding its bits from the top.  For each bit it counts the keys
+// that agree with the bits decided so far and have this bit set (a ballot
+// and a scalar popcount per key and wave, one barrier to add the four waves'
+// counts) and sets the bit when they are at least the k still wanted.  It
+// stops as soon as the keys that agree with the decided bits (the group) are
+// all wanted, or are at most TK_SMALL: the group is then ranked in LDS by
+// plain comparison.  Only when more than TK_SMALL keys share one score word
+// is the index word decided the same way.  Per bit that is two vector
+// instructions per key, with no atomics.  Keys are the 64-bit ranking keys
+// (score word, inverted column) of the dense path, so the order is the same.
+constexpr int TK_NT = 256;
+constexpr int TK_V = 64;              // keys per thread of a row segment
+constexpr int TK_SEG = TK_NT * TK_V;  // columns per segment block
+constexpr int TK_MV = 32;             // keys per thread of the row merge
+constexpr int TK_SMALL = 256;         // group size ranked by comparison
+static_assert(TK_SEG == kTopkSeg && TK_NT * TK_MV == kTopkMergeKeys, "the plan's segment and merge sizes");
+static_assert(TK_NT == SEL_NT, "the final sort is the selection's block sort");
+
+struct TkShared {
+    int cnt[2][TK_NT / kWave];
+    int wsel[TK_NT / kWave];
+    uint64_t grp[TK_SMALL];        // the group, when it is ranked by comparison
+    uint64_t sel[GENREC_KMAX];     // the k selected keys
+    uint64_t sorted[GENREC_KMAX];  // the same in ranking order
+};
+
+// Block sum of one wave-uniform count per wave.  `par` alternates between
+// calls: a wave that has passed this call's barrier writes the other slot
+// next time, while slow waves may still be reading this one.
+__device__ __forceinline__ int tk_block_sum(int c, int& par, TkShared& sh) {
+    if ((threadIdx.x & 63) == 0) sh.cnt[par][threadIdx.x >> 6] = c;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int q = 0; q < TK_NT / kWave; ++q) t += sh.cnt[par][q];
+    par ^= 1;
+    return t;
+}
+
+// Bit decisions from the top for the krem-th largest of the words w(j) over
+// the slots with in(j) (m of them, m >= krem >= 1), until the group -- the
+// slots whose word agrees with the decided bits -- is wholly wanted
+// (m == krem) or holds at most `small` slots.  On return `mask` marks the
+// decided bits, P holds them (zeros elsewhere), m is the group's size and
+// krem the number wanted from it; the slots above the group are all wanted.
+template <int V, class W, class In>
+__device__ __forceinline__ void tk_radix(const W& w, const In& in, int small, int& m, int& krem, uint32_t& P,
+                                         uint32_t& mask, int& par, TkShared& sh) {
+    P = 0;
+    mask = 0;
+    for (int b = 31; b >= 0 && m != krem && m > small; --b) {
+        const uint32_t t = (P >> b) | 1u;  // the decided bits, then bit b set
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            c += __popcll(__ballot(in(j) && (w(j) >> b) == t));
+            // a few compare results live at a time (not all V in scalar registers)
+            if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+        }
+        c = tk_block_sum(c, par, sh);
+        mask |= 1u << b;
+        if (c >= krem) {
+            P |= 1u << b;
+            m = c;
+        } else {
+            krem -= c;
+            m -= c;
+        }
+    }
+}
+
+// Slots with pred(j) to dst[0..), key(j) each, in no particular order (at most
+// cap written); returns how many there are.
+template <int V, class Pred, class Key>
+__device__ __forceinline__ int tk_compact(const Pred& pred, const Key& key, uint64_t* dst, int cap, TkShared& sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        c += __popcll(__ballot(pred(j)));
+        if ((j & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    if (lane == 0) sh.wsel[w] = c;
+    __syncthreads();
+    int base = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < TK_NT / kWave; ++q) {
+        base += q < w ? sh.wsel[q] : 0;
+        total += sh.wsel[q];
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        const bool s = pred(j);
+        const uint64_t bm = __ballot(s);
+        const int pos = base + __popcll(bm & ((1ull << lane) - 1ull));
+        if (s && pos < cap) dst[pos] = key(j);
+        base += __popcll(bm);
+    }
+    __syncthreads();
+    return total;
+}
+
+// The k largest of the valid keys (n_valid >= k >= 1) into sh.sel[0..k), in
+// no particular order.  hi(j) / lo(j): the key words of slot j; valid(j): the
+// slot holds a key.  Invalid slots must have hi(j) == 0, which never agrees
+// with a decided set bit, so the score-word decisions need no validity test.
+template <int V, class Hi, class Lo, class Valid>
+__device__ __forceinline__ void tk_select(const Hi& hi, const Lo& lo, const Valid& valid, int n_valid, int k,
+                                          TkShared& sh) {
+    int par = 0;
+    int m = n_valid, krem = k;
+    uint32_t P, pmask;
+    tk_radix<V>(hi, [](int) { return true; }, TK_SMALL, m, krem, P, pmask, par, sh);
+    auto key = [&](int j) { return ((uint64_t)hi(j) << 32) | lo(j); };
+    if (m == krem) {
+        tk_compact<V>([&](int j) { return valid(j) && (hi(j) & pmask) >= P; }, key, sh.sel, GENREC_KMAX, sh);
+    } else if (m <= TK_SMALL) {
+        // the keys above the group, then the krem largest of the group
+        const int above = k - krem;
+        tk_compact<V>([&](int j) { return valid(j) && (hi(j) & pmask) > P; }, key, sh.sel, above, sh);
+        tk_compact<V>([&](int j) { return valid(j) && (hi(j) & pmask) == P; }, key, sh.grp, TK_SMALL, sh);
+        block_rank_place(sh.grp, m, sh.sel + above, krem);
+        __syncthreads();
+    } else {
+        // more than TK_SMALL keys share the score word P (every bit decided):
+        // the krem lowest columns among them, i.e. the largest index words
+        uint32_t Q, qmask;
+        tk_radix<V>(lo, [&](int j) { return valid(j) && hi(j) == P; }, 0, m, krem, Q, qmask, par, sh);
+        tk_compact<V>([&](int j) { return valid(j) && (hi(j) > P || (hi(j) == P && (lo(j) & qmask) >= Q)); }, key,
+                      sh.sel, GENREC_KMAX, sh);
+    }
+}
+
+// sh.sel[0..k) in ranking order to the row's outputs, padded to K.
+__device__ void tk_emit(int k, int K, TkShared& sh, int32_t* oidx, float* osc) {
+    if (k <= 256) block_rank_place(sh.sel, k, sh.sorted, k);
+    else block_sort_into(sh.sel, k, sh.sorted);
+    __syncthreads();
+    for (int i = threadIdx.x; i < K; i += TK_NT) {
+        if (i < k) {
+            const uint64_t key = sh.sorted[i];
+            oidx[i] = (int32_t)key_id(key);
+            osc[i] = key_score(key);
+        } else {
+            oidx[i] = -1;
+            osc[i] = -INFINITY;
+        }
+    }
+}
+
+// Block (r, s): the top-K keys of segment s (TK_SEG columns) of row r for the
+// row merge, in no particular order (all K places written, zero keys past the
+// segment's count).
+__global__ __launch_bounds__(TK_NT) void topk_seg_kernel(TopkRowsArgs a) {
+    __shared__ TkShared sh;
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x / a.nchunk, s = blockIdx.x - r * a.nchunk;
+    const int64_t c0 = (int64_t)s * TK_SEG;
+    const int n = (int)min((int64_t)TK_SEG, a.N - c0);
+    const float* row = a.scores + (int64_t)r * a.ld + c0;
+    uint32_t hv[TK_V];
+#pragma unroll
+    for (int j = 0; j < TK_V; ++j) {
+        const int e = j * TK_NT + tid;
+        hv[j] = e < n ? order_key(row[e]) : 0u;
+    }
+    // Opaque from here on: otherwise the compiler carries "slot past the row
+    // => word 0" into every bit decision and keeps all V row-end masks live
+    // in scalar registers (spilled) across the whole selection.
+#pragma unroll
+    for (int j = 0; j < TK_V; ++j) asm volatile("" : "+v"(hv[j]));
+    const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)(c0 + tid);  // index word of slot 0
+    const int k = min(a.K, n);
+    tk_select<TK_V>([&](int j) { return hv[j]; }, [&](int j) { return lo0 - (uint32_t)(j * TK_NT); },
+                    [&](int j) {
+                        // recomputed at each use (an opaque copy of the thread
+                        // index), not kept as V live masks across the selection
+                        int t = tid;
+                        asm volatile("" : "+v"(t));
+                        return j * TK_NT + t < n;
+                    },
+                    n, k, sh);
+    uint64_t* dst = a.part + ((int64_t)r * a.nchunk + s) * a.K;
+    for (int i = tid; i < a.K; i += TK_NT) dst[i] = i < k ? sh.sel[i] : 0ull;
+}
+
+// Block r: the top-K of the row's segment results (nchunk * K <= TK_NT * TK_MV
+// keys, zero keys in unused places).
+__global__ __launch_bounds__(TK_NT) void topk_rowmerge_kernel(TopkRowsArgs a) {
+    __shared__ TkShared sh;
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x;
+    const int total = a.nchunk * a.K;
+    const uint64_t* src = a.part + (int64_t)r * total;
+    uint32_t kh[TK_MV], kl[TK_MV];
+#pragma unroll
+    for (int j = 0; j < TK_MV; ++j) {
+        const int q = j * TK_NT + tid;
+        const uint64_t key = q < total ? src[q] : 0ull;
+        kh[j] = (uint32_t)(key >> 32);
+        kl[j] = (uint32_t)key;
+        asm volatile("" : "+v"(kh[j]), "+v"(kl[j]));  // as in the segment kernel
+    }
+    // keys held: K from every segment but the last, which holds min(K, its length)
+    const int64_t n_last = a.N - (int64_t)(a.nchunk - 1) * TK_SEG;
+    const int n_valid = (a.nchunk - 1) * a.K + (int)min((int64_t)a.K, n_last);
+    const int k = (int)min((int64_t)a.K, a.N);
+    // a real key is never zero (its index word is at least 2^31)
+    tk_select<TK_MV>([&](int j) { return kh[j]; }, [&](int j) { return kl[j]; },
+                     [&](int j) { return (kh[j] | kl[j]) != 0u; }, n_valid, k, sh);
+    tk_emit(k, a.K, sh, a.out_idx + (int64_t)r * a.K, a.out_scores + (int64_t)r * a.K);
+}
+
+// ---------------------------------------------------------------------------
 // Candidate lists: CSR offsets -> pieces of at most CAND_PIECE entries
 // ---------------------------------------------------------------------------
 constexpr int PL_NT = 1024;
@@ -2019,6 +2239,13 @@ hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s) {
 
 hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s) {
     if (a.R <= 0) return hipSuccess;
+    if (a.reg) {
+        if (a.C != TK_SEG || a.K > GENREC_KMAX || a.nchunk < 2 || (int64_t)a.nchunk * a.K > TK_NT * TK_MV)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(topk_seg_kernel, dim3((unsigned)((int64_t)a.R * a.nchunk)), dim3(TK_NT), 0, s, a);
+        hipLaunchKernelGGL(topk_rowmerge_kernel, dim3(a.R), dim3(TK_NT), 0, s, a);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)((int64_t)a.R * a.nchunk)), dim3(SEL_NT), 0, s, a);
     if (a.nchunk > 1) hipLaunchKernelGGL(topk_merge_rows_kernel, dim3(a.R), dim3(SEL_NT), 0, s, a);
     return hipGetLastError();

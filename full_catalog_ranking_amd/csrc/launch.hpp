@@ -215,6 +215,7 @@ struct TopkRowsArgs {
     int64_t C;            // columns per chunk
     int nchunk;           // chunks per row (1: no merge pass)
     uint64_t* part;       // nchunk > 1: [R][nchunk][K] chunk results
+    int reg;              // register-resident selection: chunks of kTopkSeg columns, nchunk >= 2, nchunk * K <= kTopkMergeKeys
 };
 
 hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s);

@@ -86,12 +86,18 @@ def test_candidate_argument_errors(L):
     assert t(FAKE, 2, 100, 99, 5, FAKE, FAKE, None, 0, None) == INVALID        # ld < N
     assert t(FAKE, 2, 100, 100, 0, FAKE, FAKE, None, 0, None) == INVALID       # K = 0
     assert t(FAKE, 2, 100, 100, 2000, FAKE, FAKE, None, 0, None) == UNSUPPORTED  # K > KMAX
-    # one pass up to 4,096 columns; longer rows need the chunk results' workspace
+    # histogram narrowing: one pass up to 4,096 columns; longer rows need the
+    # chunk results' workspace
     assert L.genrec_topk_rows_workspace(8, 4096, 128) == 0
     assert L.genrec_topk_rows_workspace(8, 16384, 128) == 8 * 4 * 128 * 8
     need = L.genrec_topk_rows_workspace(8, 512 * 512, 512)
     assert need > 0 and need % (8 * 8 * 512) == 0 and need // (8 * 8 * 512) * 512 <= 6144
     assert t(FAKE, 8, 512 * 512, 512 * 512, 512, FAKE, FAKE, None, 0, None) == WORKSPACE
+    # register-resident selection: rows of >= 2 segments of 16,384 columns whose
+    # K keys fit the 8,192-key row merge, with >= 512 segment blocks in all
+    assert L.genrec_topk_rows_workspace(64, 512 * 512, 512) == 64 * 16 * 512 * 8
+    assert L.genrec_topk_rows_workspace(8, 64 * 16384, 128) == 8 * 64 * 128 * 8
+    assert L.genrec_topk_rows_workspace(8, 64 * 16384, 129) % (8 * 8 * 129) == 0  # 64 x 129 keys: histogram chunks
     m = L.genrec_score_lse_topk_masked
     ws = L.genrec_score_lse_topk_workspace(4, 64, 100, 10, 0)
     assert m(FAKE, FAKE, 0, 4, 64, 100, 10, None, 0, FAKE, FAKE, FAKE, FAKE, ws, None) == INVALID   # no mask

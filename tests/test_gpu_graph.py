@@ -108,13 +108,15 @@ def test_candidate_graph_replays(dev):
 
 def test_topk_rows_and_ce_graph_replays(dev):
     from full_catalog_ranking_amd import genrec
-    R, N, K = 64, 40_000, 128
-    S = torch.from_numpy(synth.gen_scores(R, N, seed=6, decimals=2)).to(dev)
-    need = genrec.lib().genrec_topk_rows_workspace(R, N, K)
-    tws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    tout = (torch.empty((R, K), dtype=torch.int32, device=dev), torch.empty((R, K), dtype=torch.float32, device=dev))
-    print("  graph topk_rows R=%d N=%d K=%d" % (R, N, K), flush=True)
-    _check_replays(lambda: genrec.topk_rows(S, K, out=tout, workspace=tws), dev, lambda: torch.cumsum(S, 1))
+    # histogram chunks, then register-resident segments (64 x 8 segment blocks)
+    for R, N, K in [(64, 40_000, 128), (64, 8 * 16_384, 128)]:
+        S = torch.from_numpy(synth.gen_scores(R, N, seed=6, decimals=2)).to(dev)
+        need = genrec.lib().genrec_topk_rows_workspace(R, N, K)
+        tws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        tout = (torch.empty((R, K), dtype=torch.int32, device=dev),
+                torch.empty((R, K), dtype=torch.float32, device=dev))
+        print("  graph topk_rows R=%d N=%d K=%d" % (R, N, K), flush=True)
+        _check_replays(lambda: genrec.topk_rows(S, K, out=tout, workspace=tws), dev, lambda: torch.cumsum(S, 1))
 
     B, D, M = 70, 64, 70_000  # two catalog chunks in the backward
     d = synth.make_dense(B, D, M, seed=7)

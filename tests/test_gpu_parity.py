@@ -398,6 +398,13 @@ def test_candidates_equal_full_catalog(dev, oracle_mod):
     (1, 1, 1, None, 0),
     (2, 100_000, 50, 2, 5),           # seven chunks merged, ties across chunks
     (3, 16_385, 100, None, 0),        # a one-column last chunk
+    (2, 16_384, 1024, 1, 0),          # K = KMAX over four chunks, heavy ties
+    (2, 20_000, 512, 0, 0),           # a handful of distinct scores: ties decided by column
+    (2, 300_000, 1024, 2, 0),
+    # register-resident selection (>= 512 segment blocks of 16,384 columns)
+    (40, 13 * 16_384, 512, None, 0),
+    (33, 16 * 16_384 + 5, 256, 0, 3),  # whole-number scores: hundreds share a score; a 5-column last segment
+    (520, 2 * 16_384, 1024, 2, 0),    # K = KMAX, the row merge's 2,048 keys
 ])
 def test_topk_rows(dev, oracle_mod, R, N, K, decimals, ld_pad):
     from full_catalog_ranking_amd import genrec
@@ -534,14 +541,15 @@ def test_poisoned_workspaces_and_outputs(dev, oracle_mod):
                                      workspace=ws, out=outs(B, K))[:3]
     parity.check_cand(tuple(x.cpu().numpy() for x in g), oracle_mod.cand(d["H"], d["E"], off, ids, K), off, ids,
                       where="poisoned cand")
-    # batched top-K rows of several chunks
-    R, N, K = 5, 50_000, 200
-    S = synth.gen_scores(R, N, seed=78, decimals=3)
-    need = genrec.lib().genrec_topk_rows_workspace(R, N, K)
-    o = outs(R, K)[:2]
-    print("  poisoned topk_rows R=%d N=%d K=%d" % (R, N, K), flush=True)
-    idx, val = genrec.topk_rows(torch.from_numpy(S).to(dev), K, out=o, workspace=poison(max(need, 1)))
-    idx, val = idx.cpu().numpy(), val.cpu().numpy()
-    for r in range(R):
-        ri, rv = oracle_mod.topk_row(S[r].astype(np.float64), K)
-        assert np.array_equal(idx[r], ri) and np.array_equal(val[r], rv.astype(np.float32))
+    # batched top-K rows of several chunks (histogram narrowing), then of many
+    # segments (register-resident selection, a 3-column last segment)
+    for R, N, K in [(5, 50_000, 200), (40, 13 * 16_384 + 3, 200)]:
+        S = synth.gen_scores(R, N, seed=78, decimals=3)
+        need = genrec.lib().genrec_topk_rows_workspace(R, N, K)
+        o = outs(R, K)[:2]
+        print("  poisoned topk_rows R=%d N=%d K=%d" % (R, N, K), flush=True)
+        idx, val = genrec.topk_rows(torch.from_numpy(S).to(dev), K, out=o, workspace=poison(max(need, 1)))
+        idx, val = idx.cpu().numpy(), val.cpu().numpy()
+        for r in range(R):
+            ri, rv = oracle_mod.topk_row(S[r].astype(np.float64), K)
+            assert np.array_equal(idx[r], ri) and np.array_equal(val[r], rv.astype(np.float32))
