@@ -2239,6 +2239,7 @@ hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s) {
 
 hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s) {
     if (a.R <= 0) return hipSuccess;
+    if ((int64_t)a.R * a.nchunk > 2147483647) return hipErrorInvalidValue;  // one block per (row, chunk)
     if (a.reg) {
         if (a.C != TK_SEG || a.K > GENREC_KMAX || a.nchunk < 2 || (int64_t)a.nchunk * a.K > TK_NT * TK_MV)
             return hipErrorInvalidValue;
