@@ -1486,8 +1486,8 @@ struct PartialSrc {
 
 // The k largest keys of a source in ranking order, written out (or, for an
 // intermediate chunk, as raw keys).
-template <class Src>
-__device__ void topk_emit(const Src& src, int k, int K, SelShared& sh, int32_t* oidx, float* osc, uint64_t* okeys) {
+template <class Src, class Sh>
+__device__ void topk_emit(const Src& src, int k, int K, Sh& sh, int32_t* oidx, float* osc, uint64_t* okeys) {
     const int tid = threadIdx.x;
     if (k > 0) {
         block_select<true>(src, k, sh);
@@ -1515,9 +1515,12 @@ __device__ void topk_emit(const Src& src, int k, int K, SelShared& sh, int32_t* 
 }
 
 // Block (r, c): the top-K of chunk c of row r -- the final result when the row
-// is one chunk, else its keys for the merge.
+// is one chunk, else its keys for the merge.  GCAP: the selection's LDS
+// gather; the smaller build fits about twice the blocks on a CU, which pays
+// for small K (width-128 beam step 51 -> 43 us) and not for K of 512 or more.
+template <int GCAP>
 __global__ __launch_bounds__(SEL_NT) void topk_chunk_kernel(TopkRowsArgs a) {
-    __shared__ SelShared sh;
+    __shared__ SelSharedT<GCAP> sh;
     const int r = blockIdx.x / a.nchunk, c = blockIdx.x - r * a.nchunk;
     const int64_t c0 = (int64_t)c * a.C;
     const int64_t n = min(a.C, a.N - c0);
@@ -2247,7 +2250,9 @@ hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(topk_rowmerge_kernel, dim3(a.R), dim3(TK_NT), 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)((int64_t)a.R * a.nchunk)), dim3(SEL_NT), 0, s, a);
+    const dim3 grid((unsigned)((int64_t)a.R * a.nchunk));
+    if (a.K <= 256) hipLaunchKernelGGL((topk_chunk_kernel<MG_GCAP_SMALL>), grid, dim3(SEL_NT), 0, s, a);
+    else hipLaunchKernelGGL((topk_chunk_kernel<SEL_GCAP>), grid, dim3(SEL_NT), 0, s, a);
     if (a.nchunk > 1) hipLaunchKernelGGL(topk_merge_rows_kernel, dim3(a.R), dim3(SEL_NT), 0, s, a);
     return hipGetLastError();
 }
