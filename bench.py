@@ -216,9 +216,11 @@ def bench_beam(args):
         "ms_per_step_min": mn, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload, "R": R, "N": N, "K": K},
+        # the whole call, both of its passes (selection per chunk or segment,
+        # then per row), timed with events on the stream they run on
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "kernel": "topk_rows_kernel", "kernel_ms": ms,
-                     "traffic": traffic_from_profile("topk_rows_kernel", args.workload)},
+                     "frac": achieved / HBM_PEAK_GBS, "kernel": "genrec_topk_rows (both passes)", "kernel_ms": ms,
+                     "traffic": None},
     }
     if not args.no_cpu_baseline:
         from oracle import oracle
