@@ -238,7 +238,7 @@ constexpr int64_t kTopkGather = 6144;  // the merge kernel's LDS gather capacity
 // keys (at most kTopkMergeKeys).  Measured on MI355X it beats the histogram
 // narrowing on long rows with many segments (64 rows x 262,144, K 512: 0.18
 // against 0.22 ms) but not on one segment per row (256 x 16,384, K 128: 65
-// against 52 us), so it is used only with at least kTopkRegMinBlocks segment
+// against 42 us), so it is used only with at least kTopkRegMinBlocks segment
 // blocks; other shapes take the histogram-narrowing kernels.
 constexpr int64_t kTopkSeg = 16384;
 constexpr int64_t kTopkMergeKeys = 8192;
