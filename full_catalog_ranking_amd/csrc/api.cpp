@@ -559,6 +559,19 @@ size_t genrec_ce_backward_workspace(int B, int D, int64_t M) {
     return p.ok ? p.bwd_total : 0;
 }
 
+int genrec_describe_ce_plan(int B, int D, int64_t M, char* buf, size_t len) {
+    if (B <= 0 || D <= 0 || M <= 0 || !buf || len == 0) return GENREC_ERR_INVALID_ARG;
+    if (M >= ((int64_t)1 << 31) || D > GENREC_DMAX) return GENREC_ERR_UNSUPPORTED;
+    const CePlan p = plan_ce(B, D, M);
+    if (!p.ok) return GENREC_ERR_UNSUPPORTED;
+    snprintf(buf, len,
+             "{\"chunk\":%lld,\"Mcp\":%lld,\"n_chunks\":%lld,\"Bp\":%lld,\"splits\":%d,"
+             "\"depth_h\":%lld,\"depth_e\":%lld,\"workspace\":%zu}",
+             (long long)p.chunk, (long long)p.Mcp, (long long)p.n_chunks, (long long)p.Bp, p.splits,
+             (long long)ce_depth_h(p), (long long)ce_depth_e(p), p.bwd_total);
+    return GENREC_OK;
+}
+
 int genrec_ce_forward_profiled(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels,
                                const float* weights, float* out_loss, float* out_lse, void* workspace,
                                size_t workspace_bytes, void* stream, genrec_profiler* prof) {

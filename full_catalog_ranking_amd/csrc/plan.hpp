@@ -337,4 +337,11 @@ inline CePlan plan_ce(int B, int D, int64_t M) {
     return p;
 }
 
+// Longest chains of fp32 additions into one output of the backward's two
+// products: a dH entry sums Mcp / splits products within a split, is added
+// into its partial once per chunk, and the partials are summed at the end; a
+// dE entry sums the Bp (padded) users' products.
+inline int64_t ce_depth_h(const CePlan& p) { return p.Mcp / p.splits + p.n_chunks + p.splits; }
+inline int64_t ce_depth_e(const CePlan& p) { return p.Bp; }
+
 }  // namespace genrec

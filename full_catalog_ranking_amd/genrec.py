@@ -31,6 +31,7 @@ EXPORTED = (
     "genrec_topk_rows",
     "genrec_topk_rows_workspace",
     "genrec_describe_plan",
+    "genrec_describe_ce_plan",
     "genrec_status_string",
     "genrec_version",
     "genrec_profiler_create",
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.genrec_get_rescued_users.restype = I
         L.genrec_describe_plan.argtypes = [I, I, I64, I, I, ctypes.c_char_p, SZ]
         L.genrec_describe_plan.restype = I
+        L.genrec_describe_ce_plan.argtypes = [I, I, I64, ctypes.c_char_p, SZ]
+        L.genrec_describe_ce_plan.restype = I
         L.genrec_status_string.argtypes = [I]
         L.genrec_status_string.restype = ctypes.c_char_p
         L.genrec_version.restype = I
@@ -145,6 +148,16 @@ def describe_plan(B: int, D: int, M: int, K: int, dtype: torch.dtype) -> dict:
     st = lib().genrec_describe_plan(B, D, M, K, dtype_code(dtype), buf, 512)
     if st != 0:
         raise GenrecError(st, "genrec_describe_plan")
+    return json.loads(buf.value.decode())
+
+
+def describe_ce_plan(B: int, D: int, M: int) -> dict:
+    """The cross-entropy backward's plan: chunking, splits and the longest
+    fp32 addition chains of its two gradient products (depth_h, depth_e)."""
+    buf = ctypes.create_string_buffer(512)
+    st = lib().genrec_describe_ce_plan(B, D, M, buf, 512)
+    if st != 0:
+        raise GenrecError(st, "genrec_describe_ce_plan")
     return json.loads(buf.value.decode())
 
 

@@ -218,6 +218,20 @@ int genrec_ce_backward(const void* H, const void* E, int B, int D, int64_t M,
  * shape. */
 int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, size_t len);
 
+/* Introspection of the cross-entropy backward's plan for these sizes: writes
+ * into buf (at most len bytes, NUL-terminated) a JSON object with the catalog
+ * rows per backward chunk ("chunk", "Mcp" = the chunk rounded up to 256),
+ * the number of chunks, the users padded to 32 ("Bp"), the reduction splits
+ * of the dH product ("splits"), and the longest chains of fp32 additions into
+ * one output of the two gradient products: "depth_h" = Mcp / splits (one
+ * split's reduction) + n_chunks (accumulation over the chunks) + splits (the
+ * final sum of the partials), "depth_e" = Bp (the reduction over the padded
+ * users).  These bound the products' rounding (depth * 2^-24 relative).
+ * Host-only.  Returns GENREC_OK, GENREC_ERR_INVALID_ARG for non-positive
+ * sizes or a null / empty buf, GENREC_ERR_UNSUPPORTED where
+ * genrec_ce_backward_workspace() returns 0. */
+int genrec_describe_ce_plan(int B, int D, int64_t M, char* buf, size_t len);
+
 /*
  * Kernel-level timing with HIP events.  A profiler records an event pair
  * around every kernel that the *_profiled entry points launch, without

@@ -221,3 +221,19 @@ def test_plans_at_the_largest_supported_sizes(L):
     # cross-entropy: the chunk shrinks so that each blocked operand stays under 1 GiB
     assert L.genrec_ce_backward_workspace(1 << 21, 8, M) > 0
     assert L.genrec_ce_backward_workspace((1 << 21) + 1, 8, M) == 0
+
+
+def test_ce_plan_query(L):
+    """The backward's plan as the library reports it: consistent with its
+    workspace query, and the addition depths follow from chunking and splits."""
+    for B, D, M in ((1024, 4096, 1_000_000), (3, 64, 1000), (8, 16384, 36_000), (300, 200, 5000)):
+        p = genrec.describe_ce_plan(B, D, M)
+        assert p["workspace"] == L.genrec_ce_backward_workspace(B, D, M)
+        assert p["Mcp"] % 256 == 0 and p["Mcp"] >= p["chunk"] and p["n_chunks"] == -(-M // p["chunk"])
+        assert p["Bp"] == -(-B // 32) * 32 and p["splits"] in (1, 2, 4, 8)
+        assert p["depth_h"] == p["Mcp"] // p["splits"] + p["n_chunks"] + p["splits"]
+        assert p["depth_e"] == p["Bp"]
+    buf = ctypes.create_string_buffer(64)
+    assert L.genrec_describe_ce_plan(0, 64, 100, buf, 64) == INVALID
+    assert L.genrec_describe_ce_plan(4, 64, 100, None, 64) == INVALID
+    assert L.genrec_describe_ce_plan(4, 64, 1 << 31, buf, 64) == UNSUPPORTED

@@ -45,17 +45,11 @@ def run_ce(d, labels, weights, dev, backward=True, de_dtype=None):
 
 
 def _depths(B, D, M):
-    """Longest fp32 addition chains of the two products (see parity.check_ce)."""
-    bp = -(-B // 32) * 32
-    cap = (1 << 30) // 2 // max(D, bp) // 256 * 256  # blocked operands stay under 1 GiB
-    chunk = min(M, 65536, cap)
-    mcp = -(-chunk // 256) * 256
-    tiles = -(-B // 256) * -(-D // 256)
-    splits = 1
-    while splits < 8 and tiles * splits < 256:
-        splits *= 2
-    n_chunks = -(-M // chunk)
-    return mcp // splits + n_chunks + splits, -(-B // 32) * 32
+    """Longest fp32 addition chains of the two products, from the library's own
+    plan (see parity.check_ce)."""
+    from full_catalog_ranking_amd import genrec
+    p = genrec.describe_ce_plan(B, D, M)
+    return p["depth_h"], p["depth_e"]
 
 
 @pytest.mark.parametrize("B,D,M,seed,bad,weighted", [

@@ -80,11 +80,26 @@ def test_batch_b256_all_users(dev, oracle_mod):
 
 
 def test_large_b1024_sampled_users(dev, oracle_mod):
+    """40 users against the oracle: ten in each of the four 256-user tiles, at
+    tile positions that cover every wave's user columns (64 per wave tile, two
+    32-wide blocks each); their top-K items come from every one of the eight
+    XCD groups of catalog chunks."""
+    from full_catalog_ranking_amd import genrec
     d = synth.make_workload("large")
     g = run_dense(d, d["K"], dev)
-    users = [0, 1, 255, 256, 511, 512, 767, 768, 1000, 1023]
+    offs = [0, 31, 32, 63, 64, 100, 127, 160, 200, 255]
+    users = [256 * t + o for t in range(4) for o in offs]
     ref = oracle_mod.full(d["H"], d["E"], d["K"], users=users)
     parity.check_dense(g, ref, where="large")
+    # chunk c of the main pass runs on XCD group c // (P / 8); every group's
+    # catalog range holds some of the checked users' top-K items
+    P = genrec.describe_plan(d["B"], d["D"], d["M"], d["K"], torch.bfloat16)["P"]
+    assert P % 8 == 0
+    base, rem = divmod(-(-d["M"] // 256), P)  # chunk c = tiles [c base + min(c, rem), ...)
+    starts = np.array([c * base + min(c, rem) for c in range(P)])
+    chunk_of = np.searchsorted(starts, ref["idx"].ravel() // 256, side="right") - 1
+    groups = set((chunk_of // (P // 8)).tolist())
+    assert groups == set(range(8)), groups
     # every user: lse and scores are finite and descending, ids distinct and in range
     idx, sc, ls = g
     assert np.isfinite(ls).all() and (idx >= 0).all() and (idx < d["M"]).all()

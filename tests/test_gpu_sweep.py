@@ -149,13 +149,6 @@ def test_random_shapes(dev, oracle_mod, family, case):
         torch.cuda.synchronize()
         g = (loss.cpu().numpy(), lse.cpu().numpy(), dH.cpu().numpy(), dE.cpu().numpy())
         ref = oracle.ce(d["H"], d["E"], labels, w)
-        bp = -(-B // 32) * 32
-        cap = (1 << 30) // 2 // max(D, bp) // 256 * 256
-        chunk = min(M, 65536, cap)
-        mcp = -(-chunk // 256) * 256
-        tiles = -(-B // 256) * -(-D // 256)
-        sp = 1  # the dH product's reduction splits
-        while sp < 8 and tiles * sp < 512:
-            sp *= 2
-        parity.check_ce(g, ref, d["E"], d["H"], oracle.widen, mcp // sp + -(-M // chunk) + sp, bp,
+        plan = genrec.describe_ce_plan(B, D, M)  # the products' addition depths, from the library
+        parity.check_ce(g, ref, d["E"], d["H"], oracle.widen, plan["depth_h"], plan["depth_e"],
                         where="sweep %s %d" % (family, case))

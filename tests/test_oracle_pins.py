@@ -367,3 +367,124 @@ def test_ce_invariants_and_library(oracle_mod):
     # a subset of users gives the same rows
     rs = oracle_mod.ce(H, E, y, w, users=[5, 0])
     assert np.allclose(rs["dH"], r["dH"][[5, 0]], rtol=0, atol=0) and "dE" not in rs
+
+
+# ---------------------------------------------------------------------------
+# Catalog cross-entropy on bf16 inputs (the precision the GPU entry points take)
+# ---------------------------------------------------------------------------
+def _bf16_decode(bits: int) -> Fraction:
+    """Exact value of a finite bf16 bit pattern from its fields: sign, 8-bit
+    biased exponent, 7-bit fraction (subnormal when the exponent field is 0)."""
+    sign = -1 if bits & 0x8000 else 1
+    ex = (bits >> 7) & 0xFF
+    fr = bits & 0x7F
+    if ex == 0:
+        return sign * Fraction(fr, 128) * Fraction(1, 2 ** 126)
+    return sign * (1 + Fraction(fr, 128)) * (Fraction(2) ** (ex - 127))
+
+
+def test_widen_bf16_every_pattern(oracle_mod):
+    """The oracle's bf16 widening equals the field decode on every finite bit
+    pattern, and torch's own bfloat16 conversion."""
+    torch = pytest.importorskip("torch")
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    bits = bits[finite]
+    got = oracle_mod.widen(bits)
+    ref_torch = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, ref_torch)
+    for b in bits[::97].tolist() + [0x0001, 0x007F, 0x0080, 0x3F80, 0xBF80, 0x7F7F, 0xFF7F, 0x8001]:
+        assert Fraction(float(oracle_mod.widen(np.array([b], dtype=np.uint16))[0])) == _bf16_decode(b), hex(b)
+
+
+def _bf16_grid(rng, shape, k_max=250, e=8):
+    """bf16 bit patterns of k * 2^-e with |k| <= k_max: every value and its
+    neighbours (k +- 2) * 2^-e are exact in bf16 (at most 8 significant bits)."""
+    k = rng.integers(-k_max, k_max + 1, shape)
+    f = (k * 2.0 ** -e).astype(np.float32)
+    u = f.view(np.uint32)
+    assert (u & 0xFFFF == 0).all()
+    return (u >> 16).astype(np.uint16)
+
+
+def _bf16_of(f32):
+    u = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32)
+    assert (u & 0xFFFF == 0).all(), "value not exact in bf16"
+    return (u >> 16).astype(np.uint16)
+
+
+def test_ce_bf16_gradients_match_central_differences(oracle_mod):
+    """On bf16 inputs: dH and dE equal the derivatives of sum_b loss_b, from
+    central differences of the oracle's own forward with steps h and 2h
+    combined by Richardson extrapolation (error O(h^4)), every perturbed input
+    exact in bf16.  No use of the gradient formula."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(21)
+    B, D, M, e = 3, 5, 7, 8
+    h = 2.0 ** -e
+    H = _bf16_grid(rng, (B, D), e=e)
+    E = _bf16_grid(rng, (M, D), e=e)
+    y = rng.integers(0, M, B).astype(np.int32)
+    w = rng.uniform(0.25, 2.0, B)
+    r = oracle_mod.ce(H, E, y, w)
+    total = lambda H_, E_: oracle_mod.ce(H_, E_, y, w, grads=False)["loss"].sum()
+    f32 = lambda X: torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).float().numpy()
+    for X, g, name in ((H, r["dH"], "dH"), (E, r["dE"], "dE")):
+        num = np.zeros_like(g)
+        Xf = f32(X)
+        for idx in np.ndindex(*X.shape):
+            def diff(step):
+                Xp, Xm = Xf.copy(), Xf.copy()
+                Xp[idx] += step
+                Xm[idx] -= step
+                Xp, Xm = _bf16_of(Xp), _bf16_of(Xm)
+                if name == "dH":
+                    return (total(Xp, E) - total(Xm, E)) / (2 * step)
+                return (total(H, Xp) - total(H, Xm)) / (2 * step)
+            num[idx] = (4 * diff(h) - diff(2 * h)) / 3
+        assert np.abs(g).max() > 0.05, "gradient too small to test"
+        assert np.abs(num - g).max() <= 1e-7 * max(1.0, np.abs(g).max()), (name, np.abs(num - g).max())
+
+
+def test_ce_bf16_closed_form_zero_catalog(oracle_mod):
+    """bf16 H, all-zero bf16 catalog: lse = ln M, loss_b = w_b ln M, dH = 0 and
+    dE_i = sum_b w_b (1/M - [i == y_b]) h_b, with h_b from torch's bf16
+    conversion (not the oracle's)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(22)
+    B, D, M = 4, 6, 9
+    Hf = torch.from_numpy(rng.standard_normal((B, D)).astype(np.float32)).to(torch.bfloat16)
+    H = Hf.view(torch.int16).numpy().view(np.uint16)
+    E = np.zeros((M, D), dtype=np.uint16)
+    y = rng.integers(0, M, B).astype(np.int32)
+    w = rng.uniform(0.25, 2.0, B)
+    r = oracle_mod.ce(H, E, y, w)
+    h64 = Hf.double().numpy()
+    assert np.allclose(r["lse"], math.log(M), rtol=0, atol=1e-14)
+    assert np.allclose(r["loss"], w * math.log(M), rtol=1e-14, atol=0)
+    assert np.abs(r["dH"]).max() == 0.0
+    expect = np.zeros((M, D))
+    for b in range(B):
+        for i in range(M):
+            expect[i] += w[b] * ((1.0 / M) - (1.0 if i == y[b] else 0.0)) * h64[b]
+    assert np.allclose(r["dE"], expect, rtol=1e-13, atol=1e-15)
+
+
+def test_ce_bf16_equals_fp32_branch(oracle_mod):
+    """bf16 inputs give bit-identical results to the same values passed as
+    fp32 (converted by torch), whose branch the fp32 pins above cover; also
+    with an ignored label and no weights."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(23)
+    B, D, M = 5, 16, 40
+    Ht = torch.from_numpy(rng.standard_normal((B, D)).astype(np.float32)).to(torch.bfloat16)
+    Et = torch.from_numpy((rng.standard_normal((M, D)) / 4).astype(np.float32)).to(torch.bfloat16)
+    Hb = Ht.view(torch.int16).numpy().view(np.uint16)
+    Eb = Et.view(torch.int16).numpy().view(np.uint16)
+    y = rng.integers(0, M, B).astype(np.int32)
+    y[3] = M  # ignored
+    for w in (rng.uniform(0.25, 2.0, B), None):
+        rb = oracle_mod.ce(Hb, Eb, y, w)
+        rf = oracle_mod.ce(Ht.float().numpy(), Et.float().numpy(), y, w)
+        for k in ("loss", "lse", "S", "G", "dH", "dE"):
+            assert np.array_equal(rb[k], rf[k]), k
