@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <chrono>
 #include <new>
 
 #include "../../include/genrec.h"
@@ -35,6 +37,25 @@ int check_common(const void* H, const void* E, int dtype, int B, int D, int64_t 
 }
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? GENREC_OK : GENREC_ERR_HIP; }
+
+// Per-call tickets of the fused path's arrival words: 40 bits, never 0 or all
+// ones, unique within the process (a counter from a start that differs from
+// run to run, so that a word another process or tensor left in reused memory
+// is unlikely to hold a live ticket).
+uint64_t next_ticket() {
+    constexpr uint64_t kMask = (1ull << 40) - 1;
+    static std::atomic<uint64_t> counter{[] {
+        uint64_t x = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        x ^= (uint64_t)(uintptr_t)&counter;
+        x ^= x >> 31;
+        x *= 0x9E3779B97F4A7C15ull;
+        return x ^ (x >> 29);
+    }()};
+    for (;;) {
+        const uint64_t t = counter.fetch_add(1, std::memory_order_relaxed) & kMask;
+        if (t != 0 && t != kMask) return t;
+    }
+}
 
 template <class T>
 inline T* at(void* ws, size_t off) {
@@ -158,10 +179,11 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
     const DensePlan p = plan_dense(B, D, M, K, dtype);
     snprintf(buf, len,
              "{\"path\":\"%s\",\"sample\":%d,\"stride\":%lld,\"n_sample\":%lld,\"fast\":%d,\"r_fast\":%d,"
-             "\"UT\":%d,\"P\":%d,\"tiles_per_chunk\":%d,\"CH\":%lld,\"merge_small\":%d,\"workspace\":%zu}",
+             "\"UT\":%d,\"P\":%d,\"tiles_per_chunk\":%d,\"CH\":%lld,\"merge_small\":%d,\"fused\":%d,"
+             "\"workspace\":%zu}",
              p.mfma ? "mfma" : "stream", p.sample ? 1 : 0, (long long)p.stride, (long long)p.n_sample,
              p.fast ? 1 : 0, p.r_fast, p.main.UT, p.main.P, p.main.base + (p.main.rem ? 1 : 0),
-             (long long)p.main.CH, p.merge_small ? 1 : 0, p.total);
+             (long long)p.main.CH, p.merge_small ? 1 : 0, p.fused ? 1 : 0, p.total);
     return GENREC_OK;
 }
 
@@ -186,6 +208,37 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     if (!workspace || workspace_bytes < p.total) return GENREC_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
+
+    if (p.fused) {
+        // the whole call in one launch: scoring blocks, and per user the last
+        // of its blocks computes lse and the top-K
+        StreamArgs a{};
+        a.H = H;
+        a.E = E;
+        a.B = B;
+        a.D = D;
+        a.M = M;
+        a.mask = mask;
+        a.mask_stride = mask_stride;
+        a.n_items = M;
+        a.tile_stride = 1;
+        a.CH = p.main.CH;
+        a.P = p.main.P;
+        a.pm = at<float>(workspace, p.off_pm);
+        a.pl = at<float>(workspace, p.off_pl);
+        a.err = at<int64_t>(workspace, p.off_hdr);
+        a.rows = at<float>(workspace, p.off_rows);
+        a.arrive = at<uint64_t>(workspace, p.off_arrive);
+        a.elect = at<uint64_t>(workspace, p.off_elect);
+        a.ticket = next_ticket();
+        a.K = K;
+        a.out_idx = out_idx;
+        a.out_scores = out_scores;
+        a.out_lse = out_lse;
+        return hip_status(timed(prof, KIND_MAIN, s, [&] {
+            return launch_fused(a, dtype == GENREC_F32, (int64_t)B * p.main.P, s);
+        }));
+    }
 
     float* theta_fast = at<float>(workspace, p.off_theta);
     float* theta_safe = at<float>(workspace, p.off_theta_safe);

@@ -466,222 +466,6 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming (VALU) path: few users, fp32 inputs, per-user candidate lists
-// ---------------------------------------------------------------------------
-constexpr int ST_NT = 256;
-constexpr int ST_U = 8;  // rows in flight per wave
-
-template <typename T>
-struct Vec16;
-template <>
-struct Vec16<uint16_t> {
-    static constexpr int N = 8;
-    static __device__ __forceinline__ float dot(uint4 e, uint4 h, float acc) {
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.x), __builtin_bit_cast(bf16x2_t, h.x), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.y), __builtin_bit_cast(bf16x2_t, h.y), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.z), __builtin_bit_cast(bf16x2_t, h.z), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.w), __builtin_bit_cast(bf16x2_t, h.w), acc, false);
-        return acc;
-    }
-};
-template <>
-struct Vec16<float> {
-    static constexpr int N = 4;
-    static __device__ __forceinline__ float dot(uint4 e, uint4 h, float acc) {
-        acc = fmaf(__uint_as_float(e.x), __uint_as_float(h.x), acc);
-        acc = fmaf(__uint_as_float(e.y), __uint_as_float(h.y), acc);
-        acc = fmaf(__uint_as_float(e.z), __uint_as_float(h.z), acc);
-        acc = fmaf(__uint_as_float(e.w), __uint_as_float(h.w), acc);
-        return acc;
-    }
-};
-
-// Sum eight per-lane partials over the wave so that lanes 8g..8g+7 end with
-// the total of partial g (a butterfly reduce-scatter: 10 shuffles, not 48).
-__device__ __forceinline__ float reduce_scatter8(float (&v)[ST_U], int lane) {
-    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float send = b5 ? v[i] : v[i + 4];
-        const float keep = b5 ? v[i + 4] : v[i];
-        v[i] = keep + __shfl_xor(send, 32);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const float send = b4 ? v[i] : v[i + 2];
-        const float keep = b4 ? v[i + 2] : v[i];
-        v[i] = keep + __shfl_xor(send, 16);
-    }
-    {
-        const float send = b3 ? v[0] : v[1];
-        const float keep = b3 ? v[1] : v[0];
-        v[0] = keep + __shfl_xor(send, 8);
-    }
-    float s = v[0];
-    s += __shfl_xor(s, 4);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 1);
-    return s;
-}
-
-static_assert(ST_NT == CAND_PIECE, "one thread per list entry of a piece");
-
-template <typename T, int MODE>
-__global__ __launch_bounds__(ST_NT) void stream_score_kernel(StreamArgs a) {
-    __shared__ int s_cnt;
-    __shared__ float2 s_ml[ST_NT / kWave];
-    __shared__ int s_cold[MODE == 2 ? CAND_PIECE : 1];  // list mode: ids still to gather
-    __shared__ int s_wc[ST_NT / kWave];
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    constexpr int VEC = Vec16<T>::N;
-
-    int b;
-    int64_t n, region, piece, jbeg = 0, e0 = 0;
-    if (MODE == 2) {
-        piece = blockIdx.x;
-        if (piece >= *a.n_pieces) return;
-        const CandPiece rec = a.table[piece];
-        b = rec.user;
-        n = rec.len;
-        e0 = rec.e0;
-        region = e0;
-    } else {
-        const int cidx = blockIdx.x / a.B;
-        b = blockIdx.x - cidx * a.B;
-        jbeg = (int64_t)cidx * a.CH;
-        n = min((int64_t)a.CH, a.n_items - jbeg);
-        piece = (int64_t)b * a.P + cidx;
-        region = (int64_t)b * a.M + jbeg;
-    }
-    if (tid == 0) s_cnt = 0;
-    __syncthreads();
-
-    const T* E = (const T*)a.E;
-    const T* h = (const T*)a.H + (int64_t)b * a.D;
-    float th = -FLT_MAX;
-    if (MODE != 0 && a.theta != nullptr) th = fmaxf(a.theta[b], -FLT_MAX);
-    LseState st;
-    st.init();
-
-    if (MODE == 2) {
-        // One thread per entry: ids outside [0, M) are counted and skipped; a
-        // hot id's score is looked up in the dense hot scores; the remaining
-        // ids go, in list order, to a block-wide list that the gather loop
-        // below works through.
-        const int e = tid;
-        int id = 0;
-        bool valid = false;
-        if (e < n) {
-            id = a.ids[e0 + e];
-            valid = id >= 0 && (int64_t)id < a.M;
-        }
-        const uint64_t badmask = __ballot(e < n && !valid);
-        if (lane == 0 && badmask) atomicAdd((unsigned long long*)a.err, (unsigned long long)__popcll(badmask));
-        bool cold = valid;
-        if (valid && a.hot_idx != nullptr) {
-            const int hi = a.hot_idx[id];
-            if (hi >= 0) {
-                cold = false;
-                const float s = a.s_hot[(int64_t)b * a.t_hot + hi];
-                st.add(s);
-                if (s >= th) {
-                    const int pos = atomicAdd(&s_cnt, 1);
-                    a.keys[region + pos] = rank_key(s, (uint32_t)id);
-                }
-            }
-        }
-        const uint64_t cm = __ballot(cold);
-        if (lane == 0) s_wc[w] = __popcll(cm);
-        __syncthreads();
-        int base = 0, tot = 0;
-#pragma unroll
-        for (int q = 0; q < ST_NT / kWave; ++q) {
-            base += q < w ? s_wc[q] : 0;
-            tot += s_wc[q];
-        }
-        if (cold) s_cold[base + __popcll(cm & ((1ull << lane) - 1ull))] = id;
-        n = tot;
-        __syncthreads();
-    }
-
-    for (int64_t g0 = (int64_t)w * ST_U; g0 < n; g0 += (ST_NT / kWave) * ST_U) {
-        int64_t item[ST_U];
-        bool ok[ST_U];
-        if (MODE == 2) {
-#pragma unroll
-            for (int u = 0; u < ST_U; ++u) {
-                ok[u] = g0 + u < n;
-                item[u] = ok[u] ? s_cold[g0 + u] : 0;
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < ST_U; ++u) {
-                ok[u] = g0 + u < n;
-                const int64_t j = jbeg + g0 + u;  // pass index -> catalog row (tile-strided sample)
-                item[u] = (j >> 8) * a.tile_stride * 256 + (j & 255);
-            }
-        }
-        float acc[ST_U];
-#pragma unroll
-        for (int u = 0; u < ST_U; ++u) acc[u] = 0.f;
-#pragma unroll 2
-        for (int d = lane * VEC; d < a.D; d += kWave * VEC) {
-            const uint4 hv = *(const uint4*)(h + d);
-            uint4 ev[ST_U];
-#pragma unroll
-            for (int u = 0; u < ST_U; ++u)
-                ev[u] = ok[u] ? *(const uint4*)(E + item[u] * a.D + d) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int u = 0; u < ST_U; ++u) acc[u] = Vec16<T>::dot(ev[u], hv, acc[u]);
-        }
-        const float s = reduce_scatter8(acc, lane);
-        const int u = lane >> 3;
-        bool mine = (lane & 7) == 0;
-#pragma unroll
-        for (int q = 0; q < ST_U; ++q)
-            if (q == u) mine = mine && ok[q];
-        if (mine) {
-            int64_t it = 0;
-#pragma unroll
-            for (int q = 0; q < ST_U; ++q)
-                if (q == u) it = item[q];
-            float sv = s;
-            if (MODE != 2 && a.mask != nullptr && !((a.mask[(int64_t)b * a.mask_stride + (it >> 5)] >> (it & 31)) & 1u))
-                sv = -INFINITY;  // masked item: nothing to the sum, never a candidate
-            if (MODE == 0) {
-                a.sample_out[(int64_t)b * a.n_items + jbeg + g0 + u] = sv;
-            } else if (sv != -INFINITY) {
-                const float s = sv;
-                st.add(s);
-                if (s >= th) {
-                    const int pos = atomicAdd(&s_cnt, 1);
-                    a.keys[region + pos] = rank_key(s, (uint32_t)it);
-                }
-            }
-        }
-    }
-    if (MODE == 0) return;
-
-    // (max, sum-exp) over the wave, then over the four waves.
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float m2 = __shfl_xor(st.m, o), l2 = __shfl_xor(st.l, o);
-        st.merge(m2, l2);
-    }
-    if (lane == 0) s_ml[w] = make_float2(st.m, st.l);
-    __syncthreads();
-    if (tid == 0) {
-        LseState t;
-        t.init();
-        for (int q = 0; q < ST_NT / kWave; ++q) t.merge(s_ml[q].x, s_ml[q].y);
-        a.pm[piece] = t.m;
-        a.pl[piece] = t.l;
-        a.pcnt[piece] = s_cnt;
-        a.preg[piece] = region;
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Block-level selection of the k-th largest 64-bit key
 // ---------------------------------------------------------------------------
 constexpr int SEL_NT = 256;
@@ -824,7 +608,8 @@ __device__ void block_rank_place(const uint64_t* in, int n, uint64_t* out, int l
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
         const uint64_t x = in[i];
         int r = 0;
-        for (int j = 0; j < n; ++j) {
+#pragma unroll 8
+        for (int j = 0; j < n; ++j) {  // (unrolled: several LDS reads in flight)
             const uint64_t y = in[j];
             r += (y > x) | ((y == x) & (j < i));
         }
@@ -1760,6 +1545,504 @@ __global__ __launch_bounds__(TK_NT) void topk_rowmerge_kernel(TopkRowsArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Streaming (VALU) path: few users, fp32 inputs, per-user candidate lists
+// ---------------------------------------------------------------------------
+constexpr int ST_NT = 256;
+constexpr int ST_U = 8;  // rows in flight per wave
+
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<uint16_t> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ float dot(uint4 e, uint4 h, float acc) {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.x), __builtin_bit_cast(bf16x2_t, h.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.y), __builtin_bit_cast(bf16x2_t, h.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.z), __builtin_bit_cast(bf16x2_t, h.z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, e.w), __builtin_bit_cast(bf16x2_t, h.w), acc, false);
+        return acc;
+    }
+};
+template <>
+struct Vec16<float> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ float dot(uint4 e, uint4 h, float acc) {
+        acc = fmaf(__uint_as_float(e.x), __uint_as_float(h.x), acc);
+        acc = fmaf(__uint_as_float(e.y), __uint_as_float(h.y), acc);
+        acc = fmaf(__uint_as_float(e.z), __uint_as_float(h.z), acc);
+        acc = fmaf(__uint_as_float(e.w), __uint_as_float(h.w), acc);
+        return acc;
+    }
+};
+
+// Sum eight per-lane partials over the wave so that lanes 8g..8g+7 end with
+// the total of partial g (a butterfly reduce-scatter: 10 shuffles, not 48).
+__device__ __forceinline__ float reduce_scatter8(float (&v)[ST_U], int lane) {
+    const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float send = b5 ? v[i] : v[i + 4];
+        const float keep = b5 ? v[i + 4] : v[i];
+        v[i] = keep + __shfl_xor(send, 32);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float send = b4 ? v[i] : v[i + 2];
+        const float keep = b4 ? v[i + 2] : v[i];
+        v[i] = keep + __shfl_xor(send, 16);
+    }
+    {
+        const float send = b3 ? v[0] : v[1];
+        const float keep = b3 ? v[1] : v[0];
+        v[0] = keep + __shfl_xor(send, 8);
+    }
+    float s = v[0];
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 1);
+    return s;
+}
+
+static_assert(ST_NT == CAND_PIECE, "one thread per list entry of a piece");
+static_assert(ST_NT == TK_NT, "the fused finish is the register-resident selection of one block");
+static_assert(ST_NT * 32 == kFusedMaxM, "the fused path's largest catalog: 32 keys per thread of the finishing block");
+
+// ---------------------------------------------------------------------------
+// Fused small-catalog path: one launch for the whole call
+// ---------------------------------------------------------------------------
+// Each block of the streaming pass writes its rows' scores into the user's
+// dense score row and its (max, sum-exp) piece; the block that arrives last
+// for a user finishes that user: lse from the pieces, and the top-K of the
+// row by the register-resident radix selection (FV keys per thread, so rows
+// of up to ST_NT * FV scores).
+//
+// Finding the last block without fences or a contended counter.  Every
+// value one block hands to another (score rows, pieces, flags) is written
+// with agent-scope stores (sc1: written through to the device's point of
+// coherence) and read with agent-scope loads, so no L2 writeback or
+// invalidation (a whole-cache operation per wave) is needed.  A block first
+// waits until its own stores have completed, then sets its flag to the call's
+// ticket (40 bits, unique to the call, never 0 or all ones, from the host),
+// waits again, and reads all of its user's flags: whichever block sees every
+// flag holding the ticket may finish the user.  Since each block's flag is
+// complete before it reads the others, the last block to set its flag sees
+// them all.  Several blocks can see them all; an exchange on the user's
+// election word picks one (the first to find a value other than the ticket
+// there), and it clears the flags and the word when done, so that a replay of
+// the same captured call (same ticket) starts clean.  Stale workspace
+// contents are recognised by their ticket: only a word that happens to hold
+// this call's ticket could be misread.
+template <class V>
+__device__ __forceinline__ void put_agent(V* p, V v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class V>
+__device__ __forceinline__ V get_agent(const V* p) {
+    return __hip_atomic_load((V*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every vector memory operation of this wave completed (stores acknowledged)
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Block-uniform: true for the block that finishes the user whose flags are
+// flags[0 .. P); `mine` is this block's flag.
+__device__ bool arrive_elect(uint64_t* flags, uint64_t* mine, uint64_t* elect, uint64_t ticket, int P, int* s_red) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    wait_stores();
+    __syncthreads();  // every wave's stores of this block have completed
+    if (tid == 0) {
+        put_agent(mine, ticket);
+        wait_stores();
+    }
+    __syncthreads();
+    int c = 0;
+    for (int q = tid; q < P; q += blockDim.x) c += get_agent(flags + q) == ticket ? 1 : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o);
+    if (lane == 0) s_red[w] = c;
+    __syncthreads();
+    int all = 0;
+    for (int q = 0; q < (int)(blockDim.x >> 6); ++q) all += s_red[q];
+    __syncthreads();
+    if (all < P) return false;
+    if (tid == 0) {
+        const uint64_t prev = __hip_atomic_exchange(elect, ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_red[0] = prev != ticket ? 1 : 0;
+    }
+    __syncthreads();
+    return s_red[0] != 0;
+}
+
+// Order key of a dense-row score; masked items (-inf) are no key (0, below
+// every score's key: order_key is never 0 for a non-NaN value).
+__device__ __forceinline__ uint32_t row_key(float s) { return s == -INFINITY ? 0u : order_key(s); }
+
+// The finishing block of a user.  One round of loads brings the user's
+// pieces (the blocks' (max, sum-exp), at most one per thread: P <= 256) and
+// its dense score row (FV keys per thread, kept in LDS as order keys too).
+// lse merges the pieces.  For the top-K (K <= 256) the threshold T is the
+// K-th largest of the P block maxima: each thread ranks its block's maximum
+// against all P (LDS broadcast reads, four keys at a time) and T is the
+// smallest maximum of rank < K.  At least K blocks hold a key >= T, so at
+// least K keys reach T and all of the top K do.  Those keys -- about K + K/2
+// when the rows are exchangeable -- are compacted as 64-bit ranking keys
+// (score word, inverted column: distinct) and each is placed at its rank.
+// More than kFastCap keys at T (many equal scores) or K > 256: the
+// register-resident radix selection instead, exact in every case.  This code
+// runs once per user on one block, so every step is spread over the block's
+// threads: a serial chain (one wave deciding bits one at a time, one thread
+// per candidate walking a long loop) costs microseconds here.
+constexpr int kFastCap = GENREC_KMAX;
+constexpr int kFusedKeys = ST_NT * 32;  // keys per user at most (32 per thread)
+
+struct FastShared {
+    uint32_t keys[kFusedKeys];  // the row's order keys, slot j of thread t at j * ST_NT + t (0: none)
+    uint32_t bmax[ST_NT];       // order keys of the block maxima (0: none)
+    uint32_t tred[ST_NT / kWave];
+    int wcnt[ST_NT / kWave];
+    float2 ml[ST_NT / kWave];
+};
+
+// Radix selection over the keys staged in LDS (FV per thread), then the
+// ranked output.
+template <int FV>
+__device__ __noinline__ void fused_topk_radix(const uint32_t* lkeys, int K, TkShared& sh, int32_t* oidx,
+                                              float* osc) {
+    const int tid = threadIdx.x;
+    uint32_t hv[FV];
+#pragma unroll
+    for (int j = 0; j < FV; ++j) hv[j] = lkeys[j * ST_NT + tid];
+#pragma unroll
+    for (int j = 0; j < FV; ++j) asm volatile("" : "+v"(hv[j]));
+    int cv = 0;
+#pragma unroll
+    for (int j = 0; j < FV; ++j) cv += __popcll(__ballot(hv[j] != 0u));
+    // slot 1 of the count pair: the selection's first count writes slot 0
+    // while a slow wave may still be reading this one
+    int par = 1;
+    const int n_valid = tk_block_sum(cv, par, sh);
+    const int k = min(K, n_valid);
+    const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)tid;  // index word of slot 0
+    if (k > 0)
+        tk_select<FV>([&](int j) { return hv[j]; }, [&](int j) { return lo0 - (uint32_t)(j * ST_NT); },
+                      [&](int j) { return hv[j] != 0u; }, n_valid, k, sh);
+    tk_emit(k, K, sh, oidx, osc);
+}
+
+template <int FV>
+__device__ void fused_finish(const StreamArgs& a, int b, TkShared& sh, FastShared& fs) {
+    static_assert(FV <= 32, "a 32-bit pass mask per thread");
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n = (int)a.n_items, P = a.P, K = a.K;
+    const float* row = a.rows + (int64_t)b * a.n_items;
+    // every load issued before any is waited for: indices are clamped into
+    // range instead of branching around the loads
+    const int pq = min(tid, P - 1);
+    const float pmv = get_agent(a.pm + (int64_t)b * P + pq), plv = get_agent(a.pl + (int64_t)b * P + pq);
+    float rv[FV];
+#pragma unroll
+    for (int j = 0; j < FV; ++j) rv[j] = get_agent(row + min(j * ST_NT + tid, n - 1));
+    uint32_t hv[FV];
+#pragma unroll
+    for (int j = 0; j < FV; ++j) {
+        hv[j] = j * ST_NT + tid < n ? row_key(rv[j]) : 0u;
+        fs.keys[j * ST_NT + tid] = hv[j];
+    }
+    const bool has_piece = tid < P;
+    // lse over the pieces; the pieces' maxima for the threshold
+    LseState st;
+    st.init();
+    if (has_piece) st.merge(pmv, plv);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) st.merge(__shfl_xor(st.m, o), __shfl_xor(st.l, o));
+    if (lane == 0) fs.ml[w] = make_float2(st.m, st.l);
+    const uint32_t mykey = has_piece ? row_key(pmv) : 0u;
+    fs.bmax[tid] = mykey;
+    __syncthreads();
+    if (tid == 0) {
+        LseState t;
+        t.init();
+        for (int q = 0; q < ST_NT / kWave; ++q) t.merge(fs.ml[q].x, fs.ml[q].y);
+        a.out_lse[b] = t.l > 0.f ? t.m + __builtin_amdgcn_logf(t.l) * kLn2 : -INFINITY;
+    }
+    int32_t* oidx = a.out_idx + (int64_t)b * K;
+    float* osc = a.out_scores + (int64_t)b * K;
+    if (K > ST_NT) {  // block-uniform
+        fused_topk_radix<FV>(fs.keys, K, sh, oidx, osc);
+        return;
+    }
+    // T: the smallest block maximum whose rank (maxima strictly larger) is
+    // below K; with fewer than K blocks holding a key, a zero maximum
+    // qualifies and T = 0 admits every key (fewer than K blocks: T = 0 too)
+    uint32_t tcand = 0xFFFFFFFFu;
+    if (has_piece) {
+        int r = 0;
+        const uint4* bm4 = (const uint4*)fs.bmax;
+#pragma unroll 4
+        for (int q = 0; q < (P + 3) / 4; ++q) {  // entries past P hold 0: never larger
+            const uint4 v = bm4[q];
+            r += (v.x > mykey) + (v.y > mykey) + (v.z > mykey) + (v.w > mykey);
+        }
+        if (r < K) tcand = mykey;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tcand = min(tcand, (uint32_t)__shfl_xor((int)tcand, o));
+    // keys at T: a pass mask per thread (slot j = bit j), counted and scanned
+    uint32_t T;
+    {
+        if (lane == 0) fs.tred[w] = tcand;
+        __syncthreads();
+        T = fs.tred[0];
+#pragma unroll
+        for (int q = 1; q < ST_NT / kWave; ++q) T = min(T, fs.tred[q]);
+        if (P < K) T = 0u;
+    }
+    uint32_t mask = 0;
+#pragma unroll
+    for (int j = 0; j < FV; ++j) mask |= (hv[j] != 0u && hv[j] >= T) ? (1u << j) : 0u;
+    const int c = __popc(mask);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) fs.wcnt[w] = incl;
+    __syncthreads();
+    int base = incl - c, total = 0;
+#pragma unroll
+    for (int q = 0; q < ST_NT / kWave; ++q) {
+        base += q < w ? fs.wcnt[q] : 0;
+        total += fs.wcnt[q];
+    }
+    if (total > kFastCap) {  // block-uniform
+        fused_topk_radix<FV>(fs.keys, K, sh, oidx, osc);
+        return;
+    }
+    uint64_t* cand = sh.sel;
+    for (uint32_t m = mask; m != 0u; m &= m - 1u) {
+        const int j = __ffs(m) - 1;
+        cand[base++] = ((uint64_t)fs.keys[j * ST_NT + tid] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(j * ST_NT + tid));
+    }
+    __syncthreads();
+    // total >= K unless fewer than K keys exist (T = 0: all of them)
+    const int k = min(K, total);
+    if (total <= ST_NT) {
+        // rank of each candidate = the number of larger keys (all distinct)
+        if (tid < total) {
+            const uint64_t x = cand[tid];
+            int r = 0;
+            const ulonglong2* c2 = (const ulonglong2*)cand;
+#pragma unroll 4
+            for (int j = 0; j < total / 2; ++j) {
+                const ulonglong2 y = c2[j];
+                r += (y.x > x) + (y.y > x);
+            }
+            if (total & 1) r += cand[total - 1] > x ? 1 : 0;
+            if (r < k) sh.sorted[r] = x;
+        }
+    } else {
+        block_sort_into(cand, total, sh.sorted);
+    }
+    __syncthreads();
+    for (int i = tid; i < K; i += ST_NT) {
+        if (i < k) {
+            const uint64_t key = sh.sorted[i];
+            oidx[i] = (int32_t)key_id(key);
+            osc[i] = key_score(key);
+        } else {
+            oidx[i] = -1;
+            osc[i] = -INFINITY;
+        }
+    }
+}
+
+template <bool FUSED>
+struct FusedShared {};
+template <>
+struct FusedShared<true> {
+    TkShared tk;
+    FastShared fast;
+    int red[ST_NT / kWave];
+};
+
+template <typename T, int MODE, int FV = 0>
+__global__ __launch_bounds__(ST_NT) void stream_score_kernel(StreamArgs a) {
+    __shared__ int s_cnt;
+    __shared__ float2 s_ml[ST_NT / kWave];
+    __shared__ int s_cold[MODE == 2 ? CAND_PIECE : 1];  // list mode: ids still to gather
+    __shared__ int s_wc[ST_NT / kWave];
+    __shared__ FusedShared<MODE == 3> fsh;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    constexpr int VEC = Vec16<T>::N;
+
+    int b;
+    int64_t n, region, piece, jbeg = 0, e0 = 0;
+    if (MODE == 2) {
+        piece = blockIdx.x;
+        if (piece >= *a.n_pieces) return;
+        const CandPiece rec = a.table[piece];
+        b = rec.user;
+        n = rec.len;
+        e0 = rec.e0;
+        region = e0;
+    } else {
+        const int cidx = blockIdx.x / a.B;
+        b = blockIdx.x - cidx * a.B;
+        jbeg = (int64_t)cidx * a.CH;
+        n = min((int64_t)a.CH, a.n_items - jbeg);
+        piece = (int64_t)b * a.P + cidx;
+        region = (int64_t)b * a.M + jbeg;
+    }
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+
+    const T* E = (const T*)a.E;
+    const T* h = (const T*)a.H + (int64_t)b * a.D;
+    float th = -FLT_MAX;
+    if (MODE != 0 && a.theta != nullptr) th = fmaxf(a.theta[b], -FLT_MAX);
+    LseState st;
+    st.init();
+
+    if (MODE == 2) {
+        // One thread per entry: ids outside [0, M) are counted and skipped; a
+        // hot id's score is looked up in the dense hot scores; the remaining
+        // ids go, in list order, to a block-wide list that the gather loop
+        // below works through.
+        const int e = tid;
+        int id = 0;
+        bool valid = false;
+        if (e < n) {
+            id = a.ids[e0 + e];
+            valid = id >= 0 && (int64_t)id < a.M;
+        }
+        const uint64_t badmask = __ballot(e < n && !valid);
+        if (lane == 0 && badmask) atomicAdd((unsigned long long*)a.err, (unsigned long long)__popcll(badmask));
+        bool cold = valid;
+        if (valid && a.hot_idx != nullptr) {
+            const int hi = a.hot_idx[id];
+            if (hi >= 0) {
+                cold = false;
+                const float s = a.s_hot[(int64_t)b * a.t_hot + hi];
+                st.add(s);
+                if (s >= th) {
+                    const int pos = atomicAdd(&s_cnt, 1);
+                    a.keys[region + pos] = rank_key(s, (uint32_t)id);
+                }
+            }
+        }
+        const uint64_t cm = __ballot(cold);
+        if (lane == 0) s_wc[w] = __popcll(cm);
+        __syncthreads();
+        int base = 0, tot = 0;
+#pragma unroll
+        for (int q = 0; q < ST_NT / kWave; ++q) {
+            base += q < w ? s_wc[q] : 0;
+            tot += s_wc[q];
+        }
+        if (cold) s_cold[base + __popcll(cm & ((1ull << lane) - 1ull))] = id;
+        n = tot;
+        __syncthreads();
+    }
+
+    for (int64_t g0 = (int64_t)w * ST_U; g0 < n; g0 += (ST_NT / kWave) * ST_U) {
+        int64_t item[ST_U];
+        bool ok[ST_U];
+        if (MODE == 2) {
+#pragma unroll
+            for (int u = 0; u < ST_U; ++u) {
+                ok[u] = g0 + u < n;
+                item[u] = ok[u] ? s_cold[g0 + u] : 0;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < ST_U; ++u) {
+                ok[u] = g0 + u < n;
+                const int64_t j = jbeg + g0 + u;  // pass index -> catalog row (tile-strided sample)
+                item[u] = (j >> 8) * a.tile_stride * 256 + (j & 255);
+            }
+        }
+        float acc[ST_U];
+#pragma unroll
+        for (int u = 0; u < ST_U; ++u) acc[u] = 0.f;
+#pragma unroll 2
+        for (int d = lane * VEC; d < a.D; d += kWave * VEC) {
+            const uint4 hv = *(const uint4*)(h + d);
+            uint4 ev[ST_U];
+#pragma unroll
+            for (int u = 0; u < ST_U; ++u)
+                ev[u] = ok[u] ? *(const uint4*)(E + item[u] * a.D + d) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < ST_U; ++u) acc[u] = Vec16<T>::dot(ev[u], hv, acc[u]);
+        }
+        const float s = reduce_scatter8(acc, lane);
+        const int u = lane >> 3;
+        bool mine = (lane & 7) == 0;
+#pragma unroll
+        for (int q = 0; q < ST_U; ++q)
+            if (q == u) mine = mine && ok[q];
+        if (mine) {
+            int64_t it = 0;
+#pragma unroll
+            for (int q = 0; q < ST_U; ++q)
+                if (q == u) it = item[q];
+            float sv = s;
+            if (MODE != 2 && a.mask != nullptr && !((a.mask[(int64_t)b * a.mask_stride + (it >> 5)] >> (it & 31)) & 1u))
+                sv = -INFINITY;  // masked item: nothing to the sum, never a candidate
+            if (MODE == 0) {
+                a.sample_out[(int64_t)b * a.n_items + jbeg + g0 + u] = sv;
+            } else if (MODE == 3) {
+                put_agent(a.rows + (int64_t)b * a.n_items + jbeg + g0 + u, sv);
+                if (sv != -INFINITY) st.add(sv);
+            } else if (sv != -INFINITY) {
+                const float s = sv;
+                st.add(s);
+                if (s >= th) {
+                    const int pos = atomicAdd(&s_cnt, 1);
+                    a.keys[region + pos] = rank_key(s, (uint32_t)it);
+                }
+            }
+        }
+    }
+    if (MODE == 0) return;
+
+    // (max, sum-exp) over the wave, then over the four waves.
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float m2 = __shfl_xor(st.m, o), l2 = __shfl_xor(st.l, o);
+        st.merge(m2, l2);
+    }
+    if (lane == 0) s_ml[w] = make_float2(st.m, st.l);
+    __syncthreads();
+    if (tid == 0) {
+        LseState t;
+        t.init();
+        for (int q = 0; q < ST_NT / kWave; ++q) t.merge(s_ml[q].x, s_ml[q].y);
+        if (MODE == 3) {
+            put_agent(a.pm + piece, t.m);
+            put_agent(a.pl + piece, t.l);
+        } else {
+            a.pm[piece] = t.m;
+            a.pl[piece] = t.l;
+            a.pcnt[piece] = s_cnt;
+            a.preg[piece] = region;
+        }
+    }
+    if constexpr (MODE == 3) {
+        if (tid == 0 && blockIdx.x == 0) {  // the call's header: no candidate errors, no rescued users
+            a.err[0] = 0;
+            a.err[1] = 0;
+            a.err[3] = 0;
+        }
+        uint64_t* flags = a.arrive + (int64_t)b * a.P;  // user b's blocks, by chunk
+        if (!arrive_elect(flags, flags + piece - (int64_t)b * a.P, a.elect + b, a.ticket, a.P, fsh.red)) return;
+        fused_finish<FV>(a, b, fsh.tk, fsh.fast);
+        // clean for the next call: flags and election word back to zero
+        for (int q = tid; q < a.P; q += ST_NT) put_agent(flags + q, (uint64_t)0);
+        if (tid == 0) put_agent(a.elect + b, (uint64_t)0);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Candidate lists: CSR offsets -> pieces of at most CAND_PIECE entries
 // ---------------------------------------------------------------------------
 constexpr int PL_NT = 1024;
@@ -2209,6 +2492,25 @@ hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s) {
         }
     }
 #undef GENREC_MFMA
+    return hipGetLastError();
+}
+
+hipError_t launch_fused(const StreamArgs& a, bool f32, int64_t grid, hipStream_t s) {
+    // the finishing block holds one piece per thread and 32 row keys per thread
+    if (grid <= 0 || a.n_items > (int64_t)kFusedKeys || a.P > ST_NT || grid != (int64_t)a.B * a.P)
+        return hipErrorInvalidValue;
+    const int64_t per = (a.n_items + ST_NT - 1) / ST_NT;  // keys per thread of the finishing block
+#define GENREC_FUSED(T, FV) hipLaunchKernelGGL((stream_score_kernel<T, 3, FV>), dim3(grid), dim3(ST_NT), 0, s, a)
+    if (f32) {
+        if (per <= 8) GENREC_FUSED(float, 8);
+        else if (per <= 16) GENREC_FUSED(float, 16);
+        else GENREC_FUSED(float, 32);
+    } else {
+        if (per <= 8) GENREC_FUSED(uint16_t, 8);
+        else if (per <= 16) GENREC_FUSED(uint16_t, 16);
+        else GENREC_FUSED(uint16_t, 32);
+    }
+#undef GENREC_FUSED
     return hipGetLastError();
 }
 

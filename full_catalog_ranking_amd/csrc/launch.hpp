@@ -134,6 +134,19 @@ struct StreamArgs {
     // dense modes: item mask as in MfmaArgs (null: every item)
     const uint32_t* mask;
     int64_t mask_stride;
+    // fused mode (one launch, rows of at most 8,192 items): dense score rows
+    // [B][n_items], per-block arrival flags [B][P] (block of user b, chunk c
+    // at b * P + c), per-user election words [B], this call's ticket (40 bits,
+    // not 0 or all ones), K and the outputs; err = the workspace header (error
+    // words and rescued count cleared by the call)
+    float* rows;
+    uint64_t* arrive;
+    uint64_t* elect;
+    uint64_t ticket;
+    int K;
+    int32_t* out_idx;
+    float* out_scores;
+    float* out_lse;
 };
 
 // Hot head of the candidate lists: per-item list counts, the count threshold,
@@ -221,6 +234,8 @@ struct TopkRowsArgs {
 hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s);
 hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s);
 hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, hipStream_t s);
+// the whole call in one launch (fused mode): grid = B * P blocks
+hipError_t launch_fused(const StreamArgs& a, bool f32, int64_t grid, hipStream_t s);
 hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_cand_plan(const CandPlanArgs& a, hipStream_t s);

@@ -28,6 +28,11 @@ constexpr int64_t kFastMinRank = 32;
 constexpr int64_t kStreamPieces = 2048;  // target work pieces of the VALU path
 constexpr int64_t kStreamChunkAlign = 32;
 constexpr int kCandPiece = 256;        // candidate entries per piece (matches the kernels)
+// Fused small-catalog path: on the VALU path without a sample, catalogs of up
+// to this many items run as one launch (the last block of each user selects
+// its top-K from the user's dense score row held in registers, 32 keys per
+// thread of a 256-thread block; 64 would spill).
+constexpr int64_t kFusedMaxM = 256 * 32;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -60,8 +65,10 @@ struct DensePlan {
     int64_t n_pieces = 0;
     int64_t key_stride = 0;    // candidate-region elements per user
     bool merge_small = false;  // the merge's smaller build serves this shape (a speed choice)
+    bool fused = false;        // one launch: dense rows [B][M] f32 and per-user arrival words
     size_t off_hdr = 0, off_theta = 0, off_theta_safe = 0, off_uflag = 0, off_tflag = 0, off_sample = 0,
-           off_pm = 0, off_pl = 0, off_pcnt = 0, off_preg = 0, off_keys = 0, total = 0;
+           off_pm = 0, off_pl = 0, off_pcnt = 0, off_preg = 0, off_keys = 0, off_arrive = 0, off_elect = 0, off_rows = 0,
+           total = 0;
 };
 
 inline Chunking chunk_mfma(int B, int64_t n_tiles) {
@@ -113,9 +120,24 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
                                       : (p.sample ? ceil_div((int64_t)K * M, p.n_sample) : M);
         p.merge_small = (int64_t)p.main.P * p.pieces_per_chunk <= kMergeSmallPieces && expect <= kMergeSmallGather;
     }
+    p.fused = !p.mfma && !p.sample && M <= kFusedMaxM;
     size_t o = 0;
     p.off_hdr = o;
     o += 256;
+    if (p.fused) {
+        p.off_arrive = o;  // a flag per block: B x P
+        o = align_up(o + sizeof(uint64_t) * (size_t)p.n_pieces, 256);
+        p.off_elect = o;
+        o = align_up(o + sizeof(uint64_t) * (size_t)B, 256);
+        p.off_pm = o;
+        o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
+        p.off_pl = o;
+        o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
+        p.off_rows = o;
+        o = align_up(o + sizeof(float) * (size_t)B * (size_t)M, 256);
+        p.total = o;
+        return p;
+    }
     p.off_theta = o;
     o = align_up(o + sizeof(float) * (size_t)B, 256);
     p.off_theta_safe = o;

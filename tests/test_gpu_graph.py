@@ -135,3 +135,23 @@ def test_topk_rows_and_ce_graph_replays(dev):
         return loss, lse, dH, dE
     print("  graph ce B=%d D=%d M=%d" % (B, D, M), flush=True)
     _check_replays(ce_step, dev, lambda: torch.cumsum(H.float(), 0))
+
+
+def test_fused_graph_replays_share_workspace_with_eager_calls(dev):
+    """The fused path's captured call replays correctly while eager fused calls
+    of another shape (each with its own ticket) use the same workspace between
+    the replays."""
+    from full_catalog_ranking_amd import genrec
+    B, D, M, K = 4, 256, 5000, 10
+    d = synth.make_dense(B, D, M, seed=8, bf16=False)
+    d2 = synth.make_dense(1, D, 3000, seed=9, bf16=False)
+    H, E = _td(d["H"], dev), _td(d["E"], dev)
+    H2, E2 = _td(d2["H"], dev), _td(d2["E"], dev)
+    ws = torch.empty(max(genrec.workspace_bytes(B, D, M, K, H.dtype), genrec.workspace_bytes(1, D, 3000, 20, H.dtype)),
+                     dtype=torch.uint8, device=dev)
+    out = (torch.empty((B, K), dtype=torch.int32, device=dev), torch.empty((B, K), dtype=torch.float32, device=dev),
+           torch.empty((B,), dtype=torch.float32, device=dev))
+    assert genrec.describe_plan(B, D, M, K, H.dtype)["fused"] == 1
+    print("  graph fused B=%d D=%d M=%d K=%d" % (B, D, M, K), flush=True)
+    _check_replays(lambda: genrec.score_lse_topk(H, E, K, workspace=ws, out=out), dev,
+                   lambda: genrec.score_lse_topk(H2, E2, 20, workspace=ws))

@@ -193,18 +193,19 @@ def _pack_mask(allowed):
     return (bits << np.arange(32, dtype=np.uint64)).sum(axis=-1).astype(np.uint32)
 
 
-@pytest.mark.parametrize("case,B,D,M,K,per_user", [
-    ("global 90%, sampled fast path", 256, 512, 100_000, 100, False),
-    ("per-user densities incl. none and < K, ragged, k tail", 300, 200, 70_001, 37, True),
-    ("per-user, VALU path with sample", 3, 96, 70_000, 50, True),
-    ("global 2% (< K allowed), unsampled MFMA", 17, 128, 3000, 64, False),
+@pytest.mark.parametrize("case,B,D,M,K,per_user,bf16", [
+    ("global 90%, sampled fast path", 256, 512, 100_000, 100, False, True),
+    ("per-user densities incl. none and < K, ragged, k tail", 300, 200, 70_001, 37, True, True),
+    ("per-user, VALU path with sample", 3, 96, 70_000, 50, True, True),
+    ("global 2% (< K allowed), unsampled MFMA", 17, 128, 3000, 64, False, True),
+    ("per-user incl. none and < K, fused one-launch path (fp32)", 3, 64, 5000, 40, True, False),
 ])
-def test_masked_head(dev, oracle_mod, case, B, D, M, K, per_user):
+def test_masked_head(dev, oracle_mod, case, B, D, M, K, per_user, bf16):
     from full_catalog_ranking_amd import genrec
-    d = synth.make_dense(B, D, M, seed=B + D)
+    d = synth.make_dense(B, D, M, seed=B + D, bf16=bf16)
     rng = np.random.default_rng(B * 31 + M)
     if per_user:
-        dens = np.concatenate([[0.0, 1e-4, 1.0], rng.uniform(0.005, 1.0, B - 3)])[:B]
+        dens = np.concatenate([[0.0, 1e-4, 1.0], rng.uniform(0.005, 1.0, max(0, B - 3))])[:B]
         allowed = rng.random((B, M)) < dens[:, None]
     else:
         allowed = np.broadcast_to(rng.random(M) < (0.9 if M > 10_000 else 0.02), (B, M))
@@ -216,6 +217,8 @@ def test_masked_head(dev, oracle_mod, case, B, D, M, K, per_user):
     idx, sc, ls = genrec.score_lse_topk(H, E, K, workspace=ws, mask=mask)
     g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
     users = sorted(set([0, 1, 2, B - 1] + list(range(0, B, max(1, B // 10)))))
+    if not bf16:
+        assert genrec.describe_plan(B, D, M, K, H.dtype)["fused"] == 1
     ref = oracle_mod.full_masked(d["H"], d["E"], K, words, users=users)
     parity.check_dense(g, ref, where="masked %s" % case)
     for b in range(B):  # every returned item is allowed, every padded slot is (-1, -inf)
@@ -260,7 +263,7 @@ def test_permuted_popularity_batch(dev, oracle_mod):
 
 def test_exact_ties_break_by_lower_id(dev):
     # rows 10, 500, 2000 and 4999 identical: equal scores for every user
-    for B in (2, 64):  # VALU and MFMA paths
+    for B in (1, 2, 64):  # fused one-launch path, MFMA paths
         d = synth.make_dense(B, 256, 5000, seed=11)
         E = d["E"].copy()
         H = synth.bf16_bits_to_f32(d["H"])
@@ -281,13 +284,15 @@ def test_exact_ties_break_by_lower_id(dev):
 
 
 def test_all_equal_scores(dev):
-    for B in (3, 40):
+    # B = 1: the fused path, its fast selection (1,000 keys at the threshold)
+    # and its radix fallback (3,000 keys at the threshold); then the MFMA path
+    for B, M in ((1, 1000), (1, 3000), (3, 1000), (40, 1000)):
         H = synth.f32_to_bf16_bits(np.ones((B, 64), dtype=np.float32))
-        E = np.zeros((1000, 64), dtype=np.uint16)
-        g = run_dense(dict(H=H, E=E, B=B, D=64, M=1000), 20, dev)
+        E = np.zeros((M, 64), dtype=np.uint16)
+        g = run_dense(dict(H=H, E=E, B=B, D=64, M=M), 20, dev)
         idx, sc, ls = g
         assert (idx == np.arange(20)).all() and (sc == 0).all()
-        assert np.allclose(ls, math.log(1000), atol=1e-4)
+        assert np.allclose(ls, math.log(M), atol=1e-4)
 
 
 def test_deterministic(dev):
@@ -527,7 +532,8 @@ def test_poisoned_workspaces_and_outputs(dev, oracle_mod):
         return o
 
     # dense: MFMA with sample, fast threshold and rescue; VALU (B = 1); masked
-    for B, D, M, K, mask in [(70, 200, 70_000, 40, False), (1, 136, 40_000, 30, False), (33, 72, 9_000, 25, True)]:
+    for B, D, M, K, mask in [(70, 200, 70_000, 40, False), (1, 136, 40_000, 30, False), (33, 72, 9_000, 25, True),
+                             (1, 136, 7_000, 30, True), (1, 2048, 5_000, 100, False)]:
         d = synth.make_dense(B, D, M, seed=B + D)
         H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
         ws = poison(genrec.workspace_bytes(B, D, M, K, H.dtype))
@@ -568,3 +574,85 @@ def test_poisoned_workspaces_and_outputs(dev, oracle_mod):
         for r in range(R):
             ri, rv = oracle_mod.topk_row(S[r].astype(np.float64), K)
             assert np.array_equal(idx[r], ri) and np.array_equal(val[r], rv.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# The fused one-launch path (VALU path, no sample, catalogs up to 8,192 items)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,D,M,K,bf16", [
+    (1, 64, 8192, 1024, True),    # largest catalog, K = KMAX (wave sorts and rank merge)
+    (300, 32, 2000, 64, False),   # many users, several blocks each
+    (5, 256, 257, 300, False),    # K > M: padding; 8 keys per thread
+    (2, 12, 4097, 7, False),      # ragged: 32 keys per thread, a one-item last block
+    (1, 2048, 4096, 1, True),     # K = 1, 16 keys per thread
+])
+def test_fused_small_catalog(dev, oracle_mod, B, D, M, K, bf16):
+    from full_catalog_ranking_amd import genrec
+    dt = torch.bfloat16 if bf16 else torch.float32
+    assert genrec.describe_plan(B, D, M, K, dt)["fused"] == 1
+    d = synth.make_dense(B, D, M, seed=B * 13 + M, bf16=bf16)
+    g = run_dense(d, K, dev)
+    users = sorted(set([0, B - 1] + list(range(0, B, max(1, B // 16)))))
+    ref = oracle_mod.full(d["H"], d["E"], K, users=users)
+    parity.check_dense(g, ref, where="fused %s" % ((B, D, M, K, bf16),))
+
+
+def test_fused_workspace_contents_do_not_matter(dev, oracle_mod):
+    """The per-user arrival words of the fused path live in the workspace: any
+    earlier contents -- zeros, 0xFF, random bytes, a previous call of another
+    shape, or the same call again -- give the same results."""
+    from full_catalog_ranking_amd import genrec
+    B, D, M, K = 3, 128, 6000, 50
+    d = synth.make_dense(B, D, M, seed=61, bf16=False)
+    d2 = synth.make_dense(7, D, 300, seed=62, bf16=False)
+    H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
+    H2, E2 = to_dev(d2["H"], dev), to_dev(d2["E"], dev)
+    need = max(genrec.workspace_bytes(B, D, M, K, H.dtype), genrec.workspace_bytes(7, D, 300, 9, H.dtype))
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ref = oracle_mod.full(d["H"], d["E"], K)
+    first = None
+    rng = np.random.default_rng(63)
+    for fill in ("zeros", "ff", "random", "other call", "again"):
+        if fill == "zeros":
+            ws.zero_()
+        elif fill == "ff":
+            ws.fill_(255)
+        elif fill == "random":
+            ws.copy_(torch.from_numpy(rng.integers(0, 256, need, dtype=np.uint8)).to(dev))
+        elif fill == "other call":
+            genrec.score_lse_topk(H2, E2, 9, workspace=ws)
+        print("  fused workspace %s" % fill, flush=True)
+        g = tuple(x.cpu().numpy() for x in genrec.score_lse_topk(H, E, K, workspace=ws))
+        parity.check_dense(g, ref, where="fused ws %s" % fill)
+        if first is None:
+            first = g
+        for x, y in zip(g, first):
+            assert np.array_equal(x, y)
+
+
+def test_fused_two_streams(dev, oracle_mod):
+    """Fused calls on two streams at once, each with its own workspace."""
+    from full_catalog_ranking_amd import genrec
+    d1 = synth.make_dense(1, 2048, 5000, seed=71)
+    d2 = synth.make_dense(4, 256, 5000, seed=72, bf16=False)
+    H1, E1 = to_dev(d1["H"], dev), to_dev(d1["E"], dev)
+    H2, E2 = to_dev(d2["H"], dev), to_dev(d2["E"], dev)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            r1 = genrec.score_lse_topk(H1, E1, 100)
+        with torch.cuda.stream(s2):
+            r2 = genrec.score_lse_topk(H2, E2, 10)
+        torch.cuda.synchronize()
+        outs.append([tuple(x.cpu().numpy() for x in r) for r in (r1, r2)])
+    ref1 = oracle_mod.full(d1["H"], d1["E"], 100)
+    ref2 = oracle_mod.full(d2["H"], d2["E"], 10)
+    for g1, g2 in outs:
+        parity.check_dense(g1, ref1, where="fused stream 1")
+        parity.check_dense(g2, ref2, where="fused stream 2")
+    for rep in outs[1:]:
+        for a, b in zip(rep, outs[0]):
+            for x, y in zip(a, b):
+                assert np.array_equal(x, y)
