@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <new>
 
 #include "../../include/genrec.h"
@@ -160,6 +161,7 @@ const char* genrec_status_string(int status) {
         case GENREC_ERR_UNSUPPORTED: return "GENREC_ERR_UNSUPPORTED";
         case GENREC_ERR_WORKSPACE: return "GENREC_ERR_WORKSPACE";
         case GENREC_ERR_HIP: return "GENREC_ERR_HIP";
+        case GENREC_ERR_TOO_LARGE: return "GENREC_ERR_TOO_LARGE";
         default: return "GENREC_UNKNOWN_STATUS";
     }
 }
@@ -379,6 +381,49 @@ int genrec_score_lse_topk_profiled(const void* H, const void* E, int dtype, int 
                                    size_t workspace_bytes, void* stream, genrec_profiler* prof) {
     return score_dense(H, E, dtype, B, D, M, K, nullptr, 0, out_idx, out_scores, out_lse, workspace,
                        workspace_bytes, stream, prof);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the allocation-free entry point: one array per GPU (each
+// device that loads the library holds its own copy until the process ends).
+// In host code `scratch` is only a stand-in for the device symbol: kernels
+// get the address hipGetSymbolAddress returns on each device, never this name.
+static __device__ __align__(256) uint8_t scratch[GENREC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch's address on the current device, looked up once per device.
+int scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GENREC_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GENREC_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GENREC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int genrec_score_lse_topk_noalloc(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K,
+                                  int32_t* out_idx, float* out_scores, float* out_lse, void* stream) {
+    int st = check_common(H, E, dtype, B, D, M, K, out_idx, out_scores, out_lse);
+    if (st != GENREC_OK) return st;
+    if (plan_dense(B, D, M, K, dtype).total > GENREC_NOALLOC_SCRATCH_BYTES) return GENREC_ERR_TOO_LARGE;
+    void* ws = nullptr;
+    if ((st = scratch_on_current_device(&ws)) != GENREC_OK) return st;
+    return score_dense(H, E, dtype, B, D, M, K, nullptr, 0, out_idx, out_scores, out_lse, ws,
+                       GENREC_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 int genrec_score_lse_topk_masked_profiled(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K,

@@ -18,10 +18,12 @@ LIB_PATH = os.path.join(PKG, "libgenrec.so")
 
 GENREC_BF16, GENREC_F32 = 0, 1
 KMAX = 1024
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GENREC_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = (
     "genrec_score_lse_topk_workspace",
     "genrec_score_lse_topk",
+    "genrec_score_lse_topk_noalloc",
     "genrec_score_lse_topk_masked",
     "genrec_score_lse_topk_masked_profiled",
     "genrec_score_candidates_topk_workspace",
@@ -73,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.genrec_score_lse_topk_workspace.restype = SZ
         L.genrec_score_lse_topk.argtypes = [P, P, I, I, I, I64, I, P, P, P, P, SZ, P]
         L.genrec_score_lse_topk.restype = I
+        L.genrec_score_lse_topk_noalloc.argtypes = [P, P, I, I, I, I64, I, P, P, P, P]
+        L.genrec_score_lse_topk_noalloc.restype = I
         L.genrec_score_candidates_topk_workspace.argtypes = [I, I, I64, I64, I, I]
         L.genrec_score_candidates_topk_workspace.restype = SZ
         L.genrec_score_candidates_topk.argtypes = [P, P, I, P, P, I, I, I64, I64, I, P, P, P, P, SZ, P]
@@ -317,6 +321,23 @@ def score_lse_topk(H: torch.Tensor, E: torch.Tensor, K: int, workspace: torch.Te
             st = getattr(lib(), name + "_profiled")(*args, profiler.h)
     if st != 0:
         raise GenrecError(st, name)
+    return idx, sc, ls
+
+
+def score_lse_topk_noalloc(H: torch.Tensor, E: torch.Tensor, K: int, out):
+    """genrec_score_lse_topk_noalloc: the full-catalog head on the library's
+    fixed per-GPU scratch (no workspace); out = (idx int32 [B,K], scores f32
+    [B,K], lse f32 [B]) provided by the caller."""
+    _check_inputs(H, E)
+    B, D = H.shape
+    M = E.shape[0]
+    _check_outs(out, B, K, H.device)
+    idx, sc, ls = out
+    with _on_device(H.device):
+        st = lib().genrec_score_lse_topk_noalloc(_ptr(H), _ptr(E), dtype_code(H.dtype), B, D, M, K, _ptr(idx),
+                                                 _ptr(sc), _ptr(ls), _stream_handle(H.device))
+    if st != 0:
+        raise GenrecError(st, "genrec_score_lse_topk_noalloc")
     return idx, sc, ls
 
 

@@ -58,7 +58,9 @@ typedef enum {
     GENREC_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad alignment      */
     GENREC_ERR_UNSUPPORTED = -2, /* shape outside the supported set (K, D multiple, M)  */
     GENREC_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than the query returned    */
-    GENREC_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed           */
+    GENREC_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed           */
+    GENREC_ERR_TOO_LARGE = -5    /* allocation-free entry point: the call needs more
+                                    workspace than its fixed scratch holds              */
 } genrec_status;
 
 typedef enum { GENREC_BF16 = 0, GENREC_F32 = 1 } genrec_dtype;
@@ -83,6 +85,27 @@ int genrec_score_lse_topk(const void* H, const void* E, int dtype,
                           int B, int D, int64_t M, int K,
                           int32_t* out_idx, float* out_scores, float* out_lse,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free variant of genrec_score_lse_topk, for callers that cannot
+ * allocate device memory around the call (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same
+ * computation and outputs, with the workspace taken from a fixed scratch
+ * array that the library holds on each GPU (GENREC_NOALLOC_SCRATCH_BYTES per
+ * device, kept until the process ends).  The caller passes inputs and
+ * outputs as for genrec_score_lse_topk; nothing is allocated or freed.
+ * Shapes whose genrec_score_lse_topk_workspace() exceeds the scratch size
+ * return GENREC_ERR_TOO_LARGE before anything is launched.  Every call on
+ * one GPU shares that GPU's scratch: calls that may overlap on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller.
+ * The first call on a device looks the scratch's address up on that device
+ * (hipGetSymbolAddress); GENREC_ERR_HIP if that fails.
+ */
+#define GENREC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int genrec_score_lse_topk_noalloc(const void* H, const void* E, int dtype,
+                                  int B, int D, int64_t M, int K,
+                                  int32_t* out_idx, float* out_scores, float* out_lse,
+                                  void* stream);
 
 /*
  * Masked full-catalog head: as genrec_score_lse_topk, over the items a

@@ -237,3 +237,17 @@ def test_ce_plan_query(L):
     assert L.genrec_describe_ce_plan(0, 64, 100, buf, 64) == INVALID
     assert L.genrec_describe_ce_plan(4, 64, 100, None, 64) == INVALID
     assert L.genrec_describe_ce_plan(4, 64, 1 << 31, buf, 64) == UNSUPPORTED
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(L):
+    """The allocation-free entry point refuses a call whose workspace exceeds
+    its fixed scratch before touching the device (argument errors first)."""
+    f = L.genrec_score_lse_topk_noalloc
+    big = (1024, 4096, 1_000_000, 500)
+    assert L.genrec_score_lse_topk_workspace(*big, 0) > genrec.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, FAKE, 0, *big, FAKE, FAKE, FAKE, None) == -5
+    assert genrec.status_string(-5) == "GENREC_ERR_TOO_LARGE"
+    assert f(None, FAKE, 0, *big, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 0, 4, 64, 100, 0, FAKE, FAKE, FAKE, None) == INVALID
+    small = (1, 2048, 5000, 100)
+    assert L.genrec_score_lse_topk_workspace(*small, 0) <= genrec.NOALLOC_SCRATCH_BYTES
