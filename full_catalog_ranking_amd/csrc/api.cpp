@@ -13,29 +13,11 @@
 #include "../../include/genrec.h"
 #include "launch.hpp"
 #include "plan.hpp"
+#include "validate.hpp"
 
 using namespace genrec;
 
 namespace {
-
-inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-
-// Shape/pointer checks shared by both entry points.  Returns GENREC_OK or the
-// status to report; never touches the device.
-int check_common(const void* H, const void* E, int dtype, int B, int D, int64_t M, int K,
-                 const int32_t* out_idx, const float* out_scores, const float* out_lse) {
-    if (dtype != GENREC_BF16 && dtype != GENREC_F32) return GENREC_ERR_INVALID_ARG;
-    if (B <= 0 || D <= 0 || M <= 0 || K <= 0) return GENREC_ERR_INVALID_ARG;
-    if (!H || !E || !out_idx || !out_scores || !out_lse) return GENREC_ERR_INVALID_ARG;
-    if (!aligned(H, 16) || !aligned(E, 16)) return GENREC_ERR_INVALID_ARG;
-    if (!aligned(out_idx, 4) || !aligned(out_scores, 4) || !aligned(out_lse, 4))
-        return GENREC_ERR_INVALID_ARG;
-    if (K > GENREC_KMAX) return GENREC_ERR_UNSUPPORTED;
-    if (M >= ((int64_t)1 << 31)) return GENREC_ERR_UNSUPPORTED;
-    if (D % (dtype == GENREC_BF16 ? 8 : 4) != 0) return GENREC_ERR_UNSUPPORTED;
-    if (D > GENREC_DMAX) return GENREC_ERR_UNSUPPORTED;
-    return GENREC_OK;
-}
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? GENREC_OK : GENREC_ERR_HIP; }
 
@@ -170,7 +152,7 @@ size_t genrec_score_lse_topk_workspace(int B, int D, int64_t M, int K, int dtype
     static const float dummy[4] = {0, 0, 0, 0};
     if (check_common(dummy, dummy, dtype, B, D, M, K, (const int32_t*)dummy, dummy, dummy) != GENREC_OK)
         return 0;
-    return plan_dense(B, D, M, K, dtype).total;
+    return plan_dense(B, D, M, K, dtype).total;  // 0 when the plan is unsupported
 }
 
 int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, size_t len) {
@@ -179,6 +161,7 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
     if (st != GENREC_OK) return st;
     if (!buf || len == 0) return GENREC_ERR_INVALID_ARG;
     const DensePlan p = plan_dense(B, D, M, K, dtype);
+    if (!p.ok) return GENREC_ERR_UNSUPPORTED;
     snprintf(buf, len,
              "{\"path\":\"%s\",\"sample\":%d,\"stride\":%lld,\"n_sample\":%lld,\"fast\":%d,\"r_fast\":%d,"
              "\"UT\":%d,\"P\":%d,\"tiles_per_chunk\":%d,\"CH\":%lld,\"merge_small\":%d,\"fused\":%d,"
@@ -207,6 +190,7 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     int st = check_common(H, E, dtype, B, D, M, K, out_idx, out_scores, out_lse);
     if (st != GENREC_OK) return st;
     const DensePlan p = plan_dense(B, D, M, K, dtype);
+    if (!p.ok) return GENREC_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < p.total) return GENREC_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
@@ -419,7 +403,9 @@ int genrec_score_lse_topk_noalloc(const void* H, const void* E, int dtype, int B
                                   int32_t* out_idx, float* out_scores, float* out_lse, void* stream) {
     int st = check_common(H, E, dtype, B, D, M, K, out_idx, out_scores, out_lse);
     if (st != GENREC_OK) return st;
-    if (plan_dense(B, D, M, K, dtype).total > GENREC_NOALLOC_SCRATCH_BYTES) return GENREC_ERR_TOO_LARGE;
+    const DensePlan p = plan_dense(B, D, M, K, dtype);
+    if (!p.ok) return GENREC_ERR_UNSUPPORTED;
+    if (p.total > GENREC_NOALLOC_SCRATCH_BYTES) return GENREC_ERR_TOO_LARGE;
     void* ws = nullptr;
     if ((st = scratch_on_current_device(&ws)) != GENREC_OK) return st;
     return score_dense(H, E, dtype, B, D, M, K, nullptr, 0, out_idx, out_scores, out_lse, ws,
@@ -470,6 +456,7 @@ int genrec_score_candidates_topk_profiled(const void* H, const void* E, int dtyp
     if (nnz < 0 || !cand_offsets || (nnz > 0 && !cand_ids)) return GENREC_ERR_INVALID_ARG;
     if (!aligned(cand_offsets, 8) || !aligned(cand_ids, 4)) return GENREC_ERR_INVALID_ARG;
     const CandPlan p = plan_cand(B, D, M, nnz, dtype);
+    if (!p.ok) return GENREC_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < p.total) return GENREC_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
@@ -597,6 +584,7 @@ int genrec_topk_rows(const float* scores, int R, int64_t N, int64_t ld, int K, i
     if (K > GENREC_KMAX) return GENREC_ERR_UNSUPPORTED;
     if (N >= ((int64_t)1 << 31)) return GENREC_ERR_UNSUPPORTED;
     const TopkPlan p = plan_topk(R, N, K);
+    if (!p.ok) return GENREC_ERR_UNSUPPORTED;
     if (p.workspace > 0 && (!workspace || workspace_bytes < p.workspace)) return GENREC_ERR_WORKSPACE;
     if (p.workspace > 0 && !aligned(workspace, 8)) return GENREC_ERR_INVALID_ARG;
     TopkRowsArgs a{};
@@ -619,16 +607,6 @@ int genrec_topk_rows(const float* scores, int R, int64_t N, int64_t ld, int K, i
 // ---------------------------------------------------------------------------
 namespace {
 
-int check_ce(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels, const float* weights) {
-    if (B <= 0 || D <= 0 || M <= 0) return GENREC_ERR_INVALID_ARG;
-    if (!H || !E || !labels) return GENREC_ERR_INVALID_ARG;
-    if (!aligned(H, 16) || !aligned(E, 16) || !aligned(labels, 4) || (weights && !aligned(weights, 4)))
-        return GENREC_ERR_INVALID_ARG;
-    if (M >= ((int64_t)1 << 31)) return GENREC_ERR_UNSUPPORTED;
-    if (D % 8 != 0 || D > GENREC_DMAX) return GENREC_ERR_UNSUPPORTED;
-    return GENREC_OK;
-}
-
 CeArgs ce_args(const void* H, const void* E, int B, int D, int64_t M, const int32_t* labels, const float* weights,
                void* workspace, const CePlan& p) {
     CeArgs c{};
@@ -648,7 +626,7 @@ CeArgs ce_args(const void* H, const void* E, int B, int D, int64_t M, const int3
 
 size_t genrec_ce_forward_workspace(int B, int D, int64_t M) {
     if (B <= 0 || D <= 0 || M <= 0 || M >= ((int64_t)1 << 31) || D > GENREC_DMAX) return 0;
-    return plan_ce(B, D, M).fwd_total;
+    return plan_ce(B, D, M).fwd_total;  // 0 when unsupported
 }
 
 size_t genrec_ce_backward_workspace(int B, int D, int64_t M) {
@@ -677,6 +655,7 @@ int genrec_ce_forward_profiled(const void* H, const void* E, int B, int D, int64
     if (st != GENREC_OK) return st;
     if (!out_loss || !out_lse || !aligned(out_loss, 4) || !aligned(out_lse, 4)) return GENREC_ERR_INVALID_ARG;
     const CePlan p = plan_ce(B, D, M);
+    if (!p.fwd_ok) return GENREC_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < p.fwd_total) return GENREC_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;

@@ -37,6 +37,29 @@ constexpr int64_t kFusedMaxM = 256 * 32;
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Workspace layouts: regions at 256-byte-aligned offsets, sizes checked so
+// that a huge shape makes the plan unsupported instead of wrapping a size_t
+// around to a small workspace.
+constexpr uint64_t kMaxWorkspace = (uint64_t)1 << 56;
+constexpr int64_t kMaxGrid = 2147483647;  // blocks per launch dimension
+
+struct Layout {
+    size_t o = 0;
+    bool ok = true;
+    // Reserves count elements of elem bytes; returns the region's offset.
+    size_t take(uint64_t elem, uint64_t count) {
+        const size_t at = o;
+        uint64_t bytes = 0;
+        if (__builtin_mul_overflow(elem, count, &bytes) || bytes > kMaxWorkspace || o > kMaxWorkspace - bytes) {
+            ok = false;
+            o = kMaxWorkspace;
+            return at;
+        }
+        o = align_up(o + bytes, 256);
+        return at;
+    }
+};
+
 struct Chunking {
     int UT = 1, P = 1, base = 0, rem = 0;  // MFMA: P chunks of base(+1) tiles over UT user tiles
     int64_t CH = 0;                        // VALU: items per chunk (P chunks)
@@ -48,6 +71,7 @@ constexpr int kMergeSmallGather = 2048;
 constexpr int kMergeSmallPieces = 512;
 
 struct DensePlan {
+    bool ok = true;  // false: the workspace or a grid would be too large (unsupported)
     bool mfma = false;
     bool sample = false;
     int64_t stride = 1;        // G: the sample holds catalog tiles 0, G, 2G, ... (full tiles only)
@@ -121,48 +145,37 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
         p.merge_small = (int64_t)p.main.P * p.pieces_per_chunk <= kMergeSmallPieces && expect <= kMergeSmallGather;
     }
     p.fused = !p.mfma && !p.sample && M <= kFusedMaxM;
-    size_t o = 0;
-    p.off_hdr = o;
-    o += 256;
+    // launch grids: MFMA passes UT x P blocks, VALU passes B x P, merge B
+    const int64_t grid = p.mfma ? (int64_t)p.main.UT * p.main.P : p.n_pieces;
+    const int64_t pre_grid = p.sample ? (p.mfma ? (int64_t)p.pre.UT * p.pre.P : (int64_t)B * p.pre.P) : 0;
+    p.ok = grid <= kMaxGrid && pre_grid <= kMaxGrid;
+    Layout L;
+    p.off_hdr = L.take(1, 256);
     if (p.fused) {
-        p.off_arrive = o;  // a flag per block: B x P
-        o = align_up(o + sizeof(uint64_t) * (size_t)p.n_pieces, 256);
-        p.off_elect = o;
-        o = align_up(o + sizeof(uint64_t) * (size_t)B, 256);
-        p.off_pm = o;
-        o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
-        p.off_pl = o;
-        o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
-        p.off_rows = o;
-        o = align_up(o + sizeof(float) * (size_t)B * (size_t)M, 256);
-        p.total = o;
-        return p;
+        p.off_arrive = L.take(sizeof(uint64_t), (uint64_t)p.n_pieces);  // a flag per block: B x P
+        p.off_elect = L.take(sizeof(uint64_t), (uint64_t)B);
+        p.off_pm = L.take(sizeof(float), (uint64_t)p.n_pieces);
+        p.off_pl = L.take(sizeof(float), (uint64_t)p.n_pieces);
+        p.off_rows = L.take(sizeof(float), (uint64_t)B * (uint64_t)M);
+    } else {
+        p.off_theta = L.take(sizeof(float), (uint64_t)B);
+        p.off_theta_safe = L.take(sizeof(float), (uint64_t)B);
+        p.off_uflag = L.take(sizeof(int), (uint64_t)B);
+        p.off_tflag = L.take(sizeof(int), (uint64_t)ceil_div(B, kMfmaTileUsers));
+        p.off_sample = L.take(sizeof(float), p.sample ? (uint64_t)B * (uint64_t)p.n_sample : 0);
+        p.off_pm = L.take(sizeof(float), (uint64_t)p.n_pieces);
+        p.off_pl = L.take(sizeof(float), (uint64_t)p.n_pieces);
+        p.off_pcnt = L.take(sizeof(int), (uint64_t)p.n_pieces);
+        p.off_preg = L.take(sizeof(int64_t), (uint64_t)p.n_pieces);
+        p.off_keys = L.take(sizeof(uint64_t), (uint64_t)B * (uint64_t)p.key_stride);
     }
-    p.off_theta = o;
-    o = align_up(o + sizeof(float) * (size_t)B, 256);
-    p.off_theta_safe = o;
-    o = align_up(o + sizeof(float) * (size_t)B, 256);
-    p.off_uflag = o;
-    o = align_up(o + sizeof(int) * (size_t)B, 256);
-    p.off_tflag = o;
-    o = align_up(o + sizeof(int) * (size_t)ceil_div(B, kMfmaTileUsers), 256);
-    p.off_sample = o;
-    if (p.sample) o = align_up(o + sizeof(float) * (size_t)B * (size_t)p.n_sample, 256);
-    p.off_pm = o;
-    o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
-    p.off_pl = o;
-    o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
-    p.off_pcnt = o;
-    o = align_up(o + sizeof(int) * (size_t)p.n_pieces, 256);
-    p.off_preg = o;
-    o = align_up(o + sizeof(int64_t) * (size_t)p.n_pieces, 256);
-    p.off_keys = o;
-    o = align_up(o + sizeof(uint64_t) * (size_t)B * (size_t)p.key_stride, 256);
-    p.total = o;
+    p.ok = p.ok && L.ok;
+    p.total = p.ok ? L.o : 0;
     return p;
 }
 
 struct CandPlan {
+    bool ok = true;  // false: the workspace or a grid would be too large (unsupported)
     int64_t n_pieces_max = 0;
     // Hot head (bf16, B >= 64): catalog items listed at least c times over all
     // lists (in sampled counts; c >= c_min, raised until at most t_max items
@@ -210,42 +223,29 @@ inline CandPlan plan_cand(int B, int D, int64_t M, int64_t nnz, int dtype) {
             p.hot_chunks = chunk_mfma(B, t / kMfmaTileItems);
         }
     }
-    size_t o = 0;
-    p.off_hdr = o;
-    o += 256;
-    p.off_begin = o;
-    o = align_up(o + sizeof(int) * ((size_t)B + 1), 256);
-    p.off_table = o;
-    o = align_up(o + 16 * (size_t)p.n_pieces_max, 256);
-    p.off_pm = o;
-    o = align_up(o + sizeof(float) * (size_t)p.n_pieces_max, 256);
-    p.off_pl = o;
-    o = align_up(o + sizeof(float) * (size_t)p.n_pieces_max, 256);
-    p.off_pcnt = o;
-    o = align_up(o + sizeof(int) * (size_t)p.n_pieces_max, 256);
-    p.off_preg = o;
-    o = align_up(o + sizeof(int64_t) * (size_t)p.n_pieces_max, 256);
-    p.off_keys = o;
-    o = align_up(o + sizeof(uint64_t) * (size_t)std::max<int64_t>(nnz, 1), 256);
+    // the list pass runs one block per piece; the piece table is int-indexed
+    p.ok = p.n_pieces_max <= kMaxGrid && nnz <= ((int64_t)1 << 40);
+    Layout L;
+    p.off_hdr = L.take(1, 256);
+    p.off_begin = L.take(sizeof(int), (uint64_t)B + 1);
+    p.off_table = L.take(16, (uint64_t)p.n_pieces_max);
+    p.off_pm = L.take(sizeof(float), (uint64_t)p.n_pieces_max);
+    p.off_pl = L.take(sizeof(float), (uint64_t)p.n_pieces_max);
+    p.off_pcnt = L.take(sizeof(int), (uint64_t)p.n_pieces_max);
+    p.off_preg = L.take(sizeof(int64_t), (uint64_t)p.n_pieces_max);
+    p.off_keys = L.take(sizeof(uint64_t), (uint64_t)std::max<int64_t>(nnz, 1));
     if (p.hot) {
-        p.off_cnt = o;
-        o = align_up(o + sizeof(int) * (size_t)M, 256);
-        p.off_hot_idx = o;
-        o = align_up(o + sizeof(int) * (size_t)M, 256);
-        p.off_hist = o;
-        o = align_up(o + sizeof(int) * (size_t)kHotBins, 256);
-        p.off_meta = o;
-        o = align_up(o + 256, 256);
-        p.off_hblk = o;
-        o = align_up(o + sizeof(int) * (size_t)p.n_hblk, 256);
-        p.off_hot_ids = o;
-        o = align_up(o + sizeof(int) * (size_t)p.t_max, 256);
-        p.off_ehot = o;
-        o = align_up(o + 2 * (size_t)p.t_max * (size_t)D, 256);
-        p.off_shot = o;
-        o = align_up(o + sizeof(float) * (size_t)B * (size_t)p.t_max, 256);
+        p.off_cnt = L.take(sizeof(int), (uint64_t)M);
+        p.off_hot_idx = L.take(sizeof(int), (uint64_t)M);
+        p.off_hist = L.take(sizeof(int), (uint64_t)kHotBins);
+        p.off_meta = L.take(1, 256);
+        p.off_hblk = L.take(sizeof(int), (uint64_t)p.n_hblk);
+        p.off_hot_ids = L.take(sizeof(int), (uint64_t)p.t_max);
+        p.off_ehot = L.take(2, (uint64_t)p.t_max * (uint64_t)D);
+        p.off_shot = L.take(sizeof(float), (uint64_t)B * (uint64_t)p.t_max);
     }
-    p.total = o;
+    p.ok = p.ok && L.ok;
+    p.total = p.ok ? L.o : 0;
     return p;
 }
 
@@ -267,6 +267,7 @@ constexpr int64_t kTopkMergeKeys = 8192;
 constexpr int64_t kTopkRegMinBlocks = 2 * kNumCU;
 
 struct TopkPlan {
+    bool ok = true;    // false: the workspace or the grid would be too large (unsupported)
     bool reg = false;  // register-resident selection (else histogram narrowing)
     int64_t C = 0;     // columns per chunk (segment)
     int nchunk = 1;
@@ -280,15 +281,20 @@ inline TopkPlan plan_topk(int R, int64_t N, int K) {
         p.reg = true;
         p.C = kTopkSeg;
         p.nchunk = (int)nseg;
-        p.workspace = sizeof(uint64_t) * (size_t)R * (size_t)nseg * (size_t)K;
-        return p;
+    } else {
+        const int64_t max_chunks = std::max<int64_t>(1, kTopkGather / std::max(1, K));
+        int64_t C = std::max(kTopkChunkMin, ceil_div(N, max_chunks));
+        C = ceil_div(C, 4096) * 4096;
+        p.C = C;
+        p.nchunk = (int)ceil_div(N, C);
     }
-    const int64_t max_chunks = std::max<int64_t>(1, kTopkGather / std::max(1, K));
-    int64_t C = std::max(kTopkChunkMin, ceil_div(N, max_chunks));
-    C = ceil_div(C, 4096) * 4096;
-    p.C = C;
-    p.nchunk = (int)ceil_div(N, C);
-    if (p.nchunk > 1) p.workspace = sizeof(uint64_t) * (size_t)R * (size_t)p.nchunk * (size_t)K;
+    p.ok = (int64_t)R * p.nchunk <= kMaxGrid;  // one block per (row, chunk)
+    if (p.nchunk > 1) {
+        Layout L;
+        L.take(sizeof(uint64_t) * (uint64_t)p.nchunk, (uint64_t)R * (uint64_t)K);
+        p.ok = p.ok && L.ok;
+        p.workspace = p.ok ? sizeof(uint64_t) * (size_t)R * (size_t)p.nchunk * (size_t)K : 0;
+    }
     return p;
 }
 
@@ -303,7 +309,9 @@ constexpr int64_t kCeBlockedMaxBytes = (int64_t)1 << 30;
 constexpr int kCeMaxSplits = 8;      // reduction splits of the dH product (powers of two)
 
 struct CePlan {
-    bool ok = true;  // false: a blocked operand cannot fit 256 catalog rows (B or D > 2^21)
+    bool ok = true;  // backward: false when a blocked operand cannot fit 256 catalog rows (B or D > 2^21)
+                     // or the workspace would be too large
+    bool fwd_ok = true;  // forward: false when its workspace would be too large
     Chunking main;  // forward logsumexp pass over the catalog
     int64_t n_pieces = 0;
     int64_t Bp = 0;        // users padded to 32 (reduction of the dE product)
@@ -329,33 +337,26 @@ inline CePlan plan_ce(int B, int D, int64_t M) {
     const int64_t tiles = ceil_div(B, kMfmaTileUsers) * ceil_div(D, kMfmaTileItems);
     // two rounds of blocks measured faster than one round of twice the work
     while (p.splits < kCeMaxSplits && tiles * p.splits < 2 * kNumCU) p.splits *= 2;
-    size_t o = 0;
-    p.off_hdr = o;
-    o += 256;
-    p.off_w = o;
-    o = align_up(o + sizeof(float) * (size_t)B, 256);
-    const size_t common = o;
-    p.off_pm = o;
-    o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
-    p.off_pl = o;
-    o = align_up(o + sizeof(float) * (size_t)p.n_pieces, 256);
-    p.off_pcnt = o;
-    o = align_up(o + sizeof(int) * (size_t)p.n_pieces, 256);
-    p.off_preg = o;
-    o = align_up(o + sizeof(int64_t) * (size_t)p.n_pieces, 256);
-    p.fwd_total = o;
-    o = common;
-    p.off_ht = o;
-    o = align_up(o + 2 * (size_t)D * (size_t)p.Bp, 256);
-    p.off_et = o;
-    o = align_up(o + 2 * (size_t)D * (size_t)p.Mcp, 256);
-    p.off_grows = o;  // k-blocked, Bp rows per block of 32 catalog rows
-    o = align_up(o + 2 * (size_t)p.Bp * (size_t)p.Mcp, 256);
-    p.off_gcols = o;
-    o = align_up(o + 2 * (size_t)p.Mcp * (size_t)p.Bp, 256);
-    p.off_dhp = o;
-    o = align_up(o + sizeof(float) * (size_t)p.splits * (size_t)B * (size_t)D, 256);
-    p.bwd_total = o;
+    Layout L;
+    p.off_hdr = L.take(1, 256);
+    p.off_w = L.take(sizeof(float), (uint64_t)B);
+    Layout F = L;  // forward: the logsumexp pieces after the common part
+    p.off_pm = F.take(sizeof(float), (uint64_t)p.n_pieces);
+    p.off_pl = F.take(sizeof(float), (uint64_t)p.n_pieces);
+    p.off_pcnt = F.take(sizeof(int), (uint64_t)p.n_pieces);
+    p.off_preg = F.take(sizeof(int64_t), (uint64_t)p.n_pieces);
+    p.off_ht = L.take(2, (uint64_t)D * (uint64_t)p.Bp);
+    p.off_et = L.take(2, (uint64_t)D * (uint64_t)p.Mcp);
+    p.off_grows = L.take(2, (uint64_t)p.Bp * (uint64_t)p.Mcp);  // k-blocked, Bp rows per block of 32 catalog rows
+    p.off_gcols = L.take(2, (uint64_t)p.Mcp * (uint64_t)p.Bp);
+    p.off_dhp = L.take(sizeof(float), (uint64_t)p.splits * (uint64_t)B * (uint64_t)D);
+    // the forward's MFMA grid (UT x P) and the merge's (B) are small; the
+    // dH product's is ceil(B/256) x P x splits
+    const bool grids = (int64_t)p.main.UT * p.main.P <= kMaxGrid;
+    p.fwd_ok = F.ok && grids;
+    p.ok = p.ok && L.ok && grids;
+    p.fwd_total = p.fwd_ok ? F.o : 0;
+    p.bwd_total = p.ok ? L.o : 0;
     return p;
 }
 
