@@ -257,6 +257,7 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     if (p.mfma) {
         a.H = (const uint16_t*)H;
         a.E = (const uint16_t*)E;
+        a.f32 = f32 ? 1 : 0;
         a.B = B;
         a.D = D;
         a.M = M;

@@ -51,9 +51,20 @@ namespace genrec {
 #define MF_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0F70 | ((n) & 15))
 #define MF_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt((((n) >> 4) << 14) | 0x0070 | ((n) & 15))
 
-template <int MODE, bool KTAIL, bool MASKED>
+// F32: fp32 operands on the fp32 matrix cores (v_mfma_f32_32x32x2_f32).  The
+// staged rows are 64 bytes either way -- 32 bf16 or 16 fp32 of the reduction
+// per k-step -- so the DMA, the LDS layout and the fragment reads are the same;
+// a 16-byte fragment holds 4 fp32 (not 8 bf16) and feeds four MFMAs of depth
+// 2 instead of one of depth 16 (each lane half takes its own 4 k values, the
+// same k for both operands: a fixed reordering of the reduction).  The
+// accumulator layout, hence the epilogue, is the same.
+template <int MODE, bool KTAIL, bool MASKED, bool F32 = false>
 __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[MF_NS][MF_STAGE];
+    static_assert(!F32 || MODE <= 1, "fp32 operands: the dense sample and main passes only");
+    constexpr int ES = F32 ? 4 : 2;         // bytes per element
+    constexpr int KE = MF_ROWB / ES;        // reduction elements per k-step (32 bf16 / 16 fp32)
+    constexpr int CE = 16 / ES;             // elements per 16-byte k-chunk
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wi = w & 1, wu = w >> 1;  // wave tile: items wi*128 .. +128, users wu*64 .. +64
@@ -71,7 +82,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     // dense pass over a partly filled catalog: chunks past its live rows are idle
     if (MODE == 0 && a.live_rows != nullptr && (int64_t)tile0 * a.tile_stride * MF_TI >= *a.live_rows) return;
     const int u0 = ut * MF_TU;
-    const int nk = (a.D + MF_BK - 1) / MF_BK;
+    const int nk = (a.D + KE - 1) / KE;
     const int D = a.D;
     // row stride of both operands, and where this block's share of the
     // reduction starts in every row (grid y splits it)
@@ -97,21 +108,22 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     // partial tile read as zeros without any clamping; k-chunks past D read
     // the next row or zeros, and the fragment reads replace them by zeros.
     const int wsu = __builtin_amdgcn_readfirstlane(w);  // wave index, provably uniform
+    const int64_t row_bytes = ldr * ES;
     uint32_t voff[MF_DMA];
 #pragma unroll
-    for (int j = 0; j < MF_DMA; ++j) voff[j] = (uint32_t)mf_dma_voff(w, lane, j, (int)ldr);
-    const int64_t row_bytes = ldr * 2;
+    for (int j = 0; j < MF_DMA; ++j) voff[j] = (uint32_t)mf_dma_voff_bytes(w, lane, j, row_bytes);
     // The user tile's resource is fixed; the catalog tile's is rebuilt when the
     // DMA moves to a new tile.  k0 rides in the scalar offset, so rows past the
     // end (and k-chunks past D on the last row) fall outside the record count.
     const int h_rows = a.B - u0 < MF_TU ? a.B - u0 : MF_TU;
     const int64_t h_off = (int64_t)u0 * (BLKD ? MF_BK : ldr) + kofs_h;  // elements
     const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.H + h_off), (short)0, (int)(BLKD ? (a.h_elems - h_off) * 2 : h_rows * row_bytes), 0x00020000);
+        (void*)((const uint8_t*)a.H + h_off * ES), (short)0, (int)(BLKD ? (a.h_elems - h_off) * 2 : h_rows * row_bytes),
+        0x00020000);
     __amdgpu_buffer_rsrc_t er;
     auto e_rsrc = [&](int t) {
         const int64_t e_off = tile_item0(t) * (BLKD ? MF_BK : ldr) + kofs_e;
-        er = __builtin_amdgcn_make_buffer_rsrc((void*)(a.E + e_off), (short)0,
+        er = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a.E + e_off * ES), (short)0,
                                                (int)(BLKD ? (a.e_elems - e_off) * 2 : tile_valid(t) * row_bytes),
                                                0x00020000);
     };
@@ -120,8 +132,8 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     auto dma_op = [&](int stg, int k0, int j) {
         uint8_t* sE = smem[stg] + mf_dma_lds_byte(wsu, 0, 0);
         uint8_t* sH = smem[stg] + MF_TI * MF_ROWB + mf_dma_lds_byte(wsu, 0, 0);
-        const int soff_e = BLKD ? (int)(k0 / MF_BK * a.blk_e * 2) : k0 * 2;
-        const int soff_h = BLKD ? (int)(k0 / MF_BK * a.blk_h * 2) : k0 * 2;
+        const int soff_e = BLKD ? (int)(k0 / MF_BK * a.blk_e * 2) : k0 * ES;
+        const int soff_h = BLKD ? (int)(k0 / MF_BK * a.blk_h * 2) : k0 * ES;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(er, (__attribute__((address_space(3))) void*)(sE + j * MF_NW * 1024),
                                                  16, (int)voff[j], soff_e, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (__attribute__((address_space(3))) void*)(sH + j * MF_NW * 1024),
@@ -142,7 +154,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         // row's first elements (or zeros), which need not be finite: the hot
         // rows of a candidate call are gathered into a workspace whose rows
         // past the live ones are stale, and NaN times zero is NaN.
-        const bool kin = !KTAIL || k0 + chunk * 8 < D;
+        const bool kin = !KTAIL || k0 + chunk * CE < D;
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) {
             f.a[ib] = *(const bf16x8_t*)(sE + mf_frag_lds_byte(wi * 128 + ib * 32 + (lane & 31), chunk));
@@ -158,8 +170,16 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-            for (int ub = 0; ub < MF_UB; ++ub)
-                acc[ib][ub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ib], f.b[ub], acc[ib][ub], 0, 0, 0);
+            for (int ub = 0; ub < MF_UB; ++ub) {
+                if constexpr (F32) {
+                    const f32x4_t fa = __builtin_bit_cast(f32x4_t, f.a[ib]), fb = __builtin_bit_cast(f32x4_t, f.b[ub]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[ib][ub] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[e], fb[e], acc[ib][ub], 0, 0, 0);
+                } else {
+                    acc[ib][ub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ib], f.b[ub], acc[ib][ub], 0, 0, 0);
+                }
+            }
     };
 
     // ---- epilogue state ---------------------------------------------------
@@ -389,8 +409,8 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     };
 #pragma unroll
     for (int q = 0; q < MF_NS - 1; ++q) {
-        dma_op(ls, lk * MF_BK, 0);
-        dma_op(ls, lk * MF_BK, 1);
+        dma_op(ls, lk * KE, 0);
+        dma_op(ls, lk * KE, 1);
         advance();
     }
     MF_WAIT_VMCNT((MF_NS - 2) * kOpsPerStep);
@@ -404,30 +424,33 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
             for (int ub = 0; ub < MF_UB; ++ub) acc[ib][ub] = f32x16_t{};
+        // MFMAs per half step, and the spacing R of the schedule's reads and DMA
+        // ops among them (one MFMA apart for bf16, four for fp32)
+        constexpr int NMF = 4 * MF_UB * (F32 ? 4 : 1), R = NMF / (4 * MF_UB);
         for (int k = 0; k < nk; ++k) {
-            dma_op(ls, lk * MF_BK, 0);
-            load_frag(f1, cs, 1, k * MF_BK);
+            dma_op(ls, lk * KE, 0);
+            load_frag(f1, cs, 1, k * KE);
             mma(f0);
-            // schedule: slice-1 reads between the MFMAs, the two DMA ops after MFMAs 3 and 6
+            // schedule: slice-1 reads between the MFMAs, the two DMA ops after MFMA groups 3 and 6
 #pragma unroll
-            for (int i = 0; i < 4 * MF_UB; ++i) {
+            for (int i = 0; i < NMF; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-                if (i < 4 + MF_UB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-                if (i == 2 || i == 5) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA)
+                if (i % R == 0 && i / R < 4 + MF_UB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                if (i == 2 * R || i == 5 * R) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (DMA)
             }
             MF_WAIT_VMCNT_LDS(kWaitOps);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
             cs = cs + 1 == MF_NS ? 0 : cs + 1;
-            dma_op(ls, lk * MF_BK, 1);
+            dma_op(ls, lk * KE, 1);
             // (on the very last step this reads a stage whose data is never used)
-            load_frag(f0, cs, 0, (k + 1 < nk ? k + 1 : 0) * MF_BK);
+            load_frag(f0, cs, 0, (k + 1 < nk ? k + 1 : 0) * KE);
             mma(f1);
 #pragma unroll
-            for (int i = 0; i < 4 * MF_UB; ++i) {
+            for (int i = 0; i < NMF; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                if (i < 4 + MF_UB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-                if (i == 2 || i == 5) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+                if (i % R == 0 && i / R < 4 + MF_UB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+                if (i == 2 * R || i == 5 * R) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
             }
             __builtin_amdgcn_sched_barrier(0);
             advance();
@@ -2475,8 +2498,29 @@ hipError_t launch_mfma_split(const MfmaArgs& a, int mode, int splits, hipStream_
 
 hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s) {
     const int grid = a.UT * a.P;
-    const bool ktail = (a.D % MF_BK) != 0;
     const bool masked = a.mask != nullptr;
+    if (a.f32) {
+        // fp32 operands: k-steps of 16 elements
+        const bool ktail = (a.D % (MF_BK / 2)) != 0;
+#define GENREC_MFMA32(MO, KT, MK) \
+    hipLaunchKernelGGL((mfma_score_kernel<MO, KT, MK, true>), dim3(grid), dim3(MF_NT), 0, s, a)
+        if (mode == 0) {
+            if (masked) {
+                if (ktail) GENREC_MFMA32(0, true, true); else GENREC_MFMA32(0, false, true);
+            } else {
+                if (ktail) GENREC_MFMA32(0, true, false); else GENREC_MFMA32(0, false, false);
+            }
+        } else {
+            if (masked) {
+                if (ktail) GENREC_MFMA32(1, true, true); else GENREC_MFMA32(1, false, true);
+            } else {
+                if (ktail) GENREC_MFMA32(1, true, false); else GENREC_MFMA32(1, false, false);
+            }
+        }
+#undef GENREC_MFMA32
+        return hipGetLastError();
+    }
+    const bool ktail = (a.D % MF_BK) != 0;
 #define GENREC_MFMA(MO, KT, MK) hipLaunchKernelGGL((mfma_score_kernel<MO, KT, MK>), dim3(grid), dim3(MF_NT), 0, s, a)
     if (mode == 0) {
         if (masked) {

@@ -11,8 +11,9 @@ namespace genrec {
 constexpr int CAND_PIECE = 256;  // candidate-list entries per work piece
 
 struct MfmaArgs {
-    const uint16_t* H;
+    const uint16_t* H;  // bf16 elements, or fp32 ones when f32 (modes 0 and 1)
     const uint16_t* E;
+    int f32;
     int B, D;
     int64_t M;
     int n_tiles, tile_stride; // pass-tile t = catalog rows [t*G*256, +256) clipped to M, G = tile_stride

@@ -42,12 +42,14 @@ GENREC_HD inline int mf_dma_row(int w, int lane, int j) { return mf_dma_row0(w, 
 // neither bit field it reads), so one k-chunk offset serves all ops.
 GENREC_HD inline int mf_dma_kchunk(int w, int lane) { return (lane & 3) ^ mf_swz(mf_dma_row0(w, lane)); }
 GENREC_HD inline int mf_dma_lds_byte(int w, int lane, int j) { return (j * MF_NW + w) * 1024 + lane * 16; }
-// Byte offset, within one operand tile of rows of D elements, that lane
+// Byte offset, within one operand tile of rows of row_bytes bytes, that lane
 // `lane` of wave `w` reads for op j (the k-chunk of the stage's k0 is added
-// through the tile base).
-GENREC_HD inline long long mf_dma_voff(int w, int lane, int j, int D) {
-    return ((long long)mf_dma_row(w, lane, j) * D + mf_dma_kchunk(w, lane) * 8) * 2;
+// through the tile base): its staged row's start plus its 16-byte k-chunk.
+GENREC_HD inline long long mf_dma_voff_bytes(int w, int lane, int j, long long row_bytes) {
+    return (long long)mf_dma_row(w, lane, j) * row_bytes + mf_dma_kchunk(w, lane) * 16;
 }
+// The same for rows of D bf16 elements.
+GENREC_HD inline long long mf_dma_voff(int w, int lane, int j, int D) { return mf_dma_voff_bytes(w, lane, j, 2LL * D); }
 
 // Fragment read: byte offset of (staged row, k-chunk) within an operand stage.
 GENREC_HD inline int mf_frag_lds_byte(int row, int kchunk) { return row * MF_ROWB + ((kchunk ^ mf_swz(row)) << 4); }

@@ -189,6 +189,8 @@ WORKLOADS = {
     "tiny":  dict(B=4, D=256, M=5000, K=10, dtype="f32"),
     "gemv":  dict(B=1, D=2048, M=5000, K=100, dtype="bf16"),
     "batch": dict(B=256, D=2048, M=100_000, K=100, dtype="bf16"),
+    # the batch shape with fp32 inputs (the fp32 matrix-core path)
+    "batch_f32": dict(B=256, D=2048, M=100_000, K=100, dtype="f32"),
     "large": dict(B=1024, D=4096, M=1_000_000, K=500, dtype="bf16"),
     "cand":  dict(B=4096, D=2048, M=1_000_000, K=100, dtype="bf16", lo=100, hi=3000),
     # one user against an 8 GB catalog: sustained catalog streaming at B = 1

@@ -144,7 +144,11 @@ def test_plan_selection(L):
     assert p["stride"] == 32 and p["n_sample"] == 123 * 256
     # small bf16 batches go to the matrix cores (E read once, not once per user)
     assert genrec.describe_plan(2, 96, 70_000, 50, torch.bfloat16)["path"] == "mfma"
-    assert genrec.describe_plan(8, 4096, 1_000_000, 100, torch.float32)["path"] == "stream"
+    # fp32 batches too, past the one-launch catalog size; one fp32 user streams
+    assert genrec.describe_plan(8, 4096, 1_000_000, 100, torch.float32)["path"] == "mfma"
+    assert genrec.describe_plan(256, 2048, 100_000, 100, torch.float32)["path"] == "mfma"
+    assert genrec.describe_plan(1, 4096, 1_000_000, 100, torch.float32)["path"] == "stream"
+    assert genrec.describe_plan(300, 256, 8192, 10, torch.float32)["fused"] == 1
     p = genrec.describe_plan(1, 2048, 5000, 100, torch.bfloat16)
     assert p["path"] == "stream" and p["sample"] == 0
     p = genrec.describe_plan(4, 256, 5000, 10, torch.float32)

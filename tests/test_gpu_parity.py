@@ -243,8 +243,8 @@ def test_masked_all_allowed_equals_unmasked(dev):
 @pytest.mark.parametrize("B,D,M,K,bf16", [
     (1, 96, 70000, 50, True),    # VALU path (B = 1) with the sampled pre-pass
     (1, 8, 1, 5, True),          # M = 1, K > M
-    (3, 64, 70000, 50, False),   # fp32 VALU path with the sampled pre-pass
-    (20, 256, 1500, 10, False),  # fp32 with many users (VALU path)
+    (1, 64, 70000, 50, False),   # fp32 VALU path with the sampled pre-pass
+    (20, 256, 1500, 10, False),  # fp32 with many users (one launch)
     (2, 4, 333, 333, False),     # K = M, smallest fp32 D
 ])
 def test_stream_ragged(dev, oracle_mod, B, D, M, K, bf16):
@@ -656,3 +656,40 @@ def test_fused_two_streams(dev, oracle_mod):
         for a, b in zip(rep, outs[0]):
             for x, y in zip(a, b):
                 assert np.array_equal(x, y)
+
+
+# ---------------------------------------------------------------------------
+# fp32 inputs on the matrix cores (v_mfma_f32_32x32x2_f32): batches of two or
+# more users over catalogs past the one-launch size
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,D,M,K", [
+    (256, 2048, 100_000, 100),   # the batch shape: sample, fast threshold
+    (300, 200, 70_001, 37),      # two user tiles (ragged), k tail (200 % 16 = 8), sampled pass
+    (3, 12, 9000, 20),           # one k-step, all of it k tail; no sample
+    (40, 64, 20_000, 1024),      # K = KMAX
+])
+def test_fp32_matrix_cores(dev, oracle_mod, B, D, M, K):
+    from full_catalog_ranking_amd import genrec
+    assert genrec.describe_plan(B, D, M, K, torch.float32)["path"] == "mfma"
+    d = synth.make_dense(B, D, M, seed=B + M + 1, bf16=False)
+    g = run_dense(d, K, dev)
+    users = sorted(set([0, 1, B // 2, B - 1] + list(range(0, B, max(1, B // 10)))))
+    ref = oracle_mod.full(d["H"], d["E"], K, users=users)
+    parity.check_dense(g, ref, where="fp32 mfma %s" % ((B, D, M, K),))
+
+
+def test_fp32_matrix_cores_masked(dev, oracle_mod):
+    from full_catalog_ranking_amd import genrec
+    B, D, M, K = 70, 96, 30_000, 25
+    d = synth.make_dense(B, D, M, seed=77, bf16=False)
+    rng = np.random.default_rng(78)
+    allowed = rng.random((B, M)) < rng.uniform(0.001, 1.0, B)[:, None]
+    words = _pack_mask(allowed)
+    mask = torch.from_numpy(words.view(np.int32)).to(dev)
+    H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
+    print("  fp32 mfma masked B=%d D=%d M=%d K=%d" % (B, D, M, K), flush=True)
+    idx, sc, ls = genrec.score_lse_topk(H, E, K, mask=mask)
+    g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
+    users = list(range(0, B, 7)) + [B - 1]
+    ref = oracle_mod.full_masked(d["H"], d["E"], K, words, users=users)
+    parity.check_dense(g, ref, where="fp32 mfma masked")
