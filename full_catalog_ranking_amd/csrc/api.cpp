@@ -165,10 +165,11 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
     snprintf(buf, len,
              "{\"path\":\"%s\",\"sample\":%d,\"stride\":%lld,\"n_sample\":%lld,\"fast\":%d,\"r_fast\":%d,"
              "\"UT\":%d,\"P\":%d,\"tiles_per_chunk\":%d,\"CH\":%lld,\"merge_small\":%d,\"fused\":%d,"
-             "\"workspace\":%zu}",
+             "\"sample_splits\":%d,\"safe_exact\":%d,\"workspace\":%zu}",
              p.mfma ? "mfma" : "stream", p.sample ? 1 : 0, (long long)p.stride, (long long)p.n_sample,
              p.fast ? 1 : 0, p.r_fast, p.main.UT, p.main.P, p.main.base + (p.main.rem ? 1 : 0),
-             (long long)p.main.CH, p.merge_small ? 1 : 0, p.fused ? 1 : 0, p.total);
+             (long long)p.main.CH, p.merge_small ? 1 : 0, p.fused ? 1 : 0, p.sample_splits, p.safe_exact ? 1 : 0,
+             p.total);
     return GENREC_OK;
 }
 
@@ -245,6 +246,8 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     th.B = B;
     th.K = K;
     th.r_fast = p.r_fast;
+    th.n_split = p.sample_splits;
+    th.split_stride = (int64_t)B * p.n_sample;
     th.theta_safe = theta_safe;
     th.theta_fast = p.fast ? theta_fast : nullptr;
     th.user_flag = uflag;
@@ -271,8 +274,20 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
             a.base = p.pre.base;
             a.rem = p.pre.rem;
             a.sample_out = sample;
-            if ((st = hip_status(timed(prof, KIND_SAMPLE, s, [&] { return launch_mfma(a, 0, s); }))) != GENREC_OK) return st;
+            // reduction split over grid y: each split's partial scores in a row
+            // block of its own, summed by the threshold kernel
+            a.ld = D;
+            a.D = D / p.sample_splits;
+            a.k_split = D / p.sample_splits;
+            a.sample_split = (int64_t)B * p.n_sample;
+            if ((st = hip_status(timed(prof, KIND_SAMPLE, s, [&] { return launch_mfma(a, 0, s, p.sample_splits); }))) !=
+                GENREC_OK)
+                return st;
             if ((st = hip_status(timed(prof, KIND_THRESHOLD, s, [&] { return launch_threshold(th, s); }))) != GENREC_OK) return st;
+            a.ld = 0;
+            a.D = D;
+            a.k_split = 0;
+            a.sample_split = 0;
         }
         a.n_tiles = (int)ceil_div(M, kMfmaTileItems);
         a.tile_stride = 1;
@@ -341,13 +356,16 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     m.rescued = rescued;
     m.theta_fast = theta_fast;
     m.theta_safe = theta_safe;
+    m.safe_exact = p.safe_exact ? 1 : 0;
     m.small = p.merge_small ? 1 : 0;
     if ((st = hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }))) != GENREC_OK) return st;
     if (!p.fast) return GENREC_OK;
     // Rescue: users the fast threshold left short of K candidates are scored
-    // again (their whole user tile) with the K-th sampled score and merged;
-    // with no flagged user both launches exit at once.
-    a.theta = theta_safe;
+    // again (their whole user tile) with the K-th sampled score -- or, when
+    // the sampled scores came from a split reduction, with no threshold at all
+    // (the regions hold every score) -- and merged; with no flagged user both
+    // launches exit at once.
+    a.theta = p.safe_exact ? theta_safe : nullptr;
     a.tile_flag = tflag;
     a.user_flag = uflag;
     if ((st = hip_status(timed(prof, KIND_RESCUE, s, [&] { return launch_mfma(a, 1, s); }))) != GENREC_OK) return st;

@@ -317,7 +317,8 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             }
             if (MODE == 0) {
                 if (u < a.B) {  // rows jq .. jq+3 of the lane are consecutive items: one 16-byte store
-                    float* orow = a.sample_out + (int64_t)u * n_pass + (int64_t)t * MF_TI;
+                    float* orow = a.sample_out + (int64_t)blockIdx.y * a.sample_split + (int64_t)u * n_pass +
+                                  (int64_t)t * MF_TI;
 #pragma unroll
                     for (int ib = 0; ib < 4; ++ib) {
                         const uint32_t mw = mask_word(ib);
@@ -897,19 +898,34 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
     }
     // key e of thread t: e = 4 TH_NT i + 4 t + j (j < 4): 16-byte loads,
     // contiguous across the block
+    // (sampled scores of a split reduction: the partial rows summed in split order)
     const float* row = a.sample + (int64_t)b * a.n_sample;
+    auto sample_at = [&](int e) {
+        float x = row[e];
+        for (int z = 1; z < a.n_split; ++z) x += row[(int64_t)z * a.split_stride + e];
+        return x;
+    };
     uint32_t key[TH_PER];  // 0 = no key (every score's key is larger)
     unsigned lo = ~0u, hi = 0u;
 #pragma unroll
     for (int i = 0; i < TH_PER / 4; ++i) {
         const int e = i * (TH_NT * 4) + tid * 4;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (e + 3 < n) v = *(const float4*)(row + e);
+        if (e + 3 < n) {
+            v = *(const float4*)(row + e);
+            for (int z = 1; z < a.n_split; ++z) {
+                const float4 p = *(const float4*)(row + (int64_t)z * a.split_stride + e);
+                v.x += p.x;
+                v.y += p.y;
+                v.z += p.z;
+                v.w += p.w;
+            }
+        }
         const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const bool in = e + 3 < n ? true : (e + j < n);
-            const float x = (e + 3 < n) ? f[j] : (e + j < n ? row[e + j] : 0.f);
+            const float x = (e + 3 < n) ? f[j] : (e + j < n ? sample_at(e + j) : 0.f);
             key[4 * i + j] = in ? order_key(x) : 0u;
             if (in) {
                 lo = min(lo, key[4 * i + j]);
@@ -1188,7 +1204,7 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     tot.init();
     unsigned long long ntot = 0;
     for (int q = 0; q < SEL_NT / kWave; ++q) { tot.merge(s_ml[q].x, s_ml[q].y); ntot += s_n[q]; }
-    if (a.mode == 1 && ntot < (unsigned long long)a.K && a.theta_fast[b] > a.theta_safe[b]) {
+    if (a.mode == 1 && ntot < (unsigned long long)a.K && (!a.safe_exact || a.theta_fast[b] > a.theta_safe[b])) {
         // the fast threshold let fewer than K items through: the rescue pass
         // recomputes this user with the K-th sampled score (when that is
         // lower: else every item it would keep was kept, e.g. a user with
@@ -2496,14 +2512,15 @@ hipError_t launch_mfma_split(const MfmaArgs& a, int mode, int splits, hipStream_
     return hipGetLastError();
 }
 
-hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s) {
-    const int grid = a.UT * a.P;
+hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s, int splits) {
+    if (splits < 1 || (splits > 1 && mode != 0)) return hipErrorInvalidValue;
+    const dim3 grid(a.UT * a.P, splits);
     const bool masked = a.mask != nullptr;
     if (a.f32) {
         // fp32 operands: k-steps of 16 elements
         const bool ktail = (a.D % (MF_BK / 2)) != 0;
 #define GENREC_MFMA32(MO, KT, MK) \
-    hipLaunchKernelGGL((mfma_score_kernel<MO, KT, MK, true>), dim3(grid), dim3(MF_NT), 0, s, a)
+    hipLaunchKernelGGL((mfma_score_kernel<MO, KT, MK, true>), grid, dim3(MF_NT), 0, s, a)
         if (mode == 0) {
             if (masked) {
                 if (ktail) GENREC_MFMA32(0, true, true); else GENREC_MFMA32(0, false, true);
@@ -2521,7 +2538,7 @@ hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s) {
         return hipGetLastError();
     }
     const bool ktail = (a.D % MF_BK) != 0;
-#define GENREC_MFMA(MO, KT, MK) hipLaunchKernelGGL((mfma_score_kernel<MO, KT, MK>), dim3(grid), dim3(MF_NT), 0, s, a)
+#define GENREC_MFMA(MO, KT, MK) hipLaunchKernelGGL((mfma_score_kernel<MO, KT, MK>), grid, dim3(MF_NT), 0, s, a)
     if (mode == 0) {
         if (masked) {
             if (ktail) GENREC_MFMA(0, true, true); else GENREC_MFMA(0, false, true);

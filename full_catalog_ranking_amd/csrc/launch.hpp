@@ -18,7 +18,8 @@ struct MfmaArgs {
     int64_t M;
     int n_tiles, tile_stride; // pass-tile t = catalog rows [t*G*256, +256) clipped to M, G = tile_stride
     int UT, P, base, rem;     // user tiles; P chunks of base(+1) pass-tiles
-    float* sample_out;        // mode 0: [B][n_tiles * 256] scores
+    float* sample_out;        // mode 0: [B][n_tiles * 256] scores (split z of grid y at + z * sample_split)
+    int64_t sample_split;
     const float* theta;       // mode 1: [B] candidate thresholds (or null)
     uint64_t* keys;           // mode 1: candidate regions, [B][key_stride]
     int64_t key_stride;       // mode 1: >= 256 * ceil(M / 256)
@@ -190,17 +191,22 @@ struct MergeArgs {
     int* tile_flag;
     int64_t* rescued;
     // mode 1: a user is flagged only when the rescue threshold is lower than
-    // the fast one (else the first pass already kept every item it would)
+    // the fast one (else the first pass already kept every item it would);
+    // when the sampled scores were summed from reduction splits (safe_exact 0)
+    // the sampled thresholds are estimates and any user short of K is flagged
     const float* theta_fast;
     const float* theta_safe;
+    int safe_exact;
     // 1: the smaller merge build (users with at most ~512 pieces and ~2,048
     // candidates expected); any value gives the same result
     int small;
 };
 
 struct ThresholdArgs {
-    const float* sample;  // [B][n_sample] sampled scores
+    const float* sample;  // [B][n_sample] sampled scores: the sum of n_split partial rows split_stride apart
     int64_t n_sample;     // <= 32768
+    int n_split;
+    int64_t split_stride;
     int B, K, r_fast;
     float* theta_safe;    // [B] lower bound of the K-th largest sampled score
     float* theta_fast;    // [B] lower bound of the r_fast-th largest (may be null)
@@ -232,7 +238,8 @@ struct TopkRowsArgs {
     int reg;              // register-resident selection: chunks of kTopkSeg columns, nchunk >= 2, nchunk * K <= kTopkMergeKeys
 };
 
-hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s);
+// modes 0 / 1; splits > 1 (mode 0): grid y splits the reduction (a.D per split, a.ld the row stride)
+hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s, int splits = 1);
 hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s);
 hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, hipStream_t s);
 // the whole call in one launch (fused mode): grid = B * P blocks

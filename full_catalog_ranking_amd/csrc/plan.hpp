@@ -19,6 +19,7 @@ constexpr int64_t kSampleMinStride = 32; // sample every G-th catalog tile, G >=
 constexpr int64_t kSampleMaxTiles = 128; // sampled items per user at most 128 * 256
 constexpr int64_t kSampleMaxItems = 32768;  // = kSampleMaxTiles * 256: one user's sample fits the threshold kernel
 constexpr int kFastOversample = 4;     // fast threshold: expected candidates ~ 4 K
+constexpr int kSampleMaxSplits = 16;   // reduction splits of an MFMA sample pass that fills few CUs
 // MFMA path: the sample only has to place the fast threshold at rank >= 32 of
 // the sampled scores.  The number of catalog items above the r-th largest of
 // n sampled scores is about M r / n with a Gamma(r)-shaped spread, so at
@@ -90,6 +91,13 @@ struct DensePlan {
     int64_t key_stride = 0;    // candidate-region elements per user
     bool merge_small = false;  // the merge's smaller build serves this shape (a speed choice)
     bool fused = false;        // one launch: dense rows [B][M] f32 and per-user arrival words
+    // MFMA sample pass: its reduction split over `sample_splits` grid rows when
+    // it would otherwise fill few CUs (one sampled tile per block is one tile's
+    // latency); the sampled scores are then sums of partials, not bit-identical
+    // to the main pass, so the K-th sampled score is no safe threshold: the
+    // rescue pass then keeps every score of a flagged user
+    int sample_splits = 1;
+    bool safe_exact = true;
     size_t off_hdr = 0, off_theta = 0, off_theta_safe = 0, off_uflag = 0, off_tflag = 0, off_sample = 0,
            off_pm = 0, off_pl = 0, off_pcnt = 0, off_preg = 0, off_keys = 0, off_arrive = 0, off_elect = 0, off_rows = 0,
            total = 0;
@@ -137,6 +145,14 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
     p.fast = p.mfma && p.sample && p.r_fast < K;
     p.main = p.mfma ? chunk_mfma(B, ceil_div(M, kMfmaTileItems)) : chunk_stream(B, M);
     if (p.sample) p.pre = p.mfma ? chunk_mfma(B, p.sample_tiles) : chunk_stream(B, p.n_sample);
+    if (p.mfma && p.sample) {
+        const int64_t ke = dtype == 0 ? kMfmaBlockK : kMfmaBlockK / 2;  // reduction elements per k-step
+        const int64_t blocks = (int64_t)p.pre.UT * p.pre.P;
+        while (p.sample_splits < kSampleMaxSplits && blocks * p.sample_splits * 2 <= kNumCU &&
+               D % (ke * p.sample_splits * 2) == 0)
+            p.sample_splits *= 2;
+        p.safe_exact = p.sample_splits == 1;
+    }
     p.pieces_per_chunk = p.mfma ? 4 : 1;
     p.n_pieces = (int64_t)B * p.main.P * p.pieces_per_chunk;
     p.key_stride = p.mfma ? ceil_div(M, kMfmaTileItems) * kMfmaTileItems : M;
@@ -165,7 +181,7 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
         p.off_theta_safe = L.take(sizeof(float), (uint64_t)B);
         p.off_uflag = L.take(sizeof(int), (uint64_t)B);
         p.off_tflag = L.take(sizeof(int), (uint64_t)ceil_div(B, kMfmaTileUsers));
-        p.off_sample = L.take(sizeof(float), p.sample ? (uint64_t)B * (uint64_t)p.n_sample : 0);
+        p.off_sample = L.take(sizeof(float), p.sample ? (uint64_t)p.sample_splits * B * (uint64_t)p.n_sample : 0);
         p.off_pm = L.take(sizeof(float), (uint64_t)p.n_pieces);
         p.off_pl = L.take(sizeof(float), (uint64_t)p.n_pieces);
         p.off_pcnt = L.take(sizeof(int), (uint64_t)p.n_pieces);

@@ -89,6 +89,13 @@ static void check_dense(int B, int D, int64_t M, int K, int dt) {
         CHECK(p.key_stride == M, "%s: VALU key stride", what);
     }
     if (p.sample) {
+        // a split sample: splits a power of two dividing the reduction into whole k-steps, only
+        // for a sample pass that would fill few CUs, and then no exact threshold
+        const int64_t ke = dt == 0 ? kMfmaBlockK : kMfmaBlockK / 2;
+        const int S = p.sample_splits;
+        CHECK(S >= 1 && S <= kSampleMaxSplits && (S & (S - 1)) == 0 && (S == 1 || D % (ke * S) == 0), "%s: sample splits", what);
+        CHECK(S == 1 || (p.mfma && (int64_t)p.pre.UT * p.pre.P * S <= kNumCU), "%s: split sample fills the GPU", what);
+        CHECK(p.safe_exact == (S == 1), "%s: safe threshold exact iff unsplit", what);
         CHECK(p.n_sample <= kSampleMaxItems, "%s: sample above the threshold kernel's capacity", what);
         CHECK((p.sample_tiles - 1) * p.stride * kMfmaTileItems + kMfmaTileItems <= M, "%s: sampled tile past M", what);
         CHECK(p.r_fast >= 1 && p.r_fast <= K, "%s: fast rank", what);
@@ -110,7 +117,7 @@ static void check_dense(int B, int D, int64_t M, int K, int dt) {
                    {p.off_theta_safe, u128(B) * 4, "theta_safe"},
                    {p.off_uflag, u128(B) * 4, "uflag"},
                    {p.off_tflag, u128(ceil_div(B, kMfmaTileUsers)) * 4, "tflag"},
-                   {p.off_sample, p.sample ? u128(B) * u128(p.n_sample) * 4 : 0, "sample"},
+                   {p.off_sample, p.sample ? u128(p.sample_splits) * u128(B) * u128(p.n_sample) * 4 : 0, "sample"},
                    {p.off_pm, u128(p.n_pieces) * 4, "pm"},
                    {p.off_pl, u128(p.n_pieces) * 4, "pl"},
                    {p.off_pcnt, u128(p.n_pieces) * 4, "pcnt"},

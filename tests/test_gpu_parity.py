@@ -152,17 +152,21 @@ def test_mfma_ragged(dev, oracle_mod, B, D, M, K):
     parity.check_dense(g, ref, where="mfma %s" % ((B, D, M, K),))
 
 
-def test_fast_threshold_rescue(dev, oracle_mod):
+@pytest.mark.parametrize("D,split", [(64, True), (72, False)])
+def test_fast_threshold_rescue(dev, oracle_mod, D, split):
     """A user whose always-sampled catalog tile 0 holds 40 scaled copies of its
     own vector: the fast threshold (a high-ranked sampled score) lets fewer
     than K catalog items through for that user, the merge flags it, and the
-    rescue pass (the K-th sampled score) must still give the exact result;
-    every other user keeps its first-pass result."""
+    rescue pass must still give the exact result -- with the K-th sampled
+    score when the sample is bit-identical to the main pass (D = 72: no
+    reduction split), with every score when the sample was a split reduction
+    (D = 64); every other user keeps its first-pass result."""
     from full_catalog_ranking_amd import genrec
-    B, D, M, K = 16, 64, 131072, 100
+    B, M, K = 16, 131072, 100
     d = synth.make_dense(B, D, M, seed=11)
     plan = genrec.describe_plan(B, D, M, K, torch.bfloat16)
     assert plan["path"] == "mfma" and plan["fast"] == 1 and plan["r_fast"] < 40 < K
+    assert (plan["sample_splits"] > 1) == split and plan["safe_exact"] == (not split)
     h = synth.bf16_bits_to_f32(d["H"][3])
     E = d["E"].copy()
     for i in range(40):
