@@ -463,7 +463,9 @@ def main():
     roof["kernel"] = "mfma_score_kernel" if roof["bound"] == "mfma" else "stream_score_kernel"
     if fused:
         roof["kernel"] = "stream_score_kernel (fused: the whole call in one launch)"
-    roof["traffic"] = traffic_from_profile(roof["kernel"].split()[0], args.workload)
+    # the masked scoring kernel is its own instance: it has its own counter summary, if any
+    roof["traffic"] = traffic_from_profile(roof["kernel"].split()[0],
+                                           args.workload + ("_masked" if args.mask_density is not None else ""))
     roof["kernel_ms"] = main_ms
 
     res = {
