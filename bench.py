@@ -266,7 +266,8 @@ def bench_ce(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ms, med, mn = timed_steps(torch, lambda: step(prof), args.steps)
+    ms, med, mn = timed_steps(torch, step, args.steps)  # the timed steps, without the profiler
+    ms_prof = timed_steps(torch, lambda: step(prof), args.steps)[0]  # per-kernel durations
     kern = prof.summary()
     per_step = {k: v[1] / args.steps for k, v in kern.items()}
     log("step %.3f ms; kernels per step %s" % (ms, {k: "%.3f ms" % v for k, v in per_step.items()}))
@@ -280,7 +281,7 @@ def bench_ce(args):
     res = {
         "metric": METRIC, "value": B * M / (ms * 1e-3), "unit": "scores/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": med,
-        "ms_per_step_min": mn, "higher_is_better": True,
+        "ms_per_step_min": mn, "ms_per_step_profiled": ms_prof, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "ce", "B": B, "D": D, "M": M, "step": "forward+backward",
                    "dE": args.de_dtype},
@@ -383,26 +384,33 @@ def main():
         step()
     torch.cuda.synchronize()
     log("warmup done")
-    # timed region: every step records its kernels into the profiler (HIP events on the
-    # stream the kernels run on); the events add no synchronisation
+    # timed region: the steps as a caller runs them; then the same steps again with
+    # the library profiler's HIP events around every kernel (on the stream the
+    # kernels run on) for the per-kernel durations -- those events add a few
+    # microseconds to a step of a few short kernels, so they stay out of the
+    # timed region
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    if args.cold:
+
+    def cold_steps(p):
         # each step after a 1 GiB scratch write; only the steps are timed
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         per = []
         for _ in range(args.steps):
             scratch.fill_(1)
             start.record()
-            step(prof)
+            step(p)
             end.record()
             torch.cuda.synchronize()
             per.append(start.elapsed_time(end))
-        ms = sum(per) / args.steps
+        del scratch
         per.sort()
         med = per[args.steps // 2] if args.steps % 2 else 0.5 * (per[args.steps // 2 - 1] + per[args.steps // 2])
-        mn = per[0]
-        del scratch
+        return sum(per) / args.steps, med, per[0]
+
+    if args.cold:
+        ms, med, mn = cold_steps(None)
+        ms_prof = cold_steps(prof)[0]
     elif args.graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -412,28 +420,11 @@ def main():
         torch.cuda.synchronize()
         ms, med, mn = timed_steps(torch, g.replay, args.steps)
         del g
-        for _ in range(args.steps):  # per-kernel durations: eager steps
-            step(prof)
-        torch.cuda.synchronize()
+        ms_prof = timed_steps(torch, lambda: step(prof), args.steps)[0]  # per-kernel durations: eager steps
     else:
-        ms, med, mn = timed_steps(torch, lambda: step(prof), args.steps)
+        ms, med, mn = timed_steps(torch, step, args.steps)
+        ms_prof = timed_steps(torch, lambda: step(prof), args.steps)[0]
     kern = prof.summary()
-    # the same steps without the library profiler's events around each kernel
-    # (they add a few microseconds to a step of one short kernel)
-    if args.cold:
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        per = []
-        for _ in range(args.steps):
-            scratch.fill_(1)
-            start.record()
-            step()
-            end.record()
-            torch.cuda.synchronize()
-            per.append(start.elapsed_time(end))
-        del scratch
-        ms_plain = sum(per) / args.steps
-    else:
-        ms_plain = timed_steps(torch, step, args.steps)[0]
     log("step %.3f ms; kernels %s" % (ms, {k: "%.3f ms x%d" % (v[1] / v[0], v[0]) for k, v in kern.items()}))
 
     n_main, t_main = kern["main_score"]
@@ -478,7 +469,7 @@ def main():
         "ms_per_step": ms,
         "ms_per_step_median": med,
         "ms_per_step_min": mn,
-        "ms_per_step_unprofiled": ms_plain,
+        "ms_per_step_profiled": ms_prof,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
