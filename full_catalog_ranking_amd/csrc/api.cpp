@@ -12,6 +12,7 @@
 
 #include "../../include/genrec.h"
 #include "launch.hpp"
+#include "mfma_layout.hpp"
 #include "plan.hpp"
 #include "validate.hpp"
 
@@ -165,11 +166,11 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
     snprintf(buf, len,
              "{\"path\":\"%s\",\"sample\":%d,\"stride\":%lld,\"n_sample\":%lld,\"fast\":%d,\"r_fast\":%d,"
              "\"UT\":%d,\"P\":%d,\"tiles_per_chunk\":%d,\"CH\":%lld,\"merge_small\":%d,\"fused\":%d,"
-             "\"sample_splits\":%d,\"safe_exact\":%d,\"workspace\":%zu}",
+             "\"sample_splits\":%d,\"safe_exact\":%d,\"first_sampled_tile\":%lld,\"workspace\":%zu}",
              p.mfma ? "mfma" : "stream", p.sample ? 1 : 0, (long long)p.stride, (long long)p.n_sample,
              p.fast ? 1 : 0, p.r_fast, p.main.UT, p.main.P, p.main.base + (p.main.rem ? 1 : 0),
              (long long)p.main.CH, p.merge_small ? 1 : 0, p.fused ? 1 : 0, p.sample_splits, p.safe_exact ? 1 : 0,
-             p.total);
+             p.sample ? mf_sample_tile(0, p.stride, M / kMfmaTileItems) : -1LL, p.total);
     return GENREC_OK;
 }
 

@@ -93,8 +93,10 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     const int64_t kofs_e = BLKD ? kofs / MF_BK * a.blk_e : kofs;  // element offsets of the split
     const int64_t kofs_h = BLKD ? kofs / MF_BK * a.blk_h : kofs;
 
-    // Pass-tile t holds catalog rows [t*G*256, t*G*256 + 256) clipped to M.
-    auto tile_item0 = [&](int t) -> int64_t { return (int64_t)t * a.tile_stride * MF_TI; };
+    // Pass-tile t holds catalog rows [256 c, 256 c + 256) clipped to M, c = t
+    // (G = 1) or, for the sample (G > 1), one full tile of the window [t G, t G + G).
+    const int64_t full_tiles = a.M / MF_TI;
+    auto tile_item0 = [&](int t) -> int64_t { return mf_sample_tile(t, a.tile_stride, full_tiles) * MF_TI; };
     auto tile_valid = [&](int t) -> int {
         const int64_t left = a.M - tile_item0(t);
         return left < MF_TI ? (int)left : MF_TI;
@@ -1996,8 +1998,8 @@ __global__ __launch_bounds__(ST_NT) void stream_score_kernel(StreamArgs a) {
 #pragma unroll
             for (int u = 0; u < ST_U; ++u) {
                 ok[u] = g0 + u < n;
-                const int64_t j = jbeg + g0 + u;  // pass index -> catalog row (tile-strided sample)
-                item[u] = (j >> 8) * a.tile_stride * 256 + (j & 255);
+                const int64_t j = jbeg + g0 + u;  // pass index -> catalog row (one tile per sample window)
+                item[u] = mf_sample_tile(j >> 8, a.tile_stride, a.M >> 8) * 256 + (j & 255);
             }
         }
         float acc[ST_U];

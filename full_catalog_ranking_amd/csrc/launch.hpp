@@ -16,7 +16,7 @@ struct MfmaArgs {
     int f32;
     int B, D;
     int64_t M;
-    int n_tiles, tile_stride; // pass-tile t = catalog rows [t*G*256, +256) clipped to M, G = tile_stride
+    int n_tiles, tile_stride; // pass-tile t = catalog tile mf_sample_tile(t, G, M / 256), G = tile_stride
     int UT, P, base, rem;     // user tiles; P chunks of base(+1) pass-tiles
     float* sample_out;        // mode 0: [B][n_tiles * 256] scores (split z of grid y at + z * sample_split)
     int64_t sample_split;
@@ -114,7 +114,7 @@ struct StreamArgs {
     int B, D;
     int64_t M;
     int64_t n_items;          // dense modes: pass items j < n_items
-    int tile_stride;          // dense modes: item j is catalog row (j/256)*G*256 + j%256, G = tile_stride
+    int tile_stride;          // dense modes: item j is catalog row 256 mf_sample_tile(j/256, G, M/256) + j%256
     int64_t CH;               // dense modes: items per chunk
     int P;                    // dense modes: chunks per user
     const int32_t* ids;       // candidate mode

@@ -51,6 +51,22 @@ GENREC_HD inline long long mf_dma_voff_bytes(int w, int lane, int j, long long r
 // The same for rows of D bf16 elements.
 GENREC_HD inline long long mf_dma_voff(int w, int lane, int j, int D) { return mf_dma_voff_bytes(w, lane, j, 2LL * D); }
 
+// The sampled pre-pass scores one full catalog tile out of every window of G
+// (tiles [t G, t G + G) clipped to the full_tiles whole tiles): window t's
+// tile sits at a fixed pseudo-random position inside it (an integer hash of
+// t), not always at its start, so that a catalog stored in a periodic or
+// clustered order is not sampled in step with it.  G = 1: tile t itself.
+GENREC_HD inline long long mf_sample_tile(long long t, long long G, long long full_tiles) {
+    if (G <= 1) return t;
+    const long long w0 = t * G;
+    const long long span = full_tiles - w0 < G ? full_tiles - w0 : G;
+    unsigned h = (unsigned)(t + 1) * 0x9E3779B1u;
+    h ^= h >> 15;
+    h *= 0x85EBCA77u;
+    h ^= h >> 13;
+    return span > 0 ? w0 + (long long)(h % (unsigned)span) : w0;
+}
+
 // Fragment read: byte offset of (staged row, k-chunk) within an operand stage.
 GENREC_HD inline int mf_frag_lds_byte(int row, int kchunk) { return row * MF_ROWB + ((kchunk ^ mf_swz(row)) << 4); }
 

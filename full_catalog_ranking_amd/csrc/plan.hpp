@@ -15,7 +15,7 @@ constexpr int kMfmaTileUsers = 256;    // users per MFMA tile
 constexpr int kMfmaBlockK = 32;        // reduction elements per k-step (and per k-block of a blocked operand)
 constexpr int kStreamMaxB = 1;         // bf16 batches up to this size use the VALU path (a half-empty MFMA tile still beats re-reading E per user)
 constexpr int64_t kSampleMinM = 65536; // smaller catalogs skip the threshold pre-pass
-constexpr int64_t kSampleMinStride = 32; // sample every G-th catalog tile, G >= 32
+constexpr int64_t kSampleMinStride = 32; // sample one catalog tile of every G, G >= 32
 constexpr int64_t kSampleMaxTiles = 128; // sampled items per user at most 128 * 256
 constexpr int64_t kSampleMaxItems = 32768;  // = kSampleMaxTiles * 256: one user's sample fits the threshold kernel
 constexpr int kFastOversample = 4;     // fast threshold: expected candidates ~ 4 K
@@ -75,7 +75,7 @@ struct DensePlan {
     bool ok = true;  // false: the workspace or a grid would be too large (unsupported)
     bool mfma = false;
     bool sample = false;
-    int64_t stride = 1;        // G: the sample holds catalog tiles 0, G, 2G, ... (full tiles only)
+    int64_t stride = 1;        // G: the sample holds one full catalog tile of every G (mf_sample_tile)
     int64_t sample_tiles = 0;  // number of sampled 256-row tiles
     int64_t n_sample = 0;      // sampled items = 256 * sample_tiles
     // Fast threshold (MFMA path): the r_fast-th largest sampled score instead

@@ -72,6 +72,24 @@ int main() {
                     CHECK(off + 2LL * k0_max + 16 <= (long long)MF_TI * D * 2 + 2LL * MF_BK,
                           "offset past the tile");
                 }
+    // 3. sampled tiles: one full tile inside each window of G, distinct, in order
+    long long sample_cases = 0;
+    const long long Gs[] = {1, 2, 32, 33, 62, 1000};
+    const long long Fs[] = {1, 31, 32, 33, 390, 3906, 4095, 1000000};
+    for (long long G : Gs)
+        for (long long F : Fs) {
+            const long long T = (F + G - 1) / G;  // sampled tiles
+            long long prev = -1;
+            for (long long t = 0; t < T; ++t) {
+                const long long c = mf_sample_tile(t, G, F);
+                ++sample_cases;
+                CHECK(c >= t * G && c < t * G + G && c < F, "G %lld F %lld: window %lld -> tile %lld", G, F, t, c);
+                CHECK(c > prev, "G %lld F %lld: tiles out of order", G, F);
+                if (G == 1) CHECK(c == t, "G = 1 must keep the tile");
+                prev = c;
+            }
+        }
+    printf("sampled tiles: %lld checked\n", sample_cases);
     if (fails) {
         printf("%d layout checks failed\n", fails);
         return 1;

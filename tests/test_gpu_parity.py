@@ -154,8 +154,8 @@ def test_mfma_ragged(dev, oracle_mod, B, D, M, K):
 
 @pytest.mark.parametrize("D,split", [(64, True), (72, False)])
 def test_fast_threshold_rescue(dev, oracle_mod, D, split):
-    """A user whose always-sampled catalog tile 0 holds 40 scaled copies of its
-    own vector: the fast threshold (a high-ranked sampled score) lets fewer
+    """A user whose sampled catalog tile (the first window's) holds 40 scaled
+    copies of its own vector: the fast threshold (a high-ranked sampled score) lets fewer
     than K catalog items through for that user, the merge flags it, and the
     rescue pass must still give the exact result -- with the K-th sampled
     score when the sample is bit-identical to the main pass (D = 72: no
@@ -169,8 +169,10 @@ def test_fast_threshold_rescue(dev, oracle_mod, D, split):
     assert (plan["sample_splits"] > 1) == split and plan["safe_exact"] == (not split)
     h = synth.bf16_bits_to_f32(d["H"][3])
     E = d["E"].copy()
+    row0 = plan["first_sampled_tile"] * 256
+    assert 0 <= row0 < plan["stride"] * 256
     for i in range(40):
-        E[i] = synth.f32_to_bf16_bits((h * np.float32(0.05 + 0.001 * i)).astype(np.float32))
+        E[row0 + i] = synth.f32_to_bf16_bits((h * np.float32(0.05 + 0.001 * i)).astype(np.float32))
     H, Ed = to_dev(d["H"], dev), to_dev(E, dev)
     ws = torch.empty(genrec.workspace_bytes(B, D, M, K, H.dtype), dtype=torch.uint8, device=dev)
     print("  rescue B=%d D=%d M=%d K=%d plan=%s" % (B, D, M, K, plan), flush=True)
@@ -179,13 +181,45 @@ def test_fast_threshold_rescue(dev, oracle_mod, D, split):
     g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
     ref = oracle_mod.full(d["H"], E, K)
     parity.check_dense(g, ref, where="rescue")
-    assert set(g[0][3, :40].tolist()) == set(range(40))
+    assert set(g[0][3, :40].tolist()) == set(range(row0, row0 + 40))
     assert n_rescued == 1
     # a second call on the same workspace without the planted rows: no rescue
     idx, sc, ls = genrec.score_lse_topk(H, to_dev(d["E"], dev), K, workspace=ws)
     assert genrec.rescued_users(ws) == 0
     parity.check_dense((idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()),
                        oracle_mod.full(d["H"], d["E"], K, users=[0, 3, 15]), where="no rescue")
+
+
+def test_periodic_catalog_is_not_sampled_in_step(dev, oracle_mod):
+    """Every 32nd catalog tile (tiles 0, 32, 64, ...) holds rows of 4x the norm,
+    so they hold every user's highest scores -- a catalog stored in a periodic
+    order.  A sample of the first tile of every 32-tile window would be exactly
+    those tiles, and its fast threshold would let fewer than K items through
+    for every user (all of them rescued).  The sample takes a hashed position
+    inside each window, so at most one or two of its 13 tiles are such tiles:
+    the threshold is representative for nearly every user (the 14th-largest
+    score of one sampled 4x tile leaves fewer than K items for a few percent
+    of users, which the rescue pass handles), and the results match the
+    oracle."""
+    from full_catalog_ranking_amd import genrec
+    B, D, M, K = 256, 128, 100_000, 100
+    plan = genrec.describe_plan(B, D, M, K, torch.bfloat16)
+    assert plan["path"] == "mfma" and plan["fast"] == 1 and plan["stride"] == 32
+    d = synth.make_dense(B, D, M, seed=12)
+    E = synth.bf16_bits_to_f32(d["E"])
+    for t in range(0, M // 256, 32):
+        E[t * 256:(t + 1) * 256] *= np.float32(4.0)
+    Eb = synth.f32_to_bf16_bits(E)
+    H, Ed = to_dev(d["H"], dev), to_dev(Eb, dev)
+    ws = torch.empty(genrec.workspace_bytes(B, D, M, K, H.dtype), dtype=torch.uint8, device=dev)
+    print("  periodic catalog B=%d D=%d M=%d K=%d plan=%s" % (B, D, M, K, plan), flush=True)
+    idx, sc, ls = genrec.score_lse_topk(H, Ed, K, workspace=ws)
+    n_rescued = genrec.rescued_users(ws)
+    print("  rescued users: %d of %d" % (n_rescued, B), flush=True)
+    assert n_rescued < B // 8
+    g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
+    users = [0, 1, 77, 128, 255]
+    parity.check_dense(g, oracle_mod.full(d["H"], Eb, K, users=users), where="periodic catalog")
 
 
 def _pack_mask(allowed):
