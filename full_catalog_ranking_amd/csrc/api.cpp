@@ -618,7 +618,7 @@ int genrec_topk_rows(const float* scores, int R, int64_t N, int64_t ld, int K, i
     a.C = p.C;
     a.nchunk = p.nchunk;
     a.part = (uint64_t*)workspace;
-    a.reg = p.reg ? 1 : 0;
+    a.reg = p.row ? 2 : (p.reg ? 1 : 0);
     return hip_status(launch_topk_rows(a, (hipStream_t)stream));
 }
 

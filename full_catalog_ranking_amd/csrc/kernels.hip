@@ -272,7 +272,19 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                 if (u < a.B) {
                     float* cz = a.c_out + (int64_t)blockIdx.y * a.c_split;
 #pragma unroll
-                    for (int ib = 0; ib < 4; ++ib)
+                    for (int ib = 0; ib < 4; ++ib) {
+                        // [u][row ..] with c_accum: the block's four old float4
+                        // are read before any is written back, one trip to
+                        // memory for the four (a load after a store that may
+                        // alias it would wait for the one before)
+                        float4 old[4];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int jq = lrow0 + ib * 32 + q * 8;
+                            old[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+                            if (a.c_trans && a.c_accum && jq + 3 < lim)
+                                old[q] = *(const float4*)(cz + (int64_t)u * a.ldc + j0 + jq);
+                        }
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int jq = lrow0 + ib * 32 + q * 8;
@@ -283,7 +295,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                                     float4 v = make_float4(acc[ib][ub][4 * q], acc[ib][ub][4 * q + 1],
                                                            acc[ib][ub][4 * q + 2], acc[ib][ub][4 * q + 3]);
                                     if (a.c_accum) {
-                                        const float4 o4 = *(const float4*)o;
+                                        const float4 o4 = old[q];
                                         v.x += o4.x;
                                         v.y += o4.y;
                                         v.z += o4.z;
@@ -314,6 +326,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                                     }
                             }
                         }
+                    }
                 }
                 continue;
             }
@@ -780,6 +793,10 @@ __device__ uint64_t block_select(const Src& src, int k, Sh& sh) {
         }
         __syncthreads();
         ng = sh.cnt_b;
+        // every thread holds its copy before thread 0 clears the count for the
+        // last pass below (with no LDS narrowing pass in between, nothing else
+        // separates that read from the clear)
+        __syncthreads();
     }
     uint64_t kth;
     if (lo == hi) {  // every key left in the range is the k-th (equal keys)
@@ -1083,13 +1100,22 @@ struct PieceSrc {
         for (int64_t pb = p0; pb < p1; pb += MG_PB) {
             const int np = (int)min((int64_t)MG_PB, p1 - pb);
             // exclusive scan of the batch's counts (4 per thread)
+            // (indices clamped into the batch, np >= 1: every load is in
+            // flight before the first is used, none behind a branch of its own)
             int cv[MG_PB / SEL_NT];
+            int64_t bv[MG_PB / SEL_NT];
+#pragma unroll
+            for (int i = 0; i < MG_PB / SEL_NT; ++i) {
+                const int64_t p = pb + min(tid * (MG_PB / SEL_NT) + i, np - 1);
+                cv[i] = pcnt[p];
+                bv[i] = preg[p];
+            }
             int tsum = 0;
 #pragma unroll
             for (int i = 0; i < MG_PB / SEL_NT; ++i) {
                 const int p = tid * (MG_PB / SEL_NT) + i;
-                cv[i] = p < np ? pcnt[pb + p] : 0;
-                if (p < np) ps->base[p] = preg[pb + p];
+                if (p < np) ps->base[p] = bv[i];
+                else cv[i] = 0;
                 tsum += cv[i];
             }
             int incl = tsum;
@@ -1124,21 +1150,24 @@ struct PieceSrc {
                 }
                 int pi = lo_p;
                 int next = ps->pref[pi + 1];
-                int64_t src = ps->base[pi] + (e_beg - ps->pref[pi]);
+                int64_t off = ps->base[pi] - ps->pref[pi];  // entry e of piece pi is keys[off + e]
                 for (int e0 = e_beg; e0 < e_end; e0 += SEL_UNR) {
-                    uint64_t kv[SEL_UNR];
+                    // addresses first (LDS only), then the loads together; an
+                    // entry past the range reads the range's last one again
+                    int64_t at[SEL_UNR];
 #pragma unroll
                     for (int q = 0; q < SEL_UNR; ++q) {
-                        const int e = e0 + q;
-                        if (e < e_end) {
-                            while (e >= next) {  // crossed into the next non-empty piece
-                                ++pi;
-                                next = ps->pref[pi + 1];
-                                src = ps->base[pi] + (e - ps->pref[pi]);
-                            }
-                            kv[q] = keys[src++];
+                        const int e = min(e0 + q, e_end - 1);
+                        while (e >= next) {  // crossed into the next non-empty piece
+                            ++pi;
+                            next = ps->pref[pi + 1];
+                            off = ps->base[pi] - ps->pref[pi];
                         }
+                        at[q] = off + e;
                     }
+                    uint64_t kv[SEL_UNR];
+#pragma unroll
+                    for (int q = 0; q < SEL_UNR; ++q) kv[q] = keys[at[q]];
 #pragma unroll
                     for (int q = 0; q < SEL_UNR; ++q)
                         if (e0 + q < e_end) f(kv[q], ebase + e0 + q);
@@ -1190,9 +1219,24 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     LseState st;
     st.init();
     unsigned long long n = 0;
-    for (int64_t p = p0 + tid; p < p1; p += SEL_NT) {
-        st.merge(a.pm[p], a.pl[p]);
-        n += (unsigned long long)a.pcnt[p];
+    // four pieces per thread and round, their loads issued together (indices
+    // clamped into the user's pieces); merged in the same order as one by one
+    for (int64_t pq = p0 + tid; pq < p1; pq += 4 * SEL_NT) {
+        float pm4[4], pl4[4];
+        int pc4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t p = min(pq + (int64_t)i * SEL_NT, p1 - 1);
+            pm4[i] = a.pm[p];
+            pl4[i] = a.pl[p];
+            pc4[i] = a.pcnt[p];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (pq + (int64_t)i * SEL_NT < p1) {
+                st.merge(pm4[i], pl4[i]);
+                n += (unsigned long long)pc4[i];
+            }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -1264,10 +1308,8 @@ struct DenseRowSrc {
         for (int64_t e0 = threadIdx.x; e0 < n; e0 += (int64_t)SEL_NT * SEL_UNR) {
             float v[SEL_UNR];
 #pragma unroll
-            for (int q = 0; q < SEL_UNR; ++q) {
-                const int64_t e = e0 + (int64_t)q * SEL_NT;
-                v[q] = e < n ? row[e] : 0.f;
-            }
+            for (int q = 0; q < SEL_UNR; ++q)  // clamped (n >= 1 here): the loads are in flight together
+                v[q] = row[min(e0 + (int64_t)q * SEL_NT, n - 1)];
 #pragma unroll
             for (int q = 0; q < SEL_UNR; ++q) {
                 const int64_t e = e0 + (int64_t)q * SEL_NT;
@@ -1522,6 +1564,21 @@ __device__ void tk_emit(int k, int K, TkShared& sh, int32_t* oidx, float* osc) {
     }
 }
 
+// Order keys of a row's first n >= 1 scores, slot j of thread t holding
+// column j * TK_NT + t (key 0 past the row).  Every load is issued before
+// the first is used: a slot past the row reads the row's last score and
+// drops it, where a guarded load would sit behind a branch of its own and be
+// waited for before the next one starts (64 round trips to memory in turn).
+template <int V>
+__device__ __forceinline__ void load_row_keys(const float* row, int n, uint32_t (&hv)[V]) {
+    const int tid = threadIdx.x;
+    float v[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] = row[min(j * TK_NT + tid, n - 1)];
+#pragma unroll
+    for (int j = 0; j < V; ++j) hv[j] = j * TK_NT + tid < n ? order_key(v[j]) : 0u;
+}
+
 // Block (r, s): the top-K keys of segment s (TK_SEG columns) of row r for the
 // row merge, in no particular order (all K places written, zero keys past the
 // segment's count).
@@ -1533,11 +1590,7 @@ __global__ __launch_bounds__(TK_NT) void topk_seg_kernel(TopkRowsArgs a) {
     const int n = (int)min((int64_t)TK_SEG, a.N - c0);
     const float* row = a.scores + (int64_t)r * a.ld + c0;
     uint32_t hv[TK_V];
-#pragma unroll
-    for (int j = 0; j < TK_V; ++j) {
-        const int e = j * TK_NT + tid;
-        hv[j] = e < n ? order_key(row[e]) : 0u;
-    }
+    load_row_keys<TK_V>(row, n, hv);
     // Opaque from here on: otherwise the compiler carries "slot past the row
     // => word 0" into every bit decision and keeps all V row-end masks live
     // in scalar registers (spilled) across the whole selection.
@@ -1560,6 +1613,114 @@ __global__ __launch_bounds__(TK_NT) void topk_seg_kernel(TopkRowsArgs a) {
 
 // Block r: the top-K of the row's segment results (nchunk * K <= TK_NT * TK_MV
 // keys, zero keys in unused places).
+// Block r: the whole row (N <= TK_SEG) in registers, its top-K written out.
+// For K <= 256: T = the K-th largest of the threads' maxima (at least K keys
+// reach it, so the top K are among the keys >= T -- for unordered scores a
+// few times K of them), compacted into LDS and ranked; more than the LDS
+// list holds (heavy ties), or K > 256: the bit-by-bit selection.
+struct TkRowShared {
+    TkShared tk;
+    uint32_t tmax[TK_NT];
+    uint32_t tred[TK_NT / kWave];
+    int wcnt[TK_NT / kWave];
+};
+
+__global__ __launch_bounds__(TK_NT) void topk_row_kernel(TopkRowsArgs a) {
+    __shared__ TkRowShared srow;
+    TkShared& sh = srow.tk;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = blockIdx.x;
+    const int n = (int)a.N;
+    const float* row = a.scores + (int64_t)r * a.ld;
+    uint32_t hv[TK_V];
+    load_row_keys<TK_V>(row, n, hv);
+#pragma unroll
+    for (int j = 0; j < TK_V; ++j) asm volatile("" : "+v"(hv[j]));  // as in the segment kernel
+    const int K = a.K;
+    const int k = min(K, n);
+    int32_t* oidx = a.out_idx + (int64_t)r * K;
+    float* osc = a.out_scores + (int64_t)r * K;
+    if (K <= TK_SMALL) {  // block-uniform
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int j = 0; j < TK_V; ++j) mx = max(mx, hv[j]);
+        srow.tmax[tid] = mx;
+        __syncthreads();
+        // rank of this thread's maximum among all of them (strictly larger);
+        // a thread without keys has maximum 0, which qualifies only when fewer
+        // than K threads hold a key: then T = 0 admits every key
+        int rk = 0;
+        const uint4* t4 = (const uint4*)srow.tmax;
+#pragma unroll 8
+        for (int q = 0; q < TK_NT / 4; ++q) {
+            const uint4 v = t4[q];
+            rk += (v.x > mx) + (v.y > mx) + (v.z > mx) + (v.w > mx);
+        }
+        uint32_t tc = rk < K ? mx : 0xFFFFFFFFu;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) tc = min(tc, (uint32_t)__shfl_xor((int)tc, o));
+        if (lane == 0) srow.tred[w] = tc;
+        __syncthreads();
+        uint32_t T = srow.tred[0];
+#pragma unroll
+        for (int q = 1; q < TK_NT / kWave; ++q) T = min(T, srow.tred[q]);
+        // keys >= T: a 64-bit mask per thread, counted and scanned
+        uint64_t mask = 0;
+#pragma unroll
+        for (int j = 0; j < TK_V; ++j) mask |= (hv[j] != 0u && hv[j] >= T) ? (1ull << j) : 0ull;
+        const int c = __popcll(mask);
+        int incl = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+        }
+        if (lane == 63) srow.wcnt[w] = incl;
+        __syncthreads();
+        int base = incl - c, total = 0;
+#pragma unroll
+        for (int q = 0; q < TK_NT / kWave; ++q) {
+            base += q < w ? srow.wcnt[q] : 0;
+            total += srow.wcnt[q];
+        }
+        if (total <= GENREC_KMAX) {  // block-uniform
+            // slot by slot (a constant index keeps hv in registers; a loop
+            // over the mask's set bits would index it at run time)
+            const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)tid;  // index word of slot 0
+#pragma unroll
+            for (int j = 0; j < TK_V; ++j)
+                if ((mask >> j) & 1ull) sh.sel[base++] = ((uint64_t)hv[j] << 32) | (uint64_t)(lo0 - (uint32_t)(j * TK_NT));
+            __syncthreads();
+            // total >= k (T = 0 when fewer than K keys exist)
+            if (total <= TK_SMALL) block_rank_place(sh.sel, total, sh.sorted, k);
+            else block_sort_into(sh.sel, total, sh.sorted);
+            __syncthreads();
+            for (int i = tid; i < K; i += TK_NT) {
+                if (i < k) {
+                    const uint64_t key = sh.sorted[i];
+                    oidx[i] = (int32_t)key_id(key);
+                    osc[i] = key_score(key);
+                } else {
+                    oidx[i] = -1;
+                    osc[i] = -INFINITY;
+                }
+            }
+            return;
+        }
+        __syncthreads();  // the counts above are read before the selection reuses the buffers
+    }
+    const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)tid;
+    if (k > 0)
+        tk_select<TK_V>([&](int j) { return hv[j]; }, [&](int j) { return lo0 - (uint32_t)(j * TK_NT); },
+                        [&](int j) {
+                            int t = tid;
+                            asm volatile("" : "+v"(t));
+                            return j * TK_NT + t < n;
+                        },
+                        n, k, sh);
+    tk_emit(k, K, sh, oidx, osc);
+}
+
 __global__ __launch_bounds__(TK_NT) void topk_rowmerge_kernel(TopkRowsArgs a) {
     __shared__ TkShared sh;
     const int tid = threadIdx.x;
@@ -1567,10 +1728,12 @@ __global__ __launch_bounds__(TK_NT) void topk_rowmerge_kernel(TopkRowsArgs a) {
     const int total = a.nchunk * a.K;
     const uint64_t* src = a.part + (int64_t)r * total;
     uint32_t kh[TK_MV], kl[TK_MV];
+    uint64_t kv[TK_MV];
+#pragma unroll
+    for (int j = 0; j < TK_MV; ++j) kv[j] = src[min(j * TK_NT + tid, total - 1)];  // clamped, as in load_row_keys
 #pragma unroll
     for (int j = 0; j < TK_MV; ++j) {
-        const int q = j * TK_NT + tid;
-        const uint64_t key = q < total ? src[q] : 0ull;
+        const uint64_t key = j * TK_NT + tid < total ? kv[j] : 0ull;
         kh[j] = (uint32_t)(key >> 32);
         kl[j] = (uint32_t)key;
         asm volatile("" : "+v"(kh[j]), "+v"(kl[j]));  // as in the segment kernel
@@ -2253,15 +2416,40 @@ __global__ __launch_bounds__(HOT_PICK_NT) void hot_pick_kernel(HotArgs a) {
     }
 }
 
+// Bit i: catalog id id0 + i is hot (count >= c; clear past the catalog).
+// The HOT_PER counts are fetched before any is tested -- four 16-byte loads
+// where the ids are all in range, else clamped ones -- rather than one
+// guarded load after another.
+static_assert(HOT_PER == 16, "four 16-byte loads of counts per thread");
+__device__ __forceinline__ uint32_t hot_mask(const HotArgs& a, int64_t id0, int c) {
+    int v[HOT_PER];
+    if (id0 + HOT_PER <= a.M) {  // id0 is a multiple of HOT_PER: 64-byte aligned
+        const int4* p = (const int4*)(a.cnt + id0);
+#pragma unroll
+        for (int q = 0; q < HOT_PER / 4; ++q) {
+            const int4 x = p[q];
+            v[4 * q] = x.x;
+            v[4 * q + 1] = x.y;
+            v[4 * q + 2] = x.z;
+            v[4 * q + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < HOT_PER; ++i) v[i] = a.cnt[min(id0 + i, a.M - 1)];
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < HOT_PER; ++i) m |= (id0 + i < a.M && v[i] >= c) ? 1u << i : 0u;
+    return m;
+}
+
 // Hot ids per block of kHotBlock catalog ids.
 __global__ __launch_bounds__(HOT_NT) void hot_blockcount_kernel(HotArgs a) {
     __shared__ int s_w[HOT_NT / kWave];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c = a.meta[0];
     const int64_t id0 = (int64_t)blockIdx.x * kHotBlock + (int64_t)tid * HOT_PER;
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < HOT_PER; ++i) n += (id0 + i < a.M && a.cnt[id0 + i] >= c) ? 1 : 0;
+    int n = __popc(hot_mask(a, id0, c));
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) n += __shfl_xor(n, o);
     if (lane == 0) s_w[w] = n;
@@ -2306,9 +2494,8 @@ __global__ __launch_bounds__(HOT_NT) void hot_assign_kernel(HotArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int c = a.meta[0];
     const int64_t id0 = (int64_t)blockIdx.x * kHotBlock + (int64_t)tid * HOT_PER;
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < HOT_PER; ++i) n += (id0 + i < a.M && a.cnt[id0 + i] >= c) ? 1 : 0;
+    const uint32_t hm = hot_mask(a, id0, c);
+    const int n = __popc(hm);
     int incl = n;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -2323,7 +2510,7 @@ __global__ __launch_bounds__(HOT_NT) void hot_assign_kernel(HotArgs a) {
     for (int i = 0; i < HOT_PER; ++i) {
         const int64_t id = id0 + i;
         if (id < a.M) {
-            const bool hotv = a.cnt[id] >= c;
+            const bool hotv = (hm >> i) & 1u;
             a.hot_idx[id] = hotv ? pos : -1;
             if (hotv) a.hot_ids[pos++] = (int)id;
         }
@@ -2608,6 +2795,11 @@ hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s) {
 hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s) {
     if (a.R <= 0) return hipSuccess;
     if ((int64_t)a.R * a.nchunk > 2147483647) return hipErrorInvalidValue;  // one block per (row, chunk)
+    if (a.reg == 2) {  // one block per row, the row in registers
+        if (a.N > TK_SEG || a.nchunk != 1 || a.K > GENREC_KMAX || a.K < 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(topk_row_kernel, dim3(a.R), dim3(TK_NT), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.reg) {
         if (a.C != TK_SEG || a.K > GENREC_KMAX || a.nchunk < 2 || (int64_t)a.nchunk * a.K > TK_NT * TK_MV)
             return hipErrorInvalidValue;

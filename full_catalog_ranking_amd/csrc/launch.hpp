@@ -235,7 +235,8 @@ struct TopkRowsArgs {
     int64_t C;            // columns per chunk
     int nchunk;           // chunks per row (1: no merge pass)
     uint64_t* part;       // nchunk > 1: [R][nchunk][K] chunk results
-    int reg;              // register-resident selection: chunks of kTopkSeg columns, nchunk >= 2, nchunk * K <= kTopkMergeKeys
+    int reg;              // 1: register-resident selection, chunks of kTopkSeg columns, nchunk >= 2, nchunk * K <= kTopkMergeKeys;
+                          // 2: one block per row, the row (N <= kTopkSeg) in registers, nchunk = 1
 };
 
 // modes 0 / 1; splits > 1 (mode 0): grid y splits the reduction (a.D per split, a.ld the row stride)

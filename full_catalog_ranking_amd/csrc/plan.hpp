@@ -284,10 +284,15 @@ constexpr int64_t kTopkGather = 6144;  // the merge kernel's LDS gather capacity
 constexpr int64_t kTopkSeg = 16384;
 constexpr int64_t kTopkMergeKeys = 8192;
 constexpr int64_t kTopkRegMinBlocks = 2 * kNumCU;
+// Rows of at most one segment with K <= kTopkRowMaxK: one block per row, the
+// top K found among the keys at or above the K-th largest of the threads'
+// maxima (a few times K keys for unordered scores), no second pass.
+constexpr int kTopkRowMaxK = 256;
 
 struct TopkPlan {
     bool ok = true;    // false: the workspace or the grid would be too large (unsupported)
     bool reg = false;  // register-resident selection (else histogram narrowing)
+    bool row = false;  // ... of a whole row per block (rows of at most kTopkSeg, K <= 256)
     int64_t C = 0;     // columns per chunk (segment)
     int nchunk = 1;
     size_t workspace = 0;
@@ -296,7 +301,11 @@ struct TopkPlan {
 inline TopkPlan plan_topk(int R, int64_t N, int K) {
     TopkPlan p;
     const int64_t nseg = ceil_div(N, kTopkSeg);
-    if (nseg > 1 && nseg * K <= kTopkMergeKeys && (int64_t)R * nseg >= kTopkRegMinBlocks) {
+    if (nseg == 1 && K <= kTopkRowMaxK) {
+        p.reg = p.row = true;
+        p.C = N;
+        p.nchunk = 1;
+    } else if (nseg > 1 && nseg * K <= kTopkMergeKeys && (int64_t)R * nseg >= kTopkRegMinBlocks) {
         p.reg = true;
         p.C = kTopkSeg;
         p.nchunk = (int)nseg;

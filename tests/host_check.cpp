@@ -171,8 +171,15 @@ static void check_topk(int R, int64_t N, int K) {
         return;
     }
     CHECK((int64_t)p.nchunk * p.C >= N && (int64_t)(p.nchunk - 1) * p.C < N, "%s: chunks cover the row", what);
-    if (p.reg) CHECK(p.C == kTopkSeg && p.nchunk >= 2 && (int64_t)p.nchunk * K <= kTopkMergeKeys, "%s: reg plan", what);
-    else if (p.nchunk > 1) CHECK((int64_t)p.nchunk * std::min<int64_t>(K, p.C) <= kTopkGather, "%s: merge gather", what);
+    if (p.row) {
+        CHECK(p.reg && N <= kTopkSeg && K <= kTopkRowMaxK && p.nchunk == 1 && p.C == N && p.workspace == 0,
+              "%s: one-block row plan", what);
+    } else if (p.reg) {
+        CHECK(p.C == kTopkSeg && p.nchunk >= 2 && (int64_t)p.nchunk * K <= kTopkMergeKeys, "%s: reg plan", what);
+    } else if (p.nchunk > 1) {
+        CHECK((int64_t)p.nchunk * std::min<int64_t>(K, p.C) <= kTopkGather, "%s: merge gather", what);
+    }
+    CHECK(p.row == (N <= kTopkSeg && K <= kTopkRowMaxK), "%s: one-block rows exactly for short rows and K <= 256", what);
     if (p.nchunk > 1) CHECK(p.workspace == u128(R) * u128(p.nchunk) * u128(K) * 8, "%s: workspace", what);
 }
 

@@ -41,7 +41,11 @@ def run_dense(d, K, dev):
     return out
 
 
-def run_cand(d, K, dev):
+def run_cand(d, K, dev, repeats=0):
+    """One call (outputs, device error counts); with repeats, that many more
+    calls on the same device inputs, each of whose outputs must equal the
+    first call's bit for bit (the selection's result does not depend on the
+    order in which threads arrive, so a difference is a race)."""
     from full_catalog_ranking_amd import genrec
     H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
     off = torch.from_numpy(d["offsets"]).to(dev)
@@ -50,6 +54,12 @@ def run_cand(d, K, dev):
     idx, sc, ls, ws = genrec.score_candidates_topk(H, E, off, ids, K)
     errs = genrec.device_errors(ws)
     out = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
+    for r in range(repeats):
+        idx2, sc2, ls2, _ = genrec.score_candidates_topk(H, E, off, ids, K)
+        again = idx2.cpu().numpy(), sc2.cpu().numpy(), ls2.cpu().numpy()
+        for name, x, y in zip(("idx", "score", "lse"), out, again):
+            bad = np.flatnonzero(~((x == y) | (np.isnan(x) & np.isnan(y))).reshape(x.shape[0], -1).all(axis=1))
+            assert bad.size == 0, ("repeat %d differs in %s for users" % (r + 1, name), bad[:8].tolist())
     return out, errs
 
 
@@ -124,8 +134,11 @@ def test_threshold_full_capacity(dev, oracle_mod, B, D, M, K):
 
 
 def test_candidates_b4096(dev, oracle_mod):
+    # lists of up to 3,000 entries take the selection's multi-pass route
+    # (more keys than its LDS gather holds); the repeats guard the barriers
+    # between its passes
     d = synth.make_workload("cand")
-    g, errs = run_cand(d, d["K"], dev)
+    g, errs = run_cand(d, d["K"], dev, repeats=3)
     assert errs == (0, 0)
     ref = oracle_mod.cand(d["H"], d["E"], d["offsets"], d["ids"], d["K"])
     parity.check_cand(g, ref, d["offsets"], d["ids"], where="cand")
@@ -463,6 +476,11 @@ def test_candidates_equal_full_catalog(dev, oracle_mod):
     (40, 13 * 16_384, 512, None, 0),
     (33, 16 * 16_384 + 5, 256, 0, 3),  # whole-number scores: hundreds share a score; a 5-column last segment
     (520, 2 * 16_384, 1024, 2, 0),    # K = KMAX, the row merge's 2,048 keys
+    # one block per row (N <= 16,384, K <= 256): threshold from the threads' maxima
+    (64, 16_384, 256, None, 7),       # K = 256, padded row stride
+    (9, 16_384, 100, 0, 0),           # whole-number scores: thousands at the threshold -> bit selection
+    (11, 300, 256, 1, 0),             # fewer columns than threads; K > N / 2, ties
+    (6, 4_097, 1, None, 0),           # K = 1
 ])
 def test_topk_rows(dev, oracle_mod, R, N, K, decimals, ld_pad):
     from full_catalog_ranking_amd import genrec
