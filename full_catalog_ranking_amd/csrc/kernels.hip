@@ -272,19 +272,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                 if (u < a.B) {
                     float* cz = a.c_out + (int64_t)blockIdx.y * a.c_split;
 #pragma unroll
-                    for (int ib = 0; ib < 4; ++ib) {
-                        // [u][row ..] with c_accum: the block's four old float4
-                        // are read before any is written back, one trip to
-                        // memory for the four (a load after a store that may
-                        // alias it would wait for the one before)
-                        float4 old[4];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int jq = lrow0 + ib * 32 + q * 8;
-                            old[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-                            if (a.c_trans && a.c_accum && jq + 3 < lim)
-                                old[q] = *(const float4*)(cz + (int64_t)u * a.ldc + j0 + jq);
-                        }
+                    for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
                             const int jq = lrow0 + ib * 32 + q * 8;
@@ -295,7 +283,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                                     float4 v = make_float4(acc[ib][ub][4 * q], acc[ib][ub][4 * q + 1],
                                                            acc[ib][ub][4 * q + 2], acc[ib][ub][4 * q + 3]);
                                     if (a.c_accum) {
-                                        const float4 o4 = old[q];
+                                        const float4 o4 = *(const float4*)o;
                                         v.x += o4.x;
                                         v.y += o4.y;
                                         v.z += o4.z;
@@ -326,7 +314,6 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                                     }
                             }
                         }
-                    }
                 }
                 continue;
             }
