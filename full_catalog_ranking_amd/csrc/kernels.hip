@@ -838,12 +838,21 @@ __device__ uint64_t block_select(const Src& src, int k, Sh& sh) {
 // ---------------------------------------------------------------------------
 constexpr int TH_KEYS = 32768;  // one user's sample at most (a 16,384-key build serves smaller samples)
 
+constexpr int TH_GROUPS = 256;  // thread groups whose maxima bound the fast route
+constexpr int TH_FAST = 1024;   // keys the fast route ranks at most
+
 template <int NW>
 struct ThShared {
     int hist[2][NW][256];  // per rank, per wave
     unsigned red_lo[NW], red_hi[NW];
     int cnt[2][NW];
     int bin[2], above[2];
+    // fast route
+    uint32_t gmax[TH_GROUPS];
+    uint32_t tred[NW];
+    int wcnt[NW];
+    uint32_t cand[TH_FAST + 4];
+    uint32_t res[2];
 };
 
 __device__ __forceinline__ int th_shift(unsigned span) { return max(0, 32 - __clz(span) - 8); }
@@ -906,37 +915,162 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
     // contiguous across the block
     // (sampled scores of a split reduction: the partial rows summed in split order)
     const float* row = a.sample + (int64_t)b * a.n_sample;
-    auto sample_at = [&](int e) {
-        float x = row[e];
-        for (int z = 1; z < a.n_split; ++z) x += row[(int64_t)z * a.split_stride + e];
-        return x;
+    // 16-byte buffer loads (n is a multiple of 4), split after split, each
+    // split's loads in flight together.  The record count ends at the row's
+    // end, so a quad past it reads zeros (dropped below) with neither a branch
+    // nor a 64-bit address per load; the split sums keep their order.
+    typedef unsigned int th_u32x4 __attribute__((ext_vector_type(4)));
+    auto quad = [&](const __amdgpu_buffer_rsrc_t& r, int i) {
+        const th_u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 16, i * TH_NT * 16, 0);
+        return make_float4(__uint_as_float(q.x), __uint_as_float(q.y), __uint_as_float(q.z), __uint_as_float(q.w));
     };
+    auto rsrc_of = [&](int z) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(row + (int64_t)z * a.split_stride), (short)0, n * 4,
+                                                 0x00020000);
+    };
+    // Chunks of at most 16 quads: loaded (and summed over the splits), then
+    // turned into keys, before the next chunk's loads start -- 64 loaded
+    // floats live at a time beside the keys.  Within a split, four quads at a
+    // time: the scheduling barriers keep the loads from all being hoisted
+    // above the adds, which would hold twice the registers and cost the
+    // many-user builds their occupancy.
+    constexpr int QC = TH_PER / 4 < 16 ? TH_PER / 4 : 16;  // quads per chunk
+    static_assert((TH_PER / 4) % QC == 0 && QC % 4 == 0, "chunk layout");
     uint32_t key[TH_PER];  // 0 = no key (every score's key is larger)
-    unsigned lo = ~0u, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < TH_PER / 4; ++i) {
-        const int e = i * (TH_NT * 4) + tid * 4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (e + 3 < n) {
-            v = *(const float4*)(row + e);
-            for (int z = 1; z < a.n_split; ++z) {
-                const float4 p = *(const float4*)(row + (int64_t)z * a.split_stride + e);
-                v.x += p.x;
-                v.y += p.y;
-                v.z += p.z;
-                v.w += p.w;
+    for (int c0 = 0; c0 < TH_PER / 4; c0 += QC) {
+        float4 v[QC];
+        {
+            const __amdgpu_buffer_rsrc_t r0 = rsrc_of(0);
+#pragma unroll
+            for (int i = 0; i < QC; ++i) v[i] = quad(r0, c0 + i);
+        }
+        for (int z = 1; z < a.n_split; ++z) {
+            const __amdgpu_buffer_rsrc_t rz = rsrc_of(z);
+#pragma unroll
+            for (int i0 = 0; i0 < QC; i0 += 4) {
+                float4 p[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) p[c] = quad(rz, c0 + i0 + c);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    v[i0 + c].x += p[c].x;
+                    v[i0 + c].y += p[c].y;
+                    v[i0 + c].z += p[c].z;
+                    v[i0 + c].w += p[c].w;
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool in = e + 3 < n ? true : (e + j < n);
-            const float x = (e + 3 < n) ? f[j] : (e + j < n ? sample_at(e + j) : 0.f);
-            key[4 * i + j] = in ? order_key(x) : 0u;
-            if (in) {
-                lo = min(lo, key[4 * i + j]);
-                hi = max(hi, key[4 * i + j]);
+        for (int i = 0; i < QC; ++i) {
+            const int e = (c0 + i) * (TH_NT * 4) + tid * 4;
+            const float f[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) key[4 * (c0 + i) + j] = e + j < n ? order_key(f[j]) : 0u;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    unsigned lo = ~0u, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < TH_PER; ++i)
+        if (key[i] != 0u) {
+            lo = min(lo, key[i]);
+            hi = max(hi, key[i]);
+        }
+    // ranks: q = 0 the K-th largest, q = 1 the r_fast-th largest
+    const int nq = a.theta_fast != nullptr ? 2 : 1;
+    int krem[2] = {a.K, max(1, min(a.r_fast, a.K))};
+    // Fast route (K <= 256 groups): the block's threads form TH_GROUPS groups
+    // of TH_NT / TH_GROUPS; T = the K-th largest of the groups' maxima.  K
+    // groups hold a key >= T, so at least K keys reach T and both ranks (K
+    // and r_fast <= K) are among the keys >= T: a few times K of them for
+    // unordered scores, every key when fewer than K groups hold one (T = 0).
+    // They are compacted and ranked exactly -- the same keys the narrowing
+    // passes below end on.  More than TH_FAST of them (heavy ties): those
+    // passes, which use none of the fast route's shared fields.  Built for
+    // the few-user launches (at most 32 keys a thread): with 64 or 128 the
+    // route's registers would cost those builds their occupancy.
+    if constexpr (TH_PER <= 32)
+    if (a.K <= TH_GROUPS) {  // block-uniform
+        constexpr int GS = TH_NT / TH_GROUPS;     // threads per group
+        constexpr int PER_T = TH_GROUPS / GS;     // group maxima each thread compares
+        static_assert(GS >= 1 && (GS & (GS - 1)) == 0 && PER_T % 4 == 0, "group layout");
+        uint32_t gm = 0u;
+#pragma unroll
+        for (int i = 0; i < TH_PER; ++i) gm = max(gm, key[i]);
+#pragma unroll
+        for (int o = 1; o < GS; o <<= 1) gm = max(gm, (uint32_t)__shfl_xor((int)gm, o));
+        const int g = tid / GS, gl = tid - g * GS;
+        if (gl == 0) sh.gmax[g] = gm;
+        __syncthreads();
+        // the group maximum's rank (maxima strictly above it), its GS threads
+        // each comparing a slice of the maxima
+        int rk = 0;
+        const uint4* g4 = (const uint4*)(sh.gmax + gl * PER_T);
+#pragma unroll 8
+        for (int q = 0; q < PER_T / 4; ++q) {
+            const uint4 m4 = g4[q];
+            rk += (m4.x > gm) + (m4.y > gm) + (m4.z > gm) + (m4.w > gm);
+        }
+#pragma unroll
+        for (int o = 1; o < GS; o <<= 1) rk += __shfl_xor(rk, o);
+        uint32_t tc = rk < a.K ? gm : 0xFFFFFFFFu;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) tc = min(tc, (uint32_t)__shfl_xor((int)tc, o));
+        if (lane == 0) sh.tred[w] = tc;
+        __syncthreads();
+        uint32_t T = sh.tred[0];
+#pragma unroll
+        for (int q = 1; q < TH_NW; ++q) T = min(T, sh.tred[q]);
+        // keys >= T as bits of the thread's own words (not one scalar mask
+        // per key held until the compaction)
+        uint32_t pass[(TH_PER + 31) / 32] = {};
+#pragma unroll
+        for (int i = 0; i < TH_PER; ++i) pass[i >> 5] |= (key[i] != 0u && key[i] >= T) ? 1u << (i & 31) : 0u;
+        int c = 0;
+#pragma unroll
+        for (int q = 0; q < (TH_PER + 31) / 32; ++q) c += __popc(pass[q]);
+        int incl = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+        }
+        if (lane == 63) sh.wcnt[w] = incl;
+        __syncthreads();
+        int base = incl - c, total = 0;
+#pragma unroll
+        for (int q = 0; q < TH_NW; ++q) {
+            base += q < w ? sh.wcnt[q] : 0;
+            total += sh.wcnt[q];
+        }
+        if (total <= TH_FAST) {  // block-uniform
+#pragma unroll
+            for (int i = 0; i < TH_PER; ++i)
+                if ((pass[i >> 5] >> (i & 31)) & 1u) sh.cand[base++] = key[i];
+            if (tid < 4) sh.cand[total + tid] = 0u;  // to whole uint4s (0 is below every key)
+            __syncthreads();
+            // the k-th largest value x: fewer than k keys above it, at least k at or above
+            const uint4* c4 = (const uint4*)sh.cand;
+            for (int i = tid; i < total; i += TH_NT) {
+                const uint32_t x = sh.cand[i];
+                int gt = 0, ge = 0;
+                for (int q = 0; q < (total + 3) / 4; ++q) {
+                    const uint4 y = c4[q];
+                    gt += (y.x > x) + (y.y > x) + (y.z > x) + (y.w > x);
+                    ge += (y.x >= x) + (y.y >= x) + (y.z >= x) + (y.w >= x);
+                }
+                // several keys may share the value: they write the same word
+                if (gt < krem[0] && krem[0] <= ge) sh.res[0] = x;
+                if (nq > 1 && gt < krem[1] && krem[1] <= ge) sh.res[1] = x;
             }
+            __syncthreads();
+            if (tid == 0) {
+                a.theta_safe[b] = th_lower(key_to_score(sh.res[0]));
+                if (a.theta_fast != nullptr) a.theta_fast[b] = th_lower(key_to_score(sh.res[1]));
+            }
+            return;
         }
     }
 #pragma unroll
@@ -953,10 +1087,7 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
         lo = min(lo, sh.red_lo[q]);
         hi = max(hi, sh.red_hi[q]);
     }
-    // ranks: q = 0 the K-th largest, q = 1 the r_fast-th largest
-    const int nq = a.theta_fast != nullptr ? 2 : 1;
     unsigned qlo[2] = {lo, lo}, qhi[2] = {hi, hi};
-    int krem[2] = {a.K, max(1, min(a.r_fast, a.K))};
     if (lo < hi) {
         // Cut the range from below first: a histogram of every 8th key places
         // the (2k/8 + 8)-th largest of that subsample; the lower edge c of its
@@ -1678,9 +1809,10 @@ __global__ __launch_bounds__(TK_NT) void topk_row_kernel(TopkRowsArgs a) {
             for (int j = 0; j < TK_V; ++j)
                 if ((mask >> j) & 1ull) sh.sel[base++] = ((uint64_t)hv[j] << 32) | (uint64_t)(lo0 - (uint32_t)(j * TK_NT));
             __syncthreads();
-            // total >= k (T = 0 when fewer than K keys exist)
-            if (total <= TK_SMALL) block_rank_place(sh.sel, total, sh.sorted, k);
-            else block_sort_into(sh.sel, total, sh.sorted);
+            // total >= k (T = 0 when fewer than K keys exist); wave sorts and a
+            // rank merge (a few hundred keys: 18.0 -> 14.7 us for 256 rows of
+            // 16,384 against the quadratic rank placement)
+            block_sort_into(sh.sel, total, sh.sorted);
             __syncthreads();
             for (int i = tid; i < K; i += TK_NT) {
                 if (i < k) {
@@ -2766,7 +2898,7 @@ hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, 
 }
 
 hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s) {
-    if (a.n_sample > (int64_t)TH_KEYS) return hipErrorInvalidValue;
+    if (a.n_sample > (int64_t)TH_KEYS || a.n_sample % 4 != 0) return hipErrorInvalidValue;
     // many threads for few users; keys per thread sized to the sample
     const bool half = a.n_sample <= (int64_t)(TH_KEYS / 2);
     if (a.B <= 512) {

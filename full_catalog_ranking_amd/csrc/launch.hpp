@@ -204,7 +204,7 @@ struct MergeArgs {
 
 struct ThresholdArgs {
     const float* sample;  // [B][n_sample] sampled scores: the sum of n_split partial rows split_stride apart
-    int64_t n_sample;     // <= 32768
+    int64_t n_sample;     // <= 32768, a multiple of 4
     int n_split;
     int64_t split_stride;
     int B, K, r_fast;

@@ -20,6 +20,7 @@ constexpr int64_t kSampleMaxTiles = 128; // sampled items per user at most 128 *
 constexpr int64_t kSampleMaxItems = 32768;  // = kSampleMaxTiles * 256: one user's sample fits the threshold kernel
 constexpr int kFastOversample = 4;     // fast threshold: expected candidates ~ 4 K
 constexpr int kSampleMaxSplits = 16;   // reduction splits of an MFMA sample pass that fills few CUs
+constexpr int64_t kSampleMinSteps = 8; // k-steps each of those splits keeps at least
 // MFMA path: the sample only has to place the fast threshold at rank >= 32 of
 // the sampled scores.  The number of catalog items above the r-th largest of
 // n sampled scores is about M r / n with a Gamma(r)-shaped spread, so at
@@ -148,8 +149,12 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
     if (p.mfma && p.sample) {
         const int64_t ke = dtype == 0 ? kMfmaBlockK : kMfmaBlockK / 2;  // reduction elements per k-step
         const int64_t blocks = (int64_t)p.pre.UT * p.pre.P;
+        // a split writes (and the threshold pass reads back) a full partial
+        // score row per sampled item: splits too short to pay for that traffic
+        // are not made (the 256-user bf16 batch at D = 2,048: 8 splits of 8
+        // k-steps beat 16 of 4 by 4 us; its fp32 twin keeps 16 of 8)
         while (p.sample_splits < kSampleMaxSplits && blocks * p.sample_splits * 2 <= kNumCU &&
-               D % (ke * p.sample_splits * 2) == 0)
+               D % (ke * p.sample_splits * 2) == 0 && D / (ke * p.sample_splits * 2) >= kSampleMinSteps)
             p.sample_splits *= 2;
         p.safe_exact = p.sample_splits == 1;
     }

@@ -94,6 +94,7 @@ static void check_dense(int B, int D, int64_t M, int K, int dt) {
         const int64_t ke = dt == 0 ? kMfmaBlockK : kMfmaBlockK / 2;
         const int S = p.sample_splits;
         CHECK(S >= 1 && S <= kSampleMaxSplits && (S & (S - 1)) == 0 && (S == 1 || D % (ke * S) == 0), "%s: sample splits", what);
+        CHECK(S == 1 || D / (ke * S) >= kSampleMinSteps, "%s: sample splits of at least the minimum k-steps", what);
         CHECK(S == 1 || (p.mfma && (int64_t)p.pre.UT * p.pre.P * S <= kNumCU), "%s: split sample fills the GPU", what);
         CHECK(p.safe_exact == (S == 1), "%s: safe threshold exact iff unsplit", what);
         CHECK(p.n_sample <= kSampleMaxItems, "%s: sample above the threshold kernel's capacity", what);
