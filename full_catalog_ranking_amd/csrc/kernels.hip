@@ -1554,7 +1554,7 @@ struct TkShared {
     int cnt[2][TK_NT / kWave];
     int wsel[TK_NT / kWave];
     uint64_t grp[TK_SMALL];        // the group, when it is ranked by comparison
-    uint64_t sel[GENREC_KMAX];     // the k selected keys
+    alignas(16) uint64_t sel[GENREC_KMAX];  // the k selected keys (read two at a time)
     uint64_t sorted[GENREC_KMAX];  // the same in ranking order
 };
 
@@ -1809,10 +1809,27 @@ __global__ __launch_bounds__(TK_NT) void topk_row_kernel(TopkRowsArgs a) {
             for (int j = 0; j < TK_V; ++j)
                 if ((mask >> j) & 1ull) sh.sel[base++] = ((uint64_t)hv[j] << 32) | (uint64_t)(lo0 - (uint32_t)(j * TK_NT));
             __syncthreads();
-            // total >= k (T = 0 when fewer than K keys exist); wave sorts and a
-            // rank merge (a few hundred keys: 18.0 -> 14.7 us for 256 rows of
-            // 16,384 against the quadratic rank placement)
-            block_sort_into(sh.sel, total, sh.sorted);
+            // total >= k (T = 0 when fewer than K keys exist).  Up to 256 keys:
+            // each one's rank = the keys above it (all distinct: the index
+            // word), two per 16-byte read; more: wave sorts and a rank merge.
+            // (256 rows of 16,384: 13.7 us; 14.7 with the sort for all,
+            // 18.0 with the general rank placement.)
+            if (total <= TK_NT) {
+                if (tid < total) {
+                    const uint64_t x = sh.sel[tid];
+                    int rk2 = 0;
+                    const ulonglong2* c2 = (const ulonglong2*)sh.sel;
+#pragma unroll 4
+                    for (int j = 0; j < total / 2; ++j) {
+                        const ulonglong2 y = c2[j];
+                        rk2 += (y.x > x) + (y.y > x);
+                    }
+                    if (total & 1) rk2 += sh.sel[total - 1] > x ? 1 : 0;
+                    if (rk2 < k) sh.sorted[rk2] = x;
+                }
+            } else {
+                block_sort_into(sh.sel, total, sh.sorted);
+            }
             __syncthreads();
             for (int i = tid; i < K; i += TK_NT) {
                 if (i < k) {
