@@ -1682,6 +1682,61 @@ __device__ void tk_emit(int k, int K, TkShared& sh, int32_t* oidx, float* osc) {
     }
 }
 
+// The k largest of a block's keys (V slots a thread, k <= 1,024 groups; the
+// one-block row route for 256 < k <= 512)
+// when a bound leaves few enough: each thread's slots form four groups, T =
+// the k-th largest of the 1,024 group maxima (one block sort), and k groups
+// hold a key >= T, so the k largest keys are among the keys that reach T --
+// for unordered scores about 1.35 k of them at k = 512.  Those are compacted
+// (whole 64-bit keys) and sorted into sh.sorted; returns how many (>= k).
+// More than GENREC_KMAX keys at T (exact ties): returns -1, having written
+// only LDS scratch.  hi(j): slot j's order key (0: no key); key(j): its
+// 64-bit key.
+template <int V, class Hi, class Key>
+__device__ __forceinline__ int tk_bound_sort(const Hi& hi, const Key& key, int k, TkShared& sh) {
+    static_assert(V % 4 == 0 && V <= 64 && 4 * TK_NT <= GENREC_KMAX, "four groups a thread, a 64-bit pass mask");
+    constexpr int GK = V / 4;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int j = q * GK; j < (q + 1) * GK; ++j) m = max(m, hi(j));
+        sh.sel[tid * 4 + q] = ((uint64_t)m << 32) | (uint32_t)(tid * 4 + q);
+    }
+    __syncthreads();
+    block_sort_into(sh.sel, 4 * TK_NT, sh.sorted);
+    __syncthreads();
+    const uint32_t T = (uint32_t)(sh.sorted[k - 1] >> 32);  // 0 when fewer than k groups hold a key: every key
+    uint64_t mask = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) mask |= (hi(j) != 0u && hi(j) >= T) ? (1ull << j) : 0ull;
+    const int c = __popcll(mask);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) sh.wsel[w] = incl;
+    __syncthreads();
+    int base = incl - c, total = 0;
+#pragma unroll
+    for (int q = 0; q < TK_NT / kWave; ++q) {
+        base += q < w ? sh.wsel[q] : 0;
+        total += sh.wsel[q];
+    }
+    __syncthreads();  // the counts are read before anyone reuses them
+    if (total > GENREC_KMAX) return -1;  // block-uniform
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+        if ((mask >> j) & 1ull) sh.sel[base++] = key(j);
+    __syncthreads();
+    block_sort_into(sh.sel, total, sh.sorted);
+    __syncthreads();
+    return total;
+}
+
 // Order keys of a row's first n >= 1 scores, slot j of thread t holding
 // column j * TK_NT + t (key 0 past the row).  Every load is issued before
 // the first is used: a slot past the row reads the row's last score and
@@ -1716,6 +1771,9 @@ __global__ __launch_bounds__(TK_NT) void topk_seg_kernel(TopkRowsArgs a) {
     for (int j = 0; j < TK_V; ++j) asm volatile("" : "+v"(hv[j]));
     const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)(c0 + tid);  // index word of slot 0
     const int k = min(a.K, n);
+    uint64_t* dst = a.part + ((int64_t)r * a.nchunk + s) * a.K;
+    // (the bound from group maxima, which serves whole rows, measured slower
+    // here: its two block sorts cost what the bit decisions do)
     tk_select<TK_V>([&](int j) { return hv[j]; }, [&](int j) { return lo0 - (uint32_t)(j * TK_NT); },
                     [&](int j) {
                         // recomputed at each use (an opaque copy of the thread
@@ -1725,17 +1783,15 @@ __global__ __launch_bounds__(TK_NT) void topk_seg_kernel(TopkRowsArgs a) {
                         return j * TK_NT + t < n;
                     },
                     n, k, sh);
-    uint64_t* dst = a.part + ((int64_t)r * a.nchunk + s) * a.K;
     for (int i = tid; i < a.K; i += TK_NT) dst[i] = i < k ? sh.sel[i] : 0ull;
 }
 
-// Block r: the top-K of the row's segment results (nchunk * K <= TK_NT * TK_MV
-// keys, zero keys in unused places).
 // Block r: the whole row (N <= TK_SEG) in registers, its top-K written out.
 // For K <= 256: T = the K-th largest of the threads' maxima (at least K keys
 // reach it, so the top K are among the keys >= T -- for unordered scores a
-// few times K of them), compacted into LDS and ranked; more than the LDS
-// list holds (heavy ties), or K > 256: the bit-by-bit selection.
+// few times K of them), compacted into LDS and ranked; K <= 512: the bound
+// from 1,024 group maxima; more than the LDS list holds (heavy ties), or
+// K > 512: the bit-by-bit selection.
 struct TkRowShared {
     TkShared tk;
     uint32_t tmax[TK_NT];
@@ -1844,6 +1900,24 @@ __global__ __launch_bounds__(TK_NT) void topk_row_kernel(TopkRowsArgs a) {
             return;
         }
         __syncthreads();  // the counts above are read before the selection reuses the buffers
+    } else if (K <= kTopkBoundMaxK) {  // block-uniform
+        const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)tid;
+        const int got = tk_bound_sort<TK_V>(
+            [&](int j) { return hv[j]; },
+            [&](int j) { return ((uint64_t)hv[j] << 32) | (uint64_t)(lo0 - (uint32_t)(j * TK_NT)); }, k, sh);
+        if (got >= 0) {
+            for (int i = tid; i < K; i += TK_NT) {
+                if (i < k) {
+                    const uint64_t key = sh.sorted[i];
+                    oidx[i] = (int32_t)key_id(key);
+                    osc[i] = key_score(key);
+                } else {
+                    oidx[i] = -1;
+                    osc[i] = -INFINITY;
+                }
+            }
+            return;
+        }
     }
     const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)tid;
     if (k > 0)
@@ -1857,6 +1931,8 @@ __global__ __launch_bounds__(TK_NT) void topk_row_kernel(TopkRowsArgs a) {
     tk_emit(k, K, sh, oidx, osc);
 }
 
+// Block r: the top-K of the row's segment results (nchunk * K <= TK_NT * TK_MV
+// keys, zero keys in unused places).
 __global__ __launch_bounds__(TK_NT) void topk_rowmerge_kernel(TopkRowsArgs a) {
     __shared__ TkShared sh;
     const int tid = threadIdx.x;

@@ -291,8 +291,10 @@ constexpr int64_t kTopkMergeKeys = 8192;
 constexpr int64_t kTopkRegMinBlocks = 2 * kNumCU;
 // Rows of at most one segment with K <= kTopkRowMaxK: one block per row, the
 // top K found among the keys at or above the K-th largest of the threads'
-// maxima (a few times K keys for unordered scores), no second pass.
-constexpr int kTopkRowMaxK = 256;
+// maxima (K <= 256) or of 1,024 group maxima (K <= 512) -- a few times K keys
+// for unordered scores -- no second pass.
+constexpr int kTopkRowMaxK = 512;
+constexpr int kTopkBoundMaxK = 512;  // the row kernel's bound from 1,024 group maxima serves K up to this
 
 struct TopkPlan {
     bool ok = true;    // false: the workspace or the grid would be too large (unsupported)

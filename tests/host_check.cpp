@@ -180,7 +180,7 @@ static void check_topk(int R, int64_t N, int K) {
     } else if (p.nchunk > 1) {
         CHECK((int64_t)p.nchunk * std::min<int64_t>(K, p.C) <= kTopkGather, "%s: merge gather", what);
     }
-    CHECK(p.row == (N <= kTopkSeg && K <= kTopkRowMaxK), "%s: one-block rows exactly for short rows and K <= 256", what);
+    CHECK(p.row == (N <= kTopkSeg && K <= kTopkRowMaxK), "%s: one-block rows exactly for short rows and K <= 512", what);
     if (p.nchunk > 1) CHECK(p.workspace == u128(R) * u128(p.nchunk) * u128(K) * 8, "%s: workspace", what);
 }
 

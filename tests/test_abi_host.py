@@ -86,14 +86,16 @@ def test_candidate_argument_errors(L):
     assert t(FAKE, 2, 100, 99, 5, FAKE, FAKE, None, 0, None) == INVALID        # ld < N
     assert t(FAKE, 2, 100, 100, 0, FAKE, FAKE, None, 0, None) == INVALID       # K = 0
     assert t(FAKE, 2, 100, 100, 2000, FAKE, FAKE, None, 0, None) == UNSUPPORTED  # K > KMAX
-    # rows of up to 16,384 columns with K <= 256: one block per row, no workspace
+    # rows of up to 16,384 columns with K <= 512: one block per row, no workspace
     assert L.genrec_topk_rows_workspace(8, 4096, 128) == 0
     assert L.genrec_topk_rows_workspace(8, 16384, 128) == 0
     assert L.genrec_topk_rows_workspace(8, 16384, 256) == 0
+    assert L.genrec_topk_rows_workspace(8, 4096, 257) == 0
+    assert L.genrec_topk_rows_workspace(8, 16384, 512) == 0
     # histogram narrowing for larger K: one pass up to 4,096 columns; longer rows
     # need the chunk results' workspace
-    assert L.genrec_topk_rows_workspace(8, 4096, 257) == 0
-    assert L.genrec_topk_rows_workspace(8, 16384, 300) == 8 * 4 * 300 * 8
+    assert L.genrec_topk_rows_workspace(8, 4096, 513) == 0
+    assert L.genrec_topk_rows_workspace(8, 16384, 600) == 8 * 4 * 600 * 8
     need = L.genrec_topk_rows_workspace(8, 512 * 512, 512)
     assert need > 0 and need % (8 * 8 * 512) == 0 and need // (8 * 8 * 512) * 512 <= 6144
     assert t(FAKE, 8, 512 * 512, 512 * 512, 512, FAKE, FAKE, None, 0, None) == WORKSPACE

@@ -508,6 +508,11 @@ def test_candidates_equal_full_catalog(dev, oracle_mod):
     (9, 16_384, 100, 0, 0),           # whole-number scores: thousands at the threshold -> bit selection
     (11, 300, 256, 1, 0),             # fewer columns than threads; K > N / 2, ties
     (6, 4_097, 1, None, 0),           # K = 1
+    # one block per row, 256 < K <= 512: the bound from 1,024 group maxima
+    (8, 16_384, 512, None, 0),        # K = 512
+    (3, 9_000, 400, None, 0),         # a short row: groups with empty slots
+    (5, 16_384, 300, 0, 0),           # whole-number scores: thousands at the bound -> bit selection
+    (24, 22 * 16_384, 300, None, 0),  # 528 segment blocks, K = 300
 ])
 def test_topk_rows(dev, oracle_mod, R, N, K, decimals, ld_pad):
     from full_catalog_ranking_amd import genrec
