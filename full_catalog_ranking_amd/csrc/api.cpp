@@ -459,6 +459,21 @@ size_t genrec_score_candidates_topk_workspace(int B, int D, int64_t M, int64_t n
     return plan_cand(B, D, M, nnz, dtype).total;
 }
 
+int genrec_describe_cand_plan(int B, int D, int64_t M, int64_t nnz, int K, int dtype, char* buf, size_t len) {
+    static const float dummy[4] = {0, 0, 0, 0};
+    const int st = check_common(dummy, dummy, dtype, B, D, M, K, (const int32_t*)dummy, dummy, dummy);
+    if (st != GENREC_OK) return st;
+    if (nnz < 0 || !buf || len == 0) return GENREC_ERR_INVALID_ARG;
+    const CandPlan p = plan_cand(B, D, M, nnz, dtype);
+    if (!p.ok) return GENREC_ERR_UNSUPPORTED;
+    snprintf(buf, len,
+             "{\"hot\":%d,\"t_max\":%d,\"c_min\":%d,\"sample_every\":%d,\"n_pieces_max\":%lld,"
+             "\"off_counts\":%lld,\"off_meta\":%lld,\"workspace\":%zu}",
+             p.hot ? 1 : 0, p.t_max, p.c_min, kHotSample, (long long)p.n_pieces_max,
+             p.hot ? (long long)p.off_cnt : -1LL, p.hot ? (long long)p.off_meta : -1LL, p.total);
+    return GENREC_OK;
+}
+
 int genrec_score_candidates_topk(const void* H, const void* E, int dtype, const int64_t* cand_offsets,
                                  const int32_t* cand_ids, int B, int D, int64_t M, int64_t nnz, int K,
                                  int32_t* out_idx, float* out_scores, float* out_lse, void* workspace,

@@ -34,6 +34,7 @@ EXPORTED = (
     "genrec_topk_rows_workspace",
     "genrec_describe_plan",
     "genrec_describe_ce_plan",
+    "genrec_describe_cand_plan",
     "genrec_status_string",
     "genrec_version",
     "genrec_profiler_create",
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.genrec_describe_plan.restype = I
         L.genrec_describe_ce_plan.argtypes = [I, I, I64, ctypes.c_char_p, SZ]
         L.genrec_describe_ce_plan.restype = I
+        L.genrec_describe_cand_plan.argtypes = [I, I, I64, I64, I, I, ctypes.c_char_p, SZ]
+        L.genrec_describe_cand_plan.restype = I
         L.genrec_status_string.argtypes = [I]
         L.genrec_status_string.restype = ctypes.c_char_p
         L.genrec_version.restype = I
@@ -152,6 +155,16 @@ def describe_plan(B: int, D: int, M: int, K: int, dtype: torch.dtype) -> dict:
     st = lib().genrec_describe_plan(B, D, M, K, dtype_code(dtype), buf, 512)
     if st != 0:
         raise GenrecError(st, "genrec_describe_plan")
+    return json.loads(buf.value.decode())
+
+
+def describe_cand_plan(B: int, D: int, M: int, nnz: int, K: int, dtype: torch.dtype) -> dict:
+    """The candidate path's plan: the hot head and where its per-item counts
+    and result sit in the workspace."""
+    buf = ctypes.create_string_buffer(512)
+    st = lib().genrec_describe_cand_plan(B, D, M, nnz, K, dtype_code(dtype), buf, 512)
+    if st != 0:
+        raise GenrecError(st, "genrec_describe_cand_plan")
     return json.loads(buf.value.decode())
 
 

@@ -259,6 +259,21 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
  * genrec_ce_backward_workspace() returns 0. */
 int genrec_describe_ce_plan(int B, int D, int64_t M, char* buf, size_t len);
 
+/* Introspection of the candidate path's plan (genrec_score_candidates_topk)
+ * for these sizes: writes into buf (at most len bytes, NUL-terminated) a
+ * JSON object with "hot" (1: the most-listed rows are scored densely on the
+ * matrix cores), "t_max" (hot rows at most), "c_min" (the smallest count that
+ * makes a row hot), "sample_every" (the list counts come from every this-many
+ * entries of the id array: entries 0, 16, 32, ...), "n_pieces_max" (work
+ * pieces at most), the byte offsets in the workspace of the per-item counts
+ * ("off_counts": int32[M], after a call the number of sampled entries naming
+ * each id; -1 without a hot head) and of the hot-head result ("off_meta":
+ * int32 count threshold c, then the number of hot rows; -1 without), and the
+ * workspace size.  Host-only.  Returns GENREC_OK, the status the compute
+ * call would return for the sizes, GENREC_ERR_INVALID_ARG for nnz < 0 or a
+ * null / empty buf. */
+int genrec_describe_cand_plan(int B, int D, int64_t M, int64_t nnz, int K, int dtype, char* buf, size_t len);
+
 /*
  * Kernel-level timing with HIP events.  A profiler records an event pair
  * around every kernel that the *_profiled entry points launch, without

@@ -429,6 +429,36 @@ def test_candidates_hot_head(dev, oracle_mod, B, M, lo, hi, seed):
         assert np.array_equal(x, y)
 
 
+def test_hot_counts_exact(dev):
+    """The hot head's per-item list counts (every 16th entry of the id array,
+    in-range ids only) equal a host count id for id, under a Zipf head whose
+    popular ids recur many times in one wave's samples; the count threshold
+    and the number of hot rows follow the plan's rule from those counts."""
+    from full_catalog_ranking_amd import genrec
+    B, D, M, K = 600, 64, 20_000, 50
+    d = synth.make_dense(B, D, M, seed=23)
+    off, ids = synth.gen_candidates(B, M, 23, 400, 800)
+    ids = ids.copy()
+    ids[16] = -5          # a sampled entry out of range: not counted
+    ids[32] = M + 1
+    plan = genrec.describe_cand_plan(B, D, M, ids.size, K, torch.bfloat16)
+    assert plan["hot"] == 1 and plan["sample_every"] == 16
+    H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
+    _, _, _, ws = genrec.score_candidates_topk(H, E, torch.from_numpy(off).to(dev), torch.from_numpy(ids).to(dev), K)
+    torch.cuda.synchronize()
+    w = ws.cpu().numpy()
+    cnt = w[plan["off_counts"]:plan["off_counts"] + 4 * M].view(np.int32)
+    s = ids[::16].astype(np.int64)
+    s = s[(s >= 0) & (s < M)]
+    expect = np.bincount(s, minlength=M)
+    assert np.array_equal(cnt, expect), np.flatnonzero(cnt != expect)[:8]
+    c, n_hot = w[plan["off_meta"]:plan["off_meta"] + 8].view(np.int32)
+    if n_hot > 0:
+        # c: the smallest count >= c_min that leaves at most t_max rows hot
+        assert c >= plan["c_min"] and n_hot == int((expect >= c).sum()) <= plan["t_max"]
+        assert c == plan["c_min"] or int((expect >= c - 1).sum()) > plan["t_max"]
+
+
 @pytest.mark.parametrize("B,D,M,lo,hi,seed", [
     (100, 264, 50, 42, 50, 54098347),  # every item hot; D % 32 = 8
     (300, 72, 3000, 50, 400, 61),      # part of the catalog hot; D % 32 = 8
