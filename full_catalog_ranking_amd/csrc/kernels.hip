@@ -571,21 +571,8 @@ __device__ void wave_sort_desc(uint64_t (&v)[C]) {
     }
 }
 
-// Count of keys in run[0..R) (descending) greater than x, or not below x
-// when `ge`.
-__device__ __forceinline__ int run_count_above(const uint64_t* run, int R, uint64_t x, bool ge) {
-    int lo = 0, hi = R;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        const uint64_t y = run[mid];
-        if (ge ? (y >= x) : (y > x)) lo = mid + 1;
-        else hi = mid;
-    }
-    return lo;
-}
-
 template <int C>
-__device__ void block_sort_runs(uint64_t* in, int n, uint64_t* out, int R) {
+__device__ void block_sort_runs(uint64_t* in, int n, uint64_t* out, int R) {  // R = 64 C
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     uint64_t v[C];
 #pragma unroll
@@ -598,14 +585,43 @@ __device__ void block_sort_runs(uint64_t* in, int n, uint64_t* out, int R) {
 #pragma unroll
     for (int t = 0; t < C; ++t) in[w * R + t * 64 + lane] = v[t];
     __syncthreads();
+    // Each key's rank: its place in its run plus, in each other run, the keys
+    // above it (earlier runs first among equal keys) -- binary searches, all
+    // C x 3 of a thread advanced in lock step so that their LDS reads are in
+    // flight together rather than one dependent chain after another.
+    constexpr int NQ = SEL_NT / kWave - 1;  // the other runs
+    constexpr int STEPS = C == 1 ? 7 : (C == 2 ? 8 : 9);  // halvings of [0, R], R = 64 C
+    static_assert(C == 1 || C == 2 || C == 4, "runs of 64, 128 or 256 keys");
+    int lo[C][NQ], hi[C][NQ];
+#pragma unroll
+    for (int t = 0; t < C; ++t)
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            lo[t][i] = 0;
+            hi[t][i] = R;
+        }
+#pragma unroll
+    for (int step = 0; step < STEPS; ++step)
+#pragma unroll
+        for (int t = 0; t < C; ++t)
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) {
+                const int q = i + (i >= w ? 1 : 0);  // wave-uniform
+                const int mid = min((lo[t][i] + hi[t][i]) >> 1, R - 1);  // (read only while lo < hi)
+                const uint64_t y = in[q * R + mid];
+                const bool above = q < w ? (y >= v[t]) : (y > v[t]);
+                if (lo[t][i] < hi[t][i]) {
+                    if (above) lo[t][i] = mid + 1;
+                    else hi[t][i] = mid;
+                }
+            }
 #pragma unroll
     for (int t = 0; t < C; ++t) {
-        const uint64_t x = v[t];
-        if (x == 0ull) continue;
+        if (v[t] == 0ull) continue;
         int r = t * 64 + lane;
-        for (int q = 0; q < SEL_NT / kWave; ++q)
-            if (q != w) r += run_count_above(in + q * R, R, x, q < w);  // earlier runs first among equal keys
-        out[r] = x;
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) r += lo[t][i];
+        out[r] = v[t];
     }
 }
 
