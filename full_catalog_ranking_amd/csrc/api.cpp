@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -39,6 +40,22 @@ uint64_t next_ticket() {
         const uint64_t t = counter.fetch_add(1, std::memory_order_relaxed) & kMask;
         if (t != 0 && t != kMask) return t;
     }
+}
+
+// Budget of the candidate regions that hold every item (8 bytes per user and
+// item); larger shapes take bounded regions.  GENREC_KEY_BUDGET (bytes) sets
+// it for the process, read at every plan, so that a workspace query and the
+// call it sizes agree while the variable is unchanged.
+size_t key_budget() {
+    const char* e = getenv("GENREC_KEY_BUDGET");
+    if (e == nullptr || *e == '\0') return kDefaultKeyBudget;
+    char* end = nullptr;
+    const unsigned long long v = strtoull(e, &end, 10);
+    return (end != nullptr && *end == '\0') ? (size_t)v : kDefaultKeyBudget;
+}
+
+DensePlan plan_dense_env(int B, int D, int64_t M, int K, int dtype) {
+    return plan_dense(B, D, M, K, dtype, key_budget());
 }
 
 template <class T>
@@ -153,7 +170,7 @@ size_t genrec_score_lse_topk_workspace(int B, int D, int64_t M, int K, int dtype
     static const float dummy[4] = {0, 0, 0, 0};
     if (check_common(dummy, dummy, dtype, B, D, M, K, (const int32_t*)dummy, dummy, dummy) != GENREC_OK)
         return 0;
-    return plan_dense(B, D, M, K, dtype).total;  // 0 when the plan is unsupported
+    return plan_dense_env(B, D, M, K, dtype).total;  // 0 when the plan is unsupported
 }
 
 int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, size_t len) {
@@ -161,16 +178,18 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
     const int st = check_common(dummy, dummy, dtype, B, D, M, K, (const int32_t*)dummy, dummy, dummy);
     if (st != GENREC_OK) return st;
     if (!buf || len == 0) return GENREC_ERR_INVALID_ARG;
-    const DensePlan p = plan_dense(B, D, M, K, dtype);
+    const DensePlan p = plan_dense_env(B, D, M, K, dtype);
     if (!p.ok) return GENREC_ERR_UNSUPPORTED;
     snprintf(buf, len,
              "{\"path\":\"%s\",\"sample\":%d,\"stride\":%lld,\"n_sample\":%lld,\"fast\":%d,\"r_fast\":%d,"
              "\"UT\":%d,\"P\":%d,\"tiles_per_chunk\":%d,\"CH\":%lld,\"merge_small\":%d,\"fused\":%d,"
-             "\"sample_splits\":%d,\"safe_exact\":%d,\"first_sampled_tile\":%lld,\"workspace\":%zu}",
+             "\"sample_splits\":%d,\"safe_exact\":%d,\"first_sampled_tile\":%lld,\"bounded\":%d,\"cap\":%d,"
+             "\"ccol\":%d,\"workspace\":%zu}",
              p.mfma ? "mfma" : "stream", p.sample ? 1 : 0, (long long)p.stride, (long long)p.n_sample,
              p.fast ? 1 : 0, p.r_fast, p.main.UT, p.main.P, p.main.base + (p.main.rem ? 1 : 0),
              (long long)p.main.CH, p.merge_small ? 1 : 0, p.fused ? 1 : 0, p.sample_splits, p.safe_exact ? 1 : 0,
-             p.sample ? mf_sample_tile(0, p.stride, M / kMfmaTileItems) : -1LL, p.total);
+             p.sample ? mf_sample_tile(0, p.stride, M / kMfmaTileItems) : -1LL, p.bounded ? 1 : 0, p.cap, p.ccol,
+             p.total);
     return GENREC_OK;
 }
 
@@ -191,7 +210,7 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
                 size_t workspace_bytes, void* stream, genrec_profiler* prof) {
     int st = check_common(H, E, dtype, B, D, M, K, out_idx, out_scores, out_lse);
     if (st != GENREC_OK) return st;
-    const DensePlan p = plan_dense(B, D, M, K, dtype);
+    const DensePlan p = plan_dense_env(B, D, M, K, dtype);
     if (!p.ok) return GENREC_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < p.total) return GENREC_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return GENREC_ERR_INVALID_ARG;
@@ -253,6 +272,7 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     th.theta_fast = p.fast ? theta_fast : nullptr;
     th.user_flag = uflag;
     th.tile_flag = tflag;
+    th.tile_cnt = p.bounded ? at<int>(workspace, p.off_tcnt) : nullptr;
     th.rescued = rescued;
     // The rescue counter is cleared by the threshold kernel when it runs,
     // else by the merge (see below).
@@ -304,6 +324,7 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
         a.pl = pl;
         a.pcnt = pcnt;
         a.preg = preg;
+        a.cap = p.bounded ? p.cap : 0;
         if ((st = hip_status(timed(prof, KIND_MAIN, s, [&] { return launch_mfma(a, 1, s); }))) != GENREC_OK) return st;
     } else {
         StreamArgs a{};
@@ -359,8 +380,65 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     m.theta_safe = theta_safe;
     m.safe_exact = p.safe_exact ? 1 : 0;
     m.small = p.merge_small ? 1 : 0;
+    NarrowState* nst = nullptr;
+    uint32_t* hist = nullptr;
+    uint64_t* coll = nullptr;
+    int* ccnt = nullptr;
+    int* tcnt = nullptr;
+    if (p.bounded) {
+        nst = at<NarrowState>(workspace, p.off_nst);
+        hist = at<uint32_t>(workspace, p.off_hist);
+        coll = at<uint64_t>(workspace, p.off_coll);
+        ccnt = at<int>(workspace, p.off_ccnt);
+        tcnt = at<int>(workspace, p.off_tcnt);
+        m.cap = p.cap;
+        m.nst = nst;
+        m.hist = hist;
+        m.coll = coll;
+        m.ccnt = ccnt;
+        m.cbase = at<int64_t>(workspace, p.off_cbase);
+        m.ccol = p.ccol;
+        m.tile_cnt = tcnt;
+    }
     if ((st = hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }))) != GENREC_OK) return st;
     if (!p.fast) return GENREC_OK;
+    if (p.bounded) {
+        // Rescue over bounded regions (users flagged by the merge for an
+        // overflowed piece or too few candidates): counting passes narrow each
+        // such user's bound on its ranking keys, a collect pass stores the
+        // keys at or above it, and the merge ranks them.  With no flagged user
+        // every launch exits at once.
+        static_assert(kNarrowBinsPlan == kNarrowBins, "histogram bins of the plan and the kernels");
+        a.cap = 0;
+        a.tile_flag = tflag;
+        a.user_flag = nullptr;
+        a.nst = nst;
+        a.hist = hist;
+        a.coll = coll;
+        a.ccnt = ccnt;
+        a.ccol = p.ccol;
+        a.tile_cnt = tcnt;
+        NarrowArgs nr{};
+        nr.nst = nst;
+        nr.hist = hist;
+        nr.tile_cnt = tcnt;
+        nr.B = B;
+        nr.K = K;
+        nr.ccol = p.ccol;
+        for (int pass = 0; pass < kNarrowPasses; ++pass) {
+            a.collect = 0;
+            if ((st = hip_status(timed(prof, KIND_RESCUE, s, [&] { return launch_mfma(a, 6, s); }))) != GENREC_OK)
+                return st;
+            if ((st = hip_status(timed(prof, KIND_RESCUE, s, [&] { return launch_narrow(nr, s); }))) != GENREC_OK)
+                return st;
+        }
+        a.collect = 1;
+        if ((st = hip_status(timed(prof, KIND_RESCUE, s, [&] { return launch_mfma(a, 6, s); }))) != GENREC_OK) return st;
+        m.mode = 3;
+        m.small = 0;
+        m.clear_err = nullptr;
+        return hip_status(timed(prof, KIND_RESCUE, s, [&] { return launch_merge(m, s); }));
+    }
     // Rescue: users the fast threshold left short of K candidates are scored
     // again (their whole user tile) with the K-th sampled score -- or, when
     // the sampled scores came from a split reduction, with no threshold at all
@@ -423,7 +501,7 @@ int genrec_score_lse_topk_noalloc(const void* H, const void* E, int dtype, int B
                                   int32_t* out_idx, float* out_scores, float* out_lse, void* stream) {
     int st = check_common(H, E, dtype, B, D, M, K, out_idx, out_scores, out_lse);
     if (st != GENREC_OK) return st;
-    const DensePlan p = plan_dense(B, D, M, K, dtype);
+    const DensePlan p = plan_dense_env(B, D, M, K, dtype);
     if (!p.ok) return GENREC_ERR_UNSUPPORTED;
     if (p.total > GENREC_NOALLOC_SCRATCH_BYTES) return GENREC_ERR_TOO_LARGE;
     void* ws = nullptr;

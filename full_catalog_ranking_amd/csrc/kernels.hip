@@ -61,7 +61,7 @@ namespace genrec {
 template <int MODE, bool KTAIL, bool MASKED, bool F32 = false>
 __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[MF_NS][MF_STAGE];
-    static_assert(!F32 || MODE <= 1, "fp32 operands: the dense sample and main passes only");
+    static_assert(!F32 || MODE <= 1 || MODE == 6, "fp32 operands: the dense sample, main and rescue passes only");
     constexpr int ES = F32 ? 4 : 2;         // bytes per element
     constexpr int KE = MF_ROWB / ES;        // reduction elements per k-step (32 bf16 / 16 fp32)
     constexpr int CE = 16 / ES;             // elements per 16-byte k-chunk
@@ -76,7 +76,8 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
     const int c = L / a.UT, ut = L - c * a.UT;
     // rescue pass: user tiles without a flagged user have nothing to redo
-    if (MODE == 1 && a.tile_flag != nullptr && a.tile_flag[ut] == 0) return;
+    if ((MODE == 1 || MODE == 6) && a.tile_flag != nullptr && a.tile_flag[ut] == 0) return;
+    if (MODE == 6 && !a.collect && a.tile_cnt[ut] == 0) return;  // every user of the tile resolved
     const int tile0 = c * a.base + min(c, a.rem);  // first pass-tile of this chunk
     const int ntiles = a.base + (c < a.rem ? 1 : 0);
     // dense pass over a partly filled catalog: chunks past its live rows are idle
@@ -197,6 +198,9 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     const int64_t n_pass = (int64_t)a.n_tiles * MF_TI;  // mode 0: row length of sample_out
     float m_[MF_UB], l_[MF_UB], th_[MF_UB];
     int cnt_[MF_UB];
+    uint64_t nlo_[MF_UB];  // mode 6: the user's key bound, bin shift and whether it takes part
+    int nsh_[MF_UB];
+    bool nin_[MF_UB];
 #pragma unroll
     for (int ub = 0; ub < MF_UB; ++ub) {
         const int u = u0 + wu * MF_WU + ub * 32 + (lane & 31);
@@ -208,6 +212,12 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         // users past B never append, nor, in the rescue pass, unflagged users
         const bool active = u < a.B && (a.user_flag == nullptr || a.user_flag[u] != 0);
         th_[ub] = active && !a.no_cand ? t : INFINITY;
+        if (MODE == 6) {
+            const bool in = u < a.B && a.nst[u].status == (a.collect ? 2 : 1);
+            nlo_[ub] = in ? a.nst[u].lo : ~0ull;
+            nsh_[ub] = in ? a.nst[u].shift : 0;
+            nin_[ub] = in;
+        }
     }
 
     auto epilogue = [&](int t) {
@@ -342,6 +352,34 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                 }
                 continue;
             }
+            if (MODE == 6) {
+                // rescue of a flagged user: count (or collect) every finite
+                // score whose ranking key is at least the user's bound
+                if (nin_[ub]) {
+                    const uint64_t lo = nlo_[ub];
+#pragma unroll
+                    for (int ib = 0; ib < 4; ++ib) {
+                        const uint32_t mw = mask_word(ib);
+                        const uint32_t idb = (uint32_t)(j0 + lrow0 + ib * 32);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float v = acc[ib][ub][r];
+                            if (MASKED && !((mw >> (mbit0 + (r >> 2) * 8 + (r & 3))) & 1u)) continue;
+                            if (!(v >= -FLT_MAX)) continue;  // rows past the catalog's end (-inf)
+                            const uint64_t key = rank_key(v, idb + (r >> 2) * 8 + (r & 3));
+                            if (key < lo) continue;
+                            if (a.collect) {
+                                const int slot = atomicAdd(a.ccnt + u, 1);
+                                if (slot < a.ccol) a.coll[(int64_t)u * a.ccol + slot] = key;
+                            } else {
+                                const uint64_t bin = (key - lo) >> nsh_[ub];
+                                if (bin < (uint64_t)kNarrowBins) atomicAdd(a.hist + (int64_t)u * kNarrowBins + bin, 1u);
+                            }
+                        }
+                    }
+                }
+                continue;
+            }
             // exact running max per 32 x 32 block: the block's max, one rescale
             // of the running sum and one exp per score against it
             const float th = th_[ub];
@@ -371,11 +409,18 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                     m_[ub] = mnew;
                 }
                 if (bmax >= th) {
-                    uint64_t* kreg = a.keys + (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles;
+                    // bounded regions: a full piece keeps counting (the merge
+                    // sends its user to the rescue) but stores nothing more
+                    const int capr = a.cap > 0 ? a.cap : INT_MAX;
+                    uint64_t* kreg = a.keys + (a.cap > 0 ? (((int64_t)u * a.P + c) * 4 + g) * a.cap
+                                                         : (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles);
                     const uint32_t idb = (uint32_t)(j0 + jb);
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
-                        if (v[r] >= th) kreg[cnt_[ub]++] = rank_key(v[r], idb + (r >> 2) * 8 + (r & 3));
+                        if (v[r] >= th) {
+                            if (cnt_[ub] < capr) kreg[cnt_[ub]] = rank_key(v[r], idb + (r >> 2) * 8 + (r & 3));
+                            ++cnt_[ub];
+                        }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -462,7 +507,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         // set once here under a uniform branch.  Folding this test into every
         // block's epilogue made the compiler keep 16 row masks per block in
         // scalar registers and spill them on every tile.
-        if (MODE == 1 && tile_valid(tile0 + t) < MF_TI) {
+        if ((MODE == 1 || MODE == 6) && tile_valid(tile0 + t) < MF_TI) {
             const int lim = tile_valid(tile0 + t);
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib)
@@ -485,7 +530,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                 a.pm[piece] = m_[ub];
                 a.pl[piece] = l_[ub];
                 a.pcnt[piece] = cnt_[ub];
-                a.preg[piece] = (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles;
+                a.preg[piece] = a.cap > 0 ? piece * a.cap : (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles;
             }
         }
     }
@@ -917,6 +962,7 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
     if (tid == 0) {
         if (a.user_flag != nullptr) a.user_flag[b] = 0;
         if (a.tile_flag != nullptr && b % MF_TU == 0) a.tile_flag[b / MF_TU] = 0;
+        if (a.tile_cnt != nullptr && b % MF_TU == 0) a.tile_cnt[b / MF_TU] = 0;
         if (a.rescued != nullptr && b == 0) *a.rescued = 0;
     }
     const int n = (int)a.n_sample;
@@ -1333,8 +1379,10 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     __shared__ PieceShared<MG_PB> ps;
     __shared__ float2 s_ml[SEL_NT / kWave];
     __shared__ unsigned long long s_n[SEL_NT / kWave];
+    __shared__ int s_ovf[SEL_NT / kWave];
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (a.mode == 2 && a.user_flag[b] == 0) return;  // rescue merge: flagged users only
+    if (a.mode == 3 && a.nst[b].status == 0) return;  // bounded rescue merge: flagged users only
     if (b == 0 && tid == 0 && a.clear_err != nullptr) {
         a.clear_err[0] = 0;
         a.clear_err[1] = 0;
@@ -1349,10 +1397,26 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
         p0 = (int64_t)b * a.P;
         p1 = p0 + a.P;
     }
+    const uint64_t* keys = a.keys;
+    const int* pcnt = a.pcnt;
+    const int64_t* preg = a.preg;
+    unsigned long long ntot = 0;
+    if (a.mode == 3) {
+        // the keys collected for this user (its lse was written by mode 1)
+        if (tid == 0 && a.ccnt[b] > a.ccol) a.ccnt[b] = a.ccol;
+        __syncthreads();
+        keys = a.coll;
+        pcnt = a.ccnt;
+        preg = a.cbase;
+        p0 = b;
+        p1 = b + 1;
+        ntot = (unsigned long long)a.ccnt[b];
+    } else {
     // lse and candidate count over the user's pieces
     LseState st;
     st.init();
     unsigned long long n = 0;
+    int ovf = 0;  // bounded regions: some piece counted more keys than it holds
     // four pieces per thread and round, their loads issued together (indices
     // clamped into the user's pieces); merged in the same order as one by one
     for (int64_t pq = p0 + tid; pq < p1; pq += 4 * SEL_NT) {
@@ -1370,6 +1434,7 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
             if (pq + (int64_t)i * SEL_NT < p1) {
                 st.merge(pm4[i], pl4[i]);
                 n += (unsigned long long)pc4[i];
+                ovf |= a.cap > 0 && pc4[i] > a.cap;
             }
     }
 #pragma unroll
@@ -1377,14 +1442,57 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
         const float m2 = __shfl_xor(st.m, o), l2 = __shfl_xor(st.l, o);
         st.merge(m2, l2);
         n += __shfl_xor(n, o);
+        ovf |= __shfl_xor(ovf, o);
     }
-    if (lane == 0) { s_ml[w] = make_float2(st.m, st.l); s_n[w] = n; }
+    if (lane == 0) { s_ml[w] = make_float2(st.m, st.l); s_n[w] = n; s_ovf[w] = ovf; }
     __syncthreads();
     LseState tot;
     tot.init();
-    unsigned long long ntot = 0;
-    for (int q = 0; q < SEL_NT / kWave; ++q) { tot.merge(s_ml[q].x, s_ml[q].y); ntot += s_n[q]; }
-    if (a.mode == 1 && ntot < (unsigned long long)a.K && (!a.safe_exact || a.theta_fast[b] > a.theta_safe[b])) {
+    ovf = 0;
+    for (int q = 0; q < SEL_NT / kWave; ++q) { tot.merge(s_ml[q].x, s_ml[q].y); ntot += s_n[q]; ovf |= s_ovf[q]; }
+    const bool short_k =
+        a.mode == 1 && ntot < (unsigned long long)a.K && (!a.safe_exact || a.theta_fast[b] > a.theta_safe[b]);
+    if (a.cap > 0 && a.mode == 1) {
+        // bounded regions: every user's rescue state is (re)set here
+        const bool flag = short_k || ovf;
+        if (tid == 0) {
+            NarrowState ns{};
+            if (flag) {
+                a.out_lse[b] = tot.l > 0.f ? tot.m + __builtin_amdgcn_logf(tot.l) * kLn2 : -INFINITY;
+                // lower bound of the keys to consider: the fast threshold when
+                // it let K keys through, else the K-th sampled score's (exact
+                // sample) or every finite score
+                const float tf = a.theta_fast[b], ts = a.theta_safe[b];
+                const float tl = ntot >= (unsigned long long)a.K ? tf : (a.safe_exact ? fminf(ts, tf) : -FLT_MAX);
+                ns.lo = (uint64_t)order_key(fmaxf(tl, -FLT_MAX)) << 32;
+                const uint64_t hi = ((uint64_t)order_key(tot.m) << 32) | 0xFFFFFFFFull;  // the user's largest key
+                ns.k_rem = a.K;
+                if (tot.l == 0.f || hi < ns.lo || (ntot >= (unsigned long long)a.K && ntot <= (unsigned long long)a.ccol)) {
+                    ns.status = 2;  // no key at all, or all of them fit: collect at once
+                } else {
+                    const uint64_t wdt = hi - ns.lo;
+                    const int bits = 64 - __builtin_clzll(wdt | 1ull);
+                    ns.shift = bits > kNarrowBits ? bits - kNarrowBits : 0;
+                    ns.status = 1;
+                    atomicAdd(a.tile_cnt + b / MF_TU, 1);
+                }
+                a.ccnt[b] = 0;
+                a.cbase[b] = (int64_t)b * a.ccol;
+                a.user_flag[b] = 1;
+                a.tile_flag[b / MF_TU] = 1;
+                atomicAdd((unsigned long long*)a.rescued, 1ull);
+            }
+            a.nst[b] = ns;
+        }
+        if (flag) {
+            if (a.nst != nullptr) {
+                uint4* hrow = (uint4*)(a.hist + (int64_t)b * kNarrowBins);
+                for (int i = tid; i < kNarrowBins / 4; i += SEL_NT) hrow[i] = make_uint4(0u, 0u, 0u, 0u);
+            }
+            return;
+        }
+    }
+    if (short_k) {
         // the fast threshold let fewer than K items through: the rescue pass
         // recomputes this user with the K-th sampled score (when that is
         // lower: else every item it would keep was kept, e.g. a user with
@@ -1398,13 +1506,14 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     }
     if (tid == 0)
         a.out_lse[b] = tot.l > 0.f ? tot.m + __builtin_amdgcn_logf(tot.l) * kLn2 : -INFINITY;
+    }
 
     const int K = a.K;
     const int keff = (int)min((unsigned long long)K, ntot);
     int32_t* oidx = a.out_idx + (int64_t)b * K;
     float* osc = a.out_scores + (int64_t)b * K;
     if (keff > 0) {
-        PieceSrc<MG_PB> src{a.keys, a.pcnt, a.preg, p0, p1, (int64_t)ntot, &ps};
+        PieceSrc<MG_PB> src{keys, pcnt, preg, p0, p1, (int64_t)ntot, &ps};
         block_select<true>(src, keff, sh);
         // the K keys in ranking order: rank placement for a few hundred
         // (quadratic compares, one barrier), wave sorts and a rank merge for more
@@ -1424,6 +1533,87 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
             oidx[i] = -1;
             osc[i] = -INFINITY;
         }
+    }
+}
+
+// One counting pass's pick for a flagged user over bounded regions: the bin
+// holding the user's k_rem-th key from the top becomes the next range (its
+// keys then split 4,096 ways), or, once the keys at or above the bin's start
+// fit the collect region, the final bound.  Bins are 2^shift keys wide, so a
+// range narrows 12 bits a pass and a bin of width 1 holds one key: at most
+// six passes for 64-bit keys.  The histogram row is zeroed for the next pass.
+constexpr int NR_NT = 256;
+static_assert(kNarrowBins == NR_NT * 16, "16 bins per thread");
+
+__global__ __launch_bounds__(NR_NT) void narrow_kernel(NarrowArgs a) {
+    __shared__ uint32_t s_w[NR_NT / kWave];
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (a.nst[b].status != 1) return;
+    const NarrowState st = a.nst[b];
+    uint4* hrow = (uint4*)(a.hist + (int64_t)b * kNarrowBins) + tid * 4;  // bins 16 tid .. 16 tid + 15
+    uint32_t v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 q = hrow[i];
+        v[4 * i] = q.x;
+        v[4 * i + 1] = q.y;
+        v[4 * i + 2] = q.z;
+        v[4 * i + 3] = q.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hrow[i] = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t tsum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tsum += v[i];
+    uint32_t incl = tsum;  // inclusive prefix sum over the threads
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) s_w[w] = incl;
+    __syncthreads();
+    uint32_t total = 0;
+    for (int q = 0; q < NR_NT / kWave; ++q) {
+        if (q < w) incl += s_w[q];
+        total += s_w[q];
+    }
+    const uint32_t above = total - incl;  // keys in the bins of the threads above this one
+    const uint32_t kr = (uint32_t)st.k_rem;
+    if (total < kr) {  // fewer keys than wanted at or above lo: keep them all
+        if (tid == 0) {
+            a.nst[b].status = 2;
+            atomicSub(a.tile_cnt + b / MF_TU, 1);
+        }
+        return;
+    }
+    if (above < kr && kr <= above + tsum) {  // exactly one thread: the one holding the k_rem-th key
+        bool found = false;
+        uint32_t cum = above, cum_at = 0, vj = 0;
+        int j = 0;
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+            if (!found && cum + v[i] >= kr) {
+                found = true;
+                j = tid * 16 + i;
+                cum_at = cum;
+                vj = v[i];
+            }
+            cum += v[i];
+        }
+        NarrowState ns = st;
+        ns.lo = st.lo + ((uint64_t)j << st.shift);
+        // keys at or above the bin's start: those above the range, those of
+        // the bins above it and the bin's own
+        const int64_t count_ge = (int64_t)(a.K - st.k_rem) + cum_at + vj;
+        if (count_ge <= a.ccol || st.shift == 0) {
+            ns.status = 2;
+            atomicSub(a.tile_cnt + b / MF_TU, 1);
+        } else {
+            ns.k_rem = st.k_rem - (int)cum_at;
+            ns.shift = st.shift > kNarrowBits ? st.shift - kNarrowBits : 0;
+        }
+        a.nst[b] = ns;
     }
 }
 
@@ -2930,7 +3120,7 @@ hipError_t launch_mfma_split(const MfmaArgs& a, int mode, int splits, hipStream_
 }
 
 hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s, int splits) {
-    if (splits < 1 || (splits > 1 && mode != 0)) return hipErrorInvalidValue;
+    if (splits < 1 || (splits > 1 && mode != 0) || (mode != 0 && mode != 1 && mode != 6)) return hipErrorInvalidValue;
     const dim3 grid(a.UT * a.P, splits);
     const bool masked = a.mask != nullptr;
     if (a.f32) {
@@ -2943,6 +3133,12 @@ hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s, int splits) {
                 if (ktail) GENREC_MFMA32(0, true, true); else GENREC_MFMA32(0, false, true);
             } else {
                 if (ktail) GENREC_MFMA32(0, true, false); else GENREC_MFMA32(0, false, false);
+            }
+        } else if (mode == 6) {
+            if (masked) {
+                if (ktail) GENREC_MFMA32(6, true, true); else GENREC_MFMA32(6, false, true);
+            } else {
+                if (ktail) GENREC_MFMA32(6, true, false); else GENREC_MFMA32(6, false, false);
             }
         } else {
             if (masked) {
@@ -2961,6 +3157,12 @@ hipError_t launch_mfma(const MfmaArgs& a, int mode, hipStream_t s, int splits) {
             if (ktail) GENREC_MFMA(0, true, true); else GENREC_MFMA(0, false, true);
         } else {
             if (ktail) GENREC_MFMA(0, true, false); else GENREC_MFMA(0, false, false);
+        }
+    } else if (mode == 6) {
+        if (masked) {
+            if (ktail) GENREC_MFMA(6, true, true); else GENREC_MFMA(6, false, true);
+        } else {
+            if (ktail) GENREC_MFMA(6, true, false); else GENREC_MFMA(6, false, false);
         }
     } else {
         if (masked) {
@@ -3047,6 +3249,11 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((merge_kernel<MG_GCAP_SMALL, MG_PB_SMALL>), dim3(a.B), dim3(SEL_NT), 0, s, a);
     else
         hipLaunchKernelGGL((merge_kernel<SEL_GCAP, MG_PB_LARGE>), dim3(a.B), dim3(SEL_NT), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_narrow(const NarrowArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(narrow_kernel, dim3(a.B), dim3(NR_NT), 0, s, a);
     return hipGetLastError();
 }
 

@@ -10,6 +10,18 @@ namespace genrec {
 
 constexpr int CAND_PIECE = 256;  // candidate-list entries per work piece
 
+// Rescue of a user over bounded candidate regions: the keys at or above lo
+// are narrowed by counting passes until they fit the user's collect region.
+struct NarrowState {
+    uint64_t lo;  // lower bound (inclusive) of the 64-bit ranking keys still considered
+    int shift;    // counting pass: key k falls in bin (k - lo) >> shift of kNarrowBins
+    int k_rem;    // keys of the top K in [lo, range end); the other K - k_rem lie above the range
+    int status;   // 0: not flagged; 1: counting; 2: resolved (collect the keys >= lo)
+    int pad;
+};
+constexpr int kNarrowBins = 4096;  // 12 bits of the key per counting pass
+constexpr int kNarrowBits = 12;
+
 struct MfmaArgs {
     const uint16_t* H;  // bf16 elements, or fp32 ones when f32 (modes 0 and 1)
     const uint16_t* E;
@@ -45,6 +57,22 @@ struct MfmaArgs {
     int64_t k_split;
     // mode 1: no candidate is kept at all (logsumexp pieces only)
     int no_cand;
+    // mode 1: keys per candidate region when the regions are bounded (piece p
+    // at keys + p * cap; a piece past it keeps counting but stores nothing);
+    // 0: region of every item (user u at keys + u * key_stride)
+    int cap;
+    // mode 6 -- exact rescue of flagged users over bounded regions: only users
+    // whose nst[u].status equals want take part; every finite score's key
+    // k >= nst[u].lo is, when collect == 0, counted into hist[u * kNarrowBins +
+    // ((k - lo) >> shift)] (keys past the last bin skipped), else stored at
+    // coll[u * ccol + slot], slot = atomicAdd(&ccnt[u], 1) (< ccol kept)
+    NarrowState* nst;
+    uint32_t* hist;
+    uint64_t* coll;
+    int* ccnt;
+    int ccol;
+    int collect;
+    const int* tile_cnt;  // mode 6 counting: user tiles with no user left counting exit at once
     // mode 3 -- softmax-minus-target tiles of the cross-entropy gradient:
     // rows are catalog items item0 + j (j < M valid), columns users;
     // g = w[u] (exp(s - lse[u]) - [item0 + j == labels[u]]) goes to
@@ -200,6 +228,28 @@ struct MergeArgs {
     // 1: the smaller merge build (users with at most ~512 pieces and ~2,048
     // candidates expected); any value gives the same result
     int small;
+    // Bounded regions (cap > 0): a piece holds at most cap keys and counts
+    // them all.  Mode 1 flags a user with an overflowed piece as well, writes
+    // its lse, and starts its rescue state (nst, a zeroed hist row, ccnt = 0,
+    // cbase = u * ccol); mode 3 ranks flagged users from their collect region
+    // (coll + cbase[u], min(ccnt[u], ccol) keys), lse left as mode 1 wrote it.
+    int cap;
+    NarrowState* nst;
+    uint32_t* hist;
+    const uint64_t* coll;
+    int* ccnt;
+    int64_t* cbase;
+    int ccol;
+    int* tile_cnt;  // per 256-user tile: users still counting (mode 1 adds them)
+};
+
+// One block per user: picks the bin of the counted histogram that holds the
+// user's K-th key and narrows the state to it (or resolves it).
+struct NarrowArgs {
+    NarrowState* nst;
+    uint32_t* hist;
+    int* tile_cnt;  // a resolved user leaves its tile's count
+    int B, K, ccol;
 };
 
 struct ThresholdArgs {
@@ -212,6 +262,7 @@ struct ThresholdArgs {
     float* theta_fast;    // [B] lower bound of the r_fast-th largest (may be null)
     int* user_flag;       // [B] cleared (may be null)
     int* tile_flag;       // [ceil(B/256)] cleared (may be null)
+    int* tile_cnt;        // [ceil(B/256)] cleared (may be null)
     int64_t* rescued;     // cleared by block 0 (may be null)
 };
 
@@ -247,6 +298,7 @@ hipError_t launch_stream(const StreamArgs& a, int mode, bool f32, int64_t grid, 
 hipError_t launch_fused(const StreamArgs& a, bool f32, int64_t grid, hipStream_t s);
 hipError_t launch_threshold(const ThresholdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_narrow(const NarrowArgs& a, hipStream_t s);
 hipError_t launch_cand_plan(const CandPlanArgs& a, hipStream_t s);
 hipError_t launch_hot_select(const HotArgs& a, hipStream_t s);
 // mode 3 / 4 of launch_mfma take grid y = splits of the reduction

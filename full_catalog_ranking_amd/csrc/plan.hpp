@@ -67,6 +67,23 @@ struct Chunking {
     int64_t CH = 0;                        // VALU: items per chunk (P chunks)
 };
 
+// Bounded candidate regions.  With a sampled threshold the main pass keeps,
+// per piece (user, chunk, lane group), at most `cap` keys -- kCapFactor times
+// the count the threshold is expected to let through there, at least
+// kCapMin -- and counts them all.  A user whose piece overflowed (or who was
+// left short of K) is finished exactly by the rescue: counting passes over
+// its user tile narrow a 4,096-bin histogram of its ranking keys (12 bits a
+// pass, kNarrowPasses passes cover 64-bit keys) until the keys at or above the
+// bound fit its collect region of `ccol` keys, which one more pass fills.
+// Regions of every item (8 bytes per user and item) are kept while they
+// take at most the key budget: they need no rescue for overflow.
+constexpr size_t kDefaultKeyBudget = (size_t)256 << 20;
+constexpr int kCapFactor = 8;
+constexpr int kCapMin = 64;
+constexpr int kNarrowPasses = 6;
+constexpr int kNarrowBinsPlan = 4096;  // = the kernels' kNarrowBins
+constexpr int kCollectSlack = 1024;    // collect region: kCapFactor K + this many keys
+
 // The merge's smaller build (LDS gather of 2,048 keys, 512-piece batches)
 // serves users expected to hold at most that many candidates and pieces.
 constexpr int kMergeSmallGather = 2048;
@@ -99,9 +116,12 @@ struct DensePlan {
     // rescue pass then keeps every score of a flagged user
     int sample_splits = 1;
     bool safe_exact = true;
+    bool bounded = false;      // candidate regions of `cap` keys per piece (else of every item)
+    int cap = 0;
+    int ccol = 0;              // bounded: keys of a flagged user's collect region
     size_t off_hdr = 0, off_theta = 0, off_theta_safe = 0, off_uflag = 0, off_tflag = 0, off_sample = 0,
            off_pm = 0, off_pl = 0, off_pcnt = 0, off_preg = 0, off_keys = 0, off_arrive = 0, off_elect = 0, off_rows = 0,
-           total = 0;
+           off_nst = 0, off_hist = 0, off_coll = 0, off_ccnt = 0, off_cbase = 0, off_tcnt = 0, total = 0;
 };
 
 inline Chunking chunk_mfma(int B, int64_t n_tiles) {
@@ -128,7 +148,7 @@ inline Chunking chunk_stream(int B, int64_t n_items) {
 // more, and for fp32 ones as well unless the catalog is small enough for the
 // one-launch VALU path (fp32 MFMA: 16 times fewer flops per cycle than bf16,
 // still twice the non-packed VALU rate, and E read once rather than per user).
-inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
+inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype, size_t key_budget = kDefaultKeyBudget) {
     (void)D;
     DensePlan p;
     p.mfma = B > kStreamMaxB && (dtype == 0 || M > kFusedMaxM);
@@ -169,6 +189,21 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
         p.merge_small = (int64_t)p.main.P * p.pieces_per_chunk <= kMergeSmallPieces && expect <= kMergeSmallGather;
     }
     p.fused = !p.mfma && !p.sample && M <= kFusedMaxM;
+    if (p.mfma && p.fast && K > 0) {
+        // full regions cost 8 bytes per (user, item); past the budget, pieces
+        // of cap keys sized from the expected count (about 4 K per user over
+        // 4 P pieces)
+        const uint64_t full = 8ull * (uint64_t)B * (uint64_t)p.key_stride;
+        const int64_t per_piece = ceil_div((int64_t)kFastOversample * K, (int64_t)p.main.P * 4);
+        const int64_t piece_max = (int64_t)64 * (p.main.base + (p.main.rem > 0 ? 1 : 0));  // items of a piece
+        int64_t cap = std::max<int64_t>(kCapMin, ceil_div(kCapFactor * per_piece, 16) * 16);
+        cap = std::min<int64_t>(cap, piece_max);
+        if (full > (uint64_t)key_budget && cap < piece_max) {
+            p.bounded = true;
+            p.cap = (int)cap;
+            p.ccol = (int)(ceil_div((int64_t)kCapFactor * K + kCollectSlack, 256) * 256);
+        }
+    }
     // launch grids: MFMA passes UT x P blocks, VALU passes B x P, merge B
     const int64_t grid = p.mfma ? (int64_t)p.main.UT * p.main.P : p.n_pieces;
     const int64_t pre_grid = p.sample ? (p.mfma ? (int64_t)p.pre.UT * p.pre.P : (int64_t)B * p.pre.P) : 0;
@@ -191,7 +226,17 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype) {
         p.off_pl = L.take(sizeof(float), (uint64_t)p.n_pieces);
         p.off_pcnt = L.take(sizeof(int), (uint64_t)p.n_pieces);
         p.off_preg = L.take(sizeof(int64_t), (uint64_t)p.n_pieces);
-        p.off_keys = L.take(sizeof(uint64_t), (uint64_t)B * (uint64_t)p.key_stride);
+        if (p.bounded) {
+            p.off_keys = L.take(sizeof(uint64_t) * (uint64_t)p.cap, (uint64_t)p.n_pieces);
+            p.off_nst = L.take(32, (uint64_t)B);
+            p.off_hist = L.take(sizeof(uint32_t) * (uint64_t)kNarrowBinsPlan, (uint64_t)B);
+            p.off_coll = L.take(sizeof(uint64_t) * (uint64_t)p.ccol, (uint64_t)B);
+            p.off_ccnt = L.take(sizeof(int), (uint64_t)B);
+            p.off_cbase = L.take(sizeof(int64_t), (uint64_t)B);
+            p.off_tcnt = L.take(sizeof(int), (uint64_t)ceil_div(B, kMfmaTileUsers));
+        } else {
+            p.off_keys = L.take(sizeof(uint64_t), (uint64_t)B * (uint64_t)p.key_stride);
+        }
     }
     p.ok = p.ok && L.ok;
     p.total = p.ok ? L.o : 0;

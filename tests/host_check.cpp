@@ -38,6 +38,8 @@ struct Region {
 
 // Regions sorted by offset: aligned, disjoint, inside the total.
 static void check_regions(std::vector<Region> r, size_t total, const char* what) {
+    // empty regions hold nothing (their offsets need not be set)
+    r.erase(std::remove_if(r.begin(), r.end(), [](const Region& x) { return x.bytes == 0; }), r.end());
     std::sort(r.begin(), r.end(), [](const Region& a, const Region& b) { return a.off < b.off; });
     for (size_t i = 0; i < r.size(); ++i) {
         CHECK(r[i].off % 256 == 0, "%s: region %s offset %zu not 256-aligned", what, r[i].name, r[i].off);
@@ -54,7 +56,8 @@ static void check_dense(int B, int D, int64_t M, int K, int dt) {
     char what[128];
     snprintf(what, sizeof what, "dense B=%d D=%d M=%lld K=%d dt=%d", B, D, (long long)M, K, dt);
     const DensePlan p = plan_dense(B, D, M, K, dt);
-    const unsigned __int128 keys_bytes = u128(B) * u128(p.key_stride) * 8;
+    const unsigned __int128 full_keys = u128(B) * u128(p.key_stride) * 8;
+    const unsigned __int128 keys_bytes = p.bounded ? u128(p.n_pieces) * u128(p.cap) * 8 : full_keys;
     if (!p.ok) {
         CHECK(p.total == 0, "%s: unsupported plan with a workspace size", what);
         // unsupported only when something really is too large
@@ -84,6 +87,13 @@ static void check_dense(int B, int D, int64_t M, int K, int dt) {
         CHECK(t == nt, "%s: chunks cover %lld of %lld tiles", what, (long long)t, (long long)nt);
         CHECK(p.key_stride >= M, "%s: key stride", what);
         CHECK((int64_t)p.main.UT * kMfmaTileUsers >= B, "%s: user tiles", what);
+        // bounded regions: only past the key budget, with a sampled fast
+        // threshold, pieces smaller than their items, a collect region that
+        // holds K keys and more
+        CHECK(!p.bounded || (full_keys > kDefaultKeyBudget && p.fast), "%s: bounded without cause", what);
+        if (p.bounded)
+            CHECK(p.cap >= kCapMin && p.cap < 64 * (p.main.base + (p.main.rem ? 1 : 0)) && p.ccol > K &&
+                  p.ccol % 256 == 0, "%s: bounded sizes", what);
     } else if (!p.fused) {
         CHECK((int64_t)p.main.P * p.main.CH >= M && (int64_t)(p.main.P - 1) * p.main.CH < M, "%s: VALU chunks", what);
         CHECK(p.key_stride == M, "%s: VALU key stride", what);
@@ -123,7 +133,13 @@ static void check_dense(int B, int D, int64_t M, int K, int dt) {
                    {p.off_pl, u128(p.n_pieces) * 4, "pl"},
                    {p.off_pcnt, u128(p.n_pieces) * 4, "pcnt"},
                    {p.off_preg, u128(p.n_pieces) * 8, "preg"},
-                   {p.off_keys, keys_bytes, "keys"}},
+                   {p.off_keys, keys_bytes, "keys"},
+                   {p.off_nst, p.bounded ? u128(B) * 32 : 0, "narrow state"},
+                   {p.off_hist, p.bounded ? u128(B) * kNarrowBinsPlan * 4 : 0, "hist"},
+                   {p.off_coll, p.bounded ? u128(B) * u128(p.ccol) * 8 : 0, "collect"},
+                   {p.off_ccnt, p.bounded ? u128(B) * 4 : 0, "collect counts"},
+                   {p.off_cbase, p.bounded ? u128(B) * 8 : 0, "collect bases"},
+                   {p.off_tcnt, p.bounded ? u128(ceil_div(B, kMfmaTileUsers)) * 4 : 0, "tile counts"}},
                   p.total, what);
 }
 

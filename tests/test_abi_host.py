@@ -115,8 +115,19 @@ def test_workspace_queries(L):
     assert L.genrec_score_lse_topk_workspace(0, 64, 100, 10, 0) == 0
     assert L.genrec_score_lse_topk_workspace(4, 64, 100, 2000, 0) == 0
     big = L.genrec_score_lse_topk_workspace(1024, 4096, 1_000_000, 500, 0)
-    # candidate regions dominate: 8 bytes per (user, item)
-    assert 1024 * 1_000_000 * 8 <= big <= 1024 * 1_000_000 * 8 * 1.05
+    # bounded candidate regions: 1,024 users x 64 chunks x 4 lane groups x 64
+    # keys of 8 bytes and 20 bytes of record each, the 16,128-item sample (4
+    # bytes a score), per-user histograms of 4,096 counts and collect regions
+    # of 5,120 keys
+    parts = 1024 * 256 * (64 * 8 + 20) + 1024 * 16128 * 4 + 1024 * 4096 * 4 + 1024 * 5120 * 8
+    assert parts <= big <= parts * 1.02 and big <= 0.5e9
+    # 4,096 users over a catalog of 10 million items: plannable, under 1 GB
+    # (regions of every item would take 328 GB)
+    huge = L.genrec_score_lse_topk_workspace(4096, 2048, 10_000_000, 100, 0)
+    assert 0 < huge < 1e9
+    # shapes whose regions of every item fit the key budget keep them
+    mid = L.genrec_score_lse_topk_workspace(256, 2048, 100_000, 100, 0)
+    assert 256 * 100_096 * 8 <= mid <= 256 * 100_096 * 8 * 1.3
     # fp32: no hot head; 8 bytes per list entry dominate
     c = L.genrec_score_candidates_topk_workspace(4096, 2048, 1_000_000, 6_400_000, 100, 1)
     assert 6_400_000 * 8 <= c <= 6_400_000 * 8 * 1.5
@@ -128,6 +139,32 @@ def test_workspace_queries(L):
     # few users: no hot head
     assert (L.genrec_score_candidates_topk_workspace(8, 2048, 1_000_000, 20_000, 100, 0)
             == L.genrec_score_candidates_topk_workspace(8, 2048, 1_000_000, 20_000, 100, 1))
+
+
+def test_key_budget(L, monkeypatch):
+    """Bounded regions past the key budget (GENREC_KEY_BUDGET overrides it):
+    pieces of 8 times the expected count (at least 64 keys), a collect region
+    of 8 K + 1,024 keys rounded to 256; below the budget, regions of every
+    item; plans without a sampled fast threshold never bound their regions."""
+    import torch
+    p = genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)
+    assert p["bounded"] == 1 and p["cap"] == 64 and p["ccol"] == 5120
+    p = genrec.describe_plan(4096, 2048, 10_000_000, 1024, torch.bfloat16)
+    # 4 K / (4 P) = 64 expected per piece (P = 16), times 8
+    assert p["bounded"] == 1 and p["P"] == 16 and p["cap"] == 512 and p["ccol"] == 9216
+    assert genrec.describe_plan(256, 2048, 100_000, 100, torch.bfloat16)["bounded"] == 0
+    monkeypatch.setenv("GENREC_KEY_BUDGET", "0")
+    p = genrec.describe_plan(256, 2048, 100_000, 100, torch.bfloat16)
+    assert p["bounded"] == 1 and p["cap"] == 64
+    w0 = genrec.workspace_bytes(256, 2048, 100_000, 100, torch.bfloat16)
+    assert genrec.describe_plan(4, 64, 50_000, 10, torch.bfloat16)["bounded"] == 0  # no sample
+    assert genrec.describe_plan(1, 2048, 1_000_000, 100, torch.bfloat16)["bounded"] == 0  # one user: VALU path
+    monkeypatch.setenv("GENREC_KEY_BUDGET", str(1 << 50))
+    assert genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)["bounded"] == 0
+    monkeypatch.setenv("GENREC_KEY_BUDGET", "not a number")  # ignored: the default budget
+    assert genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)["bounded"] == 1
+    monkeypatch.delenv("GENREC_KEY_BUDGET")
+    assert genrec.workspace_bytes(256, 2048, 100_000, 100, torch.bfloat16) > w0
 
 
 def test_plan_selection(L):
@@ -216,11 +253,12 @@ def test_plans_at_the_largest_supported_sizes(L):
     in 64-bit range and consistent (no launch)."""
     import torch
     M = (1 << 31) - 1
-    # dense: the candidate regions alone are B x 256 ceil(M / 256) keys of 8 bytes
+    # dense: bounded candidate regions (regions of every item would take
+    # B x 256 ceil(M / 256) keys of 8 bytes: 68.7 GB)
     w = L.genrec_score_lse_topk_workspace(4, 8, M, 1024, 0)
-    assert w >= 4 * ((M + 255) // 256 * 256) * 8
     p = genrec.describe_plan(4, 8, M, 1024, torch.bfloat16)
-    assert p["workspace"] == w and p["path"] == "mfma" and p["sample"] == 1
+    assert p["workspace"] == w and p["path"] == "mfma" and p["sample"] == 1 and p["bounded"] == 1
+    assert 0 < w < 4 * ((M + 255) // 256 * 256) * 8 // 100
     assert L.genrec_score_lse_topk_workspace(1, 16384, M, 1, 1) >= M * 8   # fp32, VALU path
     assert L.genrec_score_lse_topk_workspace(4, 65536, 100, 10, 0) > 0     # GENREC_DMAX
     assert L.genrec_score_lse_topk_workspace(4, 65544, 100, 10, 0) == 0    # D past the maximum
