@@ -64,6 +64,10 @@ def parse():
     ap.add_argument("--mask-density", type=float, default=None, metavar="P",
                     help="full-catalog workloads: score through the masked head with one seeded "
                          "item mask that allows a fraction P of the catalog")
+    ap.add_argument("--clusters", type=int, default=0, metavar="C",
+                    help="full-catalog workloads: a catalog stored grouped by category (C clusters of "
+                         "contiguous ids, synth.gen_E_clustered) instead of the exchangeable one; the line "
+                         "reports how many users the call rescued")
     ap.add_argument("--cold", action="store_true",
                     help="write a 1 GiB scratch buffer before every step (flushes the 256 MB Infinity "
                          "Cache and the L2s) and time each step on its own, the flush outside")
@@ -246,7 +250,9 @@ def bench_ce(args):
     dev = torch.device("cuda:0")
     genrec.lib()
     t0 = time.perf_counter()
-    d = synth.make_workload(args.workload)
+    if args.clusters and (args.workload in ("cand", "tiny") or cfg.get("kind")):
+        raise SystemExit("--clusters applies to the full-catalog workloads")
+    d = synth.make_workload(args.workload, **({"clusters": args.clusters} if args.clusters else {}))
     log("inputs generated in %.1f s" % (time.perf_counter() - t0))
     B, D, M = d["B"], d["D"], d["M"]
     H, E = to_dev(d["H"], dev, torch), to_dev(d["E"], dev, torch)
@@ -343,7 +349,9 @@ def main():
     cfg = synth.WORKLOADS[args.workload]
     K = cfg["K"]
     t0 = time.perf_counter()
-    d = synth.make_workload(args.workload)
+    if args.clusters and (args.workload in ("cand", "tiny") or cfg.get("kind")):
+        raise SystemExit("--clusters applies to the full-catalog workloads")
+    d = synth.make_workload(args.workload, **({"clusters": args.clusters} if args.clusters else {}))
     log("inputs generated in %.1f s" % (time.perf_counter() - t0))
     B, D, M = d["B"], d["D"], d["M"]
     H, E = to_dev(d["H"], dev, torch), to_dev(d["E"], dev, torch)
@@ -426,6 +434,7 @@ def main():
         ms_prof = timed_steps(torch, lambda: step(prof), args.steps)[0]
     kern = prof.summary()
     log("step %.3f ms; kernels %s" % (ms, {k: "%.3f ms x%d" % (v[1] / v[0], v[0]) for k, v in kern.items()}))
+    rescued = None if cand else genrec.rescued_users(ws)  # of the last call
 
     n_main, t_main = kern["main_score"]
     main_ms = t_main / n_main
@@ -455,8 +464,8 @@ def main():
     if fused:
         roof["kernel"] = "stream_score_kernel (fused: the whole call in one launch)"
     # the masked scoring kernel is its own instance: it has its own counter summary, if any
-    roof["traffic"] = traffic_from_profile(roof["kernel"].split()[0],
-                                           args.workload + ("_masked" if args.mask_density is not None else ""))
+    roof["traffic"] = None if args.clusters else traffic_from_profile(
+        roof["kernel"].split()[0], args.workload + ("_masked" if args.mask_density is not None else ""))
     roof["kernel_ms"] = main_ms
 
     res = {
@@ -478,11 +487,14 @@ def main():
         "config": {"workload": args.workload, "B": B, "D": D, "M": M, "K": K,
                    **({"nnz": units} if cand else {}), **({"cache": "cold"} if args.cold else {}),
                    **({"timing": "graph replay"} if args.graph and not args.cold else {}),
-                   **({"mask_density": args.mask_density} if args.mask_density is not None else {})},
+                   **({"mask_density": args.mask_density} if args.mask_density is not None else {}),
+                   **({"catalog": "clustered", "clusters": args.clusters} if args.clusters else {})},
         "tflops": flops / (ms * 1e-3) / 1e12,
         "kernels_ms": {k: v[1] / v[0] for k, v in kern.items()},
         "roofline": roof,
     }
+    if rescued is not None:
+        res["rescued_users"] = rescued
     del H, E, ws
     torch.cuda.empty_cache()
     res["measured_peaks"] = peaks(emit=False)

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <mutex>
@@ -46,16 +47,25 @@ uint64_t next_ticket() {
 // item); larger shapes take bounded regions.  GENREC_KEY_BUDGET (bytes) sets
 // it for the process, read at every plan, so that a workspace query and the
 // call it sizes agree while the variable is unchanged.
-size_t key_budget() {
-    const char* e = getenv("GENREC_KEY_BUDGET");
-    if (e == nullptr || *e == '\0') return kDefaultKeyBudget;
+// GENREC_OVERFLOW_KEYS sets the keys of each user's overflow region in the
+// bounded layout the same way (0: none).  Unparsable values are ignored.
+bool env_size(const char* name, unsigned long long& v) {
+    const char* e = getenv(name);
+    if (e == nullptr || *e == '\0') return false;
     char* end = nullptr;
-    const unsigned long long v = strtoull(e, &end, 10);
-    return (end != nullptr && *end == '\0') ? (size_t)v : kDefaultKeyBudget;
+    v = strtoull(e, &end, 10);
+    return end != nullptr && *end == '\0';
+}
+
+size_t key_budget() {
+    unsigned long long v = 0;
+    return env_size("GENREC_KEY_BUDGET", v) ? (size_t)v : kDefaultKeyBudget;
 }
 
 DensePlan plan_dense_env(int B, int D, int64_t M, int K, int dtype) {
-    return plan_dense(B, D, M, K, dtype, key_budget());
+    unsigned long long o = 0;
+    const int64_t ovf = env_size("GENREC_OVERFLOW_KEYS", o) ? (int64_t)std::min<unsigned long long>(o, 1ull << 30) : -1;
+    return plan_dense(B, D, M, K, dtype, key_budget(), ovf);
 }
 
 template <class T>
@@ -184,12 +194,12 @@ int genrec_describe_plan(int B, int D, int64_t M, int K, int dtype, char* buf, s
              "{\"path\":\"%s\",\"sample\":%d,\"stride\":%lld,\"n_sample\":%lld,\"fast\":%d,\"r_fast\":%d,"
              "\"UT\":%d,\"P\":%d,\"tiles_per_chunk\":%d,\"CH\":%lld,\"merge_small\":%d,\"fused\":%d,"
              "\"sample_splits\":%d,\"safe_exact\":%d,\"first_sampled_tile\":%lld,\"bounded\":%d,\"cap\":%d,"
-             "\"ccol\":%d,\"workspace\":%zu}",
+             "\"ccol\":%d,\"ovf_cap\":%d,\"workspace\":%zu}",
              p.mfma ? "mfma" : "stream", p.sample ? 1 : 0, (long long)p.stride, (long long)p.n_sample,
              p.fast ? 1 : 0, p.r_fast, p.main.UT, p.main.P, p.main.base + (p.main.rem ? 1 : 0),
              (long long)p.main.CH, p.merge_small ? 1 : 0, p.fused ? 1 : 0, p.sample_splits, p.safe_exact ? 1 : 0,
              p.sample ? mf_sample_tile(0, p.stride, M / kMfmaTileItems) : -1LL, p.bounded ? 1 : 0, p.cap, p.ccol,
-             p.total);
+             p.ovf_cap, p.total);
     return GENREC_OK;
 }
 
@@ -272,8 +282,18 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     th.theta_fast = p.fast ? theta_fast : nullptr;
     th.user_flag = uflag;
     th.tile_flag = tflag;
-    th.tile_cnt = p.bounded ? at<int>(workspace, p.off_tcnt) : nullptr;
+    th.rc = p.bounded ? at<int>(workspace, p.off_rc) : nullptr;
     th.rescued = rescued;
+    if (p.bounded) {
+        th.ovf_pm = at<float>(workspace, p.off_pm);
+        th.ovf_pl = at<float>(workspace, p.off_pl);
+        th.ovf_pcnt = at<int>(workspace, p.off_pcnt);
+        th.ovf_preg = at<int64_t>(workspace, p.off_preg);
+        th.rec_stride = p.rec_stride;
+        th.rec_off = p.rec_stride - 1;
+        th.ovf_base = p.n_pieces * p.cap;
+        th.ovf_cap = p.ovf_cap;
+    }
     // The rescue counter is cleared by the threshold kernel when it runs,
     // else by the merge (see below).
 
@@ -325,6 +345,11 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
         a.pcnt = pcnt;
         a.preg = preg;
         a.cap = p.bounded ? p.cap : 0;
+        if (p.bounded) {
+            a.ovf_cap = p.ovf_cap;
+            a.ovf_base = p.n_pieces * p.cap;
+            a.rec_stride = p.rec_stride;
+        }
         if ((st = hip_status(timed(prof, KIND_MAIN, s, [&] { return launch_mfma(a, 1, s); }))) != GENREC_OK) return st;
     } else {
         StreamArgs a{};
@@ -360,7 +385,7 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     MergeArgs m{};
     m.B = B;
     m.K = K;
-    m.P = p.main.P * p.pieces_per_chunk;
+    m.P = (int)p.rec_stride;
     m.piece_begin = nullptr;
     m.keys = keys;
     m.pm = pm;
@@ -384,13 +409,13 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
     uint32_t* hist = nullptr;
     uint64_t* coll = nullptr;
     int* ccnt = nullptr;
-    int* tcnt = nullptr;
+    int* rc = nullptr;
     if (p.bounded) {
         nst = at<NarrowState>(workspace, p.off_nst);
         hist = at<uint32_t>(workspace, p.off_hist);
         coll = at<uint64_t>(workspace, p.off_coll);
         ccnt = at<int>(workspace, p.off_ccnt);
-        tcnt = at<int>(workspace, p.off_tcnt);
+        rc = at<int>(workspace, p.off_rc);
         m.cap = p.cap;
         m.nst = nst;
         m.hist = hist;
@@ -398,30 +423,40 @@ int score_dense(const void* H, const void* E, int dtype, int B, int D, int64_t M
         m.ccnt = ccnt;
         m.cbase = at<int64_t>(workspace, p.off_cbase);
         m.ccol = p.ccol;
-        m.tile_cnt = tcnt;
+        m.rc = rc;
+        m.map = at<int>(workspace, p.off_map);
+        m.H = H;
+        m.hgat = at<uint8_t>(workspace, p.off_hgat);
+        m.D = D;
+        m.es = dtype == GENREC_F32 ? 4 : 2;
+        m.ovf_cap = p.ovf_cap;
     }
     if ((st = hip_status(timed(prof, KIND_MERGE, s, [&] { return launch_merge(m, s); }))) != GENREC_OK) return st;
     if (!p.fast) return GENREC_OK;
     if (p.bounded) {
-        // Rescue over bounded regions (users flagged by the merge for an
-        // overflowed piece or too few candidates): counting passes narrow each
-        // such user's bound on its ranking keys, a collect pass stores the
-        // keys at or above it, and the merge ranks them.  With no flagged user
-        // every launch exits at once.
+        // Rescue over bounded regions (users flagged by the merge for a full
+        // overflow region or too few candidates): the merge gathered their
+        // rows into the first user tiles; counting passes over those tiles
+        // narrow each such user's bound on its ranking keys, a collect pass
+        // stores the keys at or above it, and the merge ranks them.  With no
+        // flagged user every launch exits at once.
         static_assert(kNarrowBinsPlan == kNarrowBins, "histogram bins of the plan and the kernels");
         a.cap = 0;
-        a.tile_flag = tflag;
+        a.rec_stride = 0;
         a.user_flag = nullptr;
         a.nst = nst;
         a.hist = hist;
         a.coll = coll;
         a.ccnt = ccnt;
         a.ccol = p.ccol;
-        a.tile_cnt = tcnt;
+        a.rc = rc;
+        a.map = at<int>(workspace, p.off_map);
+        a.H = at<uint16_t>(workspace, p.off_hgat);  // the flagged users' rows, gathered by the merge
+        a.tile_flag = nullptr;
         NarrowArgs nr{};
         nr.nst = nst;
         nr.hist = hist;
-        nr.tile_cnt = tcnt;
+        nr.rc = rc;
         nr.B = B;
         nr.K = K;
         nr.ccol = p.ccol;

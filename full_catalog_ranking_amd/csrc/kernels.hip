@@ -74,12 +74,25 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     const int nblk = gridDim.x;
     int L = blockIdx.x;
     if ((nblk & 7) == 0) L = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    const int c = L / a.UT, ut = L - c * a.UT;
+    // Bounded regions' rescue (mode 6): the flagged users' rows were gathered
+    // into the first nut = ceil(rc[1] / 256) user tiles, and the grid's blocks
+    // split the catalog into grid / nut chunks per tile (a handful of flagged
+    // users keeps every CU busy); the counting passes stop once none counts.
+    int nut = a.UT, Pd = a.P, base = a.base, rem = a.rem;
+    if (MODE == 6) {
+        const int nf = a.rc[1];
+        if (nf == 0 || (!a.collect && a.rc[0] == 0)) return;
+        nut = (nf + MF_TU - 1) / MF_TU;
+        Pd = max(1, min(a.n_tiles, nblk / nut));
+        base = a.n_tiles / Pd;
+        rem = a.n_tiles - base * Pd;
+    }
+    const int c = L / nut, ut = L - c * nut;
+    if (MODE == 6 && c >= Pd) return;
     // rescue pass: user tiles without a flagged user have nothing to redo
-    if ((MODE == 1 || MODE == 6) && a.tile_flag != nullptr && a.tile_flag[ut] == 0) return;
-    if (MODE == 6 && !a.collect && a.tile_cnt[ut] == 0) return;  // every user of the tile resolved
-    const int tile0 = c * a.base + min(c, a.rem);  // first pass-tile of this chunk
-    const int ntiles = a.base + (c < a.rem ? 1 : 0);
+    if (MODE == 1 && a.tile_flag != nullptr && a.tile_flag[ut] == 0) return;
+    const int tile0 = c * base + min(c, rem);  // first pass-tile of this chunk
+    const int ntiles = base + (c < rem ? 1 : 0);
     // dense pass over a partly filled catalog: chunks past its live rows are idle
     if (MODE == 0 && a.live_rows != nullptr && (int64_t)tile0 * a.tile_stride * MF_TI >= *a.live_rows) return;
     const int u0 = ut * MF_TU;
@@ -201,6 +214,7 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
     uint64_t nlo_[MF_UB];  // mode 6: the user's key bound, bin shift and whether it takes part
     int nsh_[MF_UB];
     bool nin_[MF_UB];
+    int mu_[MF_UB];  // mode 6: the user whose gathered row this column holds (B: none)
 #pragma unroll
     for (int ub = 0; ub < MF_UB; ++ub) {
         const int u = u0 + wu * MF_WU + ub * 32 + (lane & 31);
@@ -213,10 +227,12 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         const bool active = u < a.B && (a.user_flag == nullptr || a.user_flag[u] != 0);
         th_[ub] = active && !a.no_cand ? t : INFINITY;
         if (MODE == 6) {
-            const bool in = u < a.B && a.nst[u].status == (a.collect ? 2 : 1);
-            nlo_[ub] = in ? a.nst[u].lo : ~0ull;
-            nsh_[ub] = in ? a.nst[u].shift : 0;
+            const int mu = u < a.rc[1] ? a.map[u] : a.B;
+            const bool in = mu < a.B && a.nst[mu].status == (a.collect ? 2 : 1);
+            nlo_[ub] = in ? a.nst[mu].lo : ~0ull;
+            nsh_[ub] = in ? a.nst[mu].shift : 0;
             nin_[ub] = in;
+            mu_[ub] = mu;
         }
     }
 
@@ -229,7 +245,8 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
         // scheduling barrier, which keeps the live register set small.
 #pragma unroll
         for (int ub = 0; ub < MF_UB; ++ub) {
-            const int u = u0 + wu * MF_WU + ub * 32 + (lane & 31);
+            // (mode 6: the user of the gathered row in this column)
+            const int u = MODE == 6 ? mu_[ub] : u0 + wu * MF_WU + ub * 32 + (lane & 31);
             // Item mask: the 32 rows of block ib that this lane group covers
             // (rows wi*128 + ib*32 + 4*(lane/32) + 8q + e) lie in one mask word;
             // masked items score -inf (nothing to the sum, never a candidate).
@@ -409,18 +426,35 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
                     m_[ub] = mnew;
                 }
                 if (bmax >= th) {
-                    // bounded regions: a full piece keeps counting (the merge
-                    // sends its user to the rescue) but stores nothing more
+                    // bounded regions: past a full piece, keys go to the
+                    // user's overflow region (an atomic slot; rare but for
+                    // catalogs stored in clusters)
                     const int capr = a.cap > 0 ? a.cap : INT_MAX;
                     uint64_t* kreg = a.keys + (a.cap > 0 ? (((int64_t)u * a.P + c) * 4 + g) * a.cap
                                                          : (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles);
                     const uint32_t idb = (uint32_t)(j0 + jb);
+                    uint32_t spill = 0;  // scores that found the piece full
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         if (v[r] >= th) {
-                            if (cnt_[ub] < capr) kreg[cnt_[ub]] = rank_key(v[r], idb + (r >> 2) * 8 + (r & 3));
-                            ++cnt_[ub];
+                            if (cnt_[ub] < capr) {
+                                kreg[cnt_[ub]] = rank_key(v[r], idb + (r >> 2) * 8 + (r & 3));
+                                ++cnt_[ub];
+                            } else {
+                                spill |= 1u << r;
+                            }
                         }
+                    if (spill != 0u) {
+                        // one slot reservation for the block's spilled keys
+                        int slot = atomicAdd(a.pcnt + (int64_t)u * a.rec_stride + (int64_t)a.P * 4, __popc(spill));
+                        uint64_t* ovr = a.keys + a.ovf_base + (int64_t)u * a.ovf_cap;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if ((spill >> r) & 1u) {
+                                if (slot < a.ovf_cap) ovr[slot] = rank_key(v[r], idb + (r >> 2) * 8 + (r & 3));
+                                ++slot;
+                            }
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -527,10 +561,11 @@ __global__ __launch_bounds__(MF_NT, 1) void mfma_score_kernel(MfmaArgs a) {
             const int u = u0 + wu * MF_WU + ub * 32 + (lane & 31);
             if (u < a.B && (a.user_flag == nullptr || a.user_flag[u] != 0)) {
                 const int64_t piece = ((int64_t)u * a.P + c) * 4 + g;
-                a.pm[piece] = m_[ub];
-                a.pl[piece] = l_[ub];
-                a.pcnt[piece] = cnt_[ub];
-                a.preg[piece] = a.cap > 0 ? piece * a.cap : (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles;
+                const int64_t rec = a.rec_stride > 0 ? (int64_t)u * a.rec_stride + c * 4 + g : piece;
+                a.pm[rec] = m_[ub];
+                a.pl[rec] = l_[ub];
+                a.pcnt[rec] = cnt_[ub];
+                a.preg[rec] = a.cap > 0 ? piece * a.cap : (int64_t)u * a.key_stride + chunk_item0 + (int64_t)g * 64 * ntiles;
             }
         }
     }
@@ -962,8 +997,18 @@ __global__ __launch_bounds__(TH_NT) void threshold_kernel(ThresholdArgs a) {
     if (tid == 0) {
         if (a.user_flag != nullptr) a.user_flag[b] = 0;
         if (a.tile_flag != nullptr && b % MF_TU == 0) a.tile_flag[b / MF_TU] = 0;
-        if (a.tile_cnt != nullptr && b % MF_TU == 0) a.tile_cnt[b / MF_TU] = 0;
+        if (a.rc != nullptr && b == 0) {
+            a.rc[0] = 0;
+            a.rc[1] = 0;
+        }
         if (a.rescued != nullptr && b == 0) *a.rescued = 0;
+        if (a.ovf_pm != nullptr) {  // the user's overflow record starts empty
+            const int64_t rec = (int64_t)b * a.rec_stride + a.rec_off;
+            a.ovf_pm[rec] = -INFINITY;
+            a.ovf_pl[rec] = 0.f;
+            a.ovf_pcnt[rec] = 0;
+            a.ovf_preg[rec] = a.ovf_base + (int64_t)b * a.ovf_cap;
+        }
     }
     const int n = (int)a.n_sample;
     if (n < a.K) {
@@ -1380,6 +1425,7 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     __shared__ float2 s_ml[SEL_NT / kWave];
     __shared__ unsigned long long s_n[SEL_NT / kWave];
     __shared__ int s_ovf[SEL_NT / kWave];
+    __shared__ int s_slot;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     if (a.mode == 2 && a.user_flag[b] == 0) return;  // rescue merge: flagged users only
     if (a.mode == 3 && a.nst[b].status == 0) return;  // bounded rescue merge: flagged users only
@@ -1434,7 +1480,8 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
             if (pq + (int64_t)i * SEL_NT < p1) {
                 st.merge(pm4[i], pl4[i]);
                 n += (unsigned long long)pc4[i];
-                ovf |= a.cap > 0 && pc4[i] > a.cap;
+                // (bounded regions: a user's last record is its overflow region's)
+                ovf |= a.cap > 0 && pq + (int64_t)i * SEL_NT == p1 - 1 && pc4[i] > a.ovf_cap;
             }
     }
 #pragma unroll
@@ -1474,21 +1521,29 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
                     const int bits = 64 - __builtin_clzll(wdt | 1ull);
                     ns.shift = bits > kNarrowBits ? bits - kNarrowBits : 0;
                     ns.status = 1;
-                    atomicAdd(a.tile_cnt + b / MF_TU, 1);
+                    atomicAdd(a.rc, 1);  // one more user counting
                 }
                 a.ccnt[b] = 0;
                 a.cbase[b] = (int64_t)b * a.ccol;
                 a.user_flag[b] = 1;
                 a.tile_flag[b / MF_TU] = 1;
                 atomicAdd((unsigned long long*)a.rescued, 1ull);
+                // the user's row joins the gathered rows of the rescue passes
+                const int slot = atomicAdd(a.rc + 1, 1);
+                a.map[slot] = b;
+                s_slot = slot;
             }
             a.nst[b] = ns;
         }
         if (flag) {
-            if (a.nst != nullptr) {
-                uint4* hrow = (uint4*)(a.hist + (int64_t)b * kNarrowBins);
-                for (int i = tid; i < kNarrowBins / 4; i += SEL_NT) hrow[i] = make_uint4(0u, 0u, 0u, 0u);
-            }
+            uint4* hrow = (uint4*)(a.hist + (int64_t)b * kNarrowBins);
+            for (int i = tid; i < kNarrowBins / 4; i += SEL_NT) hrow[i] = make_uint4(0u, 0u, 0u, 0u);
+            __syncthreads();
+            const int slot = s_slot;
+            const int64_t n16 = (int64_t)a.D * a.es / 16;  // 16-byte chunks of a row
+            const uint4* src = (const uint4*)((const uint8_t*)a.H + (int64_t)b * a.D * a.es);
+            uint4* dst = (uint4*)((uint8_t*)a.hgat + (int64_t)slot * a.D * a.es);
+            for (int64_t i = tid; i < n16; i += SEL_NT) dst[i] = src[i];
             return;
         }
     }
@@ -1583,7 +1638,7 @@ __global__ __launch_bounds__(NR_NT) void narrow_kernel(NarrowArgs a) {
     if (total < kr) {  // fewer keys than wanted at or above lo: keep them all
         if (tid == 0) {
             a.nst[b].status = 2;
-            atomicSub(a.tile_cnt + b / MF_TU, 1);
+            atomicSub(a.rc, 1);
         }
         return;
     }
@@ -1608,7 +1663,7 @@ __global__ __launch_bounds__(NR_NT) void narrow_kernel(NarrowArgs a) {
         const int64_t count_ge = (int64_t)(a.K - st.k_rem) + cum_at + vj;
         if (count_ge <= a.ccol || st.shift == 0) {
             ns.status = 2;
-            atomicSub(a.tile_cnt + b / MF_TU, 1);
+            atomicSub(a.rc, 1);
         } else {
             ns.k_rem = st.k_rem - (int)cum_at;
             ns.shift = st.shift > kNarrowBits ? st.shift - kNarrowBits : 0;

@@ -58,9 +58,15 @@ struct MfmaArgs {
     // mode 1: no candidate is kept at all (logsumexp pieces only)
     int no_cand;
     // mode 1: keys per candidate region when the regions are bounded (piece p
-    // at keys + p * cap; a piece past it keeps counting but stores nothing);
-    // 0: region of every item (user u at keys + u * key_stride)
+    // at keys + p * cap, p = (u P + c) 4 + g); a full piece's further keys go
+    // to the user's overflow region at keys + ovf_base + u * ovf_cap, slot =
+    // atomicAdd on the overflow record's count (record u * rec_stride + 4 P),
+    // and its own count stops at cap; 0: region of every item (user u at
+    // keys + u * key_stride)
     int cap;
+    int ovf_cap;
+    int64_t ovf_base;
+    int64_t rec_stride;  // piece records per user (0: 4 P)
     // mode 6 -- exact rescue of flagged users over bounded regions: only users
     // whose nst[u].status equals want take part; every finite score's key
     // k >= nst[u].lo is, when collect == 0, counted into hist[u * kNarrowBins +
@@ -72,7 +78,11 @@ struct MfmaArgs {
     int* ccnt;
     int ccol;
     int collect;
-    const int* tile_cnt;  // mode 6 counting: user tiles with no user left counting exit at once
+    // mode 6: rc[0] = users still counting (0: the counting passes exit at
+    // once), rc[1] = flagged users, whose rows the merge gathered into H (row
+    // r is user map[r]; tiles past rc[1] exit at once)
+    const int* rc;
+    const int* map;
     // mode 3 -- softmax-minus-target tiles of the cross-entropy gradient:
     // rows are catalog items item0 + j (j < M valid), columns users;
     // g = w[u] (exp(s - lse[u]) - [item0 + j == labels[u]]) goes to
@@ -240,7 +250,15 @@ struct MergeArgs {
     int* ccnt;
     int64_t* cbase;
     int ccol;
-    int* tile_cnt;  // per 256-user tile: users still counting (mode 1 adds them)
+    // rc[0]: users still counting (mode 1 adds them); rc[1]: flagged users,
+    // each one's H row (D elements of es bytes) copied to hgat row rc[1]++ and
+    // map[that row] = the user
+    int* rc;
+    int* map;
+    const void* H;
+    void* hgat;
+    int D, es;
+    int ovf_cap;    // the last record of each user is its overflow region's: full past this count
 };
 
 // One block per user: picks the bin of the counted histogram that holds the
@@ -248,7 +266,7 @@ struct MergeArgs {
 struct NarrowArgs {
     NarrowState* nst;
     uint32_t* hist;
-    int* tile_cnt;  // a resolved user leaves its tile's count
+    int* rc;        // rc[0]: users still counting; a resolved user leaves it
     int B, K, ccol;
 };
 
@@ -262,8 +280,17 @@ struct ThresholdArgs {
     float* theta_fast;    // [B] lower bound of the r_fast-th largest (may be null)
     int* user_flag;       // [B] cleared (may be null)
     int* tile_flag;       // [ceil(B/256)] cleared (may be null)
-    int* tile_cnt;        // [ceil(B/256)] cleared (may be null)
+    int* rc;              // [2] cleared by block 0 (may be null): the bounded rescue's counts
     int64_t* rescued;     // cleared by block 0 (may be null)
+    // bounded candidate regions (ovf_pm non-null): user b's overflow record,
+    // at b * rec_stride + rec_off, starts empty (max -inf, sum 0, count 0)
+    // and points at keys + ovf_base + b * ovf_cap
+    float* ovf_pm;
+    float* ovf_pl;
+    int* ovf_pcnt;
+    int64_t* ovf_preg;
+    int64_t rec_stride, rec_off, ovf_base;
+    int ovf_cap;
 };
 
 struct CandPlanArgs {

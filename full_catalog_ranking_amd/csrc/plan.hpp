@@ -83,6 +83,11 @@ constexpr int kCapMin = 64;
 constexpr int kNarrowPasses = 6;
 constexpr int kNarrowBinsPlan = 4096;  // = the kernels' kNarrowBins
 constexpr int kCollectSlack = 1024;    // collect region: kCapFactor K + this many keys
+// Keys past a full piece go to the user's overflow region (an atomic slot):
+// max(kOvfMin, 2 ccol) keys per user.  A user is rescued only when that fills
+// too (a catalog stored in clusters concentrates a user's candidates in a
+// few pieces; exchangeable catalogs never reach it).
+constexpr int kOvfMin = 16384;
 
 // The merge's smaller build (LDS gather of 2,048 keys, 512-piece batches)
 // serves users expected to hold at most that many candidates and pieces.
@@ -119,9 +124,11 @@ struct DensePlan {
     bool bounded = false;      // candidate regions of `cap` keys per piece (else of every item)
     int cap = 0;
     int ccol = 0;              // bounded: keys of a flagged user's collect region
+    int ovf_cap = 0;           // bounded: keys of a user's overflow region
+    int64_t rec_stride = 0;    // piece records per user: 4 P (+ 1: the overflow region's, bounded)
     size_t off_hdr = 0, off_theta = 0, off_theta_safe = 0, off_uflag = 0, off_tflag = 0, off_sample = 0,
            off_pm = 0, off_pl = 0, off_pcnt = 0, off_preg = 0, off_keys = 0, off_arrive = 0, off_elect = 0, off_rows = 0,
-           off_nst = 0, off_hist = 0, off_coll = 0, off_ccnt = 0, off_cbase = 0, off_tcnt = 0, total = 0;
+           off_nst = 0, off_hist = 0, off_coll = 0, off_ccnt = 0, off_cbase = 0, off_rc = 0, off_hgat = 0, off_map = 0, total = 0;
 };
 
 inline Chunking chunk_mfma(int B, int64_t n_tiles) {
@@ -148,8 +155,11 @@ inline Chunking chunk_stream(int B, int64_t n_items) {
 // more, and for fp32 ones as well unless the catalog is small enough for the
 // one-launch VALU path (fp32 MFMA: 16 times fewer flops per cycle than bf16,
 // still twice the non-packed VALU rate, and E read once rather than per user).
-inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype, size_t key_budget = kDefaultKeyBudget) {
-    (void)D;
+// ovf_keys: keys of each user's overflow region (bounded regions), -1: the
+// default max(kOvfMin, 2 ccol); 0: none (a full piece sends its user to the
+// rescue).
+inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype, size_t key_budget = kDefaultKeyBudget,
+                            int64_t ovf_keys = -1) {
     DensePlan p;
     p.mfma = B > kStreamMaxB && (dtype == 0 || M > kFusedMaxM);
     const int64_t full_tiles = M / kMfmaTileItems;
@@ -202,8 +212,11 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype, size_t ke
             p.bounded = true;
             p.cap = (int)cap;
             p.ccol = (int)(ceil_div((int64_t)kCapFactor * K + kCollectSlack, 256) * 256);
+            p.ovf_cap = ovf_keys < 0 ? std::max(kOvfMin, 2 * p.ccol) : (int)std::min<int64_t>(ovf_keys, 1 << 30);
         }
     }
+    p.rec_stride = (int64_t)p.main.P * p.pieces_per_chunk + (p.bounded ? 1 : 0);
+    const int64_t n_rec = (int64_t)B * p.rec_stride;
     // launch grids: MFMA passes UT x P blocks, VALU passes B x P, merge B
     const int64_t grid = p.mfma ? (int64_t)p.main.UT * p.main.P : p.n_pieces;
     const int64_t pre_grid = p.sample ? (p.mfma ? (int64_t)p.pre.UT * p.pre.P : (int64_t)B * p.pre.P) : 0;
@@ -222,18 +235,22 @@ inline DensePlan plan_dense(int B, int D, int64_t M, int K, int dtype, size_t ke
         p.off_uflag = L.take(sizeof(int), (uint64_t)B);
         p.off_tflag = L.take(sizeof(int), (uint64_t)ceil_div(B, kMfmaTileUsers));
         p.off_sample = L.take(sizeof(float), p.sample ? (uint64_t)p.sample_splits * B * (uint64_t)p.n_sample : 0);
-        p.off_pm = L.take(sizeof(float), (uint64_t)p.n_pieces);
-        p.off_pl = L.take(sizeof(float), (uint64_t)p.n_pieces);
-        p.off_pcnt = L.take(sizeof(int), (uint64_t)p.n_pieces);
-        p.off_preg = L.take(sizeof(int64_t), (uint64_t)p.n_pieces);
+        p.off_pm = L.take(sizeof(float), (uint64_t)n_rec);
+        p.off_pl = L.take(sizeof(float), (uint64_t)n_rec);
+        p.off_pcnt = L.take(sizeof(int), (uint64_t)n_rec);
+        p.off_preg = L.take(sizeof(int64_t), (uint64_t)n_rec);
         if (p.bounded) {
-            p.off_keys = L.take(sizeof(uint64_t) * (uint64_t)p.cap, (uint64_t)p.n_pieces);
+            // the pieces' regions, then each user's overflow region
+            p.off_keys = L.take(sizeof(uint64_t),
+                                (uint64_t)p.n_pieces * (uint64_t)p.cap + (uint64_t)B * (uint64_t)p.ovf_cap);
             p.off_nst = L.take(32, (uint64_t)B);
             p.off_hist = L.take(sizeof(uint32_t) * (uint64_t)kNarrowBinsPlan, (uint64_t)B);
             p.off_coll = L.take(sizeof(uint64_t) * (uint64_t)p.ccol, (uint64_t)B);
             p.off_ccnt = L.take(sizeof(int), (uint64_t)B);
             p.off_cbase = L.take(sizeof(int64_t), (uint64_t)B);
-            p.off_tcnt = L.take(sizeof(int), (uint64_t)ceil_div(B, kMfmaTileUsers));
+            p.off_rc = L.take(1, 256);                                                // the rescue's two counts
+            p.off_hgat = L.take((uint64_t)(dtype == 0 ? 2 : 4) * (uint64_t)D, (uint64_t)B);  // flagged users' rows
+            p.off_map = L.take(sizeof(int), (uint64_t)B);
         } else {
             p.off_keys = L.take(sizeof(uint64_t), (uint64_t)B * (uint64_t)p.key_stride);
         }

@@ -31,6 +31,8 @@ that chunked / threaded generation is bit-identical to serial generation):
   the same stream.  Keeping first occurrences of an i.i.d. weighted sequence is
   exactly successive weighted sampling without replacement, and the list keeps
   that sampled order.
+* Clustered catalog (a robustness variant, ``make_dense(..., clusters=C)``):
+  items stored grouped by category, see gen_E_clustered.
 * Cross-entropy examples: user b's label (the engaged item) is one draw with
   probability proportional to the Zipf weights, from stream (seed, 3); its
   reward weight is uniform on [0.25, 2], from stream (seed, 4).
@@ -109,6 +111,41 @@ def gen_E(M: int, D: int, seed: int, zipf: bool = True, permute: bool = False,
         r0, r1 = c * ROW_CHUNK, min(M, (c + 1) * ROW_CHUNK)
         z = _rng(seed, 1, c).standard_normal((r1 - r0, D), dtype=np.float32)
         z *= scale[r0:r1, None]
+        out[r0:r1] = f32_to_bf16_bits(z) if bf16 else z
+
+    n = threads or _threads()
+    if n == 1 or nchunk == 1:
+        for c in range(nchunk):
+            work(c)
+    else:
+        with ThreadPoolExecutor(n) as ex:
+            list(ex.map(work, range(nchunk)))
+    return out
+
+
+def gen_E_clustered(M: int, D: int, seed: int, n_clusters: int, spread: float = 0.5, bf16: bool = True,
+                    threads: int | None = None) -> np.ndarray:
+    """A catalog stored grouped by category: item i belongs to cluster
+    c = i * n_clusters // M (contiguous runs of ids), and
+    E_i = (mu_c + spread * g_i) / sqrt(1 + spread^2) with the cluster centres
+    mu_c (stream key (seed, 6)) and the item parts g_i (stream (seed, 7, chunk))
+    both N(0, I/D).  A user's best items then come from the few clusters its
+    vector favours: a handful of contiguous id ranges, unlike the exchangeable
+    catalogs of gen_E.  Returns uint16 bf16 bits when ``bf16``, else float32.
+    """
+    s = np.float32(1.0 / math.sqrt(D))
+    mu = _rng(seed, 6).standard_normal((n_clusters, D), dtype=np.float32) * s
+    cl = (np.arange(M, dtype=np.int64) * n_clusters) // M
+    a = np.float32(1.0 / math.sqrt(1.0 + spread * spread))
+    out = np.empty((M, D), dtype=np.uint16 if bf16 else np.float32)
+    nchunk = (M + ROW_CHUNK - 1) // ROW_CHUNK
+
+    def work(c: int) -> None:
+        r0, r1 = c * ROW_CHUNK, min(M, (c + 1) * ROW_CHUNK)
+        z = _rng(seed, 7, c).standard_normal((r1 - r0, D), dtype=np.float32)
+        z *= np.float32(spread) * s
+        z += mu[cl[r0:r1]]
+        z *= a
         out[r0:r1] = f32_to_bf16_bits(z) if bf16 else z
 
     n = threads or _threads()
@@ -218,10 +255,14 @@ def make_tiny(seed: int = 0, B: int = 4, D: int = 256, M: int = 5000,
 
 
 def make_dense(B: int, D: int, M: int, seed: int = 0, permute: bool = False,
-               bf16: bool = True) -> dict:
-    """H ~ N(0, 1); E rows N(0, I/D) scaled by Zipf-ranked popularity norms."""
+               bf16: bool = True, clusters: int = 0) -> dict:
+    """H ~ N(0, 1); E rows N(0, I/D) scaled by Zipf-ranked popularity norms
+    (with ``clusters``: the clustered catalog of gen_E_clustered instead)."""
     H = gen_H(B, D, seed)
-    E = gen_E(M, D, seed, zipf=True, permute=permute, bf16=bf16)
+    if clusters:
+        E = gen_E_clustered(M, D, seed, clusters, bf16=bf16)
+    else:
+        E = gen_E(M, D, seed, zipf=True, permute=permute, bf16=bf16)
     if bf16:
         H = f32_to_bf16_bits(H)
     return dict(H=H, E=E, B=B, D=D, M=M, dtype="bf16" if bf16 else "f32")
@@ -246,7 +287,8 @@ def make_workload(name: str, seed: int = 0, **over) -> dict:
     if name == "tiny":
         d = make_tiny(seed, B=cfg["B"], D=cfg["D"], M=cfg["M"])
     else:
-        d = make_dense(cfg["B"], cfg["D"], cfg["M"], seed, bf16=cfg["dtype"] == "bf16")
+        d = make_dense(cfg["B"], cfg["D"], cfg["M"], seed, bf16=cfg["dtype"] == "bf16",
+                       clusters=cfg.get("clusters", 0))
     d["K"] = cfg["K"]
     if name == "cand":
         d["offsets"], d["ids"] = gen_candidates(cfg["B"], cfg["M"], seed, cfg["lo"], cfg["hi"])

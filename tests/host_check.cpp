@@ -57,7 +57,9 @@ static void check_dense(int B, int D, int64_t M, int K, int dt) {
     snprintf(what, sizeof what, "dense B=%d D=%d M=%lld K=%d dt=%d", B, D, (long long)M, K, dt);
     const DensePlan p = plan_dense(B, D, M, K, dt);
     const unsigned __int128 full_keys = u128(B) * u128(p.key_stride) * 8;
-    const unsigned __int128 keys_bytes = p.bounded ? u128(p.n_pieces) * u128(p.cap) * 8 : full_keys;
+    const unsigned __int128 keys_bytes =
+        p.bounded ? (u128(p.n_pieces) * u128(p.cap) + u128(B) * u128(p.ovf_cap)) * 8 : full_keys;
+    const unsigned __int128 n_rec = u128(B) * u128(p.rec_stride);
     if (!p.ok) {
         CHECK(p.total == 0, "%s: unsupported plan with a workspace size", what);
         // unsupported only when something really is too large
@@ -93,7 +95,8 @@ static void check_dense(int B, int D, int64_t M, int K, int dt) {
         CHECK(!p.bounded || (full_keys > kDefaultKeyBudget && p.fast), "%s: bounded without cause", what);
         if (p.bounded)
             CHECK(p.cap >= kCapMin && p.cap < 64 * (p.main.base + (p.main.rem ? 1 : 0)) && p.ccol > K &&
-                  p.ccol % 256 == 0, "%s: bounded sizes", what);
+                  p.ccol % 256 == 0 && p.ovf_cap >= 2 * p.ccol, "%s: bounded sizes", what);
+        CHECK(p.rec_stride == (int64_t)p.main.P * 4 + (p.bounded ? 1 : 0), "%s: records per user", what);
     } else if (!p.fused) {
         CHECK((int64_t)p.main.P * p.main.CH >= M && (int64_t)(p.main.P - 1) * p.main.CH < M, "%s: VALU chunks", what);
         CHECK(p.key_stride == M, "%s: VALU key stride", what);
@@ -129,17 +132,19 @@ static void check_dense(int B, int D, int64_t M, int K, int dt) {
                    {p.off_uflag, u128(B) * 4, "uflag"},
                    {p.off_tflag, u128(ceil_div(B, kMfmaTileUsers)) * 4, "tflag"},
                    {p.off_sample, p.sample ? u128(p.sample_splits) * u128(B) * u128(p.n_sample) * 4 : 0, "sample"},
-                   {p.off_pm, u128(p.n_pieces) * 4, "pm"},
-                   {p.off_pl, u128(p.n_pieces) * 4, "pl"},
-                   {p.off_pcnt, u128(p.n_pieces) * 4, "pcnt"},
-                   {p.off_preg, u128(p.n_pieces) * 8, "preg"},
+                   {p.off_pm, n_rec * 4, "pm"},
+                   {p.off_pl, n_rec * 4, "pl"},
+                   {p.off_pcnt, n_rec * 4, "pcnt"},
+                   {p.off_preg, n_rec * 8, "preg"},
                    {p.off_keys, keys_bytes, "keys"},
                    {p.off_nst, p.bounded ? u128(B) * 32 : 0, "narrow state"},
                    {p.off_hist, p.bounded ? u128(B) * kNarrowBinsPlan * 4 : 0, "hist"},
                    {p.off_coll, p.bounded ? u128(B) * u128(p.ccol) * 8 : 0, "collect"},
                    {p.off_ccnt, p.bounded ? u128(B) * 4 : 0, "collect counts"},
                    {p.off_cbase, p.bounded ? u128(B) * 8 : 0, "collect bases"},
-                   {p.off_tcnt, p.bounded ? u128(ceil_div(B, kMfmaTileUsers)) * 4 : 0, "tile counts"}},
+                   {p.off_rc, p.bounded ? 256 : 0, "rescue counts"},
+                   {p.off_hgat, p.bounded ? u128(B) * u128(D) * (dt == 0 ? 2 : 4) : 0, "gathered rows"},
+                   {p.off_map, p.bounded ? u128(B) * 4 : 0, "gathered users"}},
                   p.total, what);
 }
 

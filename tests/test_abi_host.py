@@ -116,15 +116,18 @@ def test_workspace_queries(L):
     assert L.genrec_score_lse_topk_workspace(4, 64, 100, 2000, 0) == 0
     big = L.genrec_score_lse_topk_workspace(1024, 4096, 1_000_000, 500, 0)
     # bounded candidate regions: 1,024 users x 64 chunks x 4 lane groups x 64
-    # keys of 8 bytes and 20 bytes of record each, the 16,128-item sample (4
-    # bytes a score), per-user histograms of 4,096 counts and collect regions
-    # of 5,120 keys
-    parts = 1024 * 256 * (64 * 8 + 20) + 1024 * 16128 * 4 + 1024 * 4096 * 4 + 1024 * 5120 * 8
+    # keys of 8 bytes and 20 bytes of record each, per user an overflow region
+    # of 16,384 keys (and its record), the 16,128-item sample (4 bytes a
+    # score), per-user histograms of 4,096 counts, collect regions of 5,120
+    # keys and room to gather the rescued users' rows (4,096 bf16 each)
+    parts = (1024 * 256 * (64 * 8 + 20) + 1024 * (16384 * 8 + 20) + 1024 * 16128 * 4 + 1024 * 4096 * 4
+             + 1024 * 5120 * 8 + 1024 * 4096 * 2)
     assert parts <= big <= parts * 1.02 and big <= 0.5e9
-    # 4,096 users over a catalog of 10 million items: plannable, under 1 GB
-    # (regions of every item would take 328 GB)
+    # 4,096 users over a catalog of 10 million items: plannable, under 1.5 GB
+    # (regions of every item would take 328 GB; the overflow regions, 16,384
+    # keys a user, take 0.54 GB of it)
     huge = L.genrec_score_lse_topk_workspace(4096, 2048, 10_000_000, 100, 0)
-    assert 0 < huge < 1e9
+    assert 0 < huge < 1.5e9
     # shapes whose regions of every item fit the key budget keep them
     mid = L.genrec_score_lse_topk_workspace(256, 2048, 100_000, 100, 0)
     assert 256 * 100_096 * 8 <= mid <= 256 * 100_096 * 8 * 1.3
@@ -148,10 +151,10 @@ def test_key_budget(L, monkeypatch):
     item; plans without a sampled fast threshold never bound their regions."""
     import torch
     p = genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)
-    assert p["bounded"] == 1 and p["cap"] == 64 and p["ccol"] == 5120
+    assert p["bounded"] == 1 and p["cap"] == 64 and p["ccol"] == 5120 and p["ovf_cap"] == 16384
     p = genrec.describe_plan(4096, 2048, 10_000_000, 1024, torch.bfloat16)
     # 4 K / (4 P) = 64 expected per piece (P = 16), times 8
-    assert p["bounded"] == 1 and p["P"] == 16 and p["cap"] == 512 and p["ccol"] == 9216
+    assert p["bounded"] == 1 and p["P"] == 16 and p["cap"] == 512 and p["ccol"] == 9216 and p["ovf_cap"] == 18432
     assert genrec.describe_plan(256, 2048, 100_000, 100, torch.bfloat16)["bounded"] == 0
     monkeypatch.setenv("GENREC_KEY_BUDGET", "0")
     p = genrec.describe_plan(256, 2048, 100_000, 100, torch.bfloat16)

@@ -32,10 +32,13 @@ def to_dev(a, dev):
     return torch.from_numpy(a).to(dev)
 
 
-def run(H, E, K, budget, monkeypatch, mask=None):
-    """One call under the given key budget: (outputs on the host, plan, rescued users)."""
+def run(H, E, K, budget, monkeypatch, mask=None, ovf=None):
+    """One call under the given key budget (and overflow-region size, None:
+    the default): (outputs on the host, plan, rescued users)."""
     from full_catalog_ranking_amd import genrec
     monkeypatch.setenv("GENREC_KEY_BUDGET", str(budget))
+    if ovf is not None:
+        monkeypatch.setenv("GENREC_OVERFLOW_KEYS", str(ovf))
     B, D, M = H.shape[0], H.shape[1], E.shape[0]
     plan = genrec.describe_plan(B, D, M, K, H.dtype)
     ws = torch.empty(genrec.workspace_bytes(B, D, M, K, H.dtype), dtype=torch.uint8, device=H.device)
@@ -46,13 +49,14 @@ def run(H, E, K, budget, monkeypatch, mask=None):
     n_rescued = genrec.rescued_users(ws)
     out = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
     monkeypatch.delenv("GENREC_KEY_BUDGET")
+    monkeypatch.delenv("GENREC_OVERFLOW_KEYS", raising=False)
     return out, plan, n_rescued
 
 
-def bounded_vs_full(Hb, Eb, K, dev, monkeypatch, mask=None):
+def bounded_vs_full(Hb, Eb, K, dev, monkeypatch, mask=None, ovf=None):
     H, E = to_dev(Hb, dev), to_dev(Eb, dev)
-    g, plan, n_resc = run(H, E, K, 0, monkeypatch, mask)
-    assert plan["bounded"] == 1
+    g, plan, n_resc = run(H, E, K, 0, monkeypatch, mask, ovf)
+    assert plan["bounded"] == 1 and (ovf is None or plan["ovf_cap"] == ovf)
     f, fplan, _ = run(H, E, K, 1 << 50, monkeypatch, mask)
     assert fplan["bounded"] == 0
     for name, x, y in zip(("idx", "score", "lse"), g, f):
@@ -87,23 +91,41 @@ def test_bounded_exchangeable(dev, oracle_mod, monkeypatch):
     parity.check_dense(g, oracle_mod.full(d["H"], d["E"], K, users=users), where="bounded exchangeable")
 
 
-@pytest.mark.parametrize("n_tiles", [12, 31])
-def test_bounded_clustered_overflow(dev, oracle_mod, monkeypatch, n_tiles):
+@pytest.mark.parametrize("n_tiles,ovf", [(12, None), (31, None), (12, 0), (31, 0)])
+def test_bounded_clustered_overflow(dev, oracle_mod, monkeypatch, n_tiles, ovf):
     """Catalog tiles of 20 times the norm that the sample skips: they hold
-    every user's top K, and pieces of the first chunks overflow for nearly
-    every user.  With 12 such tiles the keys past the fast threshold fit the
-    collect region (one collect pass); with 31 they do not (counting passes
-    first)."""
+    every user's top K, and pieces of the first chunks fill for nearly every
+    user.  With the overflow regions (default size) the extra keys land there
+    and no user is rescued.  Without them (size 0) every such user is rescued:
+    with 12 scaled tiles the keys past the fast threshold fit the collect
+    region (one collect pass); with 31 they do not (counting passes first)."""
     B, D, M, K = 260, 64, 150_000, 200
     d = synth.make_dense(B, D, M, seed=42)
     E = synth.bf16_bits_to_f32(d["E"])
     plant_unsampled(E, B, D, M, K, torch.bfloat16, n_tiles, 20.0, monkeypatch)
     Eb = synth.f32_to_bf16_bits(E)
-    g, plan, n_resc = bounded_vs_full(d["H"], Eb, K, dev, monkeypatch)
-    print("  rescued users: %d of %d (cap %d)" % (n_resc, B, plan["cap"]), flush=True)
-    assert n_resc > B // 2
+    g, plan, n_resc = bounded_vs_full(d["H"], Eb, K, dev, monkeypatch, ovf=ovf)
+    print("  rescued users: %d of %d (cap %d, overflow %d)" % (n_resc, B, plan["cap"], plan["ovf_cap"]), flush=True)
+    if ovf == 0:
+        assert n_resc > B // 2
+    else:
+        assert n_resc == 0
     users = [0, 7, 100, 255, 256, 259]
     parity.check_dense(g, oracle_mod.full(d["H"], Eb, K, users=users), where="bounded clustered")
+
+
+@pytest.mark.parametrize("clusters", [150, 1500])
+def test_bounded_clustered_catalog(dev, oracle_mod, monkeypatch, clusters):
+    """A catalog stored grouped by category (contiguous runs of 1,000 or 100
+    similar items): every user's best items sit in a few id ranges, so the
+    first chunks' pieces can overflow and the sample can miss a user's best
+    clusters.  Exact either way, equal to regions of every item."""
+    B, D, M, K = 260, 64, 150_000, 200
+    d = synth.make_dense(B, D, M, seed=46, clusters=clusters)
+    g, plan, n_resc = bounded_vs_full(d["H"], d["E"], K, dev, monkeypatch)
+    print("  clustered catalog (%d clusters): rescued users %d of %d" % (clusters, n_resc, B), flush=True)
+    users = [0, 9, 128, 255, 256, 259]
+    parity.check_dense(g, oracle_mod.full(d["H"], d["E"], K, users=users), where="clustered %d" % clusters)
 
 
 @pytest.mark.parametrize("kind", ["integer scores", "all equal"])
@@ -167,9 +189,11 @@ def test_bounded_short_user_split_sample(dev, oracle_mod, monkeypatch):
     parity.check_dense(g, oracle_mod.full(d["H"], E, K, users=[0, 3, 8, 15]), where="bounded split rescue")
 
 
-def test_bounded_masked_clustered(dev, oracle_mod, monkeypatch):
+@pytest.mark.parametrize("ovf", [None, 0])
+def test_bounded_masked_clustered(dev, oracle_mod, monkeypatch, ovf):
     """The masked head over bounded regions: per-user masks (one user with
-    none allowed, one with fewer than K) on the clustered catalog."""
+    none allowed, one with fewer than K) on scaled tiles the sample skips;
+    with and without the overflow regions."""
     B, D, M, K = 70, 96, 300_000, 50
     d = synth.make_dense(B, D, M, seed=43)
     E = synth.bf16_bits_to_f32(d["E"])
@@ -183,8 +207,8 @@ def test_bounded_masked_clustered(dev, oracle_mod, monkeypatch):
     pad[:, :M] = allowed
     words = (pad.reshape(B, W, 32).astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(axis=-1).astype(np.uint32)
     mask = torch.from_numpy(words.view(np.int32)).to(dev)
-    g, plan, n_resc = bounded_vs_full(d["H"], Eb, K, dev, monkeypatch, mask=mask)
-    assert n_resc > 0
+    g, plan, n_resc = bounded_vs_full(d["H"], Eb, K, dev, monkeypatch, mask=mask, ovf=ovf)
+    assert n_resc > 0 or ovf is None
     users = [0, 1, 2, 3, 35, 69]
     parity.check_dense(g, oracle_mod.full_masked(d["H"], Eb, K, words, users=users), where="bounded masked")
     for b in range(B):
@@ -192,14 +216,16 @@ def test_bounded_masked_clustered(dev, oracle_mod, monkeypatch):
         assert allowed[b][ids[ids >= 0]].all()
 
 
-def test_bounded_fp32_matrix_cores(dev, oracle_mod, monkeypatch):
-    """fp32 operands on the matrix cores, bounded regions, clustered catalog."""
+@pytest.mark.parametrize("ovf", [None, 0])
+def test_bounded_fp32_matrix_cores(dev, oracle_mod, monkeypatch, ovf):
+    """fp32 operands on the matrix cores, bounded regions, scaled tiles the
+    sample skips; with and without the overflow regions."""
     B, D, M, K = 40, 48, 300_000, 30
     d = synth.make_dense(B, D, M, seed=45, bf16=False)
     E = d["E"].copy()
     plant_unsampled(E, B, D, M, K, torch.float32, 20, 20.0, monkeypatch)
-    g, plan, n_resc = bounded_vs_full(d["H"], E, K, dev, monkeypatch)
-    assert plan["path"] == "mfma" and n_resc > 0
+    g, plan, n_resc = bounded_vs_full(d["H"], E, K, dev, monkeypatch, ovf=ovf)
+    assert plan["path"] == "mfma" and (n_resc > 0 or ovf is None)
     parity.check_dense(g, oracle_mod.full(d["H"], E, K, users=[0, 13, 39]), where="bounded fp32")
 
 
@@ -213,6 +239,7 @@ def test_bounded_graph_replays(dev, monkeypatch):
     plant_unsampled(E, B, D, M, K, torch.bfloat16, 31, 20.0, monkeypatch)
     H, Ed = to_dev(d["H"], dev), to_dev(synth.f32_to_bf16_bits(E), dev)
     monkeypatch.setenv("GENREC_KEY_BUDGET", "0")
+    monkeypatch.setenv("GENREC_OVERFLOW_KEYS", "0")  # the rescue's launches do the work
     ws = torch.empty(genrec.workspace_bytes(B, D, M, K, H.dtype), dtype=torch.uint8, device=dev)
     out = (torch.empty((B, K), dtype=torch.int32, device=dev), torch.empty((B, K), dtype=torch.float32, device=dev),
            torch.empty((B,), dtype=torch.float32, device=dev))
@@ -235,3 +262,4 @@ def test_bounded_graph_replays(dev, monkeypatch):
             assert torch.equal(x, y), "replay %d" % rep
     del g
     monkeypatch.delenv("GENREC_KEY_BUDGET")
+    monkeypatch.delenv("GENREC_OVERFLOW_KEYS")

@@ -76,3 +76,19 @@ def test_beam_scores_seeded_and_shaped():
     assert np.unique(t[0]).size < 500   # rounding makes ties common
     w = synth.make_workload("beam128")
     assert w["scores"].shape == (256, 16384) and w["K"] == 128
+
+
+def test_clustered_catalog():
+    """Contiguous clusters: rows of one cluster share its centre (their mean
+    pairwise inner product is the centre's share, 1 / 1.25), rows of different
+    clusters do not; threaded generation equals serial generation."""
+    M, D, C = 12_000, 128, 6
+    E = synth.gen_E_clustered(M, D, 3, C, bf16=False)
+    assert np.array_equal(E, synth.gen_E_clustered(M, D, 3, C, bf16=False, threads=1))
+    assert abs(float((E * E).sum(1).mean()) - 1.0) < 0.02
+    same = float((E[:1000] * E[1000:2000]).sum(1).mean())
+    assert abs(same - 0.8) < 0.1  # rows 0..1999 are cluster 0 (M / C = 2,000 rows a cluster)
+    other = float((E[:1000] * E[M // C:M // C + 1000]).sum(1).mean())
+    assert abs(other) < 0.2
+    bits = synth.gen_E_clustered(M, D, 3, C)
+    assert np.array_equal(bits, synth.f32_to_bf16_bits(E))
