@@ -74,11 +74,12 @@ typedef enum { GENREC_BF16 = 0, GENREC_F32 = 1 } genrec_dtype;
  * (8 bytes each) are used while they take at most GENREC_KEY_BUDGET bytes
  * (an environment variable read at every call, default 256 MiB); larger
  * shapes with a sampled threshold take bounded regions (a fixed number of
- * keys per (user, catalog chunk, lane group), a per-user histogram and a
- * collect region of 8 K + 1,024 keys): 0.26 GB for B = 1,024, M = 10^6,
- * K = 500, D = 4,096, where regions of every item take 8.2 GB.  Either
- * layout gives the same results; change the variable only between a query
- * and calls that agree on it. */
+ * keys per (user, catalog chunk, lane group), a per-user overflow region of
+ * GENREC_OVERFLOW_KEYS keys, default max(16,384, 16 K + 2,048), a per-user
+ * histogram, a collect region of 8 K + 1,024 keys and room for the rescued
+ * users' rows): 0.41 GB for B = 1,024, M = 10^6, K = 500, D = 4,096, where
+ * regions of every item take 8.2 GB.  Either layout gives the same results;
+ * change the variables only between a query and calls that agree on them. */
 size_t genrec_score_lse_topk_workspace(int B, int D, int64_t M, int K, int dtype);
 
 /*
@@ -249,8 +250,9 @@ int genrec_ce_backward(const void* H, const void* E, int B, int D, int64_t M,
  * the first window of "stride" tiles, or -1 without a sample), the work
  * split, which build of the top-K merge runs ("merge_small": the one with the
  * smaller LDS gather, for few expected candidates per user), whether the
- * candidate regions are bounded ("bounded", with "cap" keys per piece and a
- * collect region of "ccol" keys per rescued user) and the workspace size.
+ * candidate regions are bounded ("bounded", with "cap" keys per piece, an
+ * overflow region of "ovf_cap" keys per user and a collect region of "ccol"
+ * keys per rescued user) and the workspace size.
  * Host-only, touches no device.
  * Returns GENREC_OK or the status the compute call would return for the
  * shape. */
