@@ -136,7 +136,7 @@ def test_ce_full_size_sampled_users(dev, oracle_mod):
     assert genrec.device_errors(ws) == (0, 0)
     col = dE.sum(dim=0, dtype=torch.float64).cpu().numpy()
     finite = bool(torch.isfinite(dE).all())
-    users = [0, 1, 511, 1023]
+    users = [0, 1, 255, 256, 511, 512, 800, 1023]  # every 256-user tile, both halves of a wave's users
     g = (loss.cpu().numpy()[users], lse.cpu().numpy()[users], dH.cpu().numpy()[users], None)
     del dE, dH, H, E
     torch.cuda.empty_cache()
