@@ -1462,7 +1462,7 @@ __global__ __launch_bounds__(SEL_NT) void merge_kernel(MergeArgs a) {
     LseState st;
     st.init();
     unsigned long long n = 0;
-    int ovf = 0;  // bounded regions: some piece counted more keys than it holds
+    int ovf = 0;  // bounded regions: the user's overflow region counted more keys than it holds
     // four pieces per thread and round, their loads issued together (indices
     // clamped into the user's pieces); merged in the same order as one by one
     for (int64_t pq = p0 + tid; pq < p1; pq += 4 * SEL_NT) {

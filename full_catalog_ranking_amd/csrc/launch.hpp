@@ -67,11 +67,13 @@ struct MfmaArgs {
     int ovf_cap;
     int64_t ovf_base;
     int64_t rec_stride;  // piece records per user (0: 4 P)
-    // mode 6 -- exact rescue of flagged users over bounded regions: only users
-    // whose nst[u].status equals want take part; every finite score's key
-    // k >= nst[u].lo is, when collect == 0, counted into hist[u * kNarrowBins +
-    // ((k - lo) >> shift)] (keys past the last bin skipped), else stored at
-    // coll[u * ccol + slot], slot = atomicAdd(&ccnt[u], 1) (< ccol kept)
+    // mode 6 -- exact rescue of flagged users over bounded regions, on their
+    // gathered rows (H row r is user u = map[r]): only users whose
+    // nst[u].status is 1 (counting, collect == 0) or 2 (collect == 1) take
+    // part; every finite score's key k >= nst[u].lo is counted into
+    // hist[u * kNarrowBins + ((k - lo) >> shift)] (keys past the last bin
+    // skipped), or stored at coll[u * ccol + slot], slot = atomicAdd(&ccnt[u],
+    // 1) (< ccol kept)
     NarrowState* nst;
     uint32_t* hist;
     uint64_t* coll;
@@ -238,11 +240,12 @@ struct MergeArgs {
     // 1: the smaller merge build (users with at most ~512 pieces and ~2,048
     // candidates expected); any value gives the same result
     int small;
-    // Bounded regions (cap > 0): a piece holds at most cap keys and counts
-    // them all.  Mode 1 flags a user with an overflowed piece as well, writes
-    // its lse, and starts its rescue state (nst, a zeroed hist row, ccnt = 0,
-    // cbase = u * ccol); mode 3 ranks flagged users from their collect region
-    // (coll + cbase[u], min(ccnt[u], ccol) keys), lse left as mode 1 wrote it.
+    // Bounded regions (cap > 0): each user's last piece record is its
+    // overflow region's.  Mode 1 flags a user whose overflow region counted
+    // more than ovf_cap keys as well, writes its lse, and starts its rescue
+    // state (nst, a zeroed hist row, ccnt = 0, cbase = u * ccol, its row
+    // gathered); mode 3 ranks flagged users from their collect region (coll +
+    // cbase[u], min(ccnt[u], ccol) keys), lse left as mode 1 wrote it.
     int cap;
     NarrowState* nst;
     uint32_t* hist;

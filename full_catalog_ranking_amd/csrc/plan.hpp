@@ -70,13 +70,15 @@ struct Chunking {
 // Bounded candidate regions.  With a sampled threshold the main pass keeps,
 // per piece (user, chunk, lane group), at most `cap` keys -- kCapFactor times
 // the count the threshold is expected to let through there, at least
-// kCapMin -- and counts them all.  A user whose piece overflowed (or who was
-// left short of K) is finished exactly by the rescue: counting passes over
-// its user tile narrow a 4,096-bin histogram of its ranking keys (12 bits a
-// pass, kNarrowPasses passes cover 64-bit keys) until the keys at or above the
-// bound fit its collect region of `ccol` keys, which one more pass fills.
-// Regions of every item (8 bytes per user and item) are kept while they
-// take at most the key budget: they need no rescue for overflow.
+// kCapMin -- and sends a full piece's further keys to the user's overflow
+// region.  A user whose overflow region fills too (or who was left short of
+// K) is finished exactly by the rescue: its row is gathered with the other
+// rescued users', and counting passes over the gathered rows narrow a
+// 4,096-bin histogram of its ranking keys (12 bits a pass, kNarrowPasses
+// passes cover 64-bit keys) until the keys at or above the bound fit its
+// collect region of `ccol` keys, which one more pass fills.  Regions of every
+// item (8 bytes per user and item) are kept while they take at most the key
+// budget: they need no rescue for overflow.
 constexpr size_t kDefaultKeyBudget = (size_t)256 << 20;
 constexpr int kCapFactor = 8;
 constexpr int kCapMin = 64;
