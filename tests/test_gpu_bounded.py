@@ -37,7 +37,9 @@ def run(H, E, K, budget, monkeypatch, mask=None, ovf=None):
     the default): (outputs on the host, plan, rescued users)."""
     from full_catalog_ranking_amd import genrec
     monkeypatch.setenv("GENREC_KEY_BUDGET", str(budget))
-    if ovf is not None:
+    if ovf is None:  # the default size, whatever the process environment says
+        monkeypatch.delenv("GENREC_OVERFLOW_KEYS", raising=False)
+    else:
         monkeypatch.setenv("GENREC_OVERFLOW_KEYS", str(ovf))
     B, D, M = H.shape[0], H.shape[1], E.shape[0]
     plan = genrec.describe_plan(B, D, M, K, H.dtype)
