@@ -51,7 +51,8 @@ uint64_t next_ticket() {
 // bounded layout the same way (0: none).  Unparsable values are ignored.
 bool env_size(const char* name, unsigned long long& v) {
     const char* e = getenv(name);
-    if (e == nullptr || *e == '\0') return false;
+    // digits only: strtoull would also take a sign (wrapping "-5" to 2^64 - 5) or leading blanks
+    if (e == nullptr || *e < '0' || *e > '9') return false;
     char* end = nullptr;
     v = strtoull(e, &end, 10);
     return end != nullptr && *end == '\0';

@@ -164,10 +164,32 @@ def test_key_budget(L, monkeypatch):
     assert genrec.describe_plan(1, 2048, 1_000_000, 100, torch.bfloat16)["bounded"] == 0  # one user: VALU path
     monkeypatch.setenv("GENREC_KEY_BUDGET", str(1 << 50))
     assert genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)["bounded"] == 0
-    monkeypatch.setenv("GENREC_KEY_BUDGET", "not a number")  # ignored: the default budget
-    assert genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)["bounded"] == 1
+    for junk in ("not a number", "-1", " 5", "5x", ""):  # ignored: the default budget
+        monkeypatch.setenv("GENREC_KEY_BUDGET", junk)
+        assert genrec.describe_plan(1024, 4096, 1_000_000, 500, torch.bfloat16)["bounded"] == 1
     monkeypatch.delenv("GENREC_KEY_BUDGET")
     assert genrec.workspace_bytes(256, 2048, 100_000, 100, torch.bfloat16) > w0
+
+
+def test_overflow_keys(L, monkeypatch):
+    """GENREC_OVERFLOW_KEYS sets each user's overflow region in the bounded
+    layout (0: none; unparsable: the default max(16,384, 2 ccol)); the
+    workspace follows it by B x 8 bytes per key; regions of every item have
+    none."""
+    import torch
+    shape = (1024, 4096, 1_000_000, 500)
+    base = genrec.workspace_bytes(*shape, torch.bfloat16)
+    assert genrec.describe_plan(*shape, torch.bfloat16)["ovf_cap"] == 16384
+    monkeypatch.setenv("GENREC_OVERFLOW_KEYS", "0")
+    assert genrec.describe_plan(*shape, torch.bfloat16)["ovf_cap"] == 0
+    assert genrec.workspace_bytes(*shape, torch.bfloat16) == base - 1024 * 16384 * 8
+    monkeypatch.setenv("GENREC_OVERFLOW_KEYS", "1000")
+    assert genrec.describe_plan(*shape, torch.bfloat16)["ovf_cap"] == 1000
+    monkeypatch.setenv("GENREC_OVERFLOW_KEYS", "-5")  # unparsable as a count: the default
+    assert genrec.describe_plan(*shape, torch.bfloat16)["ovf_cap"] == 16384
+    monkeypatch.setenv("GENREC_KEY_BUDGET", str(1 << 50))
+    p = genrec.describe_plan(*shape, torch.bfloat16)
+    assert p["bounded"] == 0 and p["ovf_cap"] == 0
 
 
 def test_plan_selection(L):
