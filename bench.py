@@ -200,7 +200,7 @@ def cpu_baseline(d, K, target_s, cand, mask_words=None):
 
 
 def bench_beam(args):
-    """Beam step: batched top-K of R dense score rows of N entries (one kernel)."""
+    """Beam step: batched top-K of R dense score rows of N entries (one call)."""
     import torch
     from full_catalog_ranking_amd import genrec, synth
     dev = torch.device("cuda:0")
@@ -221,10 +221,11 @@ def bench_beam(args):
         "ms_per_step_min": mn, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload, "R": R, "N": N, "K": K},
-        # the whole call, both of its passes (selection per chunk or segment,
-        # then per row), timed with events on the stream they run on
+        # the whole call, every pass of its route (per chunk or segment, then
+        # per row; or sample, filter and list ranking), timed with events on
+        # the stream they run on
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "kernel": "genrec_topk_rows (both passes)", "kernel_ms": ms,
+                     "frac": achieved / HBM_PEAK_GBS, "kernel": "genrec_topk_rows (every pass)", "kernel_ms": ms,
                      "traffic": None},
     }
     if not args.no_cpu_baseline:

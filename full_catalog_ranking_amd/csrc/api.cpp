@@ -747,7 +747,12 @@ int genrec_topk_rows(const float* scores, int R, int64_t N, int64_t ld, int K, i
     a.C = p.C;
     a.nchunk = p.nchunk;
     a.part = (uint64_t*)workspace;
-    a.reg = p.row ? 2 : (p.reg ? 1 : 0);
+    a.reg = p.filt ? 3 : (p.row ? 2 : (p.reg ? 1 : 0));
+    if (p.filt) {
+        a.sj = p.filt;
+        a.tthr = (uint32_t*)((char*)workspace + p.off_thr);
+        a.tcnt = (int*)((char*)workspace + p.off_cnt);
+    }
     return hip_status(launch_topk_rows(a, (hipStream_t)stream));
 }
 

@@ -2222,6 +2222,272 @@ __global__ __launch_bounds__(TK_NT) void topk_rowmerge_kernel(TopkRowsArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Batched top-K, filter route (long rows, K <= 512): a sampled bound per row,
+// the keys at or above it listed, the list ranked
+// ---------------------------------------------------------------------------
+constexpr int TF_CAP = TK_NT * TK_MV;  // keys of a row's list (one per slot of the ranking block)
+constexpr int TF_NSUB = kWave;         // the list's parts: part s takes the columns = s (mod 64)
+constexpr int TF_SUB = TF_CAP / TF_NSUB;
+constexpr int TF_COLS = 4096;          // columns per filter block
+constexpr int TF_V = TF_COLS / TK_NT;
+static_assert(TF_CAP == kTopkFiltCap && TF_COLS == kTopkFiltCols && TF_NSUB == kTopkFiltParts,
+              "the plan's list, list parts and filter block sizes");
+static_assert(TF_COLS % kWave == 0 && TK_NT % kWave == 0, "lane l of every filter wave reads columns = l (mod 64)");
+
+// Block r: the bound of row r.  Slot j of thread t samples column
+// q * (N / 256) + (t & 63) with run q = 4 j + t / 64, so each wave reads 64
+// contiguous columns per slot and the 256 runs spread evenly over the row
+// (N > 16,384: a run never passes the row's end).  T = the sj-th largest of
+// the threads' sample maxima, found as in the row kernel (each thread ranks
+// its maximum against all of them); at least sj sampled keys reach it.
+__global__ __launch_bounds__(TK_NT) void topk_sample_kernel(TopkRowsArgs a) {
+    __shared__ __align__(16) uint32_t tmax[TK_NT];  // read 16 bytes at a time
+    __shared__ uint32_t tred[TK_NT / kWave];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int r = blockIdx.x;
+    const int64_t rs = a.N / 256;
+    const float* row = a.scores + (int64_t)r * a.ld + lane;
+    float v[TK_V];
+#pragma unroll
+    for (int j = 0; j < TK_V; ++j) v[j] = row[(int64_t)(4 * j + w) * rs];
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int j = 0; j < TK_V; ++j) mx = max(mx, order_key(v[j]));
+    tmax[tid] = mx;
+    __syncthreads();
+    int rk = 0;
+    const uint4* t4 = (const uint4*)tmax;
+#pragma unroll 8
+    for (int q = 0; q < TK_NT / 4; ++q) {
+        const uint4 u = t4[q];
+        rk += (u.x > mx) + (u.y > mx) + (u.z > mx) + (u.w > mx);
+    }
+    uint32_t tc = rk < a.sj ? mx : 0xFFFFFFFFu;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) tc = min(tc, (uint32_t)__shfl_xor((int)tc, o));
+    if (lane == 0) tred[w] = tc;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t T = tred[0];
+#pragma unroll
+        for (int q = 1; q < TK_NT / kWave; ++q) T = min(T, tred[q]);
+        a.tthr[r] = T;
+    }
+    if (tid < TF_NSUB) a.tcnt[(int64_t)r * TF_NSUB + tid] = 0;
+}
+
+// Block (r, b): columns [b TF_COLS, (b + 1) TF_COLS) of row r; every key at
+// or above the row's bound is listed.  The list has 64 parts of TF_SUB keys;
+// lane l of every wave reads columns = l (mod 64) and appends its keys to
+// part l with one atomic add on that part's count, so a row's appends spread
+// over 64 counters (one counter per row, taken by every wave, made this pass
+// 153 instead of 21 us on 64 rows of 262,144) and the keys of any run of
+// columns over all parts.  Keys past a
+// full part are counted, not written: the ranking block then takes the whole
+// row.
+__global__ __launch_bounds__(TK_NT) void topk_filter_kernel(TopkRowsArgs a) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int r = blockIdx.x / a.nchunk, b = blockIdx.x - r * a.nchunk;
+    const int64_t c0 = (int64_t)b * TF_COLS;
+    const int n = (int)min((int64_t)TF_COLS, a.N - c0);
+    const float* row = a.scores + (int64_t)r * a.ld + c0;
+    const uint32_t T = a.tthr[r];
+    float v[TF_V];
+#pragma unroll
+    for (int j = 0; j < TF_V; ++j) v[j] = row[min(j * TK_NT + tid, n - 1)];  // clamped: all in flight together
+    uint32_t hv[TF_V];
+    uint32_t mask = 0u;
+#pragma unroll
+    for (int j = 0; j < TF_V; ++j) {
+        hv[j] = order_key(v[j]);
+        mask |= (j * TK_NT + tid < n && hv[j] >= T) ? (1u << j) : 0u;
+    }
+    const int c = __popc(mask);
+    if (c == 0) return;
+    int pos = atomicAdd(a.tcnt + (int64_t)r * TF_NSUB + lane, c);
+    uint64_t* dst = a.part + (int64_t)r * TF_CAP + lane * TF_SUB;
+    const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)(c0 + tid);  // index word of slot 0
+#pragma unroll
+    for (int j = 0; j < TF_V; ++j) {
+        if ((mask >> j) & 1u) {
+            if (pos < TF_SUB) dst[pos] = ((uint64_t)hv[j] << 32) | (uint64_t)(lo0 - (uint32_t)(j * TK_NT));
+            ++pos;
+        }
+    }
+}
+
+static_assert(SEL_NT == TK_NT, "the ranking block's fallback runs the histogram narrowing with its threads");
+
+constexpr int TF_BITS = 11;              // key bits decided per ranking pass
+constexpr int TF_BINS = 1 << TF_BITS;
+struct TfRank {
+    int hist[TF_BINS];
+    int wsum[TK_NT / kWave];
+    int bin, above;
+    alignas(16) uint64_t sel[GENREC_KMAX];  // the k selected keys (room for block_sort_into's runs)
+    uint64_t sorted[GENREC_KMAX];
+};
+
+union TfShared {
+    TkShared tk;
+    SelShared sel;
+    TfRank rk;
+};
+
+// The k-th largest of the block's keys (slot j of each thread; 0: no key;
+// all keys distinct, at least k of them), decided TF_BITS bits at a time from
+// the top: a histogram of the keys that agree with the bits decided so far,
+// then the bin that holds the k-th of them.  Stops early once that bin holds
+// exactly the keys still wanted; returns T with exactly k keys >= T.
+template <int V, class Key>
+__device__ __forceinline__ uint64_t tf_kth_key(const Key& key, int k, TfRank& sh) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    constexpr int PER = TF_BINS / TK_NT;  // bins per thread, counted from the top
+    uint64_t prefix = 0, dmask = 0;
+    int k_rem = k;
+    for (int shift = 64; shift > 0;) {
+        const int nb = min(TF_BITS, shift);
+        shift -= nb;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) sh.hist[i * TK_NT + tid] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const uint64_t x = key(j);
+            if (x != 0ull && ((x ^ prefix) & dmask) == 0ull) atomicAdd(&sh.hist[(int)(x >> shift) & ((1 << nb) - 1)], 1);
+        }
+        __syncthreads();
+        // thread t owns bins TF_BINS - 1 - (PER t + i), i < PER (higher bins first)
+        int h[PER], tsum = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            h[i] = sh.hist[TF_BINS - 1 - (PER * tid + i)];
+            tsum += h[i];
+        }
+        int incl = tsum;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o);
+            if (lane >= o) incl += t;
+        }
+        if (lane == 63) sh.wsum[w] = incl;
+        __syncthreads();
+        int run = incl - tsum;
+#pragma unroll
+        for (int q = 0; q < TK_NT / kWave; ++q) run += q < w ? sh.wsum[q] : 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            if (run < k_rem && k_rem <= run + h[i]) {  // exactly one bin of one thread
+                sh.bin = TF_BINS - 1 - (PER * tid + i);
+                sh.above = run;
+            }
+            run += h[i];
+        }
+        __syncthreads();
+        const int d = sh.bin, above = sh.above;
+        const int in_bin = sh.hist[d];
+        __syncthreads();  // the histogram and the choice are read before the next pass rewrites them
+        prefix |= (uint64_t)d << shift;
+        dmask |= (uint64_t)((1 << nb) - 1) << shift;
+        k_rem -= above;
+        if (in_bin == k_rem) break;  // every key of the bin is wanted: T = the bin's lowest key bound
+    }
+    return prefix;
+}
+
+// Block r: the top K of row r from its list.  Slot j of thread t is group
+// g = 4 t + j / 8 (tk_bound_sort's groups), place j % 8; it reads key
+// g / 64 + 16 (j % 8) of list part g % 64, so that the keys at the front of
+// every part are shared evenly by the groups and the bound from the 1,024
+// group maxima admits few more than K keys.  A list shorter than K keys or
+// a part that overflowed: the histogram narrowing over the whole row.
+__global__ __launch_bounds__(TK_NT) void topk_cand_kernel(TopkRowsArgs a) {
+    __shared__ TfShared sh;
+    __shared__ int s_tot, s_max;
+    const int tid = threadIdx.x;
+    const int r = blockIdx.x;
+    const int K = a.K;
+    const int k = (int)min((int64_t)K, a.N);
+    int32_t* oidx = a.out_idx + (int64_t)r * K;
+    float* osc = a.out_scores + (int64_t)r * K;
+    const int* pc = a.tcnt + (int64_t)r * TF_NSUB;
+    if (tid < kWave) {  // wave 0: the parts' total and largest count
+        int t = pc[tid], m = t;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            t += __shfl_xor(t, o);
+            m = max(m, __shfl_xor(m, o));
+        }
+        if (tid == 0) {
+            s_tot = t;
+            s_max = m;
+        }
+    }
+    __syncthreads();
+    const int cnt = s_tot;
+    if (cnt < k || s_max > TF_SUB) {  // block-uniform
+        DenseRowSrc src{a.scores + (int64_t)r * a.ld, a.N, 0};
+        topk_emit(src, k, K, sh.sel, oidx, osc, nullptr);
+        return;
+    }
+    const uint64_t* lst = a.part + (int64_t)r * TF_CAP;
+    constexpr int GK = TK_MV / 4;
+    int pcnt[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pcnt[q] = pc[(4 * tid + q) % TF_NSUB];
+    uint64_t kv[TK_MV];
+#pragma unroll
+    for (int j = 0; j < TK_MV; ++j) {  // every place is inside the list; unwritten ones are dropped below
+        const int g = 4 * tid + j / GK;
+        kv[j] = lst[(g % TF_NSUB) * TF_SUB + g / TF_NSUB + (TK_NT * 4 / TF_NSUB) * (j % GK)];
+    }
+    uint32_t kh[TK_MV], kl[TK_MV];
+#pragma unroll
+    for (int j = 0; j < TK_MV; ++j) {
+        const int g = 4 * tid + j / GK;
+        const uint64_t key = g / TF_NSUB + (TK_NT * 4 / TF_NSUB) * (j % GK) < pcnt[j / GK] ? kv[j] : 0ull;
+        kh[j] = (uint32_t)(key >> 32);
+        kl[j] = (uint32_t)key;
+        asm volatile("" : "+v"(kh[j]), "+v"(kl[j]));  // as in the segment kernel
+    }
+    auto key = [&](int j) { return ((uint64_t)kh[j] << 32) | (uint64_t)kl[j]; };
+    const uint64_t T = tf_kth_key<TK_MV>(key, k, sh.rk);
+    // the k keys >= T, compacted and sorted
+    const int lane = tid & 63, w = tid >> 6;
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < TK_MV; ++j) m |= key(j) >= T && key(j) != 0ull ? (1u << j) : 0u;
+    const int c = __popc(m);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) sh.rk.wsum[w] = incl;
+    __syncthreads();
+    int base = incl - c;
+#pragma unroll
+    for (int q = 0; q < TK_NT / kWave; ++q) base += q < w ? sh.rk.wsum[q] : 0;
+#pragma unroll
+    for (int j = 0; j < TK_MV; ++j)
+        if ((m >> j) & 1u) sh.rk.sel[base++] = key(j);
+    __syncthreads();
+    block_sort_into(sh.rk.sel, k, sh.rk.sorted);
+    __syncthreads();
+    for (int i = tid; i < K; i += TK_NT) {
+        if (i < k) {
+            const uint64_t x = sh.rk.sorted[i];
+            oidx[i] = (int32_t)key_id(x);
+            osc[i] = key_score(x);
+        } else {
+            oidx[i] = -1;
+            osc[i] = -INFINITY;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming (VALU) path: few users, fp32 inputs, per-user candidate lists
 // ---------------------------------------------------------------------------
 constexpr int ST_NT = 256;
@@ -3283,6 +3549,15 @@ hipError_t launch_topk_rows(const TopkRowsArgs& a, hipStream_t s) {
     if (a.reg == 2) {  // one block per row, the row in registers
         if (a.N > TK_SEG || a.nchunk != 1 || a.K > GENREC_KMAX || a.K < 1) return hipErrorInvalidValue;
         hipLaunchKernelGGL(topk_row_kernel, dim3(a.R), dim3(TK_NT), 0, s, a);
+        return hipGetLastError();
+    }
+    if (a.reg == 3) {  // the filter route
+        if (a.N <= TK_SEG || a.K > kTopkBoundMaxK || a.K < 1 || a.C != TF_COLS ||
+            (int64_t)a.nchunk * TF_COLS < a.N || a.sj < 1 || a.sj > TK_NT || !a.tthr || !a.tcnt || !a.part)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(topk_sample_kernel, dim3(a.R), dim3(TK_NT), 0, s, a);
+        hipLaunchKernelGGL(topk_filter_kernel, dim3((unsigned)((int64_t)a.R * a.nchunk)), dim3(TK_NT), 0, s, a);
+        hipLaunchKernelGGL(topk_cand_kernel, dim3(a.R), dim3(TK_NT), 0, s, a);
         return hipGetLastError();
     }
     if (a.reg) {

@@ -317,7 +317,11 @@ struct TopkRowsArgs {
     int nchunk;           // chunks per row (1: no merge pass)
     uint64_t* part;       // nchunk > 1: [R][nchunk][K] chunk results
     int reg;              // 1: register-resident selection, chunks of kTopkSeg columns, nchunk >= 2, nchunk * K <= kTopkMergeKeys;
-                          // 2: one block per row, the row (N <= kTopkSeg) in registers, nchunk = 1
+                          // 2: one block per row, the row (N <= kTopkSeg) in registers, nchunk = 1;
+                          // 3: the filter route, blocks of kTopkFiltCols columns (part: [R][kTopkFiltCap] lists)
+    uint32_t* tthr;       // filter route: [R] each row's bound (an order key)
+    int* tcnt;            // filter route: [R][64] keys at or above it per list part (may exceed the part)
+    int sj;               // filter route: the bound's rank among the 256 sample maxima
 };
 
 // modes 0 / 1; splits > 1 (mode 0): grid y splits the reduction (a.D per split, a.ld the row stride)

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 namespace genrec {
 
@@ -360,12 +361,48 @@ constexpr int64_t kTopkRegMinBlocks = 2 * kNumCU;
 constexpr int kTopkRowMaxK = 512;
 constexpr int kTopkBoundMaxK = 512;  // the row kernel's bound from 1,024 group maxima serves K up to this
 
+// Long rows (more than one segment), K <= kTopkBoundMaxK: the filter route
+// (xGR explainer page, xBeam: candidates filtered before they are sorted).
+// A first block per row reads a sample of the row -- 256 runs of 64 columns
+// spread evenly over it, 64 samples a thread -- and takes as the row's bound
+// T the sj-th largest of the 256 threads' sample maxima; blocks of
+// kTopkFiltCols columns then keep every key at or above T in a list of
+// kTopkFiltCap keys per row, and a block per row ranks the list.  For
+// unordered scores a thread's maximum reaches the sj-th largest with
+// probability sj / 256, so one score does with q = 1 - (1 - sj/256)^(1/64),
+// and N q keys reach T; sj is the smallest rank >= kTopkFiltMinRank that
+// makes this 3 K, and the route is taken when that is at most half the list.
+// A row whose list holds fewer than K keys or overflows (a sample that
+// misses the row's top, exact ties at T) is ranked from the whole row by the
+// histogram narrowing instead: exact either way, only slower.
+constexpr int kTopkFiltCap = 8192;
+constexpr int kTopkFiltParts = 64;  // the list's parts, each with its own count (columns = s mod 64 in part s)
+constexpr int64_t kTopkFiltCols = 4096;
+constexpr int kTopkFiltMinRank = 16;
+
+inline double topk_filt_expect(int64_t N, int sj) {
+    return (double)N * (1.0 - std::pow(1.0 - sj / 256.0, 1.0 / 64.0));
+}
+
+// The bound's rank sj for a row of N > kTopkSeg scores and K <= kTopkBoundMaxK,
+// or 0 when the route does not apply.
+inline int topk_filt_rank(int64_t N, int K) {
+    if (N <= kTopkSeg || K > kTopkBoundMaxK) return 0;
+    for (int sj = kTopkFiltMinRank; sj < 256; ++sj) {
+        const double e = topk_filt_expect(N, sj);
+        if (e >= 3.0 * K) return e <= kTopkFiltCap / 2 ? sj : 0;
+    }
+    return 0;
+}
+
 struct TopkPlan {
     bool ok = true;    // false: the workspace or the grid would be too large (unsupported)
     bool reg = false;  // register-resident selection (else histogram narrowing)
     bool row = false;  // ... of a whole row per block (rows of at most kTopkSeg, K <= 256)
-    int64_t C = 0;     // columns per chunk (segment)
+    int filt = 0;      // the filter route: the bound's rank sj (0: another route)
+    int64_t C = 0;     // columns per chunk (segment; filter block)
     int nchunk = 1;
+    size_t off_thr = 0, off_cnt = 0;  // filter route: per-row bound and list part counts (the lists at 0)
     size_t workspace = 0;
 };
 
@@ -376,6 +413,16 @@ inline TopkPlan plan_topk(int R, int64_t N, int K) {
         p.reg = p.row = true;
         p.C = N;
         p.nchunk = 1;
+    } else if ((p.filt = topk_filt_rank(N, K)) > 0) {
+        p.C = kTopkFiltCols;
+        p.nchunk = (int)ceil_div(N, kTopkFiltCols);
+        Layout L;
+        L.take(sizeof(uint64_t) * (uint64_t)kTopkFiltCap, (uint64_t)R);
+        p.off_thr = L.take(sizeof(uint32_t), (uint64_t)R);
+        p.off_cnt = L.take(sizeof(int) * (uint64_t)kTopkFiltParts, (uint64_t)R);
+        p.ok = (int64_t)R * p.nchunk <= kMaxGrid && L.ok;
+        p.workspace = p.ok ? L.o : 0;
+        return p;
     } else if (nseg > 1 && nseg * K <= kTopkMergeKeys && (int64_t)R * nseg >= kTopkRegMinBlocks) {
         p.reg = true;
         p.C = kTopkSeg;

@@ -193,6 +193,21 @@ static void check_topk(int R, int64_t N, int K) {
         return;
     }
     CHECK((int64_t)p.nchunk * p.C >= N && (int64_t)(p.nchunk - 1) * p.C < N, "%s: chunks cover the row", what);
+    if (p.filt) {
+        const int64_t rs = N / 256;
+        CHECK(N > kTopkSeg && K <= kTopkBoundMaxK && !p.reg && !p.row && p.C == kTopkFiltCols, "%s: filter plan", what);
+        CHECK(p.filt >= kTopkFiltMinRank && p.filt < 256, "%s: the bound's rank", what);
+        CHECK(255 * rs + 63 < N, "%s: sample runs inside the row", what);
+        const double e = topk_filt_expect(N, p.filt);
+        CHECK(e >= 3.0 * K && e <= kTopkFiltCap / 2, "%s: expected list length", what);
+        CHECK(p.filt == kTopkFiltMinRank || topk_filt_expect(N, p.filt - 1) < 3.0 * K, "%s: the smallest rank", what);
+        std::vector<Region> r = {{0, u128(R) * kTopkFiltCap * 8, "lists"},
+                                 {p.off_thr, u128(R) * 4, "bounds"},
+                                 {p.off_cnt, u128(R) * kTopkFiltParts * 4, "counts"}};
+        check_regions(r, p.workspace, what);
+        return;
+    }
+    CHECK(topk_filt_rank(N, K) == 0, "%s: the filter route whenever it applies", what);
     if (p.row) {
         CHECK(p.reg && N <= kTopkSeg && K <= kTopkRowMaxK && p.nchunk == 1 && p.C == N && p.workspace == 0,
               "%s: one-block row plan", what);

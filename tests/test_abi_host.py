@@ -96,14 +96,27 @@ def test_candidate_argument_errors(L):
     # need the chunk results' workspace
     assert L.genrec_topk_rows_workspace(8, 4096, 513) == 0
     assert L.genrec_topk_rows_workspace(8, 16384, 600) == 8 * 4 * 600 * 8
-    need = L.genrec_topk_rows_workspace(8, 512 * 512, 512)
-    assert need > 0 and need % (8 * 8 * 512) == 0 and need // (8 * 8 * 512) * 512 <= 6144
+    need = L.genrec_topk_rows_workspace(8, 512 * 512, 600)
+    assert need > 0 and need % (8 * 8 * 600) == 0 and need // (8 * 8 * 600) * 600 <= 6144
+    assert t(FAKE, 8, 512 * 512, 512 * 512, 600, FAKE, FAKE, None, 0, None) == WORKSPACE
+
+    # the filter route (rows of more than 16,384 columns, K <= 512, when about
+    # 3 K keys reaching the sampled bound stay within half of the 8,192-key
+    # list): per row the list, then the bounds and the counts of its 64 parts
+    def filt(R):
+        return -(-R * 8192 * 8 // 256) * 256 + -(-R * 4 // 256) * 256 + -(-R * 64 * 4 // 256) * 256
+    for R, N, K in ((8, 512 * 512, 512), (64, 512 * 512, 512), (8, 64 * 16384, 128), (1, 16385, 100),
+                    (256, 2 * 16384, 512), (1, 4_000_000, 1)):
+        assert L.genrec_topk_rows_workspace(R, N, K) == filt(R), (R, N, K)
     assert t(FAKE, 8, 512 * 512, 512 * 512, 512, FAKE, FAKE, None, 0, None) == WORKSPACE
     # register-resident selection: rows of >= 2 segments of 16,384 columns whose
-    # K keys fit the 8,192-key row merge, with >= 512 segment blocks in all
-    assert L.genrec_topk_rows_workspace(64, 512 * 512, 512) == 64 * 16 * 512 * 8
-    assert L.genrec_topk_rows_workspace(8, 64 * 16384, 128) == 8 * 64 * 128 * 8
-    assert L.genrec_topk_rows_workspace(8, 64 * 16384, 129) % (8 * 8 * 129) == 0  # 64 x 129 keys: histogram chunks
+    # K keys fit the 8,192-key row merge, with >= 512 segment blocks in all,
+    # where the filter route does not apply: K > 512, too short a row for 3 K
+    # keys at the sampled bound (N < ~36 K), or too long for the list (N > ~4e6)
+    assert L.genrec_topk_rows_workspace(520, 2 * 16384, 1024) == 520 * 2 * 1024 * 8
+    assert L.genrec_topk_rows_workspace(256, 17_000, 512) == 256 * 2 * 512 * 8
+    assert L.genrec_topk_rows_workspace(8, 5_000_000, 20) == 8 * 306 * 20 * 8
+    assert L.genrec_topk_rows_workspace(1, 4_200_000, 1) == 1026 * 8  # one row: 1,026 histogram chunks
     m = L.genrec_score_lse_topk_masked
     ws = L.genrec_score_lse_topk_workspace(4, 64, 100, 10, 0)
     assert m(FAKE, FAKE, 0, 4, 64, 100, 10, None, 0, FAKE, FAKE, FAKE, FAKE, ws, None) == INVALID   # no mask

@@ -543,6 +543,10 @@ def test_candidates_equal_full_catalog(dev, oracle_mod):
     (3, 9_000, 400, None, 0),         # a short row: groups with empty slots
     (5, 16_384, 300, 0, 0),           # whole-number scores: thousands at the bound -> bit selection
     (24, 22 * 16_384, 300, None, 0),  # 528 segment blocks, K = 300
+    # where the filter route does not apply: rows too short for 3 K keys at the
+    # sampled bound, rows too long for its list
+    (256, 17_000, 512, None, 0),      # two segments a row: register-resident selection
+    (4, 5_000_000, 20, 1, 0),         # 306 segments a row, ties
 ])
 def test_topk_rows(dev, oracle_mod, R, N, K, decimals, ld_pad):
     from full_catalog_ranking_amd import genrec
@@ -556,6 +560,37 @@ def test_topk_rows(dev, oracle_mod, R, N, K, decimals, ld_pad):
     for r in range(R):
         ri, rv = oracle_mod.topk_row(s[r].astype(np.float64), K)
         assert np.array_equal(idx[r], ri), r   # exact: same fp32 values, same (score, column) order
+        assert np.array_equal(val[r], rv.astype(np.float32)), r
+
+
+@pytest.mark.parametrize("N,K", [(512 * 512, 512), (512 * 512, 100), (40_000, 7)])
+def test_topk_rows_filter_fallbacks(dev, oracle_mod, N, K):
+    """The filter route (rows longer than 16,384 columns, K <= 512) per row:
+    the keys at or above a bound taken from 256 sampled runs of 64 columns are
+    listed and ranked; a row whose list is shorter than K (a sample that
+    misses the row's top: here every unsampled column holds -1,000) or longer
+    than the list (all scores equal) is ranked from the whole row.  Rows of
+    both kinds, ascending and descending rows and an unordered one share one
+    call; every row is exact against the oracle."""
+    from full_catalog_ranking_amd import genrec
+    assert genrec.lib().genrec_topk_rows_workspace(5, N, K) == \
+        -(-5 * 8192 * 8 // 256) * 256 + 256 + 5 * 256  # the filter route's workspace
+    rng = np.random.default_rng(N + K)
+    s = np.empty((5, N), dtype=np.float32)
+    s[0] = -1000.0
+    rs = N // 256
+    for q in range(256):  # the sampled runs
+        s[0, q * rs:q * rs + 64] = rng.random(64, dtype=np.float32)
+    s[1] = 0.25
+    s[2] = np.arange(N, dtype=np.float32) / N
+    s[3] = s[2, ::-1]
+    s[4] = rng.standard_normal(N, dtype=np.float32)
+    print("  topk_rows filter fallbacks N=%d K=%d" % (N, K), flush=True)
+    idx, val = genrec.topk_rows(torch.from_numpy(s).to(dev), K)
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    for r in range(5):
+        ri, rv = oracle_mod.topk_row(s[r].astype(np.float64), K)
+        assert np.array_equal(idx[r], ri), r
         assert np.array_equal(val[r], rv.astype(np.float32)), r
 
 
