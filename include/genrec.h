@@ -188,9 +188,15 @@ int genrec_get_rescued_users(const void* workspace, void* stream, int64_t* n_res
  * its first N entries used, ld >= N), the K largest entries ranked by score
  * descending, ties by the lower column: out_idx [R][K] int32 column indices,
  * out_scores [R][K] the scores.  K > N pads with (-1, -inf).  Long rows are
- * split into chunks merged by a second pass, which needs `workspace` of
- * genrec_topk_rows_workspace(R, N, K) bytes (8-byte aligned; 0 bytes --
- * workspace may be NULL -- when one pass suffices).  Asynchronous on
+ * either split into chunks merged by a second pass or, for K <= 512 and N
+ * between about 36 K and 4e6, filtered (xBeam's filtering before the sort):
+ * a sampled lower bound on each row's top K, one pass that lists the keys
+ * at or above it (8,192 per row at most), and a ranking of the list -- a row
+ * whose list falls short of K or overflows is ranked from the whole row, so
+ * results are exact either way.  Both need `workspace` of
+ * genrec_topk_rows_workspace(R, N, K) bytes (8-byte aligned; the filter
+ * route about 64 KiB per row; 0 bytes -- workspace may be NULL -- when one
+ * pass suffices); its contents on entry do not matter.  Asynchronous on
  * `stream`.  1 <= K <= GENREC_KMAX, 1 <= N < 2^31, R >= 1, 4-byte aligned
  * pointers; GENREC_ERR_INVALID_ARG / GENREC_ERR_UNSUPPORTED /
  * GENREC_ERR_WORKSPACE otherwise.  Non-finite scores are not supported.

@@ -108,8 +108,9 @@ def test_candidate_graph_replays(dev):
 
 def test_topk_rows_and_ce_graph_replays(dev):
     from full_catalog_ranking_amd import genrec
-    # histogram chunks, then register-resident segments (64 x 8 segment blocks)
-    for R, N, K in [(64, 40_000, 128), (64, 8 * 16_384, 128)]:
+    # the filter route (two shapes), histogram chunks (K > 512), then
+    # register-resident segments (256 x 2 segment blocks)
+    for R, N, K in [(64, 40_000, 128), (64, 8 * 16_384, 128), (64, 40_000, 600), (256, 17_000, 512)]:
         S = torch.from_numpy(synth.gen_scores(R, N, seed=6, decimals=2)).to(dev)
         need = genrec.lib().genrec_topk_rows_workspace(R, N, K)
         tws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

@@ -715,9 +715,10 @@ def test_poisoned_workspaces_and_outputs(dev, oracle_mod):
                                      workspace=ws, out=outs(B, K))[:3]
     parity.check_cand(tuple(x.cpu().numpy() for x in g), oracle_mod.cand(d["H"], d["E"], off, ids, K), off, ids,
                       where="poisoned cand")
-    # batched top-K rows of several chunks (histogram narrowing), then of many
-    # segments (register-resident selection, a 3-column last segment)
-    for R, N, K in [(5, 50_000, 200), (40, 13 * 16_384 + 3, 200)]:
+    # batched top-K rows of several chunks (histogram narrowing), of a few
+    # segments (register-resident selection, a 3-column last segment), and
+    # filtered (list parts and their counts in the workspace)
+    for R, N, K in [(5, 50_000, 600), (520, 2 * 16_384 + 3, 600), (5, 50_000, 200), (40, 13 * 16_384 + 3, 200)]:
         S = synth.gen_scores(R, N, seed=78, decimals=3)
         need = genrec.lib().genrec_topk_rows_workspace(R, N, K)
         o = outs(R, K)[:2]
