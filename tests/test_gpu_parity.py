@@ -89,14 +89,21 @@ def test_batch_b256_all_users(dev, oracle_mod):
     parity.check_dense(g, ref, where="batch")
 
 
-def test_large_b1024_sampled_users(dev, oracle_mod):
+@pytest.fixture(scope="module")
+def large_run(dev):
+    """The full-size large workload (1,024 x 1e6 x 4,096, K 500) and one call's
+    host outputs, shared by the tests below."""
+    d = synth.make_workload("large")
+    return d, run_dense(d, d["K"], dev)
+
+
+def test_large_b1024_sampled_users(dev, oracle_mod, large_run):
     """40 users against the oracle: ten in each of the four 256-user tiles, at
     tile positions that cover every wave's user columns (64 per wave tile, two
     32-wide blocks each); their top-K items come from every one of the eight
     XCD groups of catalog chunks."""
     from full_catalog_ranking_amd import genrec
-    d = synth.make_workload("large")
-    g = run_dense(d, d["K"], dev)
+    d, g = large_run
     offs = [0, 31, 32, 63, 64, 100, 127, 160, 200, 255]
     users = [256 * t + o for t in range(4) for o in offs]
     ref = oracle_mod.full(d["H"], d["E"], d["K"], users=users)
@@ -115,6 +122,59 @@ def test_large_b1024_sampled_users(dev, oracle_mod):
     assert np.isfinite(ls).all() and (idx >= 0).all() and (idx < d["M"]).all()
     assert (np.diff(sc, axis=1) <= 0).all()
     assert all(np.unique(r).size == d["K"] for r in idx[::37])
+
+
+def _widen_bf16(bits):
+    """bf16 bit patterns -> float32, exactly (the bf16 value is the top half)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_large_b1024_all_users(dev, large_run):
+    """Every one of the 1,024 users of the full-size call, by properties that
+    need no oracle row (the oracle's full sort of 1e9 scores is out of reach):
+    (1) the score returned with each id is the fp64 dot product of that user's
+    and item's bf16 rows, within the parity rule's tau; (2) no item outside a
+    user's list scores above the list's K-th score by more than tau; (3) the
+    lse is the log-sum-exp of all M scores, within the parity rule's bound.
+    (2) and (3) take the scores from a float32 library product of the widened
+    rows, chunk by chunk (its rounding, ~1e-5 relative at D = 4,096, is far
+    inside tau)."""
+    d, (idx, sc, ls) = large_run
+    B, M, K = d["B"], d["M"], d["K"]
+    assert idx.shape == (B, K) and (idx >= 0).all() and np.isfinite(sc).all()
+    Hf = _widen_bf16(d["H"])
+    tau = parity.SCORE_REL * float(np.abs(sc).max())
+    worst = 0.0
+    for b in range(B):
+        s64 = _widen_bf16(d["E"][idx[b]]).astype(np.float64) @ Hf[b].astype(np.float64)
+        worst = max(worst, float(np.abs(s64 - sc[b].astype(np.float64)).max()))
+    assert worst <= tau, ("returned scores vs fp64 rescoring", worst, tau)
+    prev = (torch.backends.cuda.matmul.allow_tf32, torch.get_float32_matmul_precision())
+    torch.backends.cuda.matmul.allow_tf32 = False
+    torch.set_float32_matmul_precision("highest")
+    try:
+        Ht = torch.from_numpy(Hf).to(dev).t().contiguous()  # [D][B]: no transposed operand view
+        thr = torch.from_numpy(sc[:, K - 1].astype(np.float32) + np.float32(tau)).to(dev)
+        lse = torch.full((B,), -math.inf, dtype=torch.float64, device=dev)
+        keys = []
+        step = 65536
+        for r0 in range(0, M, step):
+            r1 = min(M, r0 + step)
+            St = to_dev(d["E"][r0:r1], dev).float() @ Ht  # [items][B] fp32
+            lse = torch.logaddexp(lse, torch.logsumexp(St.double(), dim=0))
+            nz = torch.nonzero(St > thr[None, :]).cpu().numpy().astype(np.int64)  # (item, user)
+            keys.append(nz[:, 1] * M + nz[:, 0] + r0)
+            del St
+        lse = lse.cpu().numpy()
+    finally:
+        torch.backends.cuda.matmul.allow_tf32 = prev[0]
+        torch.set_float32_matmul_precision(prev[1])
+    above = np.concatenate(keys)
+    listed = (np.arange(B, dtype=np.int64)[:, None] * M + idx.astype(np.int64)).ravel()
+    missing = above[~np.isin(above, listed)]
+    assert missing.size == 0, ("items above the K-th score + tau not listed", (missing // M)[:8], (missing % M)[:8])
+    err = np.abs(lse - ls.astype(np.float64))
+    assert err.max() <= parity.LSE_ABS, ("lse", int(err.argmax()), float(err.max()))
 
 
 @pytest.mark.parametrize("B,D,M,K", [
