@@ -139,7 +139,31 @@ def test_large_b1024_all_users(dev, large_run):
     (2) and (3) take the scores from a float32 library product of the widened
     rows, chunk by chunk (its rounding, ~1e-5 relative at D = 4,096, is far
     inside tau)."""
-    d, (idx, sc, ls) = large_run
+    _check_all_users(large_run[0], large_run[1], dev)
+
+
+def test_large_masked_b1024_all_users(dev, large_run):
+    """The masked head at the full large shape (one global mask allowing 90% of
+    the items): every user's list holds allowed items only, and the checks of
+    test_large_b1024_all_users hold over the allowed items."""
+    from full_catalog_ranking_amd import genrec
+    d = large_run[0]
+    allowed = np.random.default_rng(91).random(d["M"]) < 0.9
+    mask = torch.from_numpy(_pack_mask(allowed).view(np.int32)).to(dev)
+    H, E = to_dev(d["H"], dev), to_dev(d["E"], dev)
+    print("  masked full size B=%d M=%d K=%d" % (d["B"], d["M"], d["K"]), flush=True)
+    idx, sc, ls = genrec.score_lse_topk(H, E, d["K"], mask=mask)
+    g = idx.cpu().numpy(), sc.cpu().numpy(), ls.cpu().numpy()
+    del H, E, idx, sc, ls
+    torch.cuda.empty_cache()
+    assert allowed[g[0].astype(np.int64)].all()
+    _check_all_users(d, g, dev, allowed)
+
+
+def _check_all_users(d, g, dev, allowed=None):
+    """The properties above for every user (over the allowed items only when a
+    mask is given)."""
+    idx, sc, ls = g
     B, M, K = d["B"], d["M"], d["K"]
     assert idx.shape == (B, K) and (idx >= 0).all() and np.isfinite(sc).all()
     Hf = _widen_bf16(d["H"])
@@ -161,6 +185,8 @@ def test_large_b1024_all_users(dev, large_run):
         for r0 in range(0, M, step):
             r1 = min(M, r0 + step)
             St = to_dev(d["E"][r0:r1], dev).float() @ Ht  # [items][B] fp32
+            if allowed is not None:
+                St[torch.from_numpy(~allowed[r0:r1]).to(dev)] = -math.inf
             lse = torch.logaddexp(lse, torch.logsumexp(St.double(), dim=0))
             nz = torch.nonzero(St > thr[None, :]).cpu().numpy().astype(np.int64)  # (item, user)
             keys.append(nz[:, 1] * M + nz[:, 0] + r0)
